@@ -1,0 +1,134 @@
+"""Seeded synthetic inputs and the named workloads they are drawn for.
+
+This module is shared by the tests, the benchmark and the smoke check; it
+holds no attention arithmetic (neither the kernels' nor the oracle's), only
+shapes, seeds, the random draw and byte/FLOP accounting for reports.
+
+Input recipe: one CPU ``torch.Generator`` per workload, seeded with the
+workload's seed; Q, K and V are drawn in that order as float32 standard
+normals and cast to the workload's dtype with round-to-nearest-even.  The same
+host tensors feed the oracle (as uint16 bit patterns) and the GPU (copied to
+the device).  i.i.d. N(0, 1) inputs with scale 1/sqrt(D) are the pages' own
+synthetic workload (the M3 Ultra test script in ml-explore/mlx PR #3293, "fix:
+add head_dim=256 to fused SDPA full attention kernel").
+"""
+
+from __future__ import annotations
+
+import dataclasses
+import math
+
+import numpy as np
+import torch
+
+FP16 = 0
+BF16 = 1
+TORCH_DTYPES = {FP16: torch.float16, BF16: torch.bfloat16}
+DTYPE_NAMES = {FP16: "f16", BF16: "bf16"}
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    B: int
+    Hq: int
+    Hkv: int
+    qL: int
+    kL: int
+    D: int
+    dtype: int
+    causal: bool
+    window: int
+    q_offset: int
+    seed: int
+    what: str
+
+    @property
+    def scale(self) -> float:
+        return float(np.float32(1.0 / math.sqrt(self.D)))
+
+    def with_(self, **kw) -> "Workload":
+        return dataclasses.replace(self, **kw)
+
+
+def _wl(name, B, Hq, Hkv, qL, kL, D, dtype, causal, window, q_offset, seed, what):
+    return Workload(name, B, Hq, Hkv, qL, kL, D, dtype, causal, window, q_offset, seed, what)
+
+
+# The five workloads the library is measured and checked on.  Shapes follow the
+# pages: n_q=16 / n_kv=8 at head_dim 256 over a 32768-key prefix (mlx PR #3660,
+# Microbenchmarks); H=64 at L=16384 (mlx PR #3293, Benchmark, H=64 table);
+# Gemma-4 31B sliding 32/16/256 window 1024 and global 32/4/512 layers, and a
+# 4-row verify block over a long KV cache (mlxcel issue #2160, Current Behavior).
+WORKLOADS = {
+    "tiny_causal": _wl("tiny_causal", 1, 2, 1, 128, 128, 256, FP16, True, 0, 0, 1,
+                       "tiny causal self-attention, B1 Hq2 Hkv1 D256 L128 fp16"),
+    "chunked_prefill_32k": _wl("chunked_prefill_32k", 1, 16, 8, 1024, 32768, 256, FP16, True, 0,
+                               32768 - 1024, 2,
+                               "chunked prefill over a 32K KV prefix, B1 Hq16 Hkv8 D256 qL1024 kL32768 fp16 causal"),
+    "causal_h64_16k": _wl("causal_h64_16k", 1, 64, 64, 16384, 16384, 256, BF16, True, 0, 0, 3,
+                          "large-head causal self-attention, B1 Hq64 Hkv64 D256 L16384 bf16"),
+    "sliding_32k": _wl("sliding_32k", 1, 32, 16, 32768, 32768, 256, BF16, True, 1024, 0, 41,
+                       "Gemma-4-31B-like sliding layer, B1 Hq32 Hkv16 D256 L32768 bf16 window 1024"),
+    "global_d512_32k": _wl("global_d512_32k", 1, 32, 4, 32768, 32768, 512, BF16, True, 0, 0, 42,
+                           "Gemma-4-31B-like global layer, B1 Hq32 Hkv4 D512 L32768 bf16 causal"),
+    "decode_q4_128k": _wl("decode_q4_128k", 1, 16, 8, 4, 131072, 256, BF16, True, 0, 131072 - 4, 5,
+                          "verify block, B1 Hq16 Hkv8 D256 qL4 kL131072 bf16 causal bottom-right"),
+    "decode_q1_128k": _wl("decode_q1_128k", 1, 16, 8, 1, 131072, 256, BF16, True, 0, 131072 - 1, 5,
+                          "decode, B1 Hq16 Hkv8 D256 qL1 kL131072 bf16 (row 3 of the qL=4 draw)"),
+}
+
+
+def draw(wl: Workload, device: str = "cpu"):
+    """Seeded Q, K, V for a workload, as torch tensors of its dtype on the CPU.
+
+    ``decode_q1_128k`` shares the qL=4 draw (seed 5) and takes its last query row.
+    """
+    if wl.name == "decode_q1_128k":
+        q4, k, v = draw(WORKLOADS["decode_q4_128k"])
+        return q4[:, :, 3:4].contiguous(), k, v
+    g = torch.Generator(device="cpu")
+    g.manual_seed(wl.seed)
+    dt = TORCH_DTYPES[wl.dtype]
+    q = torch.randn((wl.B, wl.Hq, wl.qL, wl.D), generator=g, dtype=torch.float32).to(dt)
+    k = torch.randn((wl.B, wl.Hkv, wl.kL, wl.D), generator=g, dtype=torch.float32).to(dt)
+    v = torch.randn((wl.B, wl.Hkv, wl.kL, wl.D), generator=g, dtype=torch.float32).to(dt)
+    return q, k, v
+
+
+def random_qkv(seed: int, B: int, Hq: int, Hkv: int, qL: int, kL: int, D: int, dtype: int,
+               std: float = 1.0):
+    """Seeded Q, K, V of an arbitrary shape, same recipe as ``draw``."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(seed)
+    dt = TORCH_DTYPES[dtype]
+    q = (torch.randn((B, Hq, qL, D), generator=g, dtype=torch.float32) * std).to(dt)
+    k = (torch.randn((B, Hkv, kL, D), generator=g, dtype=torch.float32) * std).to(dt)
+    v = (torch.randn((B, Hkv, kL, D), generator=g, dtype=torch.float32) * std).to(dt)
+    return q, k, v
+
+
+def bits(t: torch.Tensor) -> np.ndarray:
+    """uint16 bit patterns of a CPU fp16/bf16 tensor (no copy of values)."""
+    return t.contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+def visible_keys(qL: int, kL: int, causal: bool, window: int, q_offset: int) -> np.ndarray:
+    """Number of keys each query row may see (for FLOP accounting), int64 [qL]."""
+    p = q_offset + np.arange(qL, dtype=np.int64)
+    hi = np.minimum(p, kL - 1) if causal else np.full(qL, kL - 1, dtype=np.int64)
+    lo = np.maximum(p - window + 1, 0) if window > 0 else np.zeros(qL, dtype=np.int64)
+    return np.maximum(hi - lo + 1, 0)
+
+
+def flops(wl: Workload) -> float:
+    """Algorithmic FLOP: 4 * B * Hq * D * (visible query-key pairs per head)."""
+    pairs = int(visible_keys(wl.qL, wl.kL, wl.causal, wl.window, wl.q_offset).sum())
+    return 4.0 * wl.B * wl.Hq * wl.D * pairs
+
+
+def io_bytes(B, Hq, Hkv, qL, kL, D, elem_bytes=2) -> dict:
+    """Bytes of the inputs and the output, each read or written once."""
+    q = B * Hq * qL * D * elem_bytes
+    kv = 2 * B * Hkv * kL * D * elem_bytes
+    return {"q": q, "kv": kv, "out": q, "inputs": q + kv, "total": 2 * q + kv}

@@ -1,0 +1,159 @@
+"""fp64 CPU oracle for scaled-dot-product attention.
+
+TEST INFRASTRUCTURE.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import this package.  The HIP library
+in ``flash_attention_head_amd`` never imports it, and it imports nothing from
+there: the two share no code.
+
+The arithmetic lives in ``sdpa_oracle.c`` (plain C, double precision, one
+row at a time, ascending key order); this module only builds and loads that
+library and marshals numpy arrays of fp16/bf16 bit patterns into it.
+What it computes, and the readings taken where the pages leave a step open,
+are stated in the header of ``sdpa_oracle.c``.
+
+Every function here has a pin in ``tests/test_oracle_pins.py``; none is
+"parity unpinned".
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "sdpa_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle_sdpa.so")
+# A test may point the whole suite at another build of the oracle (a planted
+# mistake, built from a modified copy of the source) through this variable.
+_LIB_OVERRIDE = os.environ.get("SDPA_ORACLE_LIB")
+
+FP16 = 0
+BF16 = 1
+
+_lib = None
+
+
+def build(out_path: str = _LIB, src_path: str = _SRC, extra_flags: tuple = ()) -> str:
+    """Compile the oracle with gcc (no fast-math: the C order of operations holds)."""
+    cmd = [
+        "gcc", "-O2", "-fno-fast-math", "-ffp-contract=off", "-std=c11", "-fPIC", "-shared",
+        "-pthread", *extra_flags, src_path, "-o", out_path + ".tmp", "-lm",
+    ]
+    subprocess.run(cmd, check=True)
+    os.replace(out_path + ".tmp", out_path)
+    return out_path
+
+
+def load(path: str = _LIB):
+    """Load a built oracle library (building the default one if it is absent)."""
+    global _lib
+    if path == _LIB and _LIB_OVERRIDE:
+        path = _LIB_OVERRIDE
+        if _lib is not None:
+            return _lib
+        lib = load(path)
+        _lib = lib
+        return lib
+    if path == _LIB and _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        if path != _LIB:
+            raise FileNotFoundError(path)
+        build()
+    lib = ctypes.CDLL(path)
+    u16p = ctypes.POINTER(ctypes.c_uint16)
+    f64p = ctypes.POINTER(ctypes.c_double)
+    i64p = ctypes.POINTER(ctypes.c_int64)
+    ci = ctypes.c_int
+    lib.oracle_sdpa_f64.argtypes = [u16p, u16p, u16p, f64p] + [ci] * 6 + [ctypes.c_float] + [ci] * 5
+    lib.oracle_sdpa_f64.restype = ci
+    lib.oracle_sdpa_rows_f64.argtypes = (
+        [u16p, u16p, u16p, f64p] + [ci] * 6 + [ctypes.c_float] + [ci] * 4 + [i64p, ctypes.c_int64, ci]
+    )
+    lib.oracle_sdpa_rows_f64.restype = ci
+    lib.oracle_widen.argtypes = [u16p, f64p, ctypes.c_int64, ci]
+    lib.oracle_widen.restype = None
+    if path == _LIB:
+        _lib = lib
+    return lib
+
+
+def _bits(a: np.ndarray) -> np.ndarray:
+    a = np.ascontiguousarray(a)
+    if a.dtype not in (np.uint16, np.int16):
+        raise TypeError("oracle inputs are fp16/bf16 bit patterns as uint16 arrays")
+    return a.view(np.uint16)
+
+
+def _ptr(a, ctype):
+    return a.ctypes.data_as(ctypes.POINTER(ctype))
+
+
+def default_threads() -> int:
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        return os.cpu_count() or 1
+
+
+def _check_shapes(q, k, v):
+    if q.ndim != 4 or k.ndim != 4 or v.ndim != 4:
+        raise ValueError("q, k, v must be [B, H, L, D]")
+    B, Hq, qL, D = q.shape
+    Bk, Hkv, kL, Dk = k.shape
+    if v.shape != k.shape or Bk != B or Dk != D:
+        raise ValueError("shape mismatch between q, k, v")
+    return B, Hq, Hkv, qL, kL, D
+
+
+def sdpa_f64(q, k, v, *, scale: float, causal: bool = False, window: int = 0, q_offset: int = 0,
+             dtype: int = FP16, threads: int | None = None, lib=None) -> np.ndarray:
+    """All output rows, [B, Hq, qL, D] float64.
+
+    q, k, v: uint16 bit patterns of fp16 (dtype=FP16) or bf16 (dtype=BF16) values;
+    scale: converted to fp32 first, as the GPU library receives it.
+    """
+    lib = lib or load()
+    q, k, v = _bits(q), _bits(k), _bits(v)
+    B, Hq, Hkv, qL, kL, D = _check_shapes(q, k, v)
+    out = np.empty((B, Hq, qL, D), dtype=np.float64)
+    rc = lib.oracle_sdpa_f64(
+        _ptr(q, ctypes.c_uint16), _ptr(k, ctypes.c_uint16), _ptr(v, ctypes.c_uint16),
+        _ptr(out, ctypes.c_double), B, Hq, Hkv, qL, kL, D, float(np.float32(scale)),
+        int(bool(causal)), int(window), int(q_offset), int(dtype), int(threads or default_threads()),
+    )
+    if rc != 0:
+        raise RuntimeError(f"oracle_sdpa_f64 failed ({rc})")
+    return out
+
+
+def sdpa_rows_f64(q, k, v, rows, *, scale: float, causal: bool = False, window: int = 0,
+                  q_offset: int = 0, dtype: int = FP16, threads: int | None = None,
+                  lib=None) -> np.ndarray:
+    """Selected rows, [len(rows), D] float64; rows are flat indices (b*Hq + hq)*qL + i."""
+    lib = lib or load()
+    q, k, v = _bits(q), _bits(k), _bits(v)
+    B, Hq, Hkv, qL, kL, D = _check_shapes(q, k, v)
+    rows = np.ascontiguousarray(rows, dtype=np.int64)
+    out = np.empty((rows.size, D), dtype=np.float64)
+    rc = lib.oracle_sdpa_rows_f64(
+        _ptr(q, ctypes.c_uint16), _ptr(k, ctypes.c_uint16), _ptr(v, ctypes.c_uint16),
+        _ptr(out, ctypes.c_double), B, Hq, Hkv, qL, kL, D, float(np.float32(scale)),
+        int(bool(causal)), int(window), int(q_offset), int(dtype), _ptr(rows, ctypes.c_int64),
+        int(rows.size), int(threads or default_threads()),
+    )
+    if rc != 0:
+        raise RuntimeError(f"oracle_sdpa_rows_f64 failed ({rc})")
+    return out
+
+
+def widen(bits, dtype: int, lib=None) -> np.ndarray:
+    """Exact fp16/bf16 -> float64 widening of a uint16 bit-pattern array."""
+    lib = lib or load()
+    b = _bits(bits)
+    out = np.empty(b.shape, dtype=np.float64)
+    lib.oracle_widen(_ptr(b, ctypes.c_uint16), _ptr(out, ctypes.c_double), b.size, int(dtype))
+    return out

@@ -1,0 +1,261 @@
+"""Pins of the fp64 oracle to facts outside itself (CPU only).
+
+Each test ties the oracle to something it does not share code with: a library
+routine (torch's float64 attention, numpy/torch dtype widening, scipy's
+softmax), a closed form, or an invariant the definition of attention implies.
+``test_oracle_mutants.py`` checks that these pins catch planted mistakes.
+"""
+
+import itertools
+import math
+
+import numpy as np
+import pytest
+import scipy.special
+import torch
+import torch.nn.functional as F
+
+import oracle
+from flash_attention_head_amd import workloads as W
+
+FP16, BF16 = oracle.FP16, oracle.BF16
+
+
+def _np_bits(a: np.ndarray, dtype: int) -> np.ndarray:
+    t = torch.from_numpy(np.asarray(a, dtype=np.float32)).to(W.TORCH_DTYPES[dtype])
+    return W.bits(t)
+
+
+def _widened(bits: np.ndarray, dtype: int) -> np.ndarray:
+    t = torch.from_numpy(bits.view(np.int16)).view(W.TORCH_DTYPES[dtype])
+    return t.to(torch.float64).numpy()
+
+
+def _mask(qL, kL, causal, window, q_offset):
+    p = q_offset + np.arange(qL)[:, None]
+    j = np.arange(kL)[None, :]
+    m = np.ones((qL, kL), dtype=bool)
+    if causal:
+        m &= j <= p
+    if window > 0:
+        m &= (p - j) < window
+    return m
+
+
+# ---------------------------------------------------------------- widening --
+@pytest.mark.parametrize("dtype", [FP16, BF16])
+def test_widening_matches_library_for_every_bit_pattern(oracle_lib, dtype):
+    allbits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    got = oracle.widen(allbits, dtype)
+    ref = _widened(allbits, dtype)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+
+
+# ------------------------------------------------- library routine, brute --
+def _torch_ref(q, k, v, scale, causal, window, q_offset, dtype):
+    qd = torch.from_numpy(_widened(q, dtype))
+    kd = torch.from_numpy(_widened(k, dtype))
+    vd = torch.from_numpy(_widened(v, dtype))
+    mask = torch.from_numpy(_mask(q.shape[2], k.shape[2], causal, window, q_offset))
+    return F.scaled_dot_product_attention(qd, kd, vd, attn_mask=mask, scale=float(np.float32(scale)),
+                                          enable_gqa=True).numpy()
+
+
+def _cases():
+    heads = [(1, 1), (2, 1), (4, 2)]
+    out = []
+    seed = 100
+    for (Hq, Hkv), qL, kL in itertools.product(heads, [1, 3, 9], [1, 4, 9]):
+        for causal, window in [(False, 0), (True, 0), (True, 1), (True, 3)]:
+            if causal and qL > kL:
+                continue
+            offs = [0, kL - qL] if causal else [0]
+            for q_offset in sorted(set(offs)):
+                seed += 1
+                out.append((seed, Hq, Hkv, qL, kL, causal, window, q_offset))
+    return out
+
+
+@pytest.mark.parametrize("case", _cases())
+def test_matches_torch_float64_sdpa_bruteforce(oracle_lib, case):
+    seed, Hq, Hkv, qL, kL, causal, window, q_offset = case
+    for B, D, dtype in [(1, 8, FP16), (2, 5, BF16)]:
+        q, k, v = (W.bits(t) for t in W.random_qkv(seed, B, Hq, Hkv, qL, kL, D, dtype))
+        scale = 0.37
+        got = oracle.sdpa_f64(q, k, v, scale=scale, causal=causal, window=window,
+                              q_offset=q_offset, dtype=dtype, threads=2)
+        ref = _torch_ref(q, k, v, scale, causal, window, q_offset, dtype)
+        np.testing.assert_allclose(got, ref, rtol=0, atol=1e-12)
+
+
+# ------------------------------------------------------------ closed forms --
+def test_two_keys_closed_form(oracle_lib):
+    # one query q=1, keys 0 and 1, values 0 and 4: o = 4 e^s / (1 + e^s)
+    q = _np_bits(np.array([1.0]).reshape(1, 1, 1, 1), FP16)
+    k = _np_bits(np.array([0.0, 1.0]).reshape(1, 1, 2, 1), FP16)
+    v = _np_bits(np.array([0.0, 4.0]).reshape(1, 1, 2, 1), FP16)
+    s = float(np.float32(math.log(3.0)))  # weights 1/4 and 3/4 up to fp32 rounding of ln 3
+    o = oracle.sdpa_f64(q, k, v, scale=s, dtype=FP16)[0, 0, 0, 0]
+    assert abs(o - 4.0 / (1.0 + math.exp(-s))) < 1e-15
+    assert abs(o - 3.0) < 1e-6
+
+
+def test_huge_scores_select_the_largest_key(oracle_lib):
+    # scores 0, 5000, 10000, 2500: every weight but the largest underflows to 0,
+    # so the output is that key's value row exactly (no overflow on the way)
+    dtype = BF16
+    q = _np_bits(np.array([100.0]).reshape(1, 1, 1, 1), dtype)
+    k = _np_bits(np.array([0.0, 50.0, 100.0, 25.0]).reshape(1, 1, 4, 1), dtype)
+    v = _np_bits(np.array([1.0, 2.0, 3.0, 4.0]).reshape(1, 1, 4, 1), dtype)
+    o = oracle.sdpa_f64(q, k, v, scale=1.0, dtype=dtype)
+    assert o[0, 0, 0, 0] == 3.0
+
+
+@pytest.mark.parametrize("dtype", [FP16, BF16])
+def test_one_hot_values_give_softmax_weights(oracle_lib, dtype):
+    # K = V = identity: output d equals the softmax weight of key d
+    D = 7
+    rng = np.random.default_rng(7)
+    qv = rng.normal(size=D)
+    q = _np_bits(qv.reshape(1, 1, 1, D), dtype)
+    eye = _np_bits(np.eye(D).reshape(1, 1, D, D), dtype)
+    scale = 0.9
+    o = oracle.sdpa_f64(q, eye, eye, scale=scale, dtype=dtype)[0, 0, 0]
+    ref = scipy.special.softmax(float(np.float32(scale)) * _widened(q, dtype).ravel())
+    np.testing.assert_allclose(o, ref, rtol=0, atol=1e-15)
+
+
+@pytest.mark.parametrize("causal,window,q_offset,qL,kL", [
+    (False, 0, 0, 37, 300),
+    (True, 0, 0, 300, 300),
+    (True, 0, 263, 37, 300),
+    (True, 50, 0, 300, 300),
+    (True, 50, 120, 37, 300),
+    (True, 1, 5, 37, 300),
+])
+def test_zero_queries_average_the_visible_values(oracle_lib, causal, window, q_offset, qL, kL):
+    # all scores equal => the output is the plain mean of the visible value rows
+    D, dtype = 16, BF16
+    _, _, v = W.random_qkv(11, 2, 4, 2, qL, kL, D, dtype)
+    q = torch.zeros((2, 4, qL, D), dtype=torch.bfloat16)
+    o = oracle.sdpa_f64(W.bits(q), W.bits(v), W.bits(v), scale=0.0625, causal=causal,
+                        window=window, q_offset=q_offset, dtype=dtype)
+    vd = v.to(torch.float64).numpy()
+    csum = np.concatenate([np.zeros((2, 2, 1, D)), np.cumsum(vd, axis=2)], axis=2)
+    for i in range(qL):
+        p = q_offset + i
+        hi = min(p, kL - 1) if causal else kL - 1
+        lo = max(p - window + 1, 0) if window > 0 else 0
+        mean = (csum[:, :, hi + 1] - csum[:, :, lo]) / (hi - lo + 1)  # [B, Hkv, D]
+        np.testing.assert_allclose(o[:, :, i], np.repeat(mean, 2, axis=1), rtol=0, atol=1e-13)
+
+
+# ------------------------------------------------- special cases from NS --
+@pytest.mark.parametrize("dtype", [FP16, BF16])
+def test_first_causal_query_returns_first_value_row(oracle_lib, dtype):
+    q, k, v = (W.bits(t) for t in W.random_qkv(3, 1, 4, 2, 20, 20, 32, dtype))
+    o = oracle.sdpa_f64(q, k, v, scale=0.2, causal=True, q_offset=0, dtype=dtype)
+    v0 = _widened(v, dtype)[:, :, 0]
+    assert np.array_equal(o[:, :, 0], np.repeat(v0, 2, axis=1))
+
+
+@pytest.mark.parametrize("q_offset", [0, 13])
+def test_window_of_one_returns_the_diagonal_value_row(oracle_lib, q_offset):
+    dtype = BF16
+    q, k, v = (W.bits(t) for t in W.random_qkv(4, 1, 2, 2, 19, 32, 16, dtype))
+    o = oracle.sdpa_f64(q, k, v, scale=0.25, causal=True, window=1, q_offset=q_offset,
+                        dtype=dtype)
+    vd = _widened(v, dtype)
+    for i in range(19):
+        assert np.array_equal(o[:, :, i], vd[:, :, q_offset + i])
+
+
+def test_equal_value_rows_give_that_row(oracle_lib):
+    dtype = FP16
+    q, k, _ = W.random_qkv(5, 1, 2, 1, 11, 40, 24, dtype)
+    row = torch.randn((1, 1, 1, 24), generator=torch.Generator().manual_seed(9)).to(torch.float16)
+    v = row.expand(1, 1, 40, 24).contiguous()
+    for causal, window in [(False, 0), (True, 0), (True, 7)]:
+        o = oracle.sdpa_f64(W.bits(q), W.bits(k), W.bits(v), scale=0.3, causal=causal,
+                            window=window, q_offset=29, dtype=dtype)
+        r = row.to(torch.float64).numpy()[0, 0, 0]
+        assert np.max(np.abs(o - r)) <= 1e-15 * max(1.0, np.max(np.abs(r))) * 4
+
+
+def test_single_key_returns_it_exactly(oracle_lib):
+    q, k, v = (W.bits(t) for t in W.random_qkv(6, 2, 2, 1, 5, 1, 9, FP16))
+    o = oracle.sdpa_f64(q, k, v, scale=1.0, dtype=FP16)
+    assert np.array_equal(o, np.repeat(np.repeat(_widened(v, FP16), 2, axis=1), 5, axis=2))
+
+
+# -------------------------------------------------------------- invariants --
+@pytest.mark.parametrize("G", [2, 4])
+def test_gqa_equals_repeated_kv_heads(oracle_lib, G):
+    Hkv, dtype = 2, BF16
+    q, k, v = W.random_qkv(12, 2, Hkv * G, Hkv, 13, 21, 16, dtype)
+    kw = dict(scale=0.125, causal=True, window=6, q_offset=8, dtype=dtype)
+    a = oracle.sdpa_f64(W.bits(q), W.bits(k), W.bits(v), **kw)
+    kr = k.repeat_interleave(G, dim=1)
+    vr = v.repeat_interleave(G, dim=1)
+    b = oracle.sdpa_f64(W.bits(q), W.bits(kr), W.bits(vr), **kw)
+    assert np.array_equal(a, b)
+
+
+@pytest.mark.parametrize("window", [0, 5])
+def test_rows_equal_calls_over_their_trimmed_key_prefix(oracle_lib, window):
+    # a masked row equals an unmasked single-row call over exactly its visible keys
+    dtype = FP16
+    q, k, v = W.random_qkv(13, 1, 2, 1, 8, 30, 16, dtype)
+    q_offset = 22
+    o = oracle.sdpa_f64(W.bits(q), W.bits(k), W.bits(v), scale=0.25, causal=True, window=window,
+                        q_offset=q_offset, dtype=dtype)
+    for i in range(8):
+        p = q_offset + i
+        lo = max(p - window + 1, 0) if window else 0
+        ks = k[:, :, lo:p + 1].contiguous()
+        vs = v[:, :, lo:p + 1].contiguous()
+        r = oracle.sdpa_f64(W.bits(q[:, :, i:i + 1]), W.bits(ks), W.bits(vs), scale=0.25,
+                            dtype=dtype)
+        assert np.array_equal(o[:, :, i:i + 1], r)
+
+
+def test_key_permutation_changes_only_rounding(oracle_lib):
+    dtype = BF16
+    q, k, v = W.random_qkv(14, 1, 2, 2, 6, 50, 16, dtype)
+    perm = torch.randperm(50, generator=torch.Generator().manual_seed(1))
+    a = oracle.sdpa_f64(W.bits(q), W.bits(k), W.bits(v), scale=0.25, dtype=dtype)
+    b = oracle.sdpa_f64(W.bits(q), W.bits(k[:, :, perm]), W.bits(v[:, :, perm]), scale=0.25,
+                        dtype=dtype)
+    np.testing.assert_allclose(a, b, rtol=0, atol=1e-13)
+    assert not np.array_equal(W.bits(k), W.bits(k[:, :, perm]))
+
+
+def test_scale_multiplies_scores(oracle_lib):
+    # doubling q (exact) and halving scale (exact) leaves every score unchanged
+    dtype = FP16
+    q, k, v = W.random_qkv(15, 1, 2, 1, 7, 20, 8, dtype)
+    a = oracle.sdpa_f64(W.bits(q), W.bits(k), W.bits(v), scale=0.5, causal=True, q_offset=13,
+                        dtype=dtype)
+    b = oracle.sdpa_f64(W.bits(q * 2), W.bits(k), W.bits(v), scale=0.25, causal=True,
+                        q_offset=13, dtype=dtype)
+    assert np.array_equal(a, b)
+
+
+def test_selected_rows_equal_full_call(oracle_lib):
+    dtype = BF16
+    q, k, v = (W.bits(t) for t in W.random_qkv(16, 2, 4, 2, 9, 33, 16, dtype))
+    kw = dict(scale=0.3, causal=True, window=10, q_offset=24, dtype=dtype)
+    full = oracle.sdpa_f64(q, k, v, **kw).reshape(-1, 16)
+    rows = np.array([0, 5, 17, 35, 71, 70, 36], dtype=np.int64)
+    part = oracle.sdpa_rows_f64(q, k, v, rows, **kw)
+    assert np.array_equal(part, full[rows])
+
+
+def test_thread_count_does_not_change_results(oracle_lib):
+    q, k, v = (W.bits(t) for t in W.random_qkv(17, 1, 4, 2, 33, 70, 16, FP16))
+    kw = dict(scale=0.3, causal=True, window=0, q_offset=37, dtype=FP16)
+    a = oracle.sdpa_f64(q, k, v, threads=1, **kw)
+    b = oracle.sdpa_f64(q, k, v, threads=7, **kw)
+    assert np.array_equal(a, b)
