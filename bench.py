@@ -1,0 +1,202 @@
+"""Benchmark of the fused attention library on one MI355X.
+
+One "step" is one sdpa_forward call over the workload's synthetic inputs, which
+are resident in HBM before timing starts (attention kernel, plus the combine
+pass when the call splits its keys).  The headline workload is the chunked
+prefill of 1024 queries over a 32768-key prefix (B1 Hq16 Hkv8 D256 fp16,
+causal, bottom-right aligned).  Prints ONE JSON line.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                  [--extra | --no-extra] [--no-cpu-baseline]
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+# MI355X published peaks: dense fp16/bf16 MFMA (256 CU x 2.4 GHz x 4096 flop/clk)
+# and HBM3E bandwidth
+PEAK_MFMA_TFLOPS = 2516.6
+PEAK_HBM_GBS = 8000.0
+HEADLINE = "chunked_prefill_32k"
+EXTRA = ["causal_h64_16k", "sliding_32k", "global_d512_32k", "decode_q4_128k", "decode_q1_128k",
+         "tiny_causal"]
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def time_workload(wl, steps, warmup):
+    """Mean ms per call, measured with HIP events on the stream the library runs on."""
+    import torch
+
+    import flash_attention_head_amd as fa
+    from flash_attention_head_amd import workloads as W
+
+    q, k, v = (t.cuda() for t in W.draw(wl))
+    out = torch.empty_like(q)
+    need = fa.sdpa_workspace_bytes(wl.B, wl.Hq, wl.Hkv, wl.qL, wl.kL, wl.D)
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def call():
+        fa.sdpa(q, k, v, scale=wl.scale, causal=wl.causal, window=wl.window,
+                q_offset=wl.q_offset, out=out, workspace=ws, stream=stream)
+
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    t0 = time.perf_counter()
+    for a, b in ev:
+        a.record(stream)
+        call()
+        b.record(stream)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / steps
+    per = sorted(a.elapsed_time(b) for a, b in ev)
+    mean = sum(per) / len(per)
+    del q, k, v, out, ws
+    torch.cuda.empty_cache()
+    return {"wall_ms": wall_ms, "event_ms_mean": mean, "event_ms_min": per[0],
+            "event_ms_median": per[len(per) // 2], "workspace_bytes": need}
+
+
+def summarize(wl, t):
+    from flash_attention_head_amd import workloads as W
+
+    fl = W.flops(wl)
+    io = W.io_bytes(wl.B, wl.Hq, wl.Hkv, wl.qL, wl.kL, wl.D)["total"]
+    ms = t["event_ms_mean"]
+    r = {"ms": round(ms, 4), "ms_min": round(t["event_ms_min"], 4),
+         "tflops": round(fl / (ms * 1e-3) / 1e12, 2),
+         "mfma_frac": round(fl / (ms * 1e-3) / 1e12 / PEAK_MFMA_TFLOPS, 4),
+         "hbm_gbs": round(io / (ms * 1e-3) / 1e9, 1),
+         "hbm_frac": round(io / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+    return r
+
+
+def cpu_baseline(wl, target_s=15.0):
+    """The fp64 oracle on a bounded, seeded sample of the workload's rows."""
+    import numpy as np
+
+    import oracle
+    from flash_attention_head_amd import workloads as W
+
+    q, k, v = W.draw(wl)
+    qb, kb, vb = W.bits(q), W.bits(k), W.bits(v)
+    threads = min(16, oracle.default_threads())
+    rng = np.random.default_rng(wl.seed)
+    total = wl.B * wl.Hq * wl.qL
+    vis = W.visible_keys(wl.qL, wl.kL, wl.causal, wl.window, wl.q_offset)
+
+    def run(n):
+        rows = np.sort(rng.choice(total, size=min(n, total), replace=False)).astype(np.int64)
+        t0 = time.perf_counter()
+        oracle.sdpa_rows_f64(qb, kb, vb, rows, scale=wl.scale, causal=wl.causal,
+                             window=wl.window, q_offset=wl.q_offset, dtype=wl.dtype,
+                             threads=threads)
+        dt = time.perf_counter() - t0
+        fl = 4.0 * wl.D * float(vis[rows % wl.qL].sum())
+        return rows.size, dt, fl
+
+    n, dt, fl = run(4 * threads)  # calibration
+    n2 = int(max(threads, min(total, n * target_s / max(dt, 1e-3))))
+    n, dt, fl = run(n2)
+    return {"value": fl / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{n} seeded random query rows of {total} ({wl.name}), all their visible "
+                      f"keys, {fl / 1e9:.1f} GFLOP in {dt:.1f} s on {threads} host threads"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default=HEADLINE)
+    ap.add_argument("--extra", dest="extra", action="store_true", default=True)
+    ap.add_argument("--no-extra", dest="extra", action="store_false")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU only (got --gpus {args.gpus}); the "
+              "attention path has no multi-GPU mode", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import flash_attention_head_amd as fa
+    from flash_attention_head_amd import workloads as W
+
+    if not os.path.exists(fa.library_path()):
+        from flash_attention_head_amd import build
+
+        build.build()
+    fa.load_library()
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+
+    wl = W.WORKLOADS[args.workload]
+    log(f"[bench] {wl.name}: warmup {args.warmup}, steps {args.steps}")
+    t = time_workload(wl, args.steps, args.warmup)
+    head = summarize(wl, t)
+    log(f"[bench] {wl.name}: {head}")
+    fl = W.flops(wl)
+
+    extra = {}
+    if args.extra:
+        for name in EXTRA:
+            if name == wl.name:
+                continue
+            w2 = W.WORKLOADS[name]
+            log(f"[bench] extra {name}")
+            t2 = time_workload(w2, max(5, args.steps // 2), 2)
+            extra[name] = summarize(w2, t2)
+            log(f"[bench] {name}: {extra[name]}")
+
+    base = None
+    if not args.no_cpu_baseline:
+        log("[bench] cpu baseline (oracle on a row sample)")
+        base = cpu_baseline(wl)
+        log(f"[bench] cpu baseline: {base}")
+
+    achieved = fl / (t["event_ms_mean"] * 1e-3) / 1e12
+    line = {
+        "metric": "attention TFLOP/s & % MFMA peak (prefill D=256, L=32K); decode HBM GB/s",
+        "value": round(fl / (t["wall_ms"] * 1e-3) / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(t["wall_ms"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": W.DTYPE_NAMES[wl.dtype],
+        "data": "synthetic",
+        "config": {"workload": wl.name, "B": wl.B, "Hq": wl.Hq, "Hkv": wl.Hkv, "qL": wl.qL,
+                   "kL": wl.kL, "D": wl.D, "causal": wl.causal, "window": wl.window,
+                   "q_offset": wl.q_offset, "flop_per_step": fl},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_MFMA_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_MFMA_TFLOPS, 4),
+                     "traffic": None,
+                     "kernel": "attn_tile_kernel (+ combine_kernel when keys are split), one "
+                               "sdpa_forward call, HIP events on its stream"},
+        "cpu_baseline": base,
+        "extra": extra,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,148 @@
+"""Fused scaled-dot-product attention for AMD MI355X (gfx950).
+
+A thin Python binding over the C ABI of ``libsdpa_mi355x.so``
+(``include/sdpa_mi355x.h``).  Every step of the computation runs in the HIP
+kernels of that library; this package only marshals arguments.  PyTorch is
+used for device memory and streams.  There is no fallback: if the library is
+missing or cannot be loaded, every call raises.
+
+Raw entry points (same names and arguments as the C functions, pointers as
+integers): ``sdpa_forward``, ``sdpa_workspace_bytes``, ``sdpa_last_error``,
+``sdpa_version``.  Convenience wrapper on torch tensors: ``sdpa``.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+__all__ = [
+    "SDPA_OK", "SDPA_INVALID_ARG", "SDPA_UNSUPPORTED", "SDPA_WORKSPACE_TOO_SMALL",
+    "SDPA_HIP_ERROR", "SDPA_FP16", "SDPA_BF16", "SdpaError", "library_path", "load_library",
+    "sdpa_forward", "sdpa_workspace_bytes", "sdpa_last_error", "sdpa_version", "sdpa",
+    "EXPORTED_SYMBOLS",
+]
+
+SDPA_OK = 0
+SDPA_INVALID_ARG = 1
+SDPA_UNSUPPORTED = 2
+SDPA_WORKSPACE_TOO_SMALL = 3
+SDPA_HIP_ERROR = 4
+SDPA_FP16 = 0
+SDPA_BF16 = 1
+
+EXPORTED_SYMBOLS = ("sdpa_forward", "sdpa_workspace_bytes", "sdpa_last_error", "sdpa_version")
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_lib = None
+
+
+class SdpaError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"sdpa status {status}: {message}")
+        self.status = status
+        self.message = message
+
+
+def library_path() -> str:
+    return os.environ.get("SDPA_MI355X_LIB", os.path.join(_PKG, "libsdpa_mi355x.so"))
+
+
+def load_library():
+    """Load the HIP library (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = library_path()
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"{path} is missing: build it with `python -m flash_attention_head_amd.build` "
+            "(there is no fallback implementation)")
+    lib = ctypes.CDLL(path)
+    vp, ci, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+    lib.sdpa_forward.argtypes = [vp, vp, vp, vp] + [ci] * 6 + [ctypes.c_float] + [ci] * 4 + [vp, sz, vp]
+    lib.sdpa_forward.restype = ci
+    lib.sdpa_workspace_bytes.argtypes = [ci] * 6
+    lib.sdpa_workspace_bytes.restype = sz
+    lib.sdpa_last_error.argtypes = []
+    lib.sdpa_last_error.restype = ctypes.c_char_p
+    lib.sdpa_version.argtypes = []
+    lib.sdpa_version.restype = ci
+    _lib = lib
+    return lib
+
+
+# ----------------------------------------------------------- raw C entry points
+def sdpa_forward(q, k, v, out, B, Hq, Hkv, qL, kL, D, scale, causal, window, q_offset, dtype,
+                 workspace, workspace_bytes, stream) -> int:
+    """``int sdpa_forward(...)`` of the C ABI; pointer arguments are integers."""
+    return load_library().sdpa_forward(q, k, v, out, B, Hq, Hkv, qL, kL, D, scale, causal, window,
+                                       q_offset, dtype, workspace, workspace_bytes, stream)
+
+
+def sdpa_workspace_bytes(B, Hq, Hkv, qL, kL, D) -> int:
+    """``size_t sdpa_workspace_bytes(...)``; (size_t)-1 for rejected shapes."""
+    return load_library().sdpa_workspace_bytes(B, Hq, Hkv, qL, kL, D)
+
+
+def sdpa_last_error() -> str:
+    return load_library().sdpa_last_error().decode()
+
+
+def sdpa_version() -> int:
+    return load_library().sdpa_version()
+
+
+# --------------------------------------------------------- torch tensor wrapper
+def sdpa(q, k, v, *, scale: float | None = None, causal: bool = False, window: int = 0,
+         q_offset: int | None = None, out=None, workspace=None, stream=None):
+    """softmax(scale * q k^T + mask) v on device tensors.
+
+    q: [B, Hq, qL, D], k and v: [B, Hkv, kL, D], contiguous fp16 or bf16 tensors on
+    one GPU; D in {256, 512}; Hq a multiple of Hkv.  scale defaults to 1/sqrt(D)
+    (as fp32).  With causal, query row i sits at key position q_offset + i;
+    q_offset defaults to kL - qL (queries aligned to the end of the keys).
+    window > 0 limits each row to its last `window` keys (requires causal).
+    Runs on `stream` (default: torch's current stream) without synchronising.
+    """
+    import torch
+
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be 4-D [B, H, L, D]")
+    if not (q.is_cuda and k.is_cuda and v.is_cuda):
+        raise ValueError("q, k, v must be GPU tensors")
+    if q.dtype != k.dtype or q.dtype != v.dtype or q.dtype not in (torch.float16, torch.bfloat16):
+        raise ValueError("q, k, v must share one dtype, float16 or bfloat16")
+    if not (q.is_contiguous() and k.is_contiguous() and v.is_contiguous()):
+        raise ValueError("q, k, v must be contiguous")
+    B, Hq, qL, D = q.shape
+    Bk, Hkv, kL, Dk = k.shape
+    if tuple(v.shape) != tuple(k.shape) or Bk != B or Dk != D:
+        raise ValueError(f"shape mismatch: q {tuple(q.shape)}, k {tuple(k.shape)}, v {tuple(v.shape)}")
+    dtype = SDPA_FP16 if q.dtype == torch.float16 else SDPA_BF16
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if q_offset is None:
+        q_offset = kL - qL if causal else 0
+    if out is None:
+        out = torch.empty_like(q)
+    elif out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous():
+        raise ValueError("out must be a contiguous tensor shaped and typed like q")
+    need = sdpa_workspace_bytes(B, Hq, Hkv, qL, kL, D)
+    if need == ctypes.c_size_t(-1).value:
+        raise SdpaError(SDPA_UNSUPPORTED if D not in (256, 512) else SDPA_INVALID_ARG,
+                        sdpa_last_error())
+    ws_ptr, ws_bytes = 0, 0
+    if need > 0:
+        if workspace is None:
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    rc = sdpa_forward(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, Hq, Hkv, qL, kL,
+                      D, float(scale), int(bool(causal)), int(window), int(q_offset), dtype, ws_ptr,
+                      ws_bytes, stream.cuda_stream)
+    if rc != SDPA_OK:
+        raise SdpaError(rc, sdpa_last_error())
+    return out

@@ -1,0 +1,476 @@
+// Fused attention kernels for gfx950 (MI355X).
+//
+// One workgroup = 4 waves x 32 query rows.  Rows are "packed" grouped-query
+// rows: packed row r of KV head hk is query position r / G of query head
+// hk * G + r % G, so the G query heads that share a KV head sit in one
+// workgroup and every K/V tile is staged into LDS once for all of them.
+//
+// Per K/V tile (BN keys) each wave computes, with 32x32x16 MFMAs,
+//   S^T = K Q^T            (A = K rows from LDS, B = Q from registers)
+//   online softmax         (one query row per lane pair, fp32, base 2)
+//   O^T += V^T P^T         (A = V^T rows from LDS, B = P from registers)
+// Working with the transposed products keeps every row's scores, softmax
+// state and output accumulator inside the two lanes that own the row, so
+// the row max needs a single cross-lane exchange and the rescale of O is
+// lane-local.  The score matrix never exists outside registers.
+//
+// This is the fused "tile K/V so it scales" kernel whose absence at
+// head_dim 256 forces the materialized-score fallback in lablup/mlxcel issue
+// #672 (Root cause) and that ml-explore/mlx PR #3293 instantiates for
+// head_dim 256 (Changes, Routing update).  Its tile shapes are chosen for
+// gfx950's 160 KiB LDS and 512-entry register file, not taken from the
+// 32x16xBD Metal tiles discussed there (Analysis section).
+#include "sdpa_internal.h"
+
+#include <math.h>
+
+namespace sdpa {
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+template <int DT>
+struct Elem;
+
+template <>
+struct Elem<0> {  // IEEE binary16
+  static __device__ __forceinline__ f32x16_t mfma(uint4 a, uint4 b, f32x16_t c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, a),
+                                                  __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+    _Float16 a = (_Float16)lo, b = (_Float16)hi;  // round to nearest even
+    return (uint32_t)__builtin_bit_cast(uint16_t, a) |
+           ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+  }
+};
+
+template <>
+struct Elem<1> {  // bfloat16
+  static __device__ __forceinline__ f32x16_t mfma(uint4 a, uint4 b, f32x16_t c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+    __bf16 a = (__bf16)lo, b = (__bf16)hi;  // round to nearest even
+    return (uint32_t)__builtin_bit_cast(uint16_t, a) |
+           ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+  }
+};
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Position of key quad b4 (keys 4*b4 .. 4*b4+3 of a 16-key group) in the V^T
+// tile.  Quads are stored in the order 0, 2, 1, 3 so that the 8 keys one lane
+// feeds to a P.V MFMA (quads lg and lg + 2 of a group, as the S^T accumulator
+// layout hands them out) are 16 contiguous bytes.
+__device__ __forceinline__ int quad_slot(int b4) { return ((b4 & 1) << 1) | (b4 >> 1); }
+
+template <int DT, int D>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void attn_tile_kernel(AttnParams p) {
+  constexpr int DS = d_split(D);      // waves per 32-row block
+  constexpr int DH = D / DS;          // head-dim slice of one wave (256)
+  constexpr int RB = kWaves / DS;     // 32-row blocks per workgroup
+  constexpr int BM = block_rows(D);   // rows per workgroup
+  constexpr int BN = tile_keys(D);
+  constexpr int ROWCH = D / 8;        // 16-byte chunks per K row
+  constexpr int VSTR = BN + 8;        // V^T tile row stride (elements); +16 B against bank conflicts
+  constexpr int KTILE = BN * D;       // K tile: rows of D elements, chunks XOR-swizzled
+  constexpr int VTILE = D * VSTR;
+  constexpr int DC = DH / 16;         // MFMA steps over this wave's d in S^T
+  constexpr int DB = DH / 32;         // 32-wide d blocks of this wave's O^T
+  constexpr int KB = BN / 32;         // 32-key blocks of S^T
+  constexpr int KLOADS = BN * D * 2 / 1024 / kWaves;  // 1 KiB direct loads per wave
+  constexpr int VBLK_PER = (BN / 4) * (D / 8) / 256;  // 4-key x 8-d V blocks per thread
+  constexpr int XCH = DS > 1 ? kWaves * 64 * 16 : 0;  // floats: partial-score exchange
+  static_assert(BM == RB * kRowsPerWave, "row blocks");
+  static_assert(KLOADS * kWaves * 1024 == BN * D * 2, "K loads must cover the tile");
+  static_assert(ROWCH <= 64 && 64 % ROWCH == 0, "a K row must fit one wave load");
+  static_assert(VBLK_PER * 256 * 32 == BN * D, "V staging must cover the tile");
+
+  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * (KTILE + VTILE) + 2 * XCH];
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63, lr = lane & 31, lg = lane >> 5;
+  const int rb = wave % RB;  // this wave's 32-row block
+  const int dh = wave / RB;  // this wave's slice of the head dimension
+
+  // ---- work item: (b, kv head) x row block x key split -------------------
+  const int nheads = p.B * p.Hkv;
+  const int head = blockIdx.x % nheads;
+  const int mbr = blockIdx.x / nheads;
+  // causal: later row blocks see more keys; dispatch them first
+  const int mb = p.causal ? (p.mblocks - 1 - mbr) : mbr;
+  const int split = blockIdx.y;
+  const int b = head / p.Hkv, hk = head % p.Hkv;
+
+  const int row0 = mb * BM;
+  const int rows_end = min(p.rows, row0 + BM);
+  const int wrow0 = row0 + rb * kRowsPerWave;
+  const bool wave_active = wrow0 < rows_end;
+  const int my = wrow0 + lr;
+  const bool valid = my < rows_end;
+  const int qi = valid ? my / p.G : 0;
+  const int hq = hk * p.G + (valid ? my % p.G : 0);
+  const int pos = p.q_offset + qi;
+  const int wp_lo = p.q_offset + wrow0 / p.G;
+  const int wp_hi = p.q_offset + (min(rows_end, wrow0 + kRowsPerWave) - 1) / p.G;
+
+  // keys any row of this workgroup may see, clipped to the split
+  int kbeg = 0, kend = p.kL;
+  {
+    const int bp_lo = p.q_offset + row0 / p.G;
+    const int bp_hi = p.q_offset + (rows_end - 1) / p.G;
+    if (p.causal) kend = min(kend, bp_hi + 1);
+    if (p.window > 0) kbeg = max(0, bp_lo - p.window + 1);
+    if (p.partials) {
+      kbeg = max(kbeg, split * p.split_len);
+      kend = min(kend, (split + 1) * p.split_len);
+    }
+  }
+  if (kbeg >= kend) return;  // whole workgroup: no row has a key in this split
+  const int t_first = kbeg / BN, t_last = (kend - 1) / BN;
+
+  const size_t kv_off = (size_t)(b * p.Hkv + hk) * (size_t)p.kL * D;
+  const uint16_t* __restrict__ kg = p.k + kv_off;
+  const uint16_t* __restrict__ vg = p.v + kv_off;
+
+  // ---- Q fragments: B operand of S^T = K Q^T,
+  //      lane (lr, lg) holds d = dh * DH + 16 dc + 8 lg + 0..7 of its row
+  uint4 qf[DC];
+  {
+    const uint16_t* qrow = p.q + ((size_t)(b * p.Hq + hq) * p.qL + qi) * D + dh * DH;
+#pragma unroll
+    for (int dc = 0; dc < DC; ++dc)
+      qf[dc] = valid ? *(const uint4*)(qrow + dc * 16 + lg * 8) : make_uint4(0, 0, 0, 0);
+  }
+
+  f32x16_t o[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) o[db][j] = 0.f;
+  float m_run = -INFINITY;  // running max of raw scores for this row
+  float l_run = 0.f;        // this lane's share of the running sum
+
+  // ---- tile staging ------------------------------------------------------
+  // K: direct global->LDS loads, 1 KiB per wave instruction (lane l writes
+  // bytes 16 l .. 16 l + 15 of it).  Chunk c of key row r is stored at chunk
+  // position c ^ (r & 15), so the 32 rows one MFMA operand read touches fall
+  // in distinct banks.  Rows past kL load row kL - 1 (those keys are masked).
+  // V: registers, written transposed (V^T, d-major) with the key quads of
+  // every 16-key group in the order 0, 2, 1, 3.
+  uint4 vst[VBLK_PER][4];
+  auto load_tile = [&](int t, int buf) {
+    const int ts = t * BN;
+    uint16_t* kl = lds + buf * (KTILE + VTILE);
+#pragma unroll
+    for (int n = 0; n < KLOADS; ++n) {
+      const int cb = wave * KLOADS + n;  // 1 KiB block of the tile
+      const int row = cb * (64 / ROWCH) + lane / ROWCH;
+      const int pch = lane % ROWCH;      // chunk position this lane writes
+      const int c = pch ^ (row & 15);    // the K chunk that belongs there
+      const int key = min(ts + row, p.kL - 1);
+      __builtin_amdgcn_global_load_lds((const void*)(kg + (size_t)key * D + c * 8),
+                                       (__attribute__((address_space(3))) void*)(kl + cb * 512),
+                                       16, 0, 0);
+    }
+#pragma unroll
+    for (int n = 0; n < VBLK_PER; ++n) {
+      const int bi = tid + 256 * n;
+      const int kq = bi / (D / 8), d8 = bi % (D / 8);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int key = ts + kq * 4 + r;
+        vst[n][r] = (key < p.kL) ? *(const uint4*)(vg + (size_t)key * D + d8 * 8)
+                                 : make_uint4(0, 0, 0, 0);
+      }
+    }
+  };
+  auto store_tile = [&](int buf) {
+    uint16_t* vl = lds + buf * (KTILE + VTILE) + KTILE;
+#pragma unroll
+    for (int n = 0; n < VBLK_PER; ++n) {
+      const int bi = tid + 256 * n;
+      const int kq = bi / (D / 8), d8 = bi % (D / 8);
+      const int kcol = (kq >> 2) * 16 + quad_slot(kq & 3) * 4;
+      const uint32_t w[4][4] = {{vst[n][0].x, vst[n][0].y, vst[n][0].z, vst[n][0].w},
+                                {vst[n][1].x, vst[n][1].y, vst[n][1].z, vst[n][1].w},
+                                {vst[n][2].x, vst[n][2].y, vst[n][2].z, vst[n][2].w},
+                                {vst[n][3].x, vst[n][3].y, vst[n][3].z, vst[n][3].w}};
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int d = d8 * 8 + 2 * c;
+        uint2 even, odd;  // (key0,key1),(key2,key3) of column d and of column d+1
+        even.x = (w[0][c] & 0xffffu) | (w[1][c] << 16);
+        even.y = (w[2][c] & 0xffffu) | (w[3][c] << 16);
+        odd.x = (w[0][c] >> 16) | (w[1][c] & 0xffff0000u);
+        odd.y = (w[2][c] >> 16) | (w[3][c] & 0xffff0000u);
+        *(uint2*)(vl + d * VSTR + kcol) = even;
+        *(uint2*)(vl + (d + 1) * VSTR + kcol) = odd;
+      }
+    }
+  };
+
+  load_tile(t_first, 0);
+  store_tile(0);
+  __builtin_amdgcn_s_waitcnt(0);  // direct K loads have landed in LDS
+  __syncthreads();
+
+  const float sl2 = p.sl2;
+  for (int t = t_first; t <= t_last; ++t) {
+    const int cur = (t - t_first) & 1;
+    if (t < t_last) load_tile(t + 1, cur ^ 1);
+
+    const int ts = t * BN, te = ts + BN - 1;
+    // wave-uniform; equal for the DS waves that share a row block
+    const bool skip = !wave_active || (p.causal && ts > wp_hi) ||
+                      (p.window > 0 && te < wp_lo - p.window + 1);
+    const uint16_t* kl = lds + cur * (KTILE + VTILE);
+    const uint16_t* vl = kl + KTILE;
+
+    // S^T = K Q^T over this wave's d slice: one chain of DC MFMAs per 32-key
+    // block; K operands are read two steps ahead, and the scheduling barriers
+    // keep the compiler from hoisting every read of the chain at once
+    f32x16_t s[KB];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) s[kb][j] = 0.f;
+    if (!skip) {
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        const int row = kb * 32 + lr;
+        const uint16_t* krow = kl + row * D;
+        const int sw = row & 15;
+        const int c0 = dh * (DH / 8) + lg;
+        uint4 a0 = *(const uint4*)(krow + (((c0 + 0) ^ sw) << 3));
+        uint4 a1 = *(const uint4*)(krow + (((c0 + 2) ^ sw) << 3));
+#pragma unroll
+        for (int dc = 0; dc < DC; ++dc) {
+          uint4 a2 = a1;
+          if (dc + 2 < DC) a2 = *(const uint4*)(krow + (((c0 + 2 * (dc + 2)) ^ sw) << 3));
+          s[kb] = Elem<DT>::mfma(a0, qf[dc], s[kb]);
+          __builtin_amdgcn_sched_barrier(0);
+          a0 = a1;
+          a1 = a2;
+        }
+      }
+    }
+    if constexpr (DS > 1) {
+      // the two waves of a row block hold the scores of the two halves of d:
+      // swap them through LDS and add (a + b == b + a, so both waves end up
+      // with bitwise identical scores and run identical softmax arithmetic)
+      float* xch = (float*)(lds + 2 * (KTILE + VTILE));
+      if (!skip) {
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4)
+          *(float4*)(xch + (wave * 4 + q4) * 256 + lane * 4) =
+              make_float4(s[0][4 * q4 + 0], s[0][4 * q4 + 1], s[0][4 * q4 + 2], s[0][4 * q4 + 3]);
+      }
+      __syncthreads();
+      if (!skip) {
+        const int partner = wave ^ RB;
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const float4 x = *(const float4*)(xch + (partner * 4 + q4) * 256 + lane * 4);
+          s[0][4 * q4 + 0] += x.x;
+          s[0][4 * q4 + 1] += x.y;
+          s[0][4 * q4 + 2] += x.z;
+          s[0][4 * q4 + 3] += x.w;
+        }
+      }
+    }
+    if (!skip) {
+      const bool full = (te < p.kL) && (!p.causal || te <= wp_lo) &&
+                        (p.window == 0 || ts >= wp_hi - p.window + 1);
+      if (!full) {
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+          for (int j = 0; j < 16; ++j) {
+            const int key = ts + kb * 32 + 8 * (j >> 2) + 4 * lg + (j & 3);
+            const bool vis = key < p.kL && (!p.causal || key <= pos) &&
+                             (p.window == 0 || pos - key < p.window);
+            s[kb][j] = vis ? s[kb][j] : -INFINITY;
+          }
+      }
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) mx = fmaxf(mx, s[kb][j]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float m_new = fmaxf(m_run, mx);
+      const float msc = (m_new == -INFINITY) ? 0.f : m_new * sl2;
+      // alpha rescales what was accumulated so far; nothing was while m_run = -inf
+      const float alpha = (m_run == -INFINITY) ? 0.f : fast_exp2((m_run - m_new) * sl2);
+      float psum = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const float e = fast_exp2(s[kb][j] * sl2 - msc);
+          s[kb][j] = e;
+          psum += e;
+        }
+      l_run = l_run * alpha + psum;
+      m_run = m_new;
+      // x * 1 == x: skip the rescale when no row of the wave changed its max
+      if (__any(alpha != 1.f)) {
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int j = 0; j < 16; ++j) o[db][j] *= alpha;
+      }
+
+      // O^T += V^T P^T over this wave's d slice: KB * 2 key halves x DB d
+      // blocks, V^T operands read two MFMAs ahead
+      uint4 pb[KB * 2];
+#pragma unroll
+      for (int kh = 0; kh < KB * 2; ++kh) {
+        const int kb = kh >> 1, h = kh & 1;
+        pb[kh].x = Elem<DT>::pack2(s[kb][8 * h + 0], s[kb][8 * h + 1]);
+        pb[kh].y = Elem<DT>::pack2(s[kb][8 * h + 2], s[kb][8 * h + 3]);
+        pb[kh].z = Elem<DT>::pack2(s[kb][8 * h + 4], s[kb][8 * h + 5]);
+        pb[kh].w = Elem<DT>::pack2(s[kb][8 * h + 6], s[kb][8 * h + 7]);
+      }
+      constexpr int NPV = KB * 2 * DB;
+      const uint16_t* vwave = vl + (dh * DH + lr) * VSTR + 8 * lg;
+      auto vread = [&](int n) {
+        const int kh = n / DB, db = n % DB;
+        return *(const uint4*)(vwave + db * 32 * VSTR + kh * 16);
+      };
+      uint4 b0 = vread(0), b1 = vread(1);
+#pragma unroll
+      for (int n = 0; n < NPV; ++n) {
+        uint4 b2 = b1;
+        if (n + 2 < NPV) b2 = vread(n + 2);
+        o[n % DB] = Elem<DT>::mfma(b0, pb[n / DB], o[n % DB]);
+        __builtin_amdgcn_sched_barrier(0);
+        b0 = b1;
+        b1 = b2;
+      }
+    }
+
+    if (t < t_last) store_tile(cur ^ 1);
+    __builtin_amdgcn_s_waitcnt(0);  // direct K loads of the next tile have landed
+    __syncthreads();
+  }
+
+  // ---- epilogue ---------------------------------------------------------
+  const float lsum = l_run + __shfl_xor(l_run, 32);
+  if (!valid) return;
+  const size_t orow = (size_t)(b * p.Hq + hq) * p.qL + qi;
+  if (!p.partials) {
+    const float inv = 1.0f / lsum;
+    uint16_t* dst = p.out + orow * D + dh * DH;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int d = db * 32 + 8 * q4 + 4 * lg;
+        uint2 w;
+        w.x = Elem<DT>::pack2(o[db][4 * q4 + 0] * inv, o[db][4 * q4 + 1] * inv);
+        w.y = Elem<DT>::pack2(o[db][4 * q4 + 2] * inv, o[db][4 * q4 + 3] * inv);
+        *(uint2*)(dst + d) = w;
+      }
+  } else {
+    const size_t prow = orow * p.nsplit + split;
+    float* dst = p.part_o + prow * D + dh * DH;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int d = db * 32 + 8 * q4 + 4 * lg;
+        *(float4*)(dst + d) =
+            make_float4(o[db][4 * q4 + 0], o[db][4 * q4 + 1], o[db][4 * q4 + 2], o[db][4 * q4 + 3]);
+      }
+    if (lg == 0 && dh == 0) {
+      p.part_ml[prow * 2 + 0] = (m_run == -INFINITY) ? -INFINITY : m_run * sl2;
+      p.part_ml[prow * 2 + 1] = lsum;
+    }
+  }
+}
+
+// Merge of the per-split partials of each output row, in ascending split
+// order over exactly the splits that hold the row's visible keys.  One wave
+// per row; every lane recomputes the row's max and sum the same way.
+template <int DT, int D>
+__global__ __launch_bounds__(256) void combine_kernel(AttnParams p) {
+  constexpr int PER = D / 64;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const size_t row = (size_t)blockIdx.x * 4 + wave;
+  const size_t total = (size_t)p.B * p.Hq * p.qL;
+  if (row >= total) return;
+  const int qi = (int)(row % (size_t)p.qL);
+  const int pos = p.q_offset + qi;
+  const int key_hi = p.causal ? min(pos, p.kL - 1) : p.kL - 1;
+  const int key_lo = p.window > 0 ? max(0, pos - p.window + 1) : 0;
+  const int c_lo = key_lo / p.split_len, c_hi = key_hi / p.split_len;
+
+  const float* ml = p.part_ml + row * p.nsplit * 2;
+  float M = -INFINITY;
+  for (int c = c_lo; c <= c_hi; ++c) M = fmaxf(M, ml[2 * c]);
+  float L = 0.f;
+  float acc[PER];
+#pragma unroll
+  for (int e = 0; e < PER; ++e) acc[e] = 0.f;
+  if (M != -INFINITY) {
+    for (int c = c_lo; c <= c_hi; ++c) {
+      const float mc = ml[2 * c];
+      const float w = (mc == -INFINITY) ? 0.f : fast_exp2(mc - M);
+      L += ml[2 * c + 1] * w;
+      const float* po = p.part_o + (row * p.nsplit + c) * D + lane * PER;
+#pragma unroll
+      for (int e = 0; e < PER; e += 4) {
+        const float4 x = *(const float4*)(po + e);
+        acc[e + 0] += x.x * w;
+        acc[e + 1] += x.y * w;
+        acc[e + 2] += x.z * w;
+        acc[e + 3] += x.w * w;
+      }
+    }
+  }
+  const float inv = (L > 0.f) ? 1.0f / L : 0.f;
+  uint16_t* dst = p.out + row * D + lane * PER;
+#pragma unroll
+  for (int e = 0; e < PER; e += 4) {
+    uint2 w;
+    w.x = Elem<DT>::pack2(acc[e + 0] * inv, acc[e + 1] * inv);
+    w.y = Elem<DT>::pack2(acc[e + 2] * inv, acc[e + 3] * inv);
+    *(uint2*)(dst + e) = w;
+  }
+}
+
+template <int DT, int D>
+hipError_t launch_attention_t(const AttnParams& p, hipStream_t stream) {
+  const dim3 grid((unsigned)(p.B * p.Hkv * p.mblocks), (unsigned)p.nsplit, 1);
+  hipLaunchKernelGGL((attn_tile_kernel<DT, D>), grid, dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
+template <int DT, int D>
+hipError_t launch_combine_t(const AttnParams& p, hipStream_t stream) {
+  const size_t total = (size_t)p.B * p.Hq * p.qL;
+  const dim3 grid((unsigned)((total + 3) / 4), 1, 1);
+  hipLaunchKernelGGL((combine_kernel<DT, D>), grid, dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_attention(const AttnParams& p, int D, int dtype, hipStream_t stream) {
+  if (D == 256) return dtype == 0 ? launch_attention_t<0, 256>(p, stream) : launch_attention_t<1, 256>(p, stream);
+  return dtype == 0 ? launch_attention_t<0, 512>(p, stream) : launch_attention_t<1, 512>(p, stream);
+}
+
+hipError_t launch_combine(const AttnParams& p, int D, int dtype, hipStream_t stream) {
+  if (D == 256) return dtype == 0 ? launch_combine_t<0, 256>(p, stream) : launch_combine_t<1, 256>(p, stream);
+  return dtype == 0 ? launch_combine_t<0, 512>(p, stream) : launch_combine_t<1, 512>(p, stream);
+}
+
+}  // namespace sdpa

@@ -1,0 +1,174 @@
+// C ABI of the attention library: argument checks, split planning, launch.
+// The interface and its contract are documented in include/sdpa_mi355x.h.
+#include "sdpa_mi355x.h"
+
+#include <math.h>
+#include <stdarg.h>
+#include <stdint.h>
+#include <stdio.h>
+
+#include "sdpa_internal.h"
+
+#define SDPA_API extern "C" __attribute__((visibility("default")))
+
+namespace sdpa {
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+int fail(int status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Shape checks shared by sdpa_forward and sdpa_workspace_bytes.
+int check_shape(int B, int Hq, int Hkv, int qL, int kL, int D) {
+  if (B < 1 || Hq < 1 || Hkv < 1 || qL < 1 || kL < 1)
+    return fail(SDPA_INVALID_ARG, "sizes must be >= 1 (B=%d Hq=%d Hkv=%d qL=%d kL=%d)", B, Hq,
+                Hkv, qL, kL);
+  if (Hq % Hkv != 0)
+    return fail(SDPA_INVALID_ARG, "Hq (%d) must be a multiple of Hkv (%d)", Hq, Hkv);
+  if (D != 256 && D != 512)
+    return fail(SDPA_UNSUPPORTED, "head_dim %d is not supported (256 or 512)", D);
+  // index arithmetic inside the kernels: packed rows per KV head and the
+  // launch grid stay in 32-bit range; byte offsets are 64-bit
+  const int64_t rows = (int64_t)(Hq / Hkv) * qL;
+  const int64_t flat_rows = (int64_t)B * Hq * qL;
+  if (rows > INT32_MAX / 2 || flat_rows > INT32_MAX / 2 ||
+      (int64_t)B * Hkv * ceil_div(rows, block_rows(D)) > INT32_MAX / 2)
+    return fail(SDPA_INVALID_ARG, "problem too large for one call");
+  if ((int64_t)B * Hq * qL * D > INT64_MAX / 4 || (int64_t)B * Hkv * kL * D > INT64_MAX / 4)
+    return fail(SDPA_INVALID_ARG, "element count overflows");
+  return SDPA_OK;
+}
+
+size_t workspace_for(const SplitPlan& sp, int B, int Hq, int qL, int D) {
+  if (!sp.partials) return 0;
+  const size_t prow = (size_t)B * Hq * qL * (size_t)sp.nsplit;
+  return prow * (size_t)D * sizeof(float) + prow * 2 * sizeof(float);
+}
+
+bool overlap(const void* a, size_t an, const void* b, size_t bn) {
+  const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+  return a0 < b0 + bn && b0 < a0 + an;
+}
+
+}  // namespace
+
+SplitPlan plan_split(int B, int Hq, int Hkv, int qL, int kL, int D) {
+  SplitPlan sp;
+  if (qL <= kDecodeMaxRows) {
+    // decode / verify: always the split path, fixed absolute chunks
+    sp.split_len = kDecodeChunk;
+    sp.nsplit = (int)ceil_div(kL, kDecodeChunk);
+    sp.partials = 1;
+    return sp;
+  }
+  // prefill: split the keys only when the row blocks alone cannot fill the chip
+  const int64_t rows = (int64_t)(Hq / Hkv) * qL;
+  const int64_t wgs = (int64_t)B * Hkv * ceil_div(rows, block_rows(D));
+  const int64_t want = 2 * kPlannedCUs;
+  const int64_t min_split_keys = 2048;
+  sp.nsplit = 1;
+  sp.split_len = (int)(ceil_div(kL, 1024) * 1024);
+  sp.partials = 0;
+  if (wgs < want && kL >= 2 * min_split_keys) {
+    int64_t n = ceil_div(want, wgs);
+    const int64_t nmax = kL / min_split_keys;
+    if (n > nmax) n = nmax;
+    if (n > 1) {
+      const int64_t len = ceil_div(ceil_div(kL, n), 1024) * 1024;
+      sp.split_len = (int)len;
+      sp.nsplit = (int)ceil_div(kL, len);
+      sp.partials = sp.nsplit > 1;
+    }
+  }
+  return sp;
+}
+
+}  // namespace sdpa
+
+using namespace sdpa;
+
+SDPA_API size_t sdpa_workspace_bytes(int B, int Hq, int Hkv, int qL, int kL, int D) {
+  if (check_shape(B, Hq, Hkv, qL, kL, D) != SDPA_OK) return (size_t)-1;
+  return workspace_for(plan_split(B, Hq, Hkv, qL, kL, D), B, Hq, qL, D);
+}
+
+SDPA_API const char* sdpa_last_error(void) { return g_last_error; }
+
+SDPA_API int sdpa_version(void) { return 100; }
+
+SDPA_API int sdpa_forward(const void* q, const void* k, const void* v, void* out, int B, int Hq,
+                          int Hkv, int qL, int kL, int D, float scale, int causal, int window,
+                          int q_offset, int dtype, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+  g_last_error[0] = '\0';
+  if (!q || !k || !v || !out) return fail(SDPA_INVALID_ARG, "q, k, v and out must be non-null");
+  int rc = check_shape(B, Hq, Hkv, qL, kL, D);
+  if (rc != SDPA_OK) return rc;
+  if (dtype != SDPA_FP16 && dtype != SDPA_BF16)
+    return fail(SDPA_UNSUPPORTED, "dtype %d is not supported (0 = fp16, 1 = bf16)", dtype);
+  if (!isfinite(scale) || !(scale > 0.f))
+    return fail(SDPA_INVALID_ARG, "scale must be finite and > 0 (got %g)", (double)scale);
+  if (causal != 0 && causal != 1) return fail(SDPA_INVALID_ARG, "causal must be 0 or 1");
+  if (window < 0) return fail(SDPA_INVALID_ARG, "window must be >= 0 (got %d)", window);
+  if (window > 0 && !causal) return fail(SDPA_INVALID_ARG, "a sliding window requires causal=1");
+  if (causal && (q_offset < 0 || q_offset > kL - qL))
+    return fail(SDPA_INVALID_ARG,
+                "causal q_offset must lie in [0, kL - qL] = [0, %d] so every row sees a key "
+                "(got %d)",
+                kL - qL, q_offset);
+  const size_t qbytes = (size_t)B * Hq * qL * D * 2;
+  const size_t kvbytes = (size_t)B * Hkv * kL * D * 2;
+  if (overlap(out, qbytes, q, qbytes) || overlap(out, qbytes, k, kvbytes) ||
+      overlap(out, qbytes, v, kvbytes))
+    return fail(SDPA_INVALID_ARG, "out must not overlap q, k or v");
+
+  const SplitPlan sp = plan_split(B, Hq, Hkv, qL, kL, D);
+  const size_t need = workspace_for(sp, B, Hq, qL, D);
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return fail(SDPA_WORKSPACE_TOO_SMALL, "workspace of %zu bytes needed, %zu given", need,
+                workspace ? workspace_bytes : (size_t)0);
+
+  AttnParams p;
+  p.q = (const uint16_t*)q;
+  p.k = (const uint16_t*)k;
+  p.v = (const uint16_t*)v;
+  p.out = (uint16_t*)out;
+  p.B = B;
+  p.Hq = Hq;
+  p.Hkv = Hkv;
+  p.G = Hq / Hkv;
+  p.qL = qL;
+  p.kL = kL;
+  p.causal = causal;
+  p.window = window;
+  p.q_offset = causal ? q_offset : 0;
+  p.sl2 = scale * 1.4426950408889634f;
+  p.rows = p.G * qL;
+  p.mblocks = (int)ceil_div(p.rows, block_rows(D));
+  p.nsplit = sp.nsplit;
+  p.split_len = sp.split_len;
+  p.partials = sp.partials;
+  if (sp.partials) {
+    const size_t prow = (size_t)B * Hq * qL * (size_t)sp.nsplit;
+    p.part_o = (float*)workspace;
+    p.part_ml = (float*)((char*)workspace + prow * (size_t)D * sizeof(float));
+  } else {
+    p.part_o = nullptr;
+    p.part_ml = nullptr;
+  }
+  if (sp.nsplit > 65535) return fail(SDPA_INVALID_ARG, "too many key splits (%d)", sp.nsplit);
+
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = launch_attention(p, D, dtype, s);
+  if (e == hipSuccess && sp.partials) e = launch_combine(p, D, dtype, s);
+  if (e != hipSuccess) return fail(SDPA_HIP_ERROR, "kernel launch failed: %s", hipGetErrorString(e));
+  return SDPA_OK;
+}

@@ -1,0 +1,60 @@
+// Internal declarations shared by the host dispatch and the kernel launchers.
+// Not part of the public interface (that is include/sdpa_mi355x.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace sdpa {
+
+// One workgroup of the attention kernel is 4 waves; a wave owns 32 query rows
+// and D / d_split(D) of the head dimension.  At D = 512 two waves share each
+// 32-row block (one per half of D), so a workgroup holds 64 rows.
+constexpr int kWaves = 4;
+constexpr int kRowsPerWave = 32;
+constexpr int d_split(int D) { return D == 512 ? 2 : 1; }
+constexpr int block_rows(int D) { return kWaves / d_split(D) * kRowsPerWave; }
+
+// Keys per LDS tile, by head dimension.
+constexpr int tile_keys(int D) { return D == 512 ? 32 : 64; }
+
+// Key chunk of the split path used by every call with qL <= kDecodeMaxRows.
+// It is a fixed constant, so chunk boundaries sit at absolute key positions
+// (multiples of kDecodeChunk) whatever kL and qL are.
+constexpr int kDecodeChunk = 1024;
+constexpr int kDecodeMaxRows = 4;
+
+// Number of compute units the launch shapes are planned for (MI355X).
+constexpr int kPlannedCUs = 256;
+
+struct AttnParams {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  uint16_t* out;      // direct output (nsplit == 1 and !partials)
+  float* part_o;      // [rows_total, nsplit, D] unnormalised fp32 accumulators
+  float* part_ml;     // [rows_total, nsplit, 2]: running max (log2 units), sum
+  int B, Hq, Hkv, G, qL, kL;
+  int causal, window, q_offset;
+  float sl2;          // scale * log2(e)
+  int rows;           // G * qL packed rows per (b, kv head)
+  int mblocks;        // ceil(rows / block_rows(D))
+  int nsplit;         // key splits
+  int split_len;      // keys per split, a multiple of the tile width
+  int partials;       // 1: write partials for the combine pass
+};
+
+// Split plan for a shape: how many key splits, how long each, and whether
+// the partial/combine path is used.  Pure function of the shape.
+struct SplitPlan {
+  int nsplit;
+  int split_len;
+  int partials;
+};
+SplitPlan plan_split(int B, int Hq, int Hkv, int qL, int kL, int D);
+
+hipError_t launch_attention(const AttnParams& p, int D, int dtype, hipStream_t stream);
+hipError_t launch_combine(const AttnParams& p, int D, int dtype, hipStream_t stream);
+
+}  // namespace sdpa

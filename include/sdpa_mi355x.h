@@ -1,0 +1,116 @@
+/*
+ * sdpa_mi355x.h -- fused scaled-dot-product attention for AMD MI355X (gfx950).
+ *
+ * C linkage, plain pointers and sizes only.  The library computes, for every
+ * query row, softmax(scale * Q K^T + mask) V without ever forming the
+ * [heads, qL, kL] score matrix: the "fused" attention whose lack at
+ * head_dim 256 makes long prefills run out of memory in lablup/mlxcel issue
+ * #672 ("gemma-4 long-prompt prefill OOMs on CUDA because attention
+ * materializes O(heads*L^2) scores instead of using flash SDPA", Summary and
+ * Root cause), and which ml-explore/mlx PR #3293 ("fix: add head_dim=256 to
+ * fused SDPA full attention kernel") and PR #3660 ("Fused SDPA
+ * full-attention for head_dim=192/256") add to MLX for head_dim 192/256.
+ * Its result equals the unfused matmul + softmax + matmul path (mlx PR
+ * #3660, Microbenchmarks: "max abs err 0.0"; mlx PR #3293, Benchmark) up to
+ * floating-point rounding.
+ *
+ * Tensor layout (all row-major and contiguous, as the (B, H, L, D) arrays of
+ * the M3 Ultra test script in mlx PR #3293):
+ *   q, out : [B, Hq,  qL, D]
+ *   k, v   : [B, Hkv, kL, D]
+ * Query head hq reads key/value head hq / (Hq / Hkv) (grouped-query heads,
+ * e.g. n_q=16 over n_kv=8 in the mlx PR #3660 Microbenchmarks table).
+ *
+ * Query row i sits at absolute key position p = q_offset + i.  With causal
+ * set, key j is visible from row i iff j <= p; with window w > 0 also
+ * p - j < w (w keys including the row's own).  The masks are computed from
+ * these indices; no [L, L] mask array exists (mlxcel issue #672, Suggested
+ * fix direction 1: a causal flag instead of a materialized mask).
+ * q_offset = kL - qL aligns the queries to the end of the key prefix: a
+ * prefill chunk over a cached prefix (mlx PR #3660, End-to-end section) or
+ * a verify block whose rows each attend their own trimmed prefix (lablup/
+ * mlxcel issue #2160, "Gemma 4 MTP never engages on CUDA (GB10), verify
+ * probe fails", Proposed Solution step 2).
+ *
+ * Calls with qL <= 4 (decode and verify) run a split-key path whose result
+ * for a row is bit-identical to a qL = 1 call over that row's visible key
+ * prefix, whatever qL is (the byte-for-byte verify-vs-decode requirement of
+ * mlxcel issue #2160, Acceptance Criteria).
+ *
+ * Errors are returned as status codes; nothing is thrown across this
+ * boundary, nothing aborts, nothing is printed.  The library allocates no
+ * device memory; it keeps no mutable global state except a per-thread
+ * message for the last failed call.  It is safe to call from several host
+ * threads at once.
+ */
+#ifndef SDPA_MI355X_H
+#define SDPA_MI355X_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+#define SDPA_OK 0
+#define SDPA_INVALID_ARG 1          /* a pointer, size, flag or offset is out of range */
+#define SDPA_UNSUPPORTED 2          /* head_dim not 256/512, or an unknown dtype */
+#define SDPA_WORKSPACE_TOO_SMALL 3  /* workspace_bytes < sdpa_workspace_bytes(...) */
+#define SDPA_HIP_ERROR 4            /* the kernel launch reported a HIP error */
+
+/* Element types of q, k, v and out (all four share one). */
+#define SDPA_FP16 0
+#define SDPA_BF16 1
+
+/*
+ * Enqueue out = softmax(scale * q k^T + mask) v on `stream` and return
+ * without waiting for it.
+ *
+ *   q, k, v   device pointers, layouts above, element type `dtype`; read only.
+ *   out       device pointer, [B, Hq, qL, D]; written.  Must not overlap q/k/v.
+ *   B, Hq, Hkv, qL, kL  sizes, all >= 1; Hq must be a multiple of Hkv.
+ *   D         head dimension: 256 or 512 (else SDPA_UNSUPPORTED).
+ *   scale     finite fp32 factor > 0 applied to q.k (1/sqrt(D) is the usual one).
+ *   causal    0 or 1.
+ *   window    0 (none) or >= 1; a window requires causal = 1.
+ *   q_offset  absolute position of query row 0.  Ignored unless causal; with
+ *             causal it must satisfy 0 <= q_offset <= kL - qL, so that every
+ *             row sees at least one key.
+ *   dtype     SDPA_FP16 or SDPA_BF16.
+ *   workspace device scratch owned by the caller, at least
+ *             sdpa_workspace_bytes(B, Hq, Hkv, qL, kL, D) bytes (may be NULL
+ *             when that is 0).  Its contents on entry do not matter.
+ *   stream    a hipStream_t, or NULL for the default stream.
+ *
+ * Arithmetic: fp16/bf16 products with fp32 accumulation; softmax state and
+ * the output accumulator in fp32; the output rounded to `dtype` (nearest
+ * even).  Every buffer must stay valid until the stream has passed this
+ * call.  All arguments are checked on the host before anything is
+ * enqueued; on a non-zero status nothing has been enqueued except for
+ * SDPA_HIP_ERROR.
+ */
+int sdpa_forward(const void* q, const void* k, const void* v, void* out, int B, int Hq, int Hkv,
+                 int qL, int kL, int D, float scale, int causal, int window, int q_offset,
+                 int dtype, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Bytes of device workspace sdpa_forward needs for this shape: a pure
+ * function of its arguments (no device query), 0 when the call runs without
+ * a key split.  It grows with B * Hq * qL * (kL / chunk) * D, never with
+ * qL * kL.  Returns (size_t)-1 for sizes sdpa_forward would reject as
+ * SDPA_INVALID_ARG or SDPA_UNSUPPORTED.
+ */
+size_t sdpa_workspace_bytes(int B, int Hq, int Hkv, int qL, int kL, int D);
+
+/* Message for the last non-zero status returned on the calling thread ("" if none). */
+const char* sdpa_last_error(void);
+
+/* Library version, major * 10000 + minor * 100 + patch. */
+int sdpa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SDPA_MI355X_H */

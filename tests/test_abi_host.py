@@ -1,0 +1,147 @@
+"""The C ABI library on the host: it loads without a GPU, exports what the
+header declares, and rejects bad arguments with a status code and a message
+before it touches the GPU (CPU only; no call here reaches a kernel launch)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import flash_attention_head_amd as fa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sdpa_mi355x.h")
+SIZE_MAX = ctypes.c_size_t(-1).value
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(fa.library_path()):
+        from flash_attention_head_amd import build
+
+        build.build()
+    return fa.load_library()
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(sdpa_\w+)\s*\(", text, flags=re.M))
+
+
+def test_header_declares_the_binding_names():
+    assert _declared_functions() == set(fa.EXPORTED_SYMBOLS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+    assert fa.sdpa_version() >= 100
+    assert fa.sdpa_last_error() == ""
+
+
+def test_only_the_c_abi_is_exported(lib):
+    out = os.popen(f"nm -D --defined-only {fa.library_path()}").read()
+    syms = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    assert syms == set(fa.EXPORTED_SYMBOLS), syms
+
+
+# a valid argument set; individual tests break one argument at a time
+GOOD = dict(q=0x1000, k=0x100000, v=0x200000, out=0x300000, B=1, Hq=4, Hkv=2, qL=8, kL=64, D=256,
+            scale=0.0625, causal=1, window=0, q_offset=56, dtype=fa.SDPA_BF16, workspace=0x400000,
+            workspace_bytes=1 << 30, stream=None)
+ORDER = ["q", "k", "v", "out", "B", "Hq", "Hkv", "qL", "kL", "D", "scale", "causal", "window",
+         "q_offset", "dtype", "workspace", "workspace_bytes", "stream"]
+
+
+def _call(**kw):
+    args = dict(GOOD, **kw)
+    return fa.sdpa_forward(*[args[n] for n in ORDER])
+
+
+BAD = [
+    (dict(q=None), fa.SDPA_INVALID_ARG, "non-null"),
+    (dict(out=None), fa.SDPA_INVALID_ARG, "non-null"),
+    (dict(B=0), fa.SDPA_INVALID_ARG, ">= 1"),
+    (dict(kL=-3), fa.SDPA_INVALID_ARG, ">= 1"),
+    (dict(Hq=3), fa.SDPA_INVALID_ARG, "multiple"),
+    (dict(D=128), fa.SDPA_UNSUPPORTED, "head_dim"),
+    (dict(D=192), fa.SDPA_UNSUPPORTED, "head_dim"),
+    (dict(dtype=2), fa.SDPA_UNSUPPORTED, "dtype"),
+    (dict(scale=float("nan")), fa.SDPA_INVALID_ARG, "scale"),
+    (dict(scale=float("inf")), fa.SDPA_INVALID_ARG, "scale"),
+    (dict(scale=-1.0), fa.SDPA_INVALID_ARG, "scale"),
+    (dict(scale=0.0), fa.SDPA_INVALID_ARG, "scale"),
+    (dict(causal=2), fa.SDPA_INVALID_ARG, "causal"),
+    (dict(window=-1), fa.SDPA_INVALID_ARG, "window"),
+    (dict(causal=0, window=16), fa.SDPA_INVALID_ARG, "requires causal"),
+    (dict(q_offset=57), fa.SDPA_INVALID_ARG, "q_offset"),
+    (dict(q_offset=-1), fa.SDPA_INVALID_ARG, "q_offset"),
+    (dict(qL=65, q_offset=0), fa.SDPA_INVALID_ARG, "q_offset"),
+    (dict(out=0x1000 + 64), fa.SDPA_INVALID_ARG, "overlap"),
+    (dict(out=0x100000 + 4096), fa.SDPA_INVALID_ARG, "overlap"),
+    (dict(qL=2, q_offset=62, workspace=None), fa.SDPA_WORKSPACE_TOO_SMALL, "workspace"),
+    (dict(qL=2, q_offset=62, workspace_bytes=16), fa.SDPA_WORKSPACE_TOO_SMALL, "workspace"),
+]
+
+
+@pytest.mark.parametrize("kw,status,words", BAD, ids=[str(b[0]) for b in BAD])
+def test_bad_arguments_return_status_and_message(lib, kw, status, words):
+    assert _call(**kw) == status
+    assert words in fa.sdpa_last_error()
+
+
+def test_message_is_per_thread(lib):
+    import threading
+
+    assert _call(B=0) == fa.SDPA_INVALID_ARG
+    seen = []
+    t = threading.Thread(target=lambda: seen.append(fa.sdpa_last_error()))
+    t.start()
+    t.join()
+    assert seen == [""]
+    assert ">= 1" in fa.sdpa_last_error()
+
+
+def test_workspace_is_zero_without_a_split(lib):
+    # self-attention with enough row blocks to fill the chip: no split
+    assert fa.sdpa_workspace_bytes(1, 64, 64, 16384, 16384, 256) == 0
+    assert fa.sdpa_workspace_bytes(1, 32, 16, 32768, 32768, 256) == 0
+    assert fa.sdpa_workspace_bytes(1, 32, 4, 32768, 32768, 512) == 0
+    assert fa.sdpa_workspace_bytes(1, 2, 1, 128, 128, 256) == 0
+
+
+def test_workspace_is_linear_in_key_chunks_not_quadratic(lib):
+    # decode/verify: one fp32 (m, l, O[D]) partial per row and 1024-key chunk
+    for qL in (1, 2, 4):
+        prev = None
+        for kL in (1000, 1024, 1025, 4096, 65536, 131072):
+            ws = fa.sdpa_workspace_bytes(1, 16, 8, qL, kL, 256)
+            chunks = -(-kL // 1024)
+            assert ws == 16 * qL * chunks * (256 + 2) * 4
+            if prev is not None:
+                assert ws >= prev
+            prev = ws
+    # a chunked prefill over a long prefix splits its keys: bounded by rows * splits * D
+    ws = fa.sdpa_workspace_bytes(1, 16, 8, 1024, 32768, 256)
+    assert 0 < ws <= 16 * 1024 * 32 * (256 + 2) * 4
+
+
+def test_workspace_of_rejected_shapes_is_size_max(lib):
+    assert fa.sdpa_workspace_bytes(1, 4, 2, 8, 64, 128) == SIZE_MAX
+    assert fa.sdpa_workspace_bytes(1, 3, 2, 8, 64, 256) == SIZE_MAX
+    assert fa.sdpa_workspace_bytes(0, 4, 2, 8, 64, 256) == SIZE_MAX
+
+
+def test_binding_fails_loudly_without_the_library(tmp_path, monkeypatch):
+    import importlib
+
+    monkeypatch.setenv("SDPA_MI355X_LIB", str(tmp_path / "missing.so"))
+    mod = importlib.reload(fa)
+    try:
+        with pytest.raises(RuntimeError, match="no fallback"):
+            mod.sdpa_version()
+    finally:
+        monkeypatch.delenv("SDPA_MI355X_LIB")
+        importlib.reload(fa)

@@ -1,0 +1,167 @@
+"""GPU output of the HIP library against the fp64 oracle, element by element.
+
+Small shapes run every row through the oracle; they span several K/V tiles,
+several row blocks and ragged tails of both.  The named full-size workloads
+run in the launch configuration the benchmark times and are compared on
+sampled rows (the oracle computes them one by one), plus closed forms that
+hold at any size.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from flash_attention_head_amd import workloads as W
+from gpu_util import (TOL, check_close, ensure_library, f64, note, oracle_full, oracle_rows,
+                      run_gpu, sample_rows)
+
+pytestmark = pytest.mark.gpu
+
+FP16, BF16 = W.FP16, W.BF16
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    ensure_library()
+
+
+# (B, Hq, Hkv, qL, kL, D, dtype, causal, window, q_offset)
+SMALL = [
+    (2, 4, 2, 333, 333, 256, FP16, True, 0, 0),        # ragged tiles and row blocks
+    (1, 4, 2, 100, 1000, 256, BF16, True, 0, 900),     # bottom-right chunk over a prefix
+    (1, 4, 2, 100, 1000, 256, BF16, True, 77, 900),    # sliding window over a prefix
+    (1, 2, 2, 257, 190, 256, FP16, False, 0, 0),       # no mask, qL > kL
+    (1, 8, 1, 65, 700, 256, BF16, True, 33, 635),      # G = 8
+    (1, 2, 1, 5, 5, 256, FP16, True, 0, 0),            # smallest prefill, one partial tile
+    (1, 2, 1, 300, 9000, 256, FP16, True, 0, 8700),    # key split + combine, ragged last split
+    (1, 4, 2, 200, 9000, 256, BF16, True, 500, 8800),  # key split with a window
+    (1, 4, 1, 150, 150, 512, BF16, True, 0, 0),        # head_dim 512
+    (2, 2, 2, 70, 200, 512, FP16, False, 0, 0),
+    (1, 4, 2, 96, 400, 512, BF16, True, 40, 304),
+    (1, 2, 1, 130, 8300, 512, FP16, True, 0, 8170),    # head_dim 512 with key split
+    (1, 4, 2, 1, 2500, 256, BF16, True, 0, 2499),      # decode, three 1024-key chunks
+    (1, 4, 2, 4, 2500, 256, FP16, True, 0, 2496),      # verify block
+    (1, 4, 2, 3, 2500, 256, BF16, True, 100, 2497),    # verify block with a window
+    (1, 8, 2, 4, 1500, 512, BF16, True, 0, 1496),      # verify block at head_dim 512
+    (2, 2, 1, 2, 700, 256, FP16, False, 0, 0),         # unmasked decode
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=[f"B{c[0]}Hq{c[1]}Hkv{c[2]}q{c[3]}k{c[4]}D{c[5]}"
+                                             f"{'bf16' if c[6] else 'f16'}c{int(c[7])}w{c[8]}"
+                                             for c in SMALL])
+def test_small_shapes_every_row(case):
+    B, Hq, Hkv, qL, kL, D, dtype, causal, window, q_offset = case
+    q, k, v = W.random_qkv(1000 + qL + kL, B, Hq, Hkv, qL, kL, D, dtype)
+    scale = float(np.float32(1.0 / np.sqrt(D)))
+    note(f"small {case}")
+    got = f64(run_gpu(q, k, v, causal=causal, window=window, q_offset=q_offset))
+    ref = oracle_full(q, k, v, scale=scale, causal=causal, window=window, q_offset=q_offset,
+                      dtype=dtype)
+    check_close(got, ref, dtype, f"small {case}")
+
+
+def test_tiny_causal_workload_every_row():
+    wl = W.WORKLOADS["tiny_causal"]
+    q, k, v = W.draw(wl)
+    note(wl.name)
+    got = f64(run_gpu(q, k, v, causal=wl.causal, window=wl.window, q_offset=wl.q_offset))
+    ref = oracle_full(q, k, v, scale=wl.scale, causal=wl.causal, window=wl.window,
+                      q_offset=wl.q_offset, dtype=wl.dtype)
+    check_close(got, ref, wl.dtype, wl.name)
+
+
+FULL = [("chunked_prefill_32k", 160), ("causal_h64_16k", 160), ("sliding_32k", 200),
+        ("global_d512_32k", 64), ("decode_q4_128k", 32), ("decode_q1_128k", 16)]
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("name,n_random", FULL, ids=[f[0] for f in FULL])
+def test_full_size_workloads_on_sampled_rows(name, n_random):
+    wl = W.WORKLOADS[name]
+    q, k, v = W.draw(wl)
+    note(f"{name} full size")
+    got = run_gpu(q, k, v, causal=wl.causal, window=wl.window, q_offset=wl.q_offset)
+    assert torch.isfinite(got.float()).all()
+    rows = sample_rows(wl, n_random, seed=wl.seed)
+    ref = oracle_rows(q, k, v, rows, scale=wl.scale, causal=wl.causal, window=wl.window,
+                      q_offset=wl.q_offset, dtype=wl.dtype)
+    check_close(f64(got.reshape(-1, wl.D)[torch.from_numpy(rows)]), ref, wl.dtype,
+                f"{name} ({rows.size} rows)")
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("name", ["chunked_prefill_32k", "sliding_32k", "causal_h64_16k",
+                                  "global_d512_32k", "decode_q4_128k"])
+def test_zero_queries_average_visible_values_at_full_size(name):
+    # with Q = 0 every visible key has weight 1/n: each row is the mean of its
+    # visible value rows, computed here with fp64 prefix sums.  Checks every
+    # row's mask boundaries and the head mapping at full size.
+    wl = W.WORKLOADS[name]
+    _, k, v = W.draw(wl)
+    q = torch.zeros((wl.B, wl.Hq, wl.qL, wl.D), dtype=W.TORCH_DTYPES[wl.dtype])
+    note(f"{name} zero queries")
+    got = run_gpu(q, k, v, causal=wl.causal, window=wl.window, q_offset=wl.q_offset)
+    G = wl.Hq // wl.Hkv
+    p = wl.q_offset + np.arange(wl.qL)
+    hi = np.minimum(p, wl.kL - 1) if wl.causal else np.full(wl.qL, wl.kL - 1)
+    lo = np.maximum(p - wl.window + 1, 0) if wl.window else np.zeros(wl.qL, dtype=np.int64)
+    n = (hi - lo + 1).astype(np.float64)[:, None]
+    worst = 0.0
+    for hk in sorted({0, wl.Hkv // 2, wl.Hkv - 1}):
+        csum = np.zeros((wl.kL + 1, wl.D))
+        np.cumsum(v[0, hk].to(torch.float64).numpy(), axis=0, out=csum[1:])
+        mean = (csum[hi + 1] - csum[lo]) / n
+        for g in range(G):
+            o = f64(got[0, hk * G + g])
+            worst = max(worst, float(np.abs(o - mean).max()))
+    print(f"[parity] {name} zero-query mean: max err {worst:.3e}", flush=True)
+    assert worst <= TOL[wl.dtype]
+
+
+@pytest.mark.parametrize("D,dtype", [(256, FP16), (256, BF16), (512, BF16)])
+def test_first_causal_row_and_unit_window_are_exact(D, dtype):
+    # causal row 0 at q_offset 0 sees key 0 only; a window of 1 sees key p only:
+    # exp2(0) = 1, every other weight is 0, so the output is the value row bitwise
+    q, k, v = W.random_qkv(77, 1, 4, 2, 300, 300, D, dtype)
+    note(f"exact rows D{D} dtype{dtype}")
+    a = run_gpu(q, k, v, causal=True, q_offset=0)
+    expect0 = v[:, :, 0].repeat_interleave(2, dim=1)
+    assert torch.equal(a[:, :, 0].view(torch.int16), expect0.contiguous().view(torch.int16))
+    b = run_gpu(q, k, v, causal=True, window=1, q_offset=0)
+    assert torch.equal(b.view(torch.int16), v.repeat_interleave(2, dim=1).view(torch.int16))
+
+
+@pytest.mark.parametrize("D,qL,kL", [(256, 300, 300), (512, 200, 260), (256, 4, 3000)])
+def test_gqa_equals_explicitly_repeated_kv_heads(D, qL, kL):
+    G = 4
+    q, k, v = W.random_qkv(78, 1, 8, 2, qL, kL, D, BF16)
+    note(f"gqa D{D} qL{qL} kL{kL}")
+    a = run_gpu(q, k, v, causal=True, q_offset=kL - qL)
+    b = run_gpu(q, k.repeat_interleave(G, dim=1).contiguous(),
+                v.repeat_interleave(G, dim=1).contiguous(), causal=True, q_offset=kL - qL)
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def test_runs_are_bitwise_deterministic():
+    wl = W.WORKLOADS["tiny_causal"].with_(qL=700, kL=5000, q_offset=4300, Hq=8, Hkv=2)
+    q, k, v = W.random_qkv(79, 1, 8, 2, 700, 5000, 256, FP16)
+    note("determinism")
+    a = run_gpu(q, k, v, causal=True, q_offset=wl.q_offset)
+    b = run_gpu(q, k, v, causal=True, q_offset=wl.q_offset)
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+@pytest.mark.timeout(300)
+@pytest.mark.parametrize("L", [16384, 32768])
+def test_unmasked_h8_long_sequences_are_finite(L):
+    # the shape of the M3 Ultra test script in mlx PR #3293: B=1, H=8, D=256,
+    # normal inputs, scale 1/sqrt(D), no mask; output shape and finiteness
+    q, k, v = W.random_qkv(80 + L, 1, 8, 8, L, L, 256, BF16)
+    note(f"unmasked H8 L{L}")
+    out = run_gpu(q, k, v, causal=False)
+    assert out.shape == (1, 8, L, 256)
+    assert torch.isfinite(out.float()).all()
+    rows = np.array([0, 1, L - 1, 3 * L + 5, 8 * L - 1], dtype=np.int64)
+    ref = oracle_rows(q, k, v, rows, scale=1 / 16, causal=False, window=0, q_offset=0, dtype=BF16)
+    check_close(f64(out.reshape(-1, 256)[torch.from_numpy(rows)]), ref, BF16, f"unmasked L{L}")
