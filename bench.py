@@ -86,6 +86,35 @@ def summarize(wl, t):
     return r
 
 
+def measured_traffic(wl_name):
+    """HBM bytes per call from the committed counter summary, if the kernels are unchanged.
+
+    profiles/hbm_traffic_<workload>.md records FETCH_SIZE + WRITE_SIZE per call (scaled by a
+    plain copy's reading) and a hash of the kernel sources they were taken with; a different
+    hash means the counters describe older kernels, and traffic is reported as null.
+    """
+    import hashlib
+
+    path = os.path.join(ROOT, "profiles", f"hbm_traffic_{wl_name}.md")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        if ":" in line and not line.startswith(("|", "#", " ")):
+            k, _, v = line.partition(":")
+            fields[k.strip()] = v.strip()
+    h = hashlib.sha256()
+    for f in ("attn_kernels.hip", "sdpa_api.cpp", "sdpa_internal.h"):
+        with open(os.path.join(ROOT, "flash_attention_head_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    if fields.get("kernel_source_sha256") != h.hexdigest():
+        return None
+    try:
+        return int(fields["traffic_bytes_per_call"])
+    except (KeyError, ValueError):
+        return None
+
+
 def cpu_baseline(wl, target_s=15.0):
     """The fp64 oracle on a bounded, seeded sample of the workload's rows."""
     import numpy as np
@@ -127,6 +156,9 @@ def main():
     ap.add_argument("--extra", dest="extra", action="store_true", default=True)
     ap.add_argument("--no-extra", dest="extra", action="store_false")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-reference", action="store_true",
+                    help="only run a plain 1 GiB device copy three times (calibrates the "
+                         "FETCH_SIZE / WRITE_SIZE counters against known bytes)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -145,6 +177,15 @@ def main():
         build.build()
     fa.load_library()
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+
+    if args.copy_reference:
+        src = torch.ones(1 << 30, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_reference_bytes": 1 << 30, "dispatches": 3}), flush=True)
+        return
 
     wl = W.WORKLOADS[args.workload]
     log(f"[bench] {wl.name}: warmup {args.warmup}, steps {args.steps}")
@@ -189,7 +230,8 @@ def main():
                    "q_offset": wl.q_offset, "flop_per_step": fl},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_MFMA_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_MFMA_TFLOPS, 4),
-                     "traffic": None,
+                     "traffic": measured_traffic(wl.name),
+                     "traffic_unit": "bytes per call (FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
                      "kernel": "attn_tile_kernel (+ combine_kernel when keys are split), one "
                                "sdpa_forward call, HIP events on its stream"},
         "cpu_baseline": base,
