@@ -25,6 +25,10 @@ FLAGS = [
     "-fvisibility=hidden",
     # no packed-FP32 instructions in device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA accumulators in ordinary VGPRs: the softmax rescale and the epilogue
+    # read them with VALU instructions, and AGPR accumulators made the register
+    # allocator copy the whole output tile between register files every tile
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-I" + os.path.join(ROOT, "include"),
 ]
 

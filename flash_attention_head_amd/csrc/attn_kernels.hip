@@ -68,6 +68,16 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 // layout hands them out) are 16 contiguous bytes.
 __device__ __forceinline__ int quad_slot(int b4) { return ((b4 & 1) << 1) | (b4 >> 1); }
 
+// Rotation, in 8-byte units (always even, so 16-byte chunks stay whole), of
+// V^T row d.  Chosen with a 32-bank model of the transposed stores and the
+// operand reads: for 64-key rows both are conflict-free; for 32-key rows
+// (D = 512) the reads are and the stores are 4-way at worst.
+template <int D>
+__device__ __forceinline__ int vrot(int d) {
+  if constexpr (D == 512) return 2 * (((d >> 3) + (d >> 1)) & 3);
+  else return 2 * (((d & 7) + (d >> 3)) & 7);
+}
+
 template <int DT, int D>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void attn_tile_kernel(AttnParams p) {
@@ -77,9 +87,9 @@ void attn_tile_kernel(AttnParams p) {
   constexpr int BM = block_rows(D);   // rows per workgroup
   constexpr int BN = tile_keys(D);
   constexpr int ROWCH = D / 8;        // 16-byte chunks per K row
-  constexpr int VSTR = BN + 8;        // V^T tile row stride (elements); +16 B against bank conflicts
+  constexpr int UPR = BN / 4;         // 8-byte units (4 keys) per V^T row
   constexpr int KTILE = BN * D;       // K tile: rows of D elements, chunks XOR-swizzled
-  constexpr int VTILE = D * VSTR;
+  constexpr int VTILE = D * BN;       // V^T tile: rows of BN keys, units rotated per row
   constexpr int DC = DH / 16;         // MFMA steps over this wave's d in S^T
   constexpr int DB = DH / 32;         // 32-wide d blocks of this wave's O^T
   constexpr int KB = BN / 32;         // 32-key blocks of S^T
@@ -161,9 +171,19 @@ void attn_tile_kernel(AttnParams p) {
   // bytes 16 l .. 16 l + 15 of it).  Chunk c of key row r is stored at chunk
   // position c ^ (r & 15), so the 32 rows one MFMA operand read touches fall
   // in distinct banks.  Rows past kL load row kL - 1 (those keys are masked).
-  // V: registers, written transposed (V^T, d-major) with the key quads of
-  // every 16-key group in the order 0, 2, 1, 3.
+  // V: registers, written transposed (V^T, d-major): each thread owns 4-key x
+  // 8-d blocks.  The 8-byte units (4 keys) of every V^T row are in the key
+  // quad order 0, 2, 1, 3 of each 16-key group, then rotated by vrot(d) units,
+  // so that both the transposed stores (32 lanes on 8 rows 8 apart) and the
+  // MFMA operand reads (8 lanes on 8 consecutive rows) spread over all banks.
   uint4 vst[VBLK_PER][4];
+  auto vblock = [&](int n, int& kq, int& d8) {
+    // lanes pair key quads {4a+b, 4a+2+b}: units of opposite parity
+    const int bi = tid + 256 * n;
+    const int c = bi & 1, rest = (bi >> 1) / (D / 8);
+    d8 = (bi >> 1) % (D / 8);
+    kq = 4 * (rest >> 1) + 2 * c + (rest & 1);
+  };
   auto load_tile = [&](int t, int buf) {
     const int ts = t * BN;
     uint16_t* kl = lds + buf * (KTILE + VTILE);
@@ -180,8 +200,8 @@ void attn_tile_kernel(AttnParams p) {
     }
 #pragma unroll
     for (int n = 0; n < VBLK_PER; ++n) {
-      const int bi = tid + 256 * n;
-      const int kq = bi / (D / 8), d8 = bi % (D / 8);
+      int kq, d8;
+      vblock(n, kq, d8);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int key = ts + kq * 4 + r;
@@ -194,9 +214,9 @@ void attn_tile_kernel(AttnParams p) {
     uint16_t* vl = lds + buf * (KTILE + VTILE) + KTILE;
 #pragma unroll
     for (int n = 0; n < VBLK_PER; ++n) {
-      const int bi = tid + 256 * n;
-      const int kq = bi / (D / 8), d8 = bi % (D / 8);
-      const int kcol = (kq >> 2) * 16 + quad_slot(kq & 3) * 4;
+      int kq, d8;
+      vblock(n, kq, d8);
+      const int unit = (kq >> 2) * 4 + quad_slot(kq & 3);
       const uint32_t w[4][4] = {{vst[n][0].x, vst[n][0].y, vst[n][0].z, vst[n][0].w},
                                 {vst[n][1].x, vst[n][1].y, vst[n][1].z, vst[n][1].w},
                                 {vst[n][2].x, vst[n][2].y, vst[n][2].z, vst[n][2].w},
@@ -209,8 +229,8 @@ void attn_tile_kernel(AttnParams p) {
         even.y = (w[2][c] & 0xffffu) | (w[3][c] << 16);
         odd.x = (w[0][c] >> 16) | (w[1][c] & 0xffff0000u);
         odd.y = (w[2][c] >> 16) | (w[3][c] & 0xffff0000u);
-        *(uint2*)(vl + d * VSTR + kcol) = even;
-        *(uint2*)(vl + (d + 1) * VSTR + kcol) = odd;
+        *(uint2*)(vl + d * BN + ((unit + vrot<D>(d)) % UPR) * 4) = even;
+        *(uint2*)(vl + (d + 1) * BN + ((unit + vrot<D>(d + 1)) % UPR) * 4) = odd;
       }
     }
   };
@@ -232,32 +252,31 @@ void attn_tile_kernel(AttnParams p) {
     const uint16_t* kl = lds + cur * (KTILE + VTILE);
     const uint16_t* vl = kl + KTILE;
 
-    // S^T = K Q^T over this wave's d slice: one chain of DC MFMAs per 32-key
-    // block; K operands are read two steps ahead, and the scheduling barriers
-    // keep the compiler from hoisting every read of the chain at once
+    // S^T = K Q^T over this wave's d slice: the KB accumulator chains are
+    // interleaved (consecutive MFMAs are independent) and K operands are read
+    // PF MFMAs ahead; the scheduling barriers keep that order
     f32x16_t s[KB];
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
       for (int j = 0; j < 16; ++j) s[kb][j] = 0.f;
     if (!skip) {
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
+      constexpr int NQK = KB * DC, PF = 4;
+      const int c0 = dh * (DH / 8) + lg;
+      auto kread = [&](int n) {
+        const int kb = n % KB, dc = n / KB;
         const int row = kb * 32 + lr;
-        const uint16_t* krow = kl + row * D;
-        const int sw = row & 15;
-        const int c0 = dh * (DH / 8) + lg;
-        uint4 a0 = *(const uint4*)(krow + (((c0 + 0) ^ sw) << 3));
-        uint4 a1 = *(const uint4*)(krow + (((c0 + 2) ^ sw) << 3));
+        return *(const uint4*)(kl + row * D + (((c0 + 2 * dc) ^ (row & 15)) << 3));
+      };
+      uint4 a[PF];
 #pragma unroll
-        for (int dc = 0; dc < DC; ++dc) {
-          uint4 a2 = a1;
-          if (dc + 2 < DC) a2 = *(const uint4*)(krow + (((c0 + 2 * (dc + 2)) ^ sw) << 3));
-          s[kb] = Elem<DT>::mfma(a0, qf[dc], s[kb]);
-          __builtin_amdgcn_sched_barrier(0);
-          a0 = a1;
-          a1 = a2;
-        }
+      for (int i = 0; i < PF; ++i) a[i] = kread(i);
+#pragma unroll
+      for (int n = 0; n < NQK; ++n) {
+        const uint4 cur_a = a[n % PF];
+        if (n + PF < NQK) a[n % PF] = kread(n + PF);
+        s[n % KB] = Elem<DT>::mfma(cur_a, qf[n / KB], s[n % KB]);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
     if constexpr (DS > 1) {
@@ -338,21 +357,21 @@ void attn_tile_kernel(AttnParams p) {
         pb[kh].z = Elem<DT>::pack2(s[kb][8 * h + 4], s[kb][8 * h + 5]);
         pb[kh].w = Elem<DT>::pack2(s[kb][8 * h + 6], s[kb][8 * h + 7]);
       }
-      constexpr int NPV = KB * 2 * DB;
-      const uint16_t* vwave = vl + (dh * DH + lr) * VSTR + 8 * lg;
+      constexpr int NPV = KB * 2 * DB, PF = 4;
       auto vread = [&](int n) {
         const int kh = n / DB, db = n % DB;
-        return *(const uint4*)(vwave + db * 32 * VSTR + kh * 16);
+        const int d = dh * DH + db * 32 + lr;
+        return *(const uint4*)(vl + d * BN + (((2 * (kh * 2 + lg)) + vrot<D>(d)) % UPR) * 4);
       };
-      uint4 b0 = vread(0), b1 = vread(1);
+      uint4 bv[PF];
+#pragma unroll
+      for (int i = 0; i < PF; ++i) bv[i] = vread(i);
 #pragma unroll
       for (int n = 0; n < NPV; ++n) {
-        uint4 b2 = b1;
-        if (n + 2 < NPV) b2 = vread(n + 2);
-        o[n % DB] = Elem<DT>::mfma(b0, pb[n / DB], o[n % DB]);
+        const uint4 cur_b = bv[n % PF];
+        if (n + PF < NPV) bv[n % PF] = vread(n + PF);
+        o[n % DB] = Elem<DT>::mfma(cur_b, pb[n / DB], o[n % DB]);
         __builtin_amdgcn_sched_barrier(0);
-        b0 = b1;
-        b1 = b2;
       }
     }
 
