@@ -69,13 +69,36 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 __device__ __forceinline__ int quad_slot(int b4) { return ((b4 & 1) << 1) | (b4 >> 1); }
 
 // Rotation, in 8-byte units (always even, so 16-byte chunks stay whole), of
-// V^T row d.  Chosen with a 32-bank model of the transposed stores and the
-// operand reads: for 64-key rows both are conflict-free; for 32-key rows
-// (D = 512) the reads are and the stores are 4-way at worst.
+// V^T row d, chosen by measuring candidate layouts (padding x rotation) for
+// the 128-bit operand reads and the 64-bit transposed stores.
 template <int D>
 __device__ __forceinline__ int vrot(int d) {
   if constexpr (D == 512) return 2 * (((d >> 3) + (d >> 1)) & 3);
-  else return 2 * (((d & 7) + (d >> 3)) & 7);
+  else return 2 * ((d >> 3) & 7);
+}
+// Elements per V^T row: 64 keys padded to 192 bytes at D = 256 (with the
+// rotation above, the measured fastest layout for both the operand reads and
+// the transposed stores); 32 unpadded keys at D = 512, where LDS is full.
+template <int D>
+constexpr int vrow() { return D == 512 ? 32 : 96; }
+
+// One 16-byte-per-lane direct global->LDS load: lane l's 16 bytes land at
+// lds + 16 l.  Issued through inline assembly so that the compiler does not
+// treat it as a pending LDS write and wait for it before every later LDS
+// access; the kernel waits for these loads itself, before the barrier that
+// publishes the tile they fill.  M0 (the LDS base of the instruction) is
+// restored afterwards; writing M0 needs one wait state before the load.
+__device__ __forceinline__ void load_lds16(const void* src, void* lds) {
+  const unsigned base = __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)lds);
+  unsigned saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(src), "s"(base));
 }
 
 template <int DT, int D>
@@ -89,7 +112,8 @@ void attn_tile_kernel(AttnParams p) {
   constexpr int ROWCH = D / 8;        // 16-byte chunks per K row
   constexpr int UPR = BN / 4;         // 8-byte units (4 keys) per V^T row
   constexpr int KTILE = BN * D;       // K tile: rows of D elements, chunks XOR-swizzled
-  constexpr int VTILE = D * BN;       // V^T tile: rows of BN keys, units rotated per row
+  constexpr int VROW = vrow<D>();     // elements per V^T row
+  constexpr int VTILE = D * VROW;     // V^T tile: rows of BN keys, units rotated per row
   constexpr int DC = DH / 16;         // MFMA steps over this wave's d in S^T
   constexpr int DB = DH / 32;         // 32-wide d blocks of this wave's O^T
   constexpr int KB = BN / 32;         // 32-key blocks of S^T
@@ -194,9 +218,7 @@ void attn_tile_kernel(AttnParams p) {
       const int pch = lane % ROWCH;      // chunk position this lane writes
       const int c = pch ^ (row & 15);    // the K chunk that belongs there
       const int key = min(ts + row, p.kL - 1);
-      __builtin_amdgcn_global_load_lds((const void*)(kg + (size_t)key * D + c * 8),
-                                       (__attribute__((address_space(3))) void*)(kl + cb * 512),
-                                       16, 0, 0);
+      load_lds16(kg + (size_t)key * D + c * 8, kl + cb * 512);
     }
 #pragma unroll
     for (int n = 0; n < VBLK_PER; ++n) {
@@ -229,8 +251,8 @@ void attn_tile_kernel(AttnParams p) {
         even.y = (w[2][c] & 0xffffu) | (w[3][c] << 16);
         odd.x = (w[0][c] >> 16) | (w[1][c] & 0xffff0000u);
         odd.y = (w[2][c] >> 16) | (w[3][c] & 0xffff0000u);
-        *(uint2*)(vl + d * BN + ((unit + vrot<D>(d)) % UPR) * 4) = even;
-        *(uint2*)(vl + (d + 1) * BN + ((unit + vrot<D>(d + 1)) % UPR) * 4) = odd;
+        *(uint2*)(vl + d * VROW + ((unit + vrot<D>(d)) % UPR) * 4) = even;
+        *(uint2*)(vl + (d + 1) * VROW + ((unit + vrot<D>(d + 1)) % UPR) * 4) = odd;
       }
     }
   };
@@ -361,7 +383,7 @@ void attn_tile_kernel(AttnParams p) {
       auto vread = [&](int n) {
         const int kh = n / DB, db = n % DB;
         const int d = dh * DH + db * 32 + lr;
-        return *(const uint4*)(vl + d * BN + (((2 * (kh * 2 + lg)) + vrot<D>(d)) % UPR) * 4);
+        return *(const uint4*)(vl + d * VROW + (((2 * (kh * 2 + lg)) + vrot<D>(d)) % UPR) * 4);
       };
       uint4 bv[PF];
 #pragma unroll
