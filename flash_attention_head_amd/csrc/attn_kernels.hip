@@ -30,6 +30,9 @@ namespace {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 
 template <int DT>
 struct Elem;
@@ -41,9 +44,8 @@ struct Elem<0> {  // IEEE binary16
                                                   __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
   }
   static __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
-    _Float16 a = (_Float16)lo, b = (_Float16)hi;  // round to nearest even
-    return (uint32_t)__builtin_bit_cast(uint16_t, a) |
-           ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+    // one v_cvt_pk_f16_f32, round to nearest even
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){lo, hi}, f16x2_t));
   }
 };
 
@@ -54,9 +56,8 @@ struct Elem<1> {  // bfloat16
                                                    __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
   }
   static __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
-    __bf16 a = (__bf16)lo, b = (__bf16)hi;  // round to nearest even
-    return (uint32_t)__builtin_bit_cast(uint16_t, a) |
-           ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+    // one v_cvt_pk_bf16_f32, round to nearest even
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){lo, hi}, bf16x2_t));
   }
 };
 
@@ -82,24 +83,50 @@ __device__ __forceinline__ int vrot(int d) {
 template <int D>
 constexpr int vrow() { return D == 512 ? 32 : 96; }
 
-// One 16-byte-per-lane direct global->LDS load: lane l's 16 bytes land at
-// lds + 16 l.  Issued through inline assembly so that the compiler does not
-// treat it as a pending LDS write and wait for it before every later LDS
-// access; the kernel waits for these loads itself, before the barrier that
-// publishes the tile they fill.  M0 (the LDS base of the instruction) is
-// restored afterwards; writing M0 needs one wait state before the load.
-__device__ __forceinline__ void load_lds16(const void* src, void* lds) {
+// One 16-byte-per-lane direct global->LDS load from sbase + voff bytes
+// (sbase uniform, voff per lane): lane l's 16 bytes land at lds + 16 l.
+// Issued through inline assembly so that the compiler does not treat it as a
+// pending LDS write and wait for it before every later LDS access; the kernel
+// waits for these loads itself, before the barrier that publishes the tile
+// they fill.  M0 (the LDS base of the instruction) is restored afterwards;
+// writing M0 needs one wait state before the load.
+__device__ __forceinline__ void load_lds16(const void* sbase, uint32_t voff, void* lds) {
   const unsigned base = __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)lds);
+  // the 64-bit base, moved to scalar registers half by half; readfirstlane
+  // returns int, so each half goes through uint32_t (no sign extension)
+  const uint64_t a = (uint64_t)(uintptr_t)sbase;
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((unsigned)a);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((unsigned)(a >> 32));
+  const uint64_t sa = ((uint64_t)hi << 32) | (uint64_t)lo;
   unsigned saved;
   asm volatile(
       "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %2\n\t"
+      "s_mov_b32 m0, %3\n\t"
       "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %1, off\n\t"
+      "global_load_lds_dwordx4 %1, %2\n\t"
       "s_mov_b32 m0, %0"
       : "=&s"(saved)
-      : "v"(src), "s"(base));
+      : "v"(voff), "s"(sa), "s"(base));
 }
+
+// Max and sum over the two lanes (l, l ^ 32) that share a query row.
+__device__ __forceinline__ float pair_max(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(int, v),
+                                                  __builtin_bit_cast(int, v), false, false);
+  return fmaxf(__builtin_bit_cast(float, (int)r[0]), __builtin_bit_cast(float, (int)r[1]));
+}
+__device__ __forceinline__ float pair_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(int, v),
+                                                  __builtin_bit_cast(int, v), false, false);
+  return __builtin_bit_cast(float, (int)r[0]) + __builtin_bit_cast(float, (int)r[1]);
+}
+
+// Lazy rescaling: a row's reference max moves only when a tile's max exceeds
+// it by more than this many binary orders of magnitude, so exp2 arguments stay
+// <= kRescaleLog2 (weights <= 256, well inside the fp16/bf16 range) and the
+// output accumulator is rescaled only on those rare tiles.  The result is the
+// same softmax; only rounding differs.
+constexpr float kRescaleLog2 = 8.f;
 
 template <int DT, int D>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
@@ -128,7 +155,8 @@ void attn_tile_kernel(AttnParams p) {
   __shared__ __attribute__((aligned(16))) uint16_t lds[2 * (KTILE + VTILE) + 2 * XCH];
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63, lr = lane & 31, lg = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar registers
+  const int lane = tid & 63, lr = lane & 31, lg = lane >> 5;
   const int rb = wave % RB;  // this wave's 32-row block
   const int dh = wave / RB;  // this wave's slice of the head dimension
 
@@ -187,8 +215,38 @@ void attn_tile_kernel(AttnParams p) {
   for (int db = 0; db < DB; ++db)
 #pragma unroll
     for (int j = 0; j < 16; ++j) o[db][j] = 0.f;
-  float m_run = -INFINITY;  // running max of raw scores for this row
-  float l_run = 0.f;        // this lane's share of the running sum
+  float m_ref = -INFINITY;  // reference max of this row's raw scores (moves lazily)
+  float l_run = 0.f;        // this lane's share of the row's weight sum
+
+  // ---- per-lane LDS operand offsets (elements), loop invariant -------------
+  // K operand (key row kb*32 + lr, 16-byte chunk 2 dc + lg of this wave's d
+  // slice): with r = lr & 15 the swizzled chunk is
+  //   (lg ^ (r & 1)) + 2 ((dc & 8) | ((dc & 7) ^ (r >> 1)))
+  // so eight per-lane offsets plus compile-time immediates cover all (kb, dc)
+  int koff[8];
+  {
+    const int r = lr & 15;
+    const int base = lr * D + dh * DH + 8 * (lg ^ (r & 1));
+#pragma unroll
+    for (int j = 0; j < 8; ++j) koff[j] = base + 16 * (j ^ (r >> 1));
+  }
+  // V^T operand (row d = dh*DH + db*32 + lr, keys 16 kh + 8 lg .. +7): its
+  // 16-byte chunk is rotated by vrot(d), a function of the lane and, at
+  // D = 256, of db & 1
+  constexpr int NU2 = UPR / 2;  // 16-byte chunk positions per V^T row
+  int voff[NU2];
+  {
+    const int rr = (D == 512) ? (((lr >> 3) + (lr >> 1)) & 3) : (lr >> 3);
+#pragma unroll
+    for (int j = 0; j < NU2; ++j) voff[j] = (dh * DH + lr) * VROW + 8 * ((j + lg + rr) & (NU2 - 1));
+  }
+  auto kaddr = [&](int kb, int dc) {  // element offset inside a K tile
+    return koff[dc & 7] + 16 * (dc & 8) + kb * 32 * D;
+  };
+  auto vaddr = [&](int kh, int db) {  // element offset inside a V^T tile
+    const int j = (2 * kh + (D == 256 ? 4 * (db & 1) : 0)) & (NU2 - 1);
+    return voff[j] + db * 32 * VROW;
+  };
 
   // ---- tile staging ------------------------------------------------------
   // K: direct global->LDS loads, 1 KiB per wave instruction (lane l writes
@@ -211,24 +269,41 @@ void attn_tile_kernel(AttnParams p) {
   auto load_tile = [&](int t, int buf) {
     const int ts = t * BN;
     uint16_t* kl = lds + buf * (KTILE + VTILE);
-#pragma unroll
-    for (int n = 0; n < KLOADS; ++n) {
+    const uint16_t* kt = kg + (size_t)ts * D;  // tile bases: uniform
+    const uint16_t* vt = vg + (size_t)ts * D;
+    const int nrow = p.kL - ts;                // key rows of this tile inside kL
+    auto kload = [&](int n, bool clamp) {
       const int cb = wave * KLOADS + n;  // 1 KiB block of the tile
       const int row = cb * (64 / ROWCH) + lane / ROWCH;
       const int pch = lane % ROWCH;      // chunk position this lane writes
       const int c = pch ^ (row & 15);    // the K chunk that belongs there
-      const int key = min(ts + row, p.kL - 1);
-      load_lds16(kg + (size_t)key * D + c * 8, kl + cb * 512);
-    }
+      const int r = clamp ? min(row, nrow - 1) : row;
+      load_lds16(kt, (uint32_t)(r * D + c * 8) * 2u, kl + cb * 512);
+    };
+    if (nrow >= BN) {
 #pragma unroll
-    for (int n = 0; n < VBLK_PER; ++n) {
-      int kq, d8;
-      vblock(n, kq, d8);
+      for (int n = 0; n < KLOADS; ++n) kload(n, false);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int key = ts + kq * 4 + r;
-        vst[n][r] = (key < p.kL) ? *(const uint4*)(vg + (size_t)key * D + d8 * 8)
-                                 : make_uint4(0, 0, 0, 0);
+      for (int n = 0; n < VBLK_PER; ++n) {
+        int kq, d8;
+        vblock(n, kq, d8);
+        const uint32_t off = (uint32_t)(kq * 4 * D + d8 * 8);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) vst[n][r] = *(const uint4*)(vt + off + r * D);
+      }
+    } else {  // the last, partial tile: clamp K rows, zero V rows past kL
+#pragma unroll
+      for (int n = 0; n < KLOADS; ++n) kload(n, true);
+#pragma unroll
+      for (int n = 0; n < VBLK_PER; ++n) {
+        int kq, d8;
+        vblock(n, kq, d8);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int row = kq * 4 + r;
+          const uint4 x = *(const uint4*)(vt + (uint32_t)(min(row, nrow - 1) * D + d8 * 8));
+          vst[n][r] = row < nrow ? x : make_uint4(0, 0, 0, 0);
+        }
       }
     }
   };
@@ -247,10 +322,10 @@ void attn_tile_kernel(AttnParams p) {
       for (int c = 0; c < 4; ++c) {
         const int d = d8 * 8 + 2 * c;
         uint2 even, odd;  // (key0,key1),(key2,key3) of column d and of column d+1
-        even.x = (w[0][c] & 0xffffu) | (w[1][c] << 16);
-        even.y = (w[2][c] & 0xffffu) | (w[3][c] << 16);
-        odd.x = (w[0][c] >> 16) | (w[1][c] & 0xffff0000u);
-        odd.y = (w[2][c] >> 16) | (w[3][c] & 0xffff0000u);
+        even.x = __builtin_amdgcn_perm(w[1][c], w[0][c], 0x05040100u);  // low halves
+        even.y = __builtin_amdgcn_perm(w[3][c], w[2][c], 0x05040100u);
+        odd.x = __builtin_amdgcn_perm(w[1][c], w[0][c], 0x07060302u);   // high halves
+        odd.y = __builtin_amdgcn_perm(w[3][c], w[2][c], 0x07060302u);
         *(uint2*)(vl + d * VROW + ((unit + vrot<D>(d)) % UPR) * 4) = even;
         *(uint2*)(vl + (d + 1) * VROW + ((unit + vrot<D>(d + 1)) % UPR) * 4) = odd;
       }
@@ -284,12 +359,7 @@ void attn_tile_kernel(AttnParams p) {
       for (int j = 0; j < 16; ++j) s[kb][j] = 0.f;
     if (!skip) {
       constexpr int NQK = KB * DC, PF = 4;
-      const int c0 = dh * (DH / 8) + lg;
-      auto kread = [&](int n) {
-        const int kb = n % KB, dc = n / KB;
-        const int row = kb * 32 + lr;
-        return *(const uint4*)(kl + row * D + (((c0 + 2 * dc) ^ (row & 15)) << 3));
-      };
+      auto kread = [&](int n) { return *(const uint4*)(kl + kaddr(n % KB, n / KB)); };
       uint4 a[PF];
 #pragma unroll
       for (int i = 0; i < PF; ++i) a[i] = kread(i);
@@ -344,11 +414,13 @@ void attn_tile_kernel(AttnParams p) {
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
         for (int j = 0; j < 16; ++j) mx = fmaxf(mx, s[kb][j]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_new = fmaxf(m_run, mx);
-      const float msc = (m_new == -INFINITY) ? 0.f : m_new * sl2;
-      // alpha rescales what was accumulated so far; nothing was while m_run = -inf
-      const float alpha = (m_run == -INFINITY) ? 0.f : fast_exp2((m_run - m_new) * sl2);
+      mx = pair_max(mx);
+      // move the reference max only when this tile's max is far above it
+      const bool upd = mx * sl2 > m_ref * sl2 + kRescaleLog2;
+      const float alpha =
+          upd ? ((m_ref == -INFINITY) ? 0.f : fast_exp2((m_ref - mx) * sl2)) : 1.f;
+      m_ref = upd ? mx : m_ref;
+      const float msc = (m_ref == -INFINITY) ? 0.f : m_ref * sl2;
       float psum = 0.f;
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
@@ -359,8 +431,7 @@ void attn_tile_kernel(AttnParams p) {
           psum += e;
         }
       l_run = l_run * alpha + psum;
-      m_run = m_new;
-      // x * 1 == x: skip the rescale when no row of the wave changed its max
+      // x * 1 == x: skip the rescale when no row of the wave moved its reference
       if (__any(alpha != 1.f)) {
 #pragma unroll
         for (int db = 0; db < DB; ++db)
@@ -380,11 +451,7 @@ void attn_tile_kernel(AttnParams p) {
         pb[kh].w = Elem<DT>::pack2(s[kb][8 * h + 6], s[kb][8 * h + 7]);
       }
       constexpr int NPV = KB * 2 * DB, PF = 4;
-      auto vread = [&](int n) {
-        const int kh = n / DB, db = n % DB;
-        const int d = dh * DH + db * 32 + lr;
-        return *(const uint4*)(vl + d * VROW + (((2 * (kh * 2 + lg)) + vrot<D>(d)) % UPR) * 4);
-      };
+      auto vread = [&](int n) { return *(const uint4*)(vl + vaddr(n / DB, n % DB)); };
       uint4 bv[PF];
 #pragma unroll
       for (int i = 0; i < PF; ++i) bv[i] = vread(i);
@@ -403,7 +470,7 @@ void attn_tile_kernel(AttnParams p) {
   }
 
   // ---- epilogue ---------------------------------------------------------
-  const float lsum = l_run + __shfl_xor(l_run, 32);
+  const float lsum = pair_sum(l_run);
   if (!valid) return;
   const size_t orow = (size_t)(b * p.Hq + hq) * p.qL + qi;
   if (!p.partials) {
@@ -431,7 +498,7 @@ void attn_tile_kernel(AttnParams p) {
             make_float4(o[db][4 * q4 + 0], o[db][4 * q4 + 1], o[db][4 * q4 + 2], o[db][4 * q4 + 3]);
       }
     if (lg == 0 && dh == 0) {
-      p.part_ml[prow * 2 + 0] = (m_run == -INFINITY) ? -INFINITY : m_run * sl2;
+      p.part_ml[prow * 2 + 0] = (m_ref == -INFINITY) ? -INFINITY : m_ref * sl2;
       p.part_ml[prow * 2 + 1] = lsum;
     }
   }
