@@ -63,25 +63,18 @@ struct Elem<1> {  // bfloat16
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// Position of key quad b4 (keys 4*b4 .. 4*b4+3 of a 16-key group) in the V^T
-// tile.  Quads are stored in the order 0, 2, 1, 3 so that the 8 keys one lane
-// feeds to a P.V MFMA (quads lg and lg + 2 of a group, as the S^T accumulator
-// layout hands them out) are 16 contiguous bytes.
-__device__ __forceinline__ int quad_slot(int b4) { return ((b4 & 1) << 1) | (b4 >> 1); }
-
-// Rotation, in 8-byte units (always even, so 16-byte chunks stay whole), of
-// V^T row d, chosen by measuring candidate layouts (padding x rotation) for
-// the 128-bit operand reads and the 64-bit transposed stores.
-template <int D>
-__device__ __forceinline__ int vrot(int d) {
-  if constexpr (D == 512) return 2 * (((d >> 3) + (d >> 1)) & 3);
-  else return 2 * ((d >> 3) & 7);
+// Transposing LDS read (ds_read_b64_tr_b16).  In each 16-lane group, source
+// lane a + 4 t (a, t in 0..3) names 4 consecutive 16-bit elements of row t
+// of a 4-row block; result lane 4 a' + b' receives element b' of the source
+// lanes a' + 4 t for t = 0..3.  So when source lane a + 4 t points at V row
+// (key0 + t), columns d0 + 4 a .. + 3, result lane j of the group holds keys
+// key0 .. key0 + 3 of column d0 + j: a V^T operand slice, read straight from
+// the key-major V tile.
+typedef short short4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) short4_t lds_short4_t;
+__device__ __forceinline__ uint2 read_tr(const uint16_t* p) {
+  return __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4_t*)p));
 }
-// Elements per V^T row: 64 keys padded to 192 bytes at D = 256 (with the
-// rotation above, the measured fastest layout for both the operand reads and
-// the transposed stores); 32 unpadded keys at D = 512, where LDS is full.
-template <int D>
-constexpr int vrow() { return D == 512 ? 32 : 96; }
 
 // One 16-byte-per-lane direct global->LDS load from sbase + voff bytes
 // (sbase uniform, voff per lane): lane l's 16 bytes land at lds + 16 l.
@@ -137,20 +130,16 @@ void attn_tile_kernel(AttnParams p) {
   constexpr int BM = block_rows(D);   // rows per workgroup
   constexpr int BN = tile_keys(D);
   constexpr int ROWCH = D / 8;        // 16-byte chunks per K row
-  constexpr int UPR = BN / 4;         // 8-byte units (4 keys) per V^T row
   constexpr int KTILE = BN * D;       // K tile: rows of D elements, chunks XOR-swizzled
-  constexpr int VROW = vrow<D>();     // elements per V^T row
-  constexpr int VTILE = D * VROW;     // V^T tile: rows of BN keys, units rotated per row
+  constexpr int VTILE = BN * D;       // V tile: key rows of D elements, chunks swizzled
   constexpr int DC = DH / 16;         // MFMA steps over this wave's d in S^T
   constexpr int DB = DH / 32;         // 32-wide d blocks of this wave's O^T
   constexpr int KB = BN / 32;         // 32-key blocks of S^T
   constexpr int KLOADS = BN * D * 2 / 1024 / kWaves;  // 1 KiB direct loads per wave
-  constexpr int VBLK_PER = (BN / 4) * (D / 8) / 256;  // 4-key x 8-d V blocks per thread
   constexpr int XCH = DS > 1 ? kWaves * 64 * 16 : 0;  // floats: partial-score exchange
   static_assert(BM == RB * kRowsPerWave, "row blocks");
   static_assert(KLOADS * kWaves * 1024 == BN * D * 2, "K loads must cover the tile");
   static_assert(ROWCH <= 64 && 64 % ROWCH == 0, "a K row must fit one wave load");
-  static_assert(VBLK_PER * 256 * 32 == BN * D, "V staging must cover the tile");
 
   __shared__ __attribute__((aligned(16))) uint16_t lds[2 * (KTILE + VTILE) + 2 * XCH];
 
@@ -230,111 +219,58 @@ void attn_tile_kernel(AttnParams p) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) koff[j] = base + 16 * (j ^ (r >> 1));
   }
-  // V^T operand (row d = dh*DH + db*32 + lr, keys 16 kh + 8 lg .. +7): its
-  // 16-byte chunk is rotated by vrot(d), a function of the lane and, at
-  // D = 256, of db & 1
-  constexpr int NU2 = UPR / 2;  // 16-byte chunk positions per V^T row
-  int voff[NU2];
+  // V^T operand by transposing reads of the key-major V tile.  Lane l
+  // (group g = l / 16, a = l % 4, t = (l % 16) / 4) points at key
+  // 16 kh + 8 h + kq, kq = 4 (g / 2) + t, columns dh*DH + 32 db + 16 (g & 1)
+  // + 4 a; half h = 0, 1 give the MFMA k slots 0-3 and 4-7, i.e. keys
+  // 16 kh + 4 lg + 0..3 and 16 kh + 8 + 4 lg + 0..3, as P holds them.  V
+  // rows store 16-byte chunk c at c ^ ((key & 7) << 2); key & 7 == kq, so
+  // the swizzle only flips bits 5-7 of the column offset: db ^ kq.
+  int vlane;
   {
-    const int rr = (D == 512) ? (((lr >> 3) + (lr >> 1)) & 3) : (lr >> 3);
-#pragma unroll
-    for (int j = 0; j < NU2; ++j) voff[j] = (dh * DH + lr) * VROW + 8 * ((j + lg + rr) & (NU2 - 1));
+    const int g = lane >> 4, kq = 4 * (g >> 1) + ((lane >> 2) & 3);
+    vlane = kq * D + dh * DH + 32 * kq + 16 * (g & 1) + 4 * (lane & 3);
   }
   auto kaddr = [&](int kb, int dc) {  // element offset inside a K tile
     return koff[dc & 7] + 16 * (dc & 8) + kb * 32 * D;
   };
-  auto vaddr = [&](int kh, int db) {  // element offset inside a V^T tile
-    const int j = (2 * kh + (D == 256 ? 4 * (db & 1) : 0)) & (NU2 - 1);
-    return voff[j] + db * 32 * VROW;
+  auto vaddr = [&](int kh, int db) {  // element offset inside a V tile (half 0)
+    return (vlane ^ (32 * db)) + 16 * kh * D;
   };
 
   // ---- tile staging ------------------------------------------------------
-  // K: direct global->LDS loads, 1 KiB per wave instruction (lane l writes
-  // bytes 16 l .. 16 l + 15 of it).  Chunk c of key row r is stored at chunk
-  // position c ^ (r & 15), so the 32 rows one MFMA operand read touches fall
-  // in distinct banks.  Rows past kL load row kL - 1 (those keys are masked).
-  // V: registers, written transposed (V^T, d-major): each thread owns 4-key x
-  // 8-d blocks.  The 8-byte units (4 keys) of every V^T row are in the key
-  // quad order 0, 2, 1, 3 of each 16-key group, then rotated by vrot(d) units,
-  // so that both the transposed stores (32 lanes on 8 rows 8 apart) and the
-  // MFMA operand reads (8 lanes on 8 consecutive rows) spread over all banks.
-  uint4 vst[VBLK_PER][4];
-  auto vblock = [&](int n, int& kq, int& d8) {
-    // lanes pair key quads {4a+b, 4a+2+b}: units of opposite parity
-    const int bi = tid + 256 * n;
-    const int c = bi & 1, rest = (bi >> 1) / (D / 8);
-    d8 = (bi >> 1) % (D / 8);
-    kq = 4 * (rest >> 1) + 2 * c + (rest & 1);
-  };
+  // K and V: direct global->LDS loads, 1 KiB per wave instruction (lane l
+  // writes bytes 16 l .. 16 l + 15 of it), key rows of D elements.  In K,
+  // chunk c of row r sits at chunk position c ^ (r & 15), so the 32 rows one
+  // K operand read touches fall in distinct banks; in V at c ^ ((r & 7) << 2),
+  // which spreads the 8 rows x 64 bytes of one transposing read over all
+  // banks.  Rows past kL load row kL - 1: those keys are masked, P is 0.
   auto load_tile = [&](int t, int buf) {
     const int ts = t * BN;
     uint16_t* kl = lds + buf * (KTILE + VTILE);
+    uint16_t* vl = kl + KTILE;
     const uint16_t* kt = kg + (size_t)ts * D;  // tile bases: uniform
     const uint16_t* vt = vg + (size_t)ts * D;
     const int nrow = p.kL - ts;                // key rows of this tile inside kL
-    auto kload = [&](int n, bool clamp) {
+    auto kvload = [&](int n, bool clamp) {
       const int cb = wave * KLOADS + n;  // 1 KiB block of the tile
       const int row = cb * (64 / ROWCH) + lane / ROWCH;
       const int pch = lane % ROWCH;      // chunk position this lane writes
-      const int c = pch ^ (row & 15);    // the K chunk that belongs there
       const int r = clamp ? min(row, nrow - 1) : row;
-      load_lds16(kt, (uint32_t)(r * D + c * 8) * 2u, kl + cb * 512);
+      load_lds16(kt, (uint32_t)(r * D + (pch ^ (row & 15)) * 8) * 2u, kl + cb * 512);
+      load_lds16(vt, (uint32_t)(r * D + (pch ^ ((row & 7) << 2)) * 8) * 2u, vl + cb * 512);
     };
     if (nrow >= BN) {
 #pragma unroll
-      for (int n = 0; n < KLOADS; ++n) kload(n, false);
+      for (int n = 0; n < KLOADS; ++n) kvload(n, false);
+    } else {  // the last, partial tile
 #pragma unroll
-      for (int n = 0; n < VBLK_PER; ++n) {
-        int kq, d8;
-        vblock(n, kq, d8);
-        const uint32_t off = (uint32_t)(kq * 4 * D + d8 * 8);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) vst[n][r] = *(const uint4*)(vt + off + r * D);
-      }
-    } else {  // the last, partial tile: clamp K rows, zero V rows past kL
-#pragma unroll
-      for (int n = 0; n < KLOADS; ++n) kload(n, true);
-#pragma unroll
-      for (int n = 0; n < VBLK_PER; ++n) {
-        int kq, d8;
-        vblock(n, kq, d8);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int row = kq * 4 + r;
-          const uint4 x = *(const uint4*)(vt + (uint32_t)(min(row, nrow - 1) * D + d8 * 8));
-          vst[n][r] = row < nrow ? x : make_uint4(0, 0, 0, 0);
-        }
-      }
-    }
-  };
-  auto store_tile = [&](int buf) {
-    uint16_t* vl = lds + buf * (KTILE + VTILE) + KTILE;
-#pragma unroll
-    for (int n = 0; n < VBLK_PER; ++n) {
-      int kq, d8;
-      vblock(n, kq, d8);
-      const int unit = (kq >> 2) * 4 + quad_slot(kq & 3);
-      const uint32_t w[4][4] = {{vst[n][0].x, vst[n][0].y, vst[n][0].z, vst[n][0].w},
-                                {vst[n][1].x, vst[n][1].y, vst[n][1].z, vst[n][1].w},
-                                {vst[n][2].x, vst[n][2].y, vst[n][2].z, vst[n][2].w},
-                                {vst[n][3].x, vst[n][3].y, vst[n][3].z, vst[n][3].w}};
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const int d = d8 * 8 + 2 * c;
-        uint2 even, odd;  // (key0,key1),(key2,key3) of column d and of column d+1
-        even.x = __builtin_amdgcn_perm(w[1][c], w[0][c], 0x05040100u);  // low halves
-        even.y = __builtin_amdgcn_perm(w[3][c], w[2][c], 0x05040100u);
-        odd.x = __builtin_amdgcn_perm(w[1][c], w[0][c], 0x07060302u);   // high halves
-        odd.y = __builtin_amdgcn_perm(w[3][c], w[2][c], 0x07060302u);
-        *(uint2*)(vl + d * VROW + ((unit + vrot<D>(d)) % UPR) * 4) = even;
-        *(uint2*)(vl + (d + 1) * VROW + ((unit + vrot<D>(d + 1)) % UPR) * 4) = odd;
-      }
+      for (int n = 0; n < KLOADS; ++n) kvload(n, true);
     }
   };
 
   load_tile(t_first, 0);
-  store_tile(0);
-  __builtin_amdgcn_s_waitcnt(0);  // direct K loads have landed in LDS
+  __builtin_amdgcn_s_waitcnt(0);  // direct loads have landed in LDS
   __syncthreads();
 
   const float sl2 = p.sl2;
@@ -451,7 +387,11 @@ void attn_tile_kernel(AttnParams p) {
         pb[kh].w = Elem<DT>::pack2(s[kb][8 * h + 6], s[kb][8 * h + 7]);
       }
       constexpr int NPV = KB * 2 * DB, PF = 4;
-      auto vread = [&](int n) { return *(const uint4*)(vl + vaddr(n / DB, n % DB)); };
+      auto vread = [&](int n) {
+        const uint16_t* a = vl + vaddr(n / DB, n % DB);
+        const uint2 lo = read_tr(a), hi = read_tr(a + 8 * D);
+        return make_uint4(lo.x, lo.y, hi.x, hi.y);
+      };
       uint4 bv[PF];
 #pragma unroll
       for (int i = 0; i < PF; ++i) bv[i] = vread(i);
@@ -464,8 +404,7 @@ void attn_tile_kernel(AttnParams p) {
       }
     }
 
-    if (t < t_last) store_tile(cur ^ 1);
-    __builtin_amdgcn_s_waitcnt(0);  // direct K loads of the next tile have landed
+    __builtin_amdgcn_s_waitcnt(0);  // direct loads of the next tile have landed
     __syncthreads();
   }
 
