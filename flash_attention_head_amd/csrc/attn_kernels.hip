@@ -121,33 +121,57 @@ __device__ __forceinline__ float pair_sum(float v) {
 // same softmax; only rounding differs.
 constexpr float kRescaleLog2 = 8.f;
 
-template <int DT, int D>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void attn_tile_kernel(AttnParams p) {
-  constexpr int DS = d_split(D);      // waves per 32-row block
-  constexpr int DH = D / DS;          // head-dim slice of one wave (256)
-  constexpr int RB = kWaves / DS;     // 32-row blocks per workgroup
-  constexpr int BM = block_rows(D);   // rows per workgroup
-  constexpr int BN = tile_keys(D);
-  constexpr int ROWCH = D / 8;        // 16-byte chunks per K row
-  constexpr int KTILE = BN * D;       // K tile: rows of D elements, chunks XOR-swizzled
-  constexpr int VTILE = BN * D;       // V tile: key rows of D elements, chunks swizzled
-  constexpr int DC = DH / 16;         // MFMA steps over this wave's d in S^T
-  constexpr int DB = DH / 32;         // 32-wide d blocks of this wave's O^T
-  constexpr int KB = BN / 32;         // 32-key blocks of S^T
-  constexpr int KLOADS = BN * D * 2 / 1024 / kWaves;  // 1 KiB direct loads per wave
-  constexpr int XCH = DS > 1 ? kWaves * 64 * 16 : 0;  // floats: partial-score exchange
-  static_assert(BM == RB * kRowsPerWave, "row blocks");
-  static_assert(KLOADS * kWaves * 1024 == BN * D * 2, "K loads must cover the tile");
-  static_assert(ROWCH <= 64 && 64 % ROWCH == 0, "a K row must fit one wave load");
+// Waves are paired: the two waves of a pair own the same 32 query rows and
+// split the work of each K/V tile between them.
+//   D = 256 (8 waves, 2 per SIMD): wave h of a pair computes the scores of
+//     key half h of the 64-key tile over the whole head dimension; the pair
+//     swaps the halves through LDS, so both hold all 64 scores.  For P V
+//     wave h owns output columns [128 h, 128 h + 128).
+//   D = 512 (4 waves, 1 per SIMD): wave h computes the scores of all 32 keys
+//     over columns [256 h, 256 h + 256); the pair swaps the partial scores
+//     and adds them.  For P V wave h owns columns [256 h, 256 h + 256).
+// Scores move between the pair as fp32 bit patterns (and a + b == b + a), so
+// both waves run bitwise identical softmax arithmetic.  Two waves per SIMD at
+// D = 256 let one wave's softmax overlap the other's MFMAs and double the
+// LDS operand throughput a SIMD gets; the split keeps every wave within the
+// 256 registers that two waves per SIMD leave it.
+template <int D>
+struct Geom {
+  static constexpr bool kKeySplit = (D == 256);      // pair splits score keys, else d
+  static constexpr int NW = D == 256 ? 8 : 4;        // waves per workgroup
+  static constexpr int RB = NW / 2;                  // 32-row blocks (wave pairs)
+  static constexpr int BM = RB * kRowsPerWave;       // rows per workgroup
+  static constexpr int BN = tile_keys(D);            // keys per tile
+  static constexpr int KB = BN / 32;                 // 32-key score blocks per tile
+  static constexpr int DQ = 256;                     // Q columns a wave multiplies
+  static constexpr int DC = DQ / 16;                 // score MFMAs per wave per tile
+  static constexpr int DO = D / 2;                   // output columns a wave owns
+  static constexpr int DB = DO / 32;                 // 32-column output blocks
+  static constexpr int ROWCH = D / 8;                // 16-byte chunks per K/V row
+  static constexpr int TILE = BN * D;                // elements of one K or V tile
+  static constexpr int LOADS = TILE * 2 / 1024 / NW; // 1 KiB loads per wave per tile
+  static constexpr int XCH = NW * 64 * 16;           // floats of the score exchange
+  static constexpr int NT = NW * 64;                 // threads
+  static_assert(BM == block_rows(D), "row blocks");
+  static_assert(LOADS * NW * 1024 == TILE * 2, "loads must cover the tile");
+  static_assert(ROWCH <= 64 && 64 % ROWCH == 0, "a K/V row must fit one wave load");
+  static_assert(kKeySplit ? KB == 2 : KB == 1, "pair split");
+};
 
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * (KTILE + VTILE) + 2 * XCH];
+template <int DT, int D>
+__device__ __forceinline__ void attn_tile_body(const AttnParams& p, uint16_t* lds) {
+  using G = Geom<D>;
+  constexpr int NW = G::NW, BM = G::BM, BN = G::BN, KB = G::KB, DC = G::DC, DB = G::DB;
+  constexpr int ROWCH = G::ROWCH, TILE = G::TILE, LOADS = G::LOADS;
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar registers
   const int lane = tid & 63, lr = lane & 31, lg = lane >> 5;
-  const int rb = wave % RB;  // this wave's 32-row block
-  const int dh = wave / RB;  // this wave's slice of the head dimension
+  const int rb = wave >> 1;  // this pair's 32-row block
+  const int h = wave & 1;    // this wave's half of the pair's work
+  const int qd0 = G::kKeySplit ? 0 : h * G::DQ;  // first Q column this wave multiplies
+  const int od0 = h * G::DO;                      // first output column this wave owns
+  const int hk = G::kKeySplit ? h : 0;            // key block whose scores this wave computes
 
   // ---- work item: (b, kv head) x row block x key split -------------------
   const int nheads = p.B * p.Hkv;
@@ -156,7 +180,7 @@ void attn_tile_kernel(AttnParams p) {
   // causal: later row blocks see more keys; dispatch them first
   const int mb = p.causal ? (p.mblocks - 1 - mbr) : mbr;
   const int split = blockIdx.y;
-  const int b = head / p.Hkv, hk = head % p.Hkv;
+  const int b = head / p.Hkv, hkv = head % p.Hkv;
 
   const int row0 = mb * BM;
   const int rows_end = min(p.rows, row0 + BM);
@@ -165,7 +189,7 @@ void attn_tile_kernel(AttnParams p) {
   const int my = wrow0 + lr;
   const bool valid = my < rows_end;
   const int qi = valid ? my / p.G : 0;
-  const int hq = hk * p.G + (valid ? my % p.G : 0);
+  const int hq = hkv * p.G + (valid ? my % p.G : 0);
   const int pos = p.q_offset + qi;
   const int wp_lo = p.q_offset + wrow0 / p.G;
   const int wp_hi = p.q_offset + (min(rows_end, wrow0 + kRowsPerWave) - 1) / p.G;
@@ -183,17 +207,18 @@ void attn_tile_kernel(AttnParams p) {
     }
   }
   if (kbeg >= kend) return;  // whole workgroup: no row has a key in this split
-  const int t_first = kbeg / BN, t_last = (kend - 1) / BN;
+  const int t_first = __builtin_amdgcn_readfirstlane(kbeg / BN);
+  const int t_last = __builtin_amdgcn_readfirstlane((kend - 1) / BN);
 
-  const size_t kv_off = (size_t)(b * p.Hkv + hk) * (size_t)p.kL * D;
+  const size_t kv_off = (size_t)(b * p.Hkv + hkv) * (size_t)p.kL * D;
   const uint16_t* __restrict__ kg = p.k + kv_off;
   const uint16_t* __restrict__ vg = p.v + kv_off;
 
   // ---- Q fragments: B operand of S^T = K Q^T,
-  //      lane (lr, lg) holds d = dh * DH + 16 dc + 8 lg + 0..7 of its row
+  //      lane (lr, lg) holds columns qd0 + 16 dc + 8 lg + 0..7 of its row
   uint4 qf[DC];
   {
-    const uint16_t* qrow = p.q + ((size_t)(b * p.Hq + hq) * p.qL + qi) * D + dh * DH;
+    const uint16_t* qrow = p.q + ((size_t)(b * p.Hq + hq) * p.qL + qi) * D + qd0;
 #pragma unroll
     for (int dc = 0; dc < DC; ++dc)
       qf[dc] = valid ? *(const uint4*)(qrow + dc * 16 + lg * 8) : make_uint4(0, 0, 0, 0);
@@ -208,34 +233,34 @@ void attn_tile_kernel(AttnParams p) {
   float l_run = 0.f;        // this lane's share of the row's weight sum
 
   // ---- per-lane LDS operand offsets (elements), loop invariant -------------
-  // K operand (key row kb*32 + lr, 16-byte chunk 2 dc + lg of this wave's d
-  // slice): with r = lr & 15 the swizzled chunk is
-  //   (lg ^ (r & 1)) + 2 ((dc & 8) | ((dc & 7) ^ (r >> 1)))
-  // so eight per-lane offsets plus compile-time immediates cover all (kb, dc)
+  // K operand (key row 32 hk + lr, 16-byte chunk (qd0 / 8) + 2 dc + lg): with
+  // r = lr & 15 the swizzled chunk is
+  //   qd0 / 8 + (lg ^ (r & 1)) + 2 ((dc & 8) | ((dc & 7) ^ (r >> 1)))
+  // so eight per-lane offsets plus compile-time immediates cover every dc
   int koff[8];
   {
     const int r = lr & 15;
-    const int base = lr * D + dh * DH + 8 * (lg ^ (r & 1));
+    const int base = (32 * hk + lr) * D + qd0 + 8 * (lg ^ (r & 1));
 #pragma unroll
     for (int j = 0; j < 8; ++j) koff[j] = base + 16 * (j ^ (r >> 1));
   }
   // V^T operand by transposing reads of the key-major V tile.  Lane l
   // (group g = l / 16, a = l % 4, t = (l % 16) / 4) points at key
-  // 16 kh + 8 h + kq, kq = 4 (g / 2) + t, columns dh*DH + 32 db + 16 (g & 1)
-  // + 4 a; half h = 0, 1 give the MFMA k slots 0-3 and 4-7, i.e. keys
+  // 16 kh + 8 e + kq, kq = 4 (g / 2) + t, columns od0 + 32 db + 16 (g & 1)
+  // + 4 a; e = 0, 1 give the MFMA k slots 0-3 and 4-7, i.e. keys
   // 16 kh + 4 lg + 0..3 and 16 kh + 8 + 4 lg + 0..3, as P holds them.  V
   // rows store 16-byte chunk c at c ^ ((key & 7) << 2); key & 7 == kq, so
-  // the swizzle only flips bits 5-7 of the column offset: db ^ kq.
+  // the swizzle is an XOR of 32 kq into the column offset, and db enters as
+  // an XOR of 32 db (bits of the offset that nothing else occupies).
   int vlane;
   {
     const int g = lane >> 4, kq = 4 * (g >> 1) + ((lane >> 2) & 3);
-    vlane = kq * D + dh * DH + 32 * kq + 16 * (g & 1) + 4 * (lane & 3);
+    vlane = kq * D + (od0 ^ (32 * kq)) + 16 * (g & 1) + 4 * (lane & 3);
   }
-  auto kaddr = [&](int kb, int dc) {  // element offset inside a K tile
-    return koff[dc & 7] + 16 * (dc & 8) + kb * 32 * D;
-  };
-  auto vaddr = [&](int kh, int db) {  // element offset inside a V tile (half 0)
-    return (vlane ^ (32 * db)) + 16 * kh * D;
+  auto kaddr = [&](int dc) { return koff[dc & 7] + 16 * (dc & 8); };
+  // score block kb of this wave holds key block kb ^ hk of the tile
+  auto vaddr = [&](int kh, int db) {
+    return (vlane ^ (32 * db)) + 16 * D * (2 * ((kh >> 1) ^ hk) + (kh & 1));
   };
 
   // ---- tile staging ------------------------------------------------------
@@ -247,27 +272,29 @@ void attn_tile_kernel(AttnParams p) {
   // banks.  Rows past kL load row kL - 1: those keys are masked, P is 0.
   auto load_tile = [&](int t, int buf) {
     const int ts = t * BN;
-    uint16_t* kl = lds + buf * (KTILE + VTILE);
-    uint16_t* vl = kl + KTILE;
+    uint16_t* kl = lds + buf * (2 * TILE);
+    uint16_t* vl = kl + TILE;
     const uint16_t* kt = kg + (size_t)ts * D;  // tile bases: uniform
     const uint16_t* vt = vg + (size_t)ts * D;
     const int nrow = p.kL - ts;                // key rows of this tile inside kL
     auto kvload = [&](int n, bool clamp) {
-      const int cb = wave * KLOADS + n;  // 1 KiB block of the tile
+      const int cb = wave * LOADS + n;  // 1 KiB block of the tile
       const int row = cb * (64 / ROWCH) + lane / ROWCH;
-      const int pch = lane % ROWCH;      // chunk position this lane writes
+      const int pch = lane % ROWCH;     // chunk position this lane writes
       const int r = clamp ? min(row, nrow - 1) : row;
       load_lds16(kt, (uint32_t)(r * D + (pch ^ (row & 15)) * 8) * 2u, kl + cb * 512);
       load_lds16(vt, (uint32_t)(r * D + (pch ^ ((row & 7) << 2)) * 8) * 2u, vl + cb * 512);
     };
     if (nrow >= BN) {
 #pragma unroll
-      for (int n = 0; n < KLOADS; ++n) kvload(n, false);
+      for (int n = 0; n < LOADS; ++n) kvload(n, false);
     } else {  // the last, partial tile
 #pragma unroll
-      for (int n = 0; n < KLOADS; ++n) kvload(n, true);
+      for (int n = 0; n < LOADS; ++n) kvload(n, true);
     }
   };
+
+  float* xch = (float*)(lds + 4 * TILE);  // score exchange: 16 floats per lane per wave
 
   load_tile(t_first, 0);
   __builtin_amdgcn_s_waitcnt(0);  // direct loads have landed in LDS
@@ -279,59 +306,56 @@ void attn_tile_kernel(AttnParams p) {
     if (t < t_last) load_tile(t + 1, cur ^ 1);
 
     const int ts = t * BN, te = ts + BN - 1;
-    // wave-uniform; equal for the DS waves that share a row block
+    // uniform over the pair
     const bool skip = !wave_active || (p.causal && ts > wp_hi) ||
                       (p.window > 0 && te < wp_lo - p.window + 1);
-    const uint16_t* kl = lds + cur * (KTILE + VTILE);
-    const uint16_t* vl = kl + KTILE;
+    const uint16_t* kl = lds + cur * (2 * TILE);
+    const uint16_t* vl = kl + TILE;
 
-    // S^T = K Q^T over this wave's d slice: the KB accumulator chains are
-    // interleaved (consecutive MFMAs are independent) and K operands are read
-    // PF MFMAs ahead; the scheduling barriers keep that order
+    // this wave's 32 x 32 score block, S^T = K Q^T over its DQ columns, with
+    // the K operands read PF MFMAs ahead (the scheduling barriers keep it)
     f32x16_t s[KB];
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
       for (int j = 0; j < 16; ++j) s[kb][j] = 0.f;
     if (!skip) {
-      constexpr int NQK = KB * DC, PF = 4;
-      auto kread = [&](int n) { return *(const uint4*)(kl + kaddr(n % KB, n / KB)); };
+      constexpr int PF = 4;
+      auto kread = [&](int dc) { return *(const uint4*)(kl + kaddr(dc)); };
       uint4 a[PF];
 #pragma unroll
       for (int i = 0; i < PF; ++i) a[i] = kread(i);
 #pragma unroll
-      for (int n = 0; n < NQK; ++n) {
-        const uint4 cur_a = a[n % PF];
-        if (n + PF < NQK) a[n % PF] = kread(n + PF);
-        s[n % KB] = Elem<DT>::mfma(cur_a, qf[n / KB], s[n % KB]);
+      for (int dc = 0; dc < DC; ++dc) {
+        const uint4 cur_a = a[dc % PF];
+        if (dc + PF < DC) a[dc % PF] = kread(dc + PF);
+        s[0] = Elem<DT>::mfma(cur_a, qf[dc], s[0]);
         __builtin_amdgcn_sched_barrier(0);
       }
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4)
+        *(float4*)(xch + (wave * 4 + q4) * 256 + lane * 4) =
+            make_float4(s[0][4 * q4 + 0], s[0][4 * q4 + 1], s[0][4 * q4 + 2], s[0][4 * q4 + 3]);
     }
-    if constexpr (DS > 1) {
-      // the two waves of a row block hold the scores of the two halves of d:
-      // swap them through LDS and add (a + b == b + a, so both waves end up
-      // with bitwise identical scores and run identical softmax arithmetic)
-      float* xch = (float*)(lds + 2 * (KTILE + VTILE));
-      if (!skip) {
+    __syncthreads();
+    if (!skip) {
+      const float* px = xch + (wave ^ 1) * 4 * 256 + lane * 4;  // the partner's block
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4)
-          *(float4*)(xch + (wave * 4 + q4) * 256 + lane * 4) =
-              make_float4(s[0][4 * q4 + 0], s[0][4 * q4 + 1], s[0][4 * q4 + 2], s[0][4 * q4 + 3]);
-      }
-      __syncthreads();
-      if (!skip) {
-        const int partner = wave ^ RB;
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          const float4 x = *(const float4*)(xch + (partner * 4 + q4) * 256 + lane * 4);
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const float4 x = *(const float4*)(px + q4 * 256);
+        if constexpr (G::kKeySplit) {  // the other key half
+          s[1][4 * q4 + 0] = x.x;
+          s[1][4 * q4 + 1] = x.y;
+          s[1][4 * q4 + 2] = x.z;
+          s[1][4 * q4 + 3] = x.w;
+        } else {  // the other half of the columns
           s[0][4 * q4 + 0] += x.x;
           s[0][4 * q4 + 1] += x.y;
           s[0][4 * q4 + 2] += x.z;
           s[0][4 * q4 + 3] += x.w;
         }
       }
-    }
-    if (!skip) {
+
       const bool full = (te < p.kL) && (!p.causal || te <= wp_lo) &&
                         (p.window == 0 || ts >= wp_hi - p.window + 1);
       if (!full) {
@@ -339,7 +363,7 @@ void attn_tile_kernel(AttnParams p) {
         for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
           for (int j = 0; j < 16; ++j) {
-            const int key = ts + kb * 32 + 8 * (j >> 2) + 4 * lg + (j & 3);
+            const int key = ts + 32 * (kb ^ hk) + 8 * (j >> 2) + 4 * lg + (j & 3);
             const bool vis = key < p.kL && (!p.causal || key <= pos) &&
                              (p.window == 0 || pos - key < p.window);
             s[kb][j] = vis ? s[kb][j] : -INFINITY;
@@ -357,15 +381,21 @@ void attn_tile_kernel(AttnParams p) {
           upd ? ((m_ref == -INFINITY) ? 0.f : fast_exp2((m_ref - mx) * sl2)) : 1.f;
       m_ref = upd ? mx : m_ref;
       const float msc = (m_ref == -INFINITY) ? 0.f : m_ref * sl2;
-      float psum = 0.f;
+      // per-block sums, added last: the pair holds the blocks in opposite
+      // order and a + b == b + a, so both get the same total
+      float ps[KB];
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
+      for (int kb = 0; kb < KB; ++kb) {
+        ps[kb] = 0.f;
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
           const float e = fast_exp2(s[kb][j] * sl2 - msc);
           s[kb][j] = e;
-          psum += e;
+          ps[kb] += e;
         }
+      }
+      float psum = ps[0];
+      if constexpr (KB == 2) psum = ps[0] + ps[1];
       l_run = l_run * alpha + psum;
       // x * 1 == x: skip the rescale when no row of the wave moved its reference
       if (__any(alpha != 1.f)) {
@@ -375,21 +405,21 @@ void attn_tile_kernel(AttnParams p) {
           for (int j = 0; j < 16; ++j) o[db][j] *= alpha;
       }
 
-      // O^T += V^T P^T over this wave's d slice: KB * 2 key halves x DB d
-      // blocks, V^T operands read two MFMAs ahead
+      // O^T += V^T P^T over this wave's output columns: KB * 2 key halves x
+      // DB column blocks, V^T operands read PF MFMAs ahead
       uint4 pb[KB * 2];
 #pragma unroll
       for (int kh = 0; kh < KB * 2; ++kh) {
-        const int kb = kh >> 1, h = kh & 1;
-        pb[kh].x = Elem<DT>::pack2(s[kb][8 * h + 0], s[kb][8 * h + 1]);
-        pb[kh].y = Elem<DT>::pack2(s[kb][8 * h + 2], s[kb][8 * h + 3]);
-        pb[kh].z = Elem<DT>::pack2(s[kb][8 * h + 4], s[kb][8 * h + 5]);
-        pb[kh].w = Elem<DT>::pack2(s[kb][8 * h + 6], s[kb][8 * h + 7]);
+        const int kb = kh >> 1, e = kh & 1;
+        pb[kh].x = Elem<DT>::pack2(s[kb][8 * e + 0], s[kb][8 * e + 1]);
+        pb[kh].y = Elem<DT>::pack2(s[kb][8 * e + 2], s[kb][8 * e + 3]);
+        pb[kh].z = Elem<DT>::pack2(s[kb][8 * e + 4], s[kb][8 * e + 5]);
+        pb[kh].w = Elem<DT>::pack2(s[kb][8 * e + 6], s[kb][8 * e + 7]);
       }
       constexpr int NPV = KB * 2 * DB, PF = 4;
       auto vread = [&](int n) {
-        const uint16_t* a = vl + vaddr(n / DB, n % DB);
-        const uint2 lo = read_tr(a), hi = read_tr(a + 8 * D);
+        const uint16_t* va = vl + vaddr(n / DB, n % DB);
+        const uint2 lo = read_tr(va), hi = read_tr(va + 8 * D);
         return make_uint4(lo.x, lo.y, hi.x, hi.y);
       };
       uint4 bv[PF];
@@ -414,7 +444,7 @@ void attn_tile_kernel(AttnParams p) {
   const size_t orow = (size_t)(b * p.Hq + hq) * p.qL + qi;
   if (!p.partials) {
     const float inv = 1.0f / lsum;
-    uint16_t* dst = p.out + orow * D + dh * DH;
+    uint16_t* dst = p.out + orow * D + od0;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -427,7 +457,7 @@ void attn_tile_kernel(AttnParams p) {
       }
   } else {
     const size_t prow = orow * p.nsplit + split;
-    float* dst = p.part_o + prow * D + dh * DH;
+    float* dst = p.part_o + prow * D + od0;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -436,11 +466,426 @@ void attn_tile_kernel(AttnParams p) {
         *(float4*)(dst + d) =
             make_float4(o[db][4 * q4 + 0], o[db][4 * q4 + 1], o[db][4 * q4 + 2], o[db][4 * q4 + 3]);
       }
-    if (lg == 0 && dh == 0) {
+    if (lg == 0 && h == 0) {
       p.part_ml[prow * 2 + 0] = (m_ref == -INFINITY) ? -INFINITY : m_ref * sl2;
       p.part_ml[prow * 2 + 1] = lsum;
     }
   }
+}
+
+// ---------------------------------------------------------------------------
+// D = 256: one wave per SIMD, 32 rows x all 256 columns per wave, software
+// pipelined over tiles.  While the MFMAs of S(t+1) = K(t+1) Q^T run, the same
+// wave computes exp / sum / pack of tile t; while the MFMAs of O += P(t) V(t)
+// run, it masks and takes the row max of S(t+1).  MFMAs and the vector work
+// between them are independent, so the matrix unit keeps busy through the
+// softmax.  K and V have separate double buffers, V one tile behind K:
+// iteration t reads K(t+1) and V(t) and loads K(t+2) and V(t+1).
+// ---------------------------------------------------------------------------
+template <int DT>
+__device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* lds) {
+  constexpr int D = 256, NW = 4, BM = 128, BN = 64, KB = 2, DC = 16, DB = 8;
+  constexpr int ROWCH = D / 8, TILE = BN * D, LOADS = TILE * 2 / 1024 / NW;
+  static_assert(BM == block_rows(D) && BN == tile_keys(D), "geometry");
+  static_assert(LOADS == 8, "one K and one V load per wave per 1 KiB block");
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, lr = lane & 31, lg = lane >> 5;
+
+  const int nheads = p.B * p.Hkv;
+  const int head = blockIdx.x % nheads;
+  const int mbr = blockIdx.x / nheads;
+  const int mb = p.causal ? (p.mblocks - 1 - mbr) : mbr;
+  const int split = blockIdx.y;
+  const int b = head / p.Hkv, hkv = head % p.Hkv;
+
+  const int row0 = mb * BM;
+  const int rows_end = min(p.rows, row0 + BM);
+  const int wrow0 = row0 + wave * kRowsPerWave;
+  const bool wave_active = wrow0 < rows_end;
+  const int my = wrow0 + lr;
+  const bool valid = my < rows_end;
+  const int qi = valid ? my / p.G : 0;
+  const int hq = hkv * p.G + (valid ? my % p.G : 0);
+  const int pos = p.q_offset + qi;
+  const int wp_lo = p.q_offset + wrow0 / p.G;
+  const int wp_hi = p.q_offset + (min(rows_end, wrow0 + kRowsPerWave) - 1) / p.G;
+
+  int kbeg = 0, kend = p.kL;
+  {
+    const int bp_lo = p.q_offset + row0 / p.G;
+    const int bp_hi = p.q_offset + (rows_end - 1) / p.G;
+    if (p.causal) kend = min(kend, bp_hi + 1);
+    if (p.window > 0) kbeg = max(0, bp_lo - p.window + 1);
+    if (p.partials) {
+      kbeg = max(kbeg, split * p.split_len);
+      kend = min(kend, (split + 1) * p.split_len);
+    }
+  }
+  if (kbeg >= kend) return;
+  const int t_first = __builtin_amdgcn_readfirstlane(kbeg / BN);
+  const int t_last = __builtin_amdgcn_readfirstlane((kend - 1) / BN);
+
+  const size_t kv_off = (size_t)(b * p.Hkv + hkv) * (size_t)p.kL * D;
+  const uint16_t* __restrict__ kg = p.k + kv_off;
+  const uint16_t* __restrict__ vg = p.v + kv_off;
+
+  uint4 qf[DC];
+  {
+    const uint16_t* qrow = p.q + ((size_t)(b * p.Hq + hq) * p.qL + qi) * D;
+#pragma unroll
+    for (int dc = 0; dc < DC; ++dc)
+      qf[dc] = valid ? *(const uint4*)(qrow + dc * 16 + lg * 8) : make_uint4(0, 0, 0, 0);
+  }
+
+  f32x16_t o[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) o[db][j] = 0.f;
+  float m_ref = -INFINITY;
+  float l_run = 0.f;
+  const float sl2 = p.sl2;
+
+  // LDS operand offsets, as in the paired kernel with the whole head dim
+  int koff[8];
+  {
+    const int r = lr & 15;
+    const int base = lr * D + 8 * (lg ^ (r & 1));
+#pragma unroll
+    for (int j = 0; j < 8; ++j) koff[j] = base + 16 * (j ^ (r >> 1));
+  }
+  int vlane;
+  {
+    const int g = lane >> 4, kq = 4 * (g >> 1) + ((lane >> 2) & 3);
+    vlane = kq * D + 32 * kq + 16 * (g & 1) + 4 * (lane & 3);
+  }
+  uint16_t* const kbuf0 = lds;             // K(t) lives in kbuf0 + (t & 1) * TILE
+  uint16_t* const vbuf0 = lds + 2 * TILE;  // V(t) lives in vbuf0 + (t & 1) * TILE
+
+  // direct loads of one K or V tile (swizzles as in the paired kernel)
+  auto load_tile = [&](const uint16_t* g, int t, uint16_t* buf, bool is_v) {
+    const int ts = t * BN;
+    const uint16_t* gt = g + (size_t)ts * D;
+    const int nrow = p.kL - ts;
+    auto one = [&](int n, bool clamp) {
+      const int cb = wave * LOADS + n;
+      const int row = cb * (64 / ROWCH) + lane / ROWCH;
+      const int pch = lane % ROWCH;
+      const int r = clamp ? min(row, nrow - 1) : row;
+      const int c = is_v ? (pch ^ ((row & 7) << 2)) : (pch ^ (row & 15));
+      load_lds16(gt, (uint32_t)(r * D + c * 8) * 2u, buf + cb * 512);
+    };
+    if (nrow >= BN) {
+#pragma unroll
+      for (int n = 0; n < LOADS; ++n) one(n, false);
+    } else {
+#pragma unroll
+      for (int n = 0; n < LOADS; ++n) one(n, true);
+    }
+  };
+  auto load_k = [&](int t) { load_tile(kg, t, kbuf0 + (t & 1) * TILE, false); };
+  auto load_v = [&](int t) { load_tile(vg, t, vbuf0 + (t & 1) * TILE, true); };
+
+  auto skip_tile = [&](int t) {  // wave-uniform: no row of this wave sees tile t
+    const int ts = t * BN, te = ts + BN - 1;
+    return !wave_active || (p.causal && ts > wp_hi) || (p.window > 0 && te < wp_lo - p.window + 1);
+  };
+  auto full_tile = [&](int t) {  // every key of tile t visible to every row of this wave
+    const int ts = t * BN, te = ts + BN - 1;
+    return (te < p.kL) && (!p.causal || te <= wp_lo) && (p.window == 0 || ts >= wp_hi - p.window + 1);
+  };
+
+  // ---- building blocks (inlined; no scheduling barriers, so that callers
+  //      can interleave them with sched_group_barrier patterns) -------------
+  // S^T = K(t) Q^T, K operands read PF MFMAs ahead; the two key-block chains
+  // alternate
+  auto qk = [&](f32x16_t (&s)[KB], const uint16_t* kl) {
+    constexpr int NQK = KB * DC, PF = 4;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) s[kb][j] = 0.f;
+    auto kread = [&](int n) {
+      const int kb = n % KB, dc = n / KB;
+      return *(const uint4*)(kl + koff[dc & 7] + 16 * (dc & 8) + kb * 32 * D);
+    };
+    uint4 a[PF];
+#pragma unroll
+    for (int i = 0; i < PF; ++i) a[i] = kread(i);
+#pragma unroll
+    for (int n = 0; n < NQK; ++n) {
+      const uint4 cur_a = a[n % PF];
+      if (n + PF < NQK) a[n % PF] = kread(n + PF);
+      s[n % KB] = Elem<DT>::mfma(cur_a, qf[n / KB], s[n % KB]);
+    }
+  };
+  // keys of tile t a row may not see -> -inf (branch-free)
+  auto mask = [&](f32x16_t (&s)[KB], int t) {
+    const int ts = t * BN;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int key = ts + kb * 32 + 8 * (j >> 2) + 4 * lg + (j & 3);
+        const bool vis = key < p.kL && (!p.causal || key <= pos) && (p.window == 0 || pos - key < p.window);
+        s[kb][j] = vis ? s[kb][j] : -INFINITY;
+      }
+  };
+  // row max of S(t) -> reference update; returns the factor the running
+  // output and sum take before tile t is added
+  auto row_max = [&](f32x16_t (&s)[KB]) {
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) mx = fmaxf(mx, s[kb][j]);
+    mx = pair_max(mx);
+    const bool upd = mx * sl2 > m_ref * sl2 + kRescaleLog2;
+    const float alpha = upd ? ((m_ref == -INFINITY) ? 0.f : fast_exp2((m_ref - mx) * sl2)) : 1.f;
+    m_ref = upd ? mx : m_ref;
+    return alpha;
+  };
+  // weights of S(t) against the current reference, their sum, packed P
+  auto weights = [&](f32x16_t (&s)[KB], uint4 (&pb)[KB * 2]) {
+    const float msc = (m_ref == -INFINITY) ? 0.f : m_ref * sl2;
+    float psum = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const float e = fast_exp2(s[kb][j] * sl2 - msc);
+        s[kb][j] = e;
+        psum += e;
+      }
+#pragma unroll
+    for (int kh = 0; kh < KB * 2; ++kh) {
+      const int kb = kh >> 1, e = kh & 1;
+      pb[kh].x = Elem<DT>::pack2(s[kb][8 * e + 0], s[kb][8 * e + 1]);
+      pb[kh].y = Elem<DT>::pack2(s[kb][8 * e + 2], s[kb][8 * e + 3]);
+      pb[kh].z = Elem<DT>::pack2(s[kb][8 * e + 4], s[kb][8 * e + 5]);
+      pb[kh].w = Elem<DT>::pack2(s[kb][8 * e + 6], s[kb][8 * e + 7]);
+    }
+    return psum;
+  };
+  // O^T += V(t)^T P(t)^T, V^T operands by transposing reads, PF MFMAs ahead
+  auto pv = [&](const uint4 (&pb)[KB * 2], const uint16_t* vl) {
+    constexpr int NPV = KB * 2 * DB, PF = 4;
+    auto vread = [&](int n) {
+      const int kh = n / DB, db = n % DB;
+      const uint16_t* va = vl + (vlane ^ (32 * db)) + 16 * kh * D;
+      const uint2 lo = read_tr(va), hi = read_tr(va + 8 * D);
+      return make_uint4(lo.x, lo.y, hi.x, hi.y);
+    };
+    uint4 bv[PF];
+#pragma unroll
+    for (int i = 0; i < PF; ++i) bv[i] = vread(i);
+#pragma unroll
+    for (int n = 0; n < NPV; ++n) {
+      const uint4 cur_b = bv[n % PF];
+      if (n + PF < NPV) bv[n % PF] = vread(n + PF);
+      o[n % DB] = Elem<DT>::mfma(cur_b, pb[n / DB], o[n % DB]);
+    }
+  };
+  auto rescale = [&](float alpha) {  // x * 1 == x: most tiles skip it
+    if (__any(alpha != 1.f)) {
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) o[db][j] *= alpha;
+    }
+  };
+
+  // ---- interleaved regions: slot n issues MFMA n, the operand read for MFMA
+  //      n + PF and element n of the other tile's vector work; the
+  //      scheduling barriers keep that order.
+  // S(t+1) = K(t+1) Q^T  ||  weights, sum and packing of tile t
+  auto qk_weights = [&](f32x16_t (&sn)[KB], const uint16_t* kl, f32x16_t (&sc)[KB],
+                        uint4 (&pb)[KB * 2]) {
+    constexpr int NQK = KB * DC, PF = 4;
+    static_assert(NQK == KB * 16, "one score element per slot");
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) sn[kb][j] = 0.f;
+    auto kread = [&](int n) {
+      const int kb = n % KB, dc = n / KB;
+      return *(const uint4*)(kl + koff[dc & 7] + 16 * (dc & 8) + kb * 32 * D);
+    };
+    const float msc = (m_ref == -INFINITY) ? 0.f : m_ref * sl2;
+    float psum = 0.f;
+    uint4 a[PF];
+#pragma unroll
+    for (int i = 0; i < PF; ++i) a[i] = kread(i);
+#pragma unroll
+    for (int n = 0; n < NQK; ++n) {
+      const uint4 cur_a = a[n % PF];
+      if (n + PF < NQK) a[n % PF] = kread(n + PF);
+      sn[n % KB] = Elem<DT>::mfma(cur_a, qf[n / KB], sn[n % KB]);
+      const int kb = n / 16, j = n % 16;
+      const float e = fast_exp2(sc[kb][j] * sl2 - msc);
+      sc[kb][j] = e;
+      psum += e;
+      if (j & 1) {  // pack the pair (j - 1, j): P half kh = 2 kb + j / 8
+        const uint32_t w = Elem<DT>::pack2(sc[kb][j - 1], e);
+        uint4& q = pb[2 * kb + j / 8];
+        switch ((j % 8) / 2) {
+          case 0: q.x = w; break;
+          case 1: q.y = w; break;
+          case 2: q.z = w; break;
+          default: q.w = w; break;
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // an empty volatile use: the sum is formed here, slot by slot, not sunk
+    // past the next region as a serial chain
+    asm volatile("" ::"v"(psum));
+    return psum;
+  };
+  // O += P(t) V(t)  ||  (mask and) row max of S(t+1)
+  auto pv_max = [&](const uint4 (&pb)[KB * 2], const uint16_t* vl, f32x16_t (&sn)[KB], int tn,
+                    bool masked) {
+    constexpr int NPV = KB * 2 * DB, PF = 4;
+    static_assert(NPV == KB * 16, "one score element per slot");
+    auto vread = [&](int n) {
+      const int kh = n / DB, db = n % DB;
+      const uint16_t* va = vl + (vlane ^ (32 * db)) + 16 * kh * D;
+      const uint2 lo = read_tr(va), hi = read_tr(va + 8 * D);
+      return make_uint4(lo.x, lo.y, hi.x, hi.y);
+    };
+    const int ts = tn * BN;
+    float mx = -INFINITY;
+    uint4 bv[PF];
+#pragma unroll
+    for (int i = 0; i < PF; ++i) bv[i] = vread(i);
+#pragma unroll
+    for (int n = 0; n < NPV; ++n) {
+      const uint4 cur_b = bv[n % PF];
+      if (n + PF < NPV) bv[n % PF] = vread(n + PF);
+      o[n % DB] = Elem<DT>::mfma(cur_b, pb[n / DB], o[n % DB]);
+      const int kb = n / 16, j = n % 16;
+      if (masked) {
+        const int key = ts + kb * 32 + 8 * (j >> 2) + 4 * lg + (j & 3);
+        // bitwise, not short-circuit: straight-line selects
+        const bool vis = (key < p.kL) & (!p.causal | (key <= pos)) & ((p.window == 0) | (pos - key < p.window));
+        sn[kb][j] = vis ? sn[kb][j] : -INFINITY;
+      }
+      mx = fmaxf(mx, sn[kb][j]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    mx = pair_max(mx);
+    const bool upd = mx * sl2 > m_ref * sl2 + kRescaleLog2;
+    const float alpha = upd ? ((m_ref == -INFINITY) ? 0.f : fast_exp2((m_ref - mx) * sl2)) : 1.f;
+    m_ref = upd ? mx : m_ref;
+    return alpha;
+  };
+
+  // ---- prologue: K(t0), V(t0), K(t0 + 1); S(t0) and its row max ------------
+  load_k(t_first);
+  load_v(t_first);
+  if (t_first < t_last) load_k(t_first + 1);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+
+  f32x16_t sA[KB], sB[KB];
+  float alpha_cur = 1.f;
+  if (!skip_tile(t_first)) {
+    qk(sA, kbuf0 + (t_first & 1) * TILE);
+    if (!full_tile(t_first)) mask(sA, t_first);
+    alpha_cur = row_max(sA);
+  }
+  __syncthreads();  // every wave is done with K(t0) before K(t0 + 2) overwrites it
+
+  // one pipelined step: tile t's scores are in sc, tile t + 1's go to sn
+  auto step = [&](int t, f32x16_t (&sc)[KB], f32x16_t (&sn)[KB]) {
+    const bool has_next = t < t_last;
+    if (t + 2 <= t_last) load_k(t + 2);
+    if (has_next) load_v(t + 1);
+    const bool skip_c = skip_tile(t);
+    const bool skip_n = !has_next || skip_tile(t + 1);
+    const uint16_t* kl_n = kbuf0 + ((t + 1) & 1) * TILE;
+    const uint16_t* vl_c = vbuf0 + (t & 1) * TILE;
+    uint4 pb[KB * 2];
+    float alpha_next = 1.f;
+    if (!skip_c && !skip_n) {
+      // the rescale for tile t first (its factor is known since the last
+      // step), so that the interleaved regions are straight-line code
+      rescale(alpha_cur);
+      const float psum = qk_weights(sn, kl_n, sc, pb);
+      l_run = l_run * alpha_cur + psum;
+      if (full_tile(t + 1)) alpha_next = pv_max(pb, vl_c, sn, t + 1, false);
+      else alpha_next = pv_max(pb, vl_c, sn, t + 1, true);
+    } else {
+      if (!skip_c) {
+        const float psum = weights(sc, pb);
+        l_run = l_run * alpha_cur + psum;
+        rescale(alpha_cur);
+        pv(pb, vl_c);
+      }
+      if (!skip_n) {
+        qk(sn, kl_n);
+        if (!full_tile(t + 1)) mask(sn, t + 1);
+        alpha_next = row_max(sn);
+      }
+    }
+    alpha_cur = alpha_next;
+    __builtin_amdgcn_s_waitcnt(0);  // K(t+2), V(t+1) have landed
+    __syncthreads();
+  };
+
+  for (int t = t_first; t <= t_last; t += 2) {
+    step(t, sA, sB);
+    if (t + 1 <= t_last) step(t + 1, sB, sA);
+  }
+
+  // ---- epilogue ---------------------------------------------------------
+  const float lsum = pair_sum(l_run);
+  if (!valid) return;
+  const size_t orow = (size_t)(b * p.Hq + hq) * p.qL + qi;
+  if (!p.partials) {
+    const float inv = 1.0f / lsum;
+    uint16_t* dst = p.out + orow * D;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int d = db * 32 + 8 * q4 + 4 * lg;
+        uint2 w;
+        w.x = Elem<DT>::pack2(o[db][4 * q4 + 0] * inv, o[db][4 * q4 + 1] * inv);
+        w.y = Elem<DT>::pack2(o[db][4 * q4 + 2] * inv, o[db][4 * q4 + 3] * inv);
+        *(uint2*)(dst + d) = w;
+      }
+  } else {
+    const size_t prow = orow * p.nsplit + split;
+    float* dst = p.part_o + prow * D;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int d = db * 32 + 8 * q4 + 4 * lg;
+        *(float4*)(dst + d) =
+            make_float4(o[db][4 * q4 + 0], o[db][4 * q4 + 1], o[db][4 * q4 + 2], o[db][4 * q4 + 3]);
+      }
+    if (lg == 0) {
+      p.part_ml[prow * 2 + 0] = (m_ref == -INFINITY) ? -INFINITY : m_ref * sl2;
+      p.part_ml[prow * 2 + 1] = lsum;
+    }
+  }
+}
+
+template <int DT>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void attn_tile_kernel_d256(AttnParams p) {
+  __shared__ __attribute__((aligned(16))) uint16_t lds[4 * 64 * 256];  // 2 K + 2 V tiles
+  attn_pipe_body<DT>(p, lds);
+}
+template <int DT>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void attn_tile_kernel_d512(AttnParams p) {
+  __shared__ __attribute__((aligned(16))) uint16_t lds[4 * Geom<512>::TILE + 2 * Geom<512>::XCH];
+  attn_tile_body<DT, 512>(p, lds);
 }
 
 // Merge of the per-split partials of each output row, in ascending split
@@ -496,7 +941,10 @@ __global__ __launch_bounds__(256) void combine_kernel(AttnParams p) {
 template <int DT, int D>
 hipError_t launch_attention_t(const AttnParams& p, hipStream_t stream) {
   const dim3 grid((unsigned)(p.B * p.Hkv * p.mblocks), (unsigned)p.nsplit, 1);
-  hipLaunchKernelGGL((attn_tile_kernel<DT, D>), grid, dim3(256), 0, stream, p);
+  if constexpr (D == 256)
+    hipLaunchKernelGGL((attn_tile_kernel_d256<DT>), grid, dim3(256), 0, stream, p);
+  else
+    hipLaunchKernelGGL((attn_tile_kernel_d512<DT>), grid, dim3(Geom<512>::NT), 0, stream, p);
   return hipGetLastError();
 }
 
