@@ -548,14 +548,12 @@ __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* ld
   float l_run = 0.f;
   const float sl2 = p.sl2;
 
-  // LDS operand offsets, as in the paired kernel with the whole head dim
-  int koff[8];
-  {
-    const int r = lr & 15;
-    const int base = lr * D + 8 * (lg ^ (r & 1));
-#pragma unroll
-    for (int j = 0; j < 8; ++j) koff[j] = base + 16 * (j ^ (r >> 1));
-  }
+  // LDS operand offsets.  K (key row 32 kb + lr, chunk 2 dc + lg, stored at
+  // chunk position (2 dc + lg) ^ (lr & 15)): the swizzle flips bits 3-6 of
+  // the element offset, which nothing else occupies, so one per-lane base
+  // and an XOR with 16 (dc & 7) cover every dc.
+  const int kbase = lr * D + 8 * (lg ^ (lr & 1)) + 16 * ((lr & 15) >> 1);
+  auto kaddr = [&](int kb, int dc) { return (kbase ^ (16 * (dc & 7))) + 16 * (dc & 8) + kb * 32 * D; };
   int vlane;
   {
     const int g = lane >> 4, kq = 4 * (g >> 1) + ((lane >> 2) & 3);
@@ -587,11 +585,27 @@ __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* ld
   };
   auto load_k = [&](int t) { load_tile(kg, t, kbuf0 + (t & 1) * TILE, false); };
   auto load_v = [&](int t) { load_tile(vg, t, vbuf0 + (t & 1) * TILE, true); };
-
-  auto skip_tile = [&](int t) {  // wave-uniform: no row of this wave sees tile t
-    const int ts = t * BN, te = ts + BN - 1;
-    return !wave_active || (p.causal && ts > wp_hi) || (p.window > 0 && te < wp_lo - p.window + 1);
+  // one of the LOADS direct loads of a tile, rows clamped branch-free (only
+  // the last tile has rows past kL; their keys are masked), for issuing
+  // inside the MFMA regions: a burst of loads stalls the wave on the memory
+  // pipeline, while one load every few MFMAs keeps it busy in the background
+  // (tile t's data into the buffer of tile tdst: they differ only past the
+  // last tile, where a clamped reload fills a buffer no later step reads)
+  auto load_one = [&](const uint16_t* g, int t, int tdst, bool is_v, int n) {
+    const int ts = t * BN;
+    const int cb = wave * LOADS + n;
+    const int row = cb * (64 / ROWCH) + lane / ROWCH;
+    const int pch = lane % ROWCH;
+    const int r = min(row, p.kL - 1 - ts);
+    const int c = is_v ? (pch ^ ((row & 7) << 2)) : (pch ^ (row & 15));
+    uint16_t* buf = (is_v ? vbuf0 : kbuf0) + (tdst & 1) * TILE;
+    load_lds16(g + (size_t)ts * D, (uint32_t)(r * D + c * 8) * 2u, buf + cb * 512);
   };
+
+  // the keys row `pos` sees form one interval [key_lo, key_hi] (empty if
+  // key_hi < key_lo)
+  const int key_lo = p.window > 0 ? max(0, pos - p.window + 1) : 0;
+  const int key_hi = p.causal ? min(pos, p.kL - 1) : p.kL - 1;
   auto full_tile = [&](int t) {  // every key of tile t visible to every row of this wave
     const int ts = t * BN, te = ts + BN - 1;
     return (te < p.kL) && (!p.causal || te <= wp_lo) && (p.window == 0 || ts >= wp_hi - p.window + 1);
@@ -609,7 +623,7 @@ __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* ld
       for (int j = 0; j < 16; ++j) s[kb][j] = 0.f;
     auto kread = [&](int n) {
       const int kb = n % KB, dc = n / KB;
-      return *(const uint4*)(kl + koff[dc & 7] + 16 * (dc & 8) + kb * 32 * D);
+      return *(const uint4*)(kl + kaddr(kb, dc));
     };
     uint4 a[PF];
 #pragma unroll
@@ -621,17 +635,23 @@ __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* ld
       s[n % KB] = Elem<DT>::mfma(cur_a, qf[n / KB], s[n % KB]);
     }
   };
-  // keys of tile t a row may not see -> -inf (branch-free)
+  // keys of tile t a row may not see -> -inf.  Score element (kb, j) holds
+  // key ts + 4 lg + c with c = 32 kb + 8 (j / 4) + j % 4 a compile-time
+  // constant, so it is visible iff lo4 <= c <= hi4 for two per-tile values.
+  auto vis_bounds = [&](int t, int& lo4, int& hi4) {
+    lo4 = key_lo - t * BN - 4 * lg;
+    hi4 = key_hi - t * BN - 4 * lg;
+  };
+  auto mask_elem = [](float x, int c, int lo4, int hi4) {
+    return ((c >= lo4) & (c <= hi4)) ? x : -INFINITY;
+  };
   auto mask = [&](f32x16_t (&s)[KB], int t) {
-    const int ts = t * BN;
+    int lo4, hi4;
+    vis_bounds(t, lo4, hi4);
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const int key = ts + kb * 32 + 8 * (j >> 2) + 4 * lg + (j & 3);
-        const bool vis = key < p.kL && (!p.causal || key <= pos) && (p.window == 0 || pos - key < p.window);
-        s[kb][j] = vis ? s[kb][j] : -INFINITY;
-      }
+      for (int j = 0; j < 16; ++j) s[kb][j] = mask_elem(s[kb][j], 32 * kb + 8 * (j >> 2) + (j & 3), lo4, hi4);
   };
   // row max of S(t) -> reference update; returns the factor the running
   // output and sum take before tile t is added
@@ -647,47 +667,6 @@ __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* ld
     m_ref = upd ? mx : m_ref;
     return alpha;
   };
-  // weights of S(t) against the current reference, their sum, packed P
-  auto weights = [&](f32x16_t (&s)[KB], uint4 (&pb)[KB * 2]) {
-    const float msc = (m_ref == -INFINITY) ? 0.f : m_ref * sl2;
-    float psum = 0.f;
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const float e = fast_exp2(s[kb][j] * sl2 - msc);
-        s[kb][j] = e;
-        psum += e;
-      }
-#pragma unroll
-    for (int kh = 0; kh < KB * 2; ++kh) {
-      const int kb = kh >> 1, e = kh & 1;
-      pb[kh].x = Elem<DT>::pack2(s[kb][8 * e + 0], s[kb][8 * e + 1]);
-      pb[kh].y = Elem<DT>::pack2(s[kb][8 * e + 2], s[kb][8 * e + 3]);
-      pb[kh].z = Elem<DT>::pack2(s[kb][8 * e + 4], s[kb][8 * e + 5]);
-      pb[kh].w = Elem<DT>::pack2(s[kb][8 * e + 6], s[kb][8 * e + 7]);
-    }
-    return psum;
-  };
-  // O^T += V(t)^T P(t)^T, V^T operands by transposing reads, PF MFMAs ahead
-  auto pv = [&](const uint4 (&pb)[KB * 2], const uint16_t* vl) {
-    constexpr int NPV = KB * 2 * DB, PF = 4;
-    auto vread = [&](int n) {
-      const int kh = n / DB, db = n % DB;
-      const uint16_t* va = vl + (vlane ^ (32 * db)) + 16 * kh * D;
-      const uint2 lo = read_tr(va), hi = read_tr(va + 8 * D);
-      return make_uint4(lo.x, lo.y, hi.x, hi.y);
-    };
-    uint4 bv[PF];
-#pragma unroll
-    for (int i = 0; i < PF; ++i) bv[i] = vread(i);
-#pragma unroll
-    for (int n = 0; n < NPV; ++n) {
-      const uint4 cur_b = bv[n % PF];
-      if (n + PF < NPV) bv[n % PF] = vread(n + PF);
-      o[n % DB] = Elem<DT>::mfma(cur_b, pb[n / DB], o[n % DB]);
-    }
-  };
   auto rescale = [&](float alpha) {  // x * 1 == x: most tiles skip it
     if (__any(alpha != 1.f)) {
 #pragma unroll
@@ -702,7 +681,9 @@ __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* ld
   //      scheduling barriers keep that order.
   // S(t+1) = K(t+1) Q^T  ||  weights, sum and packing of tile t
   auto qk_weights = [&](f32x16_t (&sn)[KB], const uint16_t* kl, f32x16_t (&sc)[KB],
-                        uint4 (&pb)[KB * 2]) {
+                        uint4 (&pb)[KB * 2], int tk, int tkdst, int tv, int tvdst) {
+    // also loads K(tk) and V(tv): the P V region then has the LDS to itself
+    // and the loads have that whole region to land
     constexpr int NQK = KB * DC, PF = 4;
     static_assert(NQK == KB * 16, "one score element per slot");
 #pragma unroll
@@ -711,7 +692,7 @@ __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* ld
       for (int j = 0; j < 16; ++j) sn[kb][j] = 0.f;
     auto kread = [&](int n) {
       const int kb = n % KB, dc = n / KB;
-      return *(const uint4*)(kl + koff[dc & 7] + 16 * (dc & 8) + kb * 32 * D);
+      return *(const uint4*)(kl + kaddr(kb, dc));
     };
     const float msc = (m_ref == -INFINITY) ? 0.f : m_ref * sl2;
     float psum = 0.f;
@@ -723,6 +704,8 @@ __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* ld
       const uint4 cur_a = a[n % PF];
       if (n + PF < NQK) a[n % PF] = kread(n + PF);
       sn[n % KB] = Elem<DT>::mfma(cur_a, qf[n / KB], sn[n % KB]);
+      if (n % 4 == 0) load_one(kg, tk, tkdst, false, n / 4);
+      if (n % 4 == 2) load_one(vg, tv, tvdst, true, n / 4);
       const int kb = n / 16, j = n % 16;
       const float e = fast_exp2(sc[kb][j] * sl2 - msc);
       sc[kb][j] = e;
@@ -746,7 +729,7 @@ __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* ld
   };
   // O += P(t) V(t)  ||  (mask and) row max of S(t+1)
   auto pv_max = [&](const uint4 (&pb)[KB * 2], const uint16_t* vl, f32x16_t (&sn)[KB], int tn,
-                    bool masked) {
+                    bool masked, bool live) {
     constexpr int NPV = KB * 2 * DB, PF = 4;
     static_assert(NPV == KB * 16, "one score element per slot");
     auto vread = [&](int n) {
@@ -755,7 +738,8 @@ __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* ld
       const uint2 lo = read_tr(va), hi = read_tr(va + 8 * D);
       return make_uint4(lo.x, lo.y, hi.x, hi.y);
     };
-    const int ts = tn * BN;
+    int lo4, hi4;
+    vis_bounds(tn, lo4, hi4);
     float mx = -INFINITY;
     uint4 bv[PF];
 #pragma unroll
@@ -766,17 +750,13 @@ __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* ld
       if (n + PF < NPV) bv[n % PF] = vread(n + PF);
       o[n % DB] = Elem<DT>::mfma(cur_b, pb[n / DB], o[n % DB]);
       const int kb = n / 16, j = n % 16;
-      if (masked) {
-        const int key = ts + kb * 32 + 8 * (j >> 2) + 4 * lg + (j & 3);
-        // bitwise, not short-circuit: straight-line selects
-        const bool vis = (key < p.kL) & (!p.causal | (key <= pos)) & ((p.window == 0) | (pos - key < p.window));
-        sn[kb][j] = vis ? sn[kb][j] : -INFINITY;
-      }
+      if (masked) sn[kb][j] = mask_elem(sn[kb][j], 32 * kb + 8 * (j >> 2) + (j & 3), lo4, hi4);
       mx = fmaxf(mx, sn[kb][j]);
       __builtin_amdgcn_sched_barrier(0);
     }
     mx = pair_max(mx);
-    const bool upd = mx * sl2 > m_ref * sl2 + kRescaleLog2;
+    // live == false: the scores were of no tile (the step after the last)
+    const bool upd = live && (mx * sl2 > m_ref * sl2 + kRescaleLog2);
     const float alpha = upd ? ((m_ref == -INFINITY) ? 0.f : fast_exp2((m_ref - mx) * sl2)) : 1.f;
     m_ref = upd ? mx : m_ref;
     return alpha;
@@ -791,53 +771,48 @@ __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* ld
 
   f32x16_t sA[KB], sB[KB];
   float alpha_cur = 1.f;
-  if (!skip_tile(t_first)) {
+  if (wave_active) {
     qk(sA, kbuf0 + (t_first & 1) * TILE);
     if (!full_tile(t_first)) mask(sA, t_first);
     alpha_cur = row_max(sA);
   }
   __syncthreads();  // every wave is done with K(t0) before K(t0 + 2) overwrites it
 
-  // one pipelined step: tile t's scores are in sc, tile t + 1's go to sn
+  // One pipelined step: tile t's scores are in sc, tile t + 1's go to sn.
+  // Straight-line for every tile: a tile no row of this wave sees is masked
+  // like any other (its weights are 0), and in the step after the last tile
+  // the scores of the stale buffer are computed but never used (live ==
+  // false).  Loads past the last tile reload the last tile into a buffer no
+  // later step reads.
   auto step = [&](int t, f32x16_t (&sc)[KB], f32x16_t (&sn)[KB]) {
     const bool has_next = t < t_last;
-    if (t + 2 <= t_last) load_k(t + 2);
-    if (has_next) load_v(t + 1);
-    const bool skip_c = skip_tile(t);
-    const bool skip_n = !has_next || skip_tile(t + 1);
-    const uint16_t* kl_n = kbuf0 + ((t + 1) & 1) * TILE;
-    const uint16_t* vl_c = vbuf0 + (t & 1) * TILE;
+    const int tk = min(t + 2, t_last), tv = min(t + 1, t_last);
     uint4 pb[KB * 2];
-    float alpha_next = 1.f;
-    if (!skip_c && !skip_n) {
-      // the rescale for tile t first (its factor is known since the last
-      // step), so that the interleaved regions are straight-line code
-      rescale(alpha_cur);
-      const float psum = qk_weights(sn, kl_n, sc, pb);
-      l_run = l_run * alpha_cur + psum;
-      if (full_tile(t + 1)) alpha_next = pv_max(pb, vl_c, sn, t + 1, false);
-      else alpha_next = pv_max(pb, vl_c, sn, t + 1, true);
-    } else {
-      if (!skip_c) {
-        const float psum = weights(sc, pb);
-        l_run = l_run * alpha_cur + psum;
-        rescale(alpha_cur);
-        pv(pb, vl_c);
-      }
-      if (!skip_n) {
-        qk(sn, kl_n);
-        if (!full_tile(t + 1)) mask(sn, t + 1);
-        alpha_next = row_max(sn);
-      }
-    }
-    alpha_cur = alpha_next;
+    // the rescale for tile t first (its factor is known since the last
+    // step), so that the interleaved regions are straight-line code
+    rescale(alpha_cur);
+    const float psum = qk_weights(sn, kbuf0 + ((t + 1) & 1) * TILE, sc, pb, tk, t + 2, tv, t + 1);
+    l_run = l_run * alpha_cur + psum;
+    const uint16_t* vl_c = vbuf0 + (t & 1) * TILE;
+    // the mask is applied to every tile (four vector ops per MFMA slot,
+    // hidden under the MFMA): one copy of the region, no branch
+    alpha_cur = pv_max(pb, vl_c, sn, t + 1, true, has_next);
     __builtin_amdgcn_s_waitcnt(0);  // K(t+2), V(t+1) have landed
     __syncthreads();
   };
 
-  for (int t = t_first; t <= t_last; t += 2) {
-    step(t, sA, sB);
-    if (t + 1 <= t_last) step(t + 1, sB, sA);
+  if (wave_active) {
+    for (int t = t_first; t <= t_last; t += 2) {
+      step(t, sA, sB);
+      if (t + 1 <= t_last) step(t + 1, sB, sA);
+    }
+  } else {  // no rows: this wave only loads its share of every tile
+    for (int t = t_first; t <= t_last; ++t) {
+      if (t + 2 <= t_last) load_k(t + 2);
+      if (t < t_last) load_v(t + 1);
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+    }
   }
 
   // ---- epilogue ---------------------------------------------------------
