@@ -863,38 +863,55 @@ void attn_tile_kernel_d512(AttnParams p) {
   attn_tile_body<DT, 512>(p, lds);
 }
 
-// Merge of the per-split partials of each output row, in ascending split
-// order over exactly the splits that hold the row's visible keys.  One wave
-// per row; every lane recomputes the row's max and sum the same way.
+// Merge of the per-split partials of each output row.  One workgroup of nw =
+// min(kCombineWaves, nsplit) waves per row: wave w takes the row's chunks
+// c_lo + w, c_lo + w + nw, ... in ascending order (so that many chunk loads
+// are in flight per row), and the wave partials are then added in wave
+// order.  The order depends only on nsplit and the row's own chunk range,
+// so a row gets the same bits whatever else is in the call.
+constexpr int kCombineWaves = 16;
+
 template <int DT, int D>
-__global__ __launch_bounds__(256) void combine_kernel(AttnParams p) {
-  constexpr int PER = D / 64;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const size_t row = (size_t)blockIdx.x * 4 + wave;
-  const size_t total = (size_t)p.B * p.Hq * p.qL;
-  if (row >= total) return;
+__global__ __launch_bounds__(64 * kCombineWaves) void combine_kernel(AttnParams p) {
+  constexpr int PER = D / 64;  // columns per lane
+  constexpr int NW = kCombineWaves;
+  const int nw = blockDim.x >> 6;  // waves in this launch, <= NW
+  __shared__ float red[NW];
+  __shared__ __attribute__((aligned(16))) float part[NW][D];
+  __shared__ float lpart[NW];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const size_t row = blockIdx.x;
   const int qi = (int)(row % (size_t)p.qL);
   const int pos = p.q_offset + qi;
   const int key_hi = p.causal ? min(pos, p.kL - 1) : p.kL - 1;
   const int key_lo = p.window > 0 ? max(0, pos - p.window + 1) : 0;
   const int c_lo = key_lo / p.split_len, c_hi = key_hi / p.split_len;
-
   const float* ml = p.part_ml + row * p.nsplit * 2;
-  float M = -INFINITY;
-  for (int c = c_lo; c <= c_hi; ++c) M = fmaxf(M, ml[2 * c]);
-  float L = 0.f;
+
+  // the row's largest reference max (max is exact in any order)
+  float m = -INFINITY;
+  for (int c = c_lo + tid; c <= c_hi; c += 64 * nw) m = fmaxf(m, ml[2 * c]);
+  for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+  if (lane == 0) red[wave] = m;
+  __syncthreads();
+  float M = red[0];
+  for (int w = 1; w < nw; ++w) M = fmaxf(M, red[w]);
+
+  // this wave's chunks, ascending
   float acc[PER];
 #pragma unroll
   for (int e = 0; e < PER; ++e) acc[e] = 0.f;
+  float L = 0.f;
   if (M != -INFINITY) {
-    for (int c = c_lo; c <= c_hi; ++c) {
+    const float* po = p.part_o + row * (size_t)p.nsplit * D + lane * PER;
+    for (int c = c_lo + wave; c <= c_hi; c += nw) {
       const float mc = ml[2 * c];
       const float w = (mc == -INFINITY) ? 0.f : fast_exp2(mc - M);
       L += ml[2 * c + 1] * w;
-      const float* po = p.part_o + (row * p.nsplit + c) * D + lane * PER;
+      const float* src = po + (size_t)c * D;
 #pragma unroll
       for (int e = 0; e < PER; e += 4) {
-        const float4 x = *(const float4*)(po + e);
+        const float4 x = *(const float4*)(src + e);
         acc[e + 0] += x.x * w;
         acc[e + 1] += x.y * w;
         acc[e + 2] += x.z * w;
@@ -902,14 +919,32 @@ __global__ __launch_bounds__(256) void combine_kernel(AttnParams p) {
       }
     }
   }
-  const float inv = (L > 0.f) ? 1.0f / L : 0.f;
+#pragma unroll
+  for (int e = 0; e < PER; e += 4)
+    *(float4*)(&part[wave][lane * PER + e]) = make_float4(acc[e], acc[e + 1], acc[e + 2], acc[e + 3]);
+  if (lane == 0) lpart[wave] = L;
+  __syncthreads();
+
+  // wave 0: the wave partials in wave order, normalise, round
+  if (wave != 0) return;
+  float Lt = 0.f;
+  for (int w = 0; w < nw; ++w) Lt += lpart[w];
+  const float inv = (Lt > 0.f) ? 1.0f / Lt : 0.f;
   uint16_t* dst = p.out + row * D + lane * PER;
 #pragma unroll
   for (int e = 0; e < PER; e += 4) {
-    uint2 w;
-    w.x = Elem<DT>::pack2(acc[e + 0] * inv, acc[e + 1] * inv);
-    w.y = Elem<DT>::pack2(acc[e + 2] * inv, acc[e + 3] * inv);
-    *(uint2*)(dst + e) = w;
+    float4 t = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int w = 0; w < nw; ++w) {
+      const float4 x = *(const float4*)(&part[w][lane * PER + e]);
+      t.x += x.x;
+      t.y += x.y;
+      t.z += x.z;
+      t.w += x.w;
+    }
+    uint2 o2;
+    o2.x = Elem<DT>::pack2(t.x * inv, t.y * inv);
+    o2.y = Elem<DT>::pack2(t.z * inv, t.w * inv);
+    *(uint2*)(dst + e) = o2;
   }
 }
 
@@ -925,9 +960,9 @@ hipError_t launch_attention_t(const AttnParams& p, hipStream_t stream) {
 
 template <int DT, int D>
 hipError_t launch_combine_t(const AttnParams& p, hipStream_t stream) {
-  const size_t total = (size_t)p.B * p.Hq * p.qL;
-  const dim3 grid((unsigned)((total + 3) / 4), 1, 1);
-  hipLaunchKernelGGL((combine_kernel<DT, D>), grid, dim3(256), 0, stream, p);
+  const size_t total = (size_t)p.B * p.Hq * p.qL;  // one workgroup per output row
+  const int nw = p.nsplit < kCombineWaves ? p.nsplit : kCombineWaves;
+  hipLaunchKernelGGL((combine_kernel<DT, D>), dim3((unsigned)total, 1, 1), dim3(64 * nw), 0, stream, p);
   return hipGetLastError();
 }
 
