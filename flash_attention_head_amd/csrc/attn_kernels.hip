@@ -24,6 +24,8 @@
 
 #include <math.h>
 
+#include <type_traits>
+
 namespace sdpa {
 namespace {
 
@@ -559,8 +561,11 @@ __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* ld
     const int g = lane >> 4, kq = 4 * (g >> 1) + ((lane >> 2) & 3);
     vlane = kq * D + 32 * kq + 16 * (g & 1) + 4 * (lane & 3);
   }
-  uint16_t* const kbuf0 = lds;             // K(t) lives in kbuf0 + (t & 1) * TILE
-  uint16_t* const vbuf0 = lds + 2 * TILE;  // V(t) lives in vbuf0 + (t & 1) * TILE
+  // K(t) lives in K buffer (t - t_first) & 1, V(t) in V buffer (t - t_first)
+  // & 1: the steps come in pairs, so inside a step every buffer offset is a
+  // compile-time immediate of the LDS instructions
+  uint16_t* const kbuf0 = lds;
+  uint16_t* const vbuf0 = lds + 2 * TILE;
 
   // direct loads of one K or V tile (swizzles as in the paired kernel)
   auto load_tile = [&](const uint16_t* g, int t, uint16_t* buf, bool is_v) {
@@ -583,23 +588,23 @@ __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* ld
       for (int n = 0; n < LOADS; ++n) one(n, true);
     }
   };
-  auto load_k = [&](int t) { load_tile(kg, t, kbuf0 + (t & 1) * TILE, false); };
-  auto load_v = [&](int t) { load_tile(vg, t, vbuf0 + (t & 1) * TILE, true); };
+  auto load_k = [&](int t) { load_tile(kg, t, kbuf0 + ((t - t_first) & 1) * TILE, false); };
+  auto load_v = [&](int t) { load_tile(vg, t, vbuf0 + ((t - t_first) & 1) * TILE, true); };
   // one of the LOADS direct loads of a tile, rows clamped branch-free (only
   // the last tile has rows past kL; their keys are masked), for issuing
   // inside the MFMA regions: a burst of loads stalls the wave on the memory
-  // pipeline, while one load every few MFMAs keeps it busy in the background
-  // (tile t's data into the buffer of tile tdst: they differ only past the
-  // last tile, where a clamped reload fills a buffer no later step reads)
-  auto load_one = [&](const uint16_t* g, int t, int tdst, bool is_v, int n) {
-    const int ts = t * BN;
+  // pipeline, while one load every few MFMAs keeps it busy in the background.
+  // Split in two so that the lane offset can be formed a slot ahead.
+  auto load_off = [&](int t, bool is_v, int n) {
     const int cb = wave * LOADS + n;
     const int row = cb * (64 / ROWCH) + lane / ROWCH;
     const int pch = lane % ROWCH;
-    const int r = min(row, p.kL - 1 - ts);
+    const int r = min(row, p.kL - 1 - t * BN);
     const int c = is_v ? (pch ^ ((row & 7) << 2)) : (pch ^ (row & 15));
-    uint16_t* buf = (is_v ? vbuf0 : kbuf0) + (tdst & 1) * TILE;
-    load_lds16(g + (size_t)ts * D, (uint32_t)(r * D + c * 8) * 2u, buf + cb * 512);
+    return (uint32_t)(r * D + c * 8) * 2u;
+  };
+  auto load_issue = [&](const uint16_t* g, int t, uint16_t* buf, int n, uint32_t off) {
+    load_lds16(g + (size_t)(t * BN) * D, off, buf + (wave * LOADS + n) * 512);
   };
 
   // the keys row `pos` sees form one interval [key_lo, key_hi] (empty if
@@ -677,43 +682,59 @@ __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* ld
   };
 
   // ---- interleaved regions: slot n issues MFMA n, the operand read for MFMA
-  //      n + PF and element n of the other tile's vector work; the
-  //      scheduling barriers keep that order.
-  // S(t+1) = K(t+1) Q^T  ||  weights, sum and packing of tile t
+  //      n + PF and a share of the other tile's vector work; the scheduling
+  //      barriers keep that order.  With one wave per SIMD, instructions
+  //      issue in order, so a vector op that needs the result of the op just
+  //      before it stalls the MFMA stream: every dependency chain (address ->
+  //      LDS read, fma -> exp -> sum, compare -> select -> max, offset ->
+  //      load) is spread over consecutive slots instead.
+  // S(t+1) = K(t+1) Q^T  ||  weights, sum and packing of tile t; also issues
+  // the direct loads of K(tk) into kdst and V(tv) into vdst
   auto qk_weights = [&](f32x16_t (&sn)[KB], const uint16_t* kl, f32x16_t (&sc)[KB],
-                        uint4 (&pb)[KB * 2], int tk, int tkdst, int tv, int tvdst) {
-    // also loads K(tk) and V(tv): the P V region then has the LDS to itself
-    // and the loads have that whole region to land
+                        uint4 (&pb)[KB * 2], int tk, uint16_t* kdst, int tv, uint16_t* vdst) {
     constexpr int NQK = KB * DC, PF = 4;
     static_assert(NQK == KB * 16, "one score element per slot");
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
       for (int j = 0; j < 16; ++j) sn[kb][j] = 0.f;
-    auto kread = [&](int n) {
-      const int kb = n % KB, dc = n / KB;
-      return *(const uint4*)(kl + kaddr(kb, dc));
+    // K operand of MFMA n: key block n % KB, d step n / KB; the XOR part of
+    // its address is a register, the rest an immediate
+    auto kx = [&](int n) { return kbase ^ (16 * ((n / KB) & 7)); };
+    auto kread = [&](int n, int x) {
+      return *(const uint4*)(kl + x + 16 * ((n / KB) & 8) + (n % KB) * 32 * D);
     };
     const float msc = (m_ref == -INFINITY) ? 0.f : m_ref * sl2;
+    auto get = [&](int e) { return sc[e / 16][e % 16]; };
+    auto set = [&](int e, float v) { sc[e / 16][e % 16] = v; };
     float psum = 0.f;
     uint4 a[PF];
 #pragma unroll
-    for (int i = 0; i < PF; ++i) a[i] = kread(i);
+    for (int i = 0; i < PF; ++i) a[i] = kread(i, kx(i));
+    int x_next = kx(PF);
+    uint32_t loff = load_off(tk, false, 0);
+    set(0, fast_exp2(get(0) * sl2 - msc));
+    set(1, get(1) * sl2 - msc);
 #pragma unroll
     for (int n = 0; n < NQK; ++n) {
       const uint4 cur_a = a[n % PF];
-      if (n + PF < NQK) a[n % PF] = kread(n + PF);
+      if (n + PF < NQK) a[n % PF] = kread(n + PF, x_next);
       sn[n % KB] = Elem<DT>::mfma(cur_a, qf[n / KB], sn[n % KB]);
-      if (n % 4 == 0) load_one(kg, tk, tkdst, false, n / 4);
-      if (n % 4 == 2) load_one(vg, tv, tvdst, true, n / 4);
-      const int kb = n / 16, j = n % 16;
-      const float e = fast_exp2(sc[kb][j] * sl2 - msc);
-      sc[kb][j] = e;
-      psum += e;
-      if (j & 1) {  // pack the pair (j - 1, j): P half kh = 2 kb + j / 8
-        const uint32_t w = Elem<DT>::pack2(sc[kb][j - 1], e);
-        uint4& q = pb[2 * kb + j / 8];
-        switch ((j % 8) / 2) {
+      if (n + PF + 1 < NQK) x_next = kx(n + PF + 1);
+      // loads: K block n / 4 at slot n % 4 == 0, V block n / 4 at n % 4 == 2,
+      // each with its lane offset formed in the slot before
+      if (n % 4 == 0) load_issue(kg, tk, kdst, n / 4, loff);
+      if (n % 4 == 2) load_issue(vg, tv, vdst, n / 4, loff);
+      if (n % 4 == 1) loff = load_off(tv, true, n / 4);
+      if (n % 4 == 3 && n + 1 < NQK) loff = load_off(tk, false, (n + 1) / 4);
+      // weights: fma of element n + 2, exp of n + 1, sum and pack of n
+      if (n + 2 < NQK) set(n + 2, get(n + 2) * sl2 - msc);
+      if (n + 1 < NQK) set(n + 1, fast_exp2(get(n + 1)));
+      psum += get(n);
+      if (n & 1) {  // pack the pair (n - 1, n): P half kh = n / 8
+        const uint32_t w = Elem<DT>::pack2(get(n - 1), get(n));
+        uint4& q = pb[n / 8];
+        switch ((n % 8) / 2) {
           case 0: q.x = w; break;
           case 1: q.y = w; break;
           case 2: q.z = w; break;
@@ -727,33 +748,46 @@ __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* ld
     asm volatile("" ::"v"(psum));
     return psum;
   };
-  // O += P(t) V(t)  ||  (mask and) row max of S(t+1)
+  // O += P(t) V(t)  ||  mask and row max of S(t+1)
   auto pv_max = [&](const uint4 (&pb)[KB * 2], const uint16_t* vl, f32x16_t (&sn)[KB], int tn,
-                    bool masked, bool live) {
+                    bool live) {
     constexpr int NPV = KB * 2 * DB, PF = 4;
     static_assert(NPV == KB * 16, "one score element per slot");
-    auto vread = [&](int n) {
-      const int kh = n / DB, db = n % DB;
-      const uint16_t* va = vl + (vlane ^ (32 * db)) + 16 * kh * D;
+    // V^T operand of MFMA n: key half n / DB, column block n % DB; the XOR
+    // part of the address is a register, the rest an immediate
+    auto vx = [&](int n) { return vlane ^ (32 * (n % DB)); };
+    auto vread = [&](int n, int x) {
+      const uint16_t* va = vl + x + 16 * (n / DB) * D;
       const uint2 lo = read_tr(va), hi = read_tr(va + 8 * D);
       return make_uint4(lo.x, lo.y, hi.x, hi.y);
     };
     int lo4, hi4;
     vis_bounds(tn, lo4, hi4);
+    auto ce = [](int e) { return 32 * (e / 16) + 8 * ((e % 16) >> 2) + (e & 3); };
+    auto get = [&](int e) { return sn[e / 16][e % 16]; };
+    auto set = [&](int e, float v) { sn[e / 16][e % 16] = v; };
     float mx = -INFINITY;
     uint4 bv[PF];
 #pragma unroll
-    for (int i = 0; i < PF; ++i) bv[i] = vread(i);
+    for (int i = 0; i < PF; ++i) bv[i] = vread(i, vx(i));
+    int x_next = vx(PF);
+    bool vis = (ce(0) >= lo4) & (ce(0) <= hi4);
+    float xm = -INFINITY;  // masked element of the previous slot
 #pragma unroll
     for (int n = 0; n < NPV; ++n) {
       const uint4 cur_b = bv[n % PF];
-      if (n + PF < NPV) bv[n % PF] = vread(n + PF);
+      if (n + PF < NPV) bv[n % PF] = vread(n + PF, x_next);
       o[n % DB] = Elem<DT>::mfma(cur_b, pb[n / DB], o[n % DB]);
-      const int kb = n / 16, j = n % 16;
-      if (masked) sn[kb][j] = mask_elem(sn[kb][j], 32 * kb + 8 * (j >> 2) + (j & 3), lo4, hi4);
-      mx = fmaxf(mx, sn[kb][j]);
+      if (n + PF + 1 < NPV) x_next = vx(n + PF + 1);
+      // max of element n - 1, select (kept for the weights) of n, compares
+      // of n + 1
+      mx = fmaxf(mx, xm);
+      xm = vis ? get(n) : -INFINITY;
+      set(n, xm);
+      if (n + 1 < NPV) vis = (ce(n + 1) >= lo4) & (ce(n + 1) <= hi4);
       __builtin_amdgcn_sched_barrier(0);
     }
+    mx = fmaxf(mx, xm);
     mx = pair_max(mx);
     // live == false: the scores were of no tile (the step after the last)
     const bool upd = live && (mx * sl2 > m_ref * sl2 + kRescaleLog2);
@@ -772,7 +806,7 @@ __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* ld
   f32x16_t sA[KB], sB[KB];
   float alpha_cur = 1.f;
   if (wave_active) {
-    qk(sA, kbuf0 + (t_first & 1) * TILE);
+    qk(sA, kbuf0);
     if (!full_tile(t_first)) mask(sA, t_first);
     alpha_cur = row_max(sA);
   }
@@ -784,27 +818,31 @@ __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* ld
   // the scores of the stale buffer are computed but never used (live ==
   // false).  Loads past the last tile reload the last tile into a buffer no
   // later step reads.
-  auto step = [&](int t, f32x16_t (&sc)[KB], f32x16_t (&sn)[KB]) {
+  // P = (t - t_first) & 1, a compile-time constant: K(t+1) is in K buffer
+  // 1 - P and V(t) in V buffer P; K(t+2) goes to K buffer P and V(t+1) to
+  // V buffer 1 - P.
+  auto step = [&](int t, f32x16_t (&sc)[KB], f32x16_t (&sn)[KB], auto parity) {
+    constexpr int P = decltype(parity)::value;
     const bool has_next = t < t_last;
     const int tk = min(t + 2, t_last), tv = min(t + 1, t_last);
     uint4 pb[KB * 2];
     // the rescale for tile t first (its factor is known since the last
     // step), so that the interleaved regions are straight-line code
     rescale(alpha_cur);
-    const float psum = qk_weights(sn, kbuf0 + ((t + 1) & 1) * TILE, sc, pb, tk, t + 2, tv, t + 1);
+    const float psum = qk_weights(sn, kbuf0 + (1 - P) * TILE, sc, pb, tk, kbuf0 + P * TILE, tv,
+                                  vbuf0 + (1 - P) * TILE);
     l_run = l_run * alpha_cur + psum;
-    const uint16_t* vl_c = vbuf0 + (t & 1) * TILE;
-    // the mask is applied to every tile (four vector ops per MFMA slot,
+    // the mask is applied to every tile (a few vector ops per MFMA slot,
     // hidden under the MFMA): one copy of the region, no branch
-    alpha_cur = pv_max(pb, vl_c, sn, t + 1, true, has_next);
+    alpha_cur = pv_max(pb, vbuf0 + P * TILE, sn, t + 1, has_next);
     __builtin_amdgcn_s_waitcnt(0);  // K(t+2), V(t+1) have landed
     __syncthreads();
   };
 
   if (wave_active) {
     for (int t = t_first; t <= t_last; t += 2) {
-      step(t, sA, sB);
-      if (t + 1 <= t_last) step(t + 1, sB, sA);
+      step(t, sA, sB, std::integral_constant<int, 0>{});
+      if (t + 1 <= t_last) step(t + 1, sB, sA, std::integral_constant<int, 1>{});
     }
   } else {  // no rows: this wave only loads its share of every tile
     for (int t = t_first; t <= t_last; ++t) {
