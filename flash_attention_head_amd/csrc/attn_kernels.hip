@@ -1,14 +1,17 @@
 // Fused attention kernels for gfx950 (MI355X).
 //
-// One workgroup = 4 waves x 32 query rows.  Rows are "packed" grouped-query
+// One workgroup = 4 waves, one per SIMD.  Rows are "packed" grouped-query
 // rows: packed row r of KV head hk is query position r / G of query head
 // hk * G + r % G, so the G query heads that share a KV head sit in one
 // workgroup and every K/V tile is staged into LDS once for all of them.
+// At head_dim 256 a wave owns 32 packed rows and all columns (128 rows per
+// workgroup, 64-key tiles); at 512 two waves share 32 rows and split the
+// columns (64 rows per workgroup, 32-key tiles).
 //
-// Per K/V tile (BN keys) each wave computes, with 32x32x16 MFMAs,
+// Per K/V tile each wave computes, with 32x32x16 MFMAs,
 //   S^T = K Q^T            (A = K rows from LDS, B = Q from registers)
 //   online softmax         (one query row per lane pair, fp32, base 2)
-//   O^T += V^T P^T         (A = V^T rows from LDS, B = P from registers)
+//   O^T += V^T P^T         (A = V^T by transposing LDS reads, B = P from registers)
 // Working with the transposed products keeps every row's scores, softmax
 // state and output accumulator inside the two lanes that own the row, so
 // the row max needs a single cross-lane exchange and the rescale of O is
@@ -123,63 +126,45 @@ __device__ __forceinline__ float pair_sum(float v) {
 // same softmax; only rounding differs.
 constexpr float kRescaleLog2 = 8.f;
 
-// Waves are paired: the two waves of a pair own the same 32 query rows and
-// split the work of each K/V tile between them.
-//   D = 256 (8 waves, 2 per SIMD): wave h of a pair computes the scores of
-//     key half h of the 64-key tile over the whole head dimension; the pair
-//     swaps the halves through LDS, so both hold all 64 scores.  For P V
-//     wave h owns output columns [128 h, 128 h + 128).
-//   D = 512 (4 waves, 1 per SIMD): wave h computes the scores of all 32 keys
-//     over columns [256 h, 256 h + 256); the pair swaps the partial scores
-//     and adds them.  For P V wave h owns columns [256 h, 256 h + 256).
-// Scores move between the pair as fp32 bit patterns (and a + b == b + a), so
-// both waves run bitwise identical softmax arithmetic.  Two waves per SIMD at
-// D = 256 let one wave's softmax overlap the other's MFMAs and double the
-// LDS operand throughput a SIMD gets; the split keeps every wave within the
-// 256 registers that two waves per SIMD leave it.
-template <int D>
-struct Geom {
-  static constexpr bool kKeySplit = (D == 256);      // pair splits score keys, else d
-  static constexpr int NW = D == 256 ? 8 : 4;        // waves per workgroup
-  static constexpr int RB = NW / 2;                  // 32-row blocks (wave pairs)
-  static constexpr int BM = RB * kRowsPerWave;       // rows per workgroup
-  static constexpr int BN = tile_keys(D);            // keys per tile
-  static constexpr int KB = BN / 32;                 // 32-key score blocks per tile
-  static constexpr int DQ = 256;                     // Q columns a wave multiplies
-  static constexpr int DC = DQ / 16;                 // score MFMAs per wave per tile
-  static constexpr int DO = D / 2;                   // output columns a wave owns
-  static constexpr int DB = DO / 32;                 // 32-column output blocks
-  static constexpr int ROWCH = D / 8;                // 16-byte chunks per K/V row
-  static constexpr int TILE = BN * D;                // elements of one K or V tile
-  static constexpr int LOADS = TILE * 2 / 1024 / NW; // 1 KiB loads per wave per tile
-  static constexpr int XCH = NW * 64 * 16;           // floats of the score exchange
-  static constexpr int NT = NW * 64;                 // threads
-  static_assert(BM == block_rows(D), "row blocks");
-  static_assert(LOADS * NW * 1024 == TILE * 2, "loads must cover the tile");
-  static_assert(ROWCH <= 64 && 64 % ROWCH == 0, "a K/V row must fit one wave load");
-  static_assert(kKeySplit ? KB == 2 : KB == 1, "pair split");
-};
-
+// ---------------------------------------------------------------------------
+// The attention kernel body: one wave per SIMD, 32 x 256 fp32 output
+// accumulators per wave, software pipelined over K/V tiles.  While the MFMAs
+// of S(t+1) = K(t+1) Q^T run, the same wave computes exp / sum / pack of
+// tile t and issues the direct loads of the tiles after; while the MFMAs of
+// O += P(t) V(t) run, it masks and takes the row max of S(t+1).  MFMAs and
+// the vector work between them are independent, so the matrix unit keeps
+// busy through the softmax.  K and V have separate double buffers, V one
+// tile behind K: step t reads K(t+1) and V(t) and loads K(t+2) and V(t+1).
+// ---------------------------------------------------------------------------
 template <int DT, int D>
-__device__ __forceinline__ void attn_tile_body(const AttnParams& p, uint16_t* lds) {
-  using G = Geom<D>;
-  constexpr int NW = G::NW, BM = G::BM, BN = G::BN, KB = G::KB, DC = G::DC, DB = G::DB;
-  constexpr int ROWCH = G::ROWCH, TILE = G::TILE, LOADS = G::LOADS;
+__device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* lds) {
+  // D = 256: a wave owns 32 rows and all 256 columns.  D = 512: the two
+  // waves of a pair own the same 32 rows; wave h multiplies Q columns
+  // [256 h, 256 h + 256) into partial scores, the pair swaps them through LDS
+  // and adds them (a + b == b + a: both hold bitwise identical scores and run
+  // identical softmax arithmetic), and wave h accumulates output columns
+  // [256 h, 256 h + 256).  Either way 32 x 256 fp32 accumulators per wave.
+  constexpr bool PAIR = (D == 512);
+  constexpr int NW = 4, RBW = PAIR ? 2 : 4;  // 32-row blocks per workgroup
+  constexpr int BM = RBW * kRowsPerWave, BN = tile_keys(D), KB = BN / 32;
+  constexpr int DQ = 256, DO = PAIR ? D / 2 : D;  // Q columns multiplied, output columns owned
+  constexpr int DC = DQ / 16, DB = DO / 32;
+  constexpr int ROWCH = D / 8, TILE = BN * D, LOADS = TILE * 2 / 1024 / NW;
+  static_assert(BM == block_rows(D), "geometry");
+  static_assert(LOADS == 8, "one K and one V load per wave per 1 KiB block");
+  static_assert(KB * DC == KB * 16 && KB * 2 * DB == KB * 16, "one score element per MFMA slot");
 
   const int tid = threadIdx.x;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar registers
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63, lr = lane & 31, lg = lane >> 5;
-  const int rb = wave >> 1;  // this pair's 32-row block
-  const int h = wave & 1;    // this wave's half of the pair's work
-  const int qd0 = G::kKeySplit ? 0 : h * G::DQ;  // first Q column this wave multiplies
-  const int od0 = h * G::DO;                      // first output column this wave owns
-  const int hk = G::kKeySplit ? h : 0;            // key block whose scores this wave computes
+  const int rb = PAIR ? (wave >> 1) : wave;  // this wave's 32-row block
+  const int h = PAIR ? (wave & 1) : 0;       // this wave's half of the pair's work
+  const int qd0 = h * DQ * (PAIR ? 1 : 0);   // first Q column this wave multiplies
+  const int od0 = h * DO;                    // first output column this wave owns
 
-  // ---- work item: (b, kv head) x row block x key split -------------------
   const int nheads = p.B * p.Hkv;
   const int head = blockIdx.x % nheads;
   const int mbr = blockIdx.x / nheads;
-  // causal: later row blocks see more keys; dispatch them first
   const int mb = p.causal ? (p.mblocks - 1 - mbr) : mbr;
   const int split = blockIdx.y;
   const int b = head / p.Hkv, hkv = head % p.Hkv;
@@ -187,324 +172,6 @@ __device__ __forceinline__ void attn_tile_body(const AttnParams& p, uint16_t* ld
   const int row0 = mb * BM;
   const int rows_end = min(p.rows, row0 + BM);
   const int wrow0 = row0 + rb * kRowsPerWave;
-  const bool wave_active = wrow0 < rows_end;
-  const int my = wrow0 + lr;
-  const bool valid = my < rows_end;
-  const int qi = valid ? my / p.G : 0;
-  const int hq = hkv * p.G + (valid ? my % p.G : 0);
-  const int pos = p.q_offset + qi;
-  const int wp_lo = p.q_offset + wrow0 / p.G;
-  const int wp_hi = p.q_offset + (min(rows_end, wrow0 + kRowsPerWave) - 1) / p.G;
-
-  // keys any row of this workgroup may see, clipped to the split
-  int kbeg = 0, kend = p.kL;
-  {
-    const int bp_lo = p.q_offset + row0 / p.G;
-    const int bp_hi = p.q_offset + (rows_end - 1) / p.G;
-    if (p.causal) kend = min(kend, bp_hi + 1);
-    if (p.window > 0) kbeg = max(0, bp_lo - p.window + 1);
-    if (p.partials) {
-      kbeg = max(kbeg, split * p.split_len);
-      kend = min(kend, (split + 1) * p.split_len);
-    }
-  }
-  if (kbeg >= kend) return;  // whole workgroup: no row has a key in this split
-  const int t_first = __builtin_amdgcn_readfirstlane(kbeg / BN);
-  const int t_last = __builtin_amdgcn_readfirstlane((kend - 1) / BN);
-
-  const size_t kv_off = (size_t)(b * p.Hkv + hkv) * (size_t)p.kL * D;
-  const uint16_t* __restrict__ kg = p.k + kv_off;
-  const uint16_t* __restrict__ vg = p.v + kv_off;
-
-  // ---- Q fragments: B operand of S^T = K Q^T,
-  //      lane (lr, lg) holds columns qd0 + 16 dc + 8 lg + 0..7 of its row
-  uint4 qf[DC];
-  {
-    const uint16_t* qrow = p.q + ((size_t)(b * p.Hq + hq) * p.qL + qi) * D + qd0;
-#pragma unroll
-    for (int dc = 0; dc < DC; ++dc)
-      qf[dc] = valid ? *(const uint4*)(qrow + dc * 16 + lg * 8) : make_uint4(0, 0, 0, 0);
-  }
-
-  f32x16_t o[DB];
-#pragma unroll
-  for (int db = 0; db < DB; ++db)
-#pragma unroll
-    for (int j = 0; j < 16; ++j) o[db][j] = 0.f;
-  float m_ref = -INFINITY;  // reference max of this row's raw scores (moves lazily)
-  float l_run = 0.f;        // this lane's share of the row's weight sum
-
-  // ---- per-lane LDS operand offsets (elements), loop invariant -------------
-  // K operand (key row 32 hk + lr, 16-byte chunk (qd0 / 8) + 2 dc + lg): with
-  // r = lr & 15 the swizzled chunk is
-  //   qd0 / 8 + (lg ^ (r & 1)) + 2 ((dc & 8) | ((dc & 7) ^ (r >> 1)))
-  // so eight per-lane offsets plus compile-time immediates cover every dc
-  int koff[8];
-  {
-    const int r = lr & 15;
-    const int base = (32 * hk + lr) * D + qd0 + 8 * (lg ^ (r & 1));
-#pragma unroll
-    for (int j = 0; j < 8; ++j) koff[j] = base + 16 * (j ^ (r >> 1));
-  }
-  // V^T operand by transposing reads of the key-major V tile.  Lane l
-  // (group g = l / 16, a = l % 4, t = (l % 16) / 4) points at key
-  // 16 kh + 8 e + kq, kq = 4 (g / 2) + t, columns od0 + 32 db + 16 (g & 1)
-  // + 4 a; e = 0, 1 give the MFMA k slots 0-3 and 4-7, i.e. keys
-  // 16 kh + 4 lg + 0..3 and 16 kh + 8 + 4 lg + 0..3, as P holds them.  V
-  // rows store 16-byte chunk c at c ^ ((key & 7) << 2); key & 7 == kq, so
-  // the swizzle is an XOR of 32 kq into the column offset, and db enters as
-  // an XOR of 32 db (bits of the offset that nothing else occupies).
-  int vlane;
-  {
-    const int g = lane >> 4, kq = 4 * (g >> 1) + ((lane >> 2) & 3);
-    vlane = kq * D + (od0 ^ (32 * kq)) + 16 * (g & 1) + 4 * (lane & 3);
-  }
-  auto kaddr = [&](int dc) { return koff[dc & 7] + 16 * (dc & 8); };
-  // score block kb of this wave holds key block kb ^ hk of the tile
-  auto vaddr = [&](int kh, int db) {
-    return (vlane ^ (32 * db)) + 16 * D * (2 * ((kh >> 1) ^ hk) + (kh & 1));
-  };
-
-  // ---- tile staging ------------------------------------------------------
-  // K and V: direct global->LDS loads, 1 KiB per wave instruction (lane l
-  // writes bytes 16 l .. 16 l + 15 of it), key rows of D elements.  In K,
-  // chunk c of row r sits at chunk position c ^ (r & 15), so the 32 rows one
-  // K operand read touches fall in distinct banks; in V at c ^ ((r & 7) << 2),
-  // which spreads the 8 rows x 64 bytes of one transposing read over all
-  // banks.  Rows past kL load row kL - 1: those keys are masked, P is 0.
-  auto load_tile = [&](int t, int buf) {
-    const int ts = t * BN;
-    uint16_t* kl = lds + buf * (2 * TILE);
-    uint16_t* vl = kl + TILE;
-    const uint16_t* kt = kg + (size_t)ts * D;  // tile bases: uniform
-    const uint16_t* vt = vg + (size_t)ts * D;
-    const int nrow = p.kL - ts;                // key rows of this tile inside kL
-    auto kvload = [&](int n, bool clamp) {
-      const int cb = wave * LOADS + n;  // 1 KiB block of the tile
-      const int row = cb * (64 / ROWCH) + lane / ROWCH;
-      const int pch = lane % ROWCH;     // chunk position this lane writes
-      const int r = clamp ? min(row, nrow - 1) : row;
-      load_lds16(kt, (uint32_t)(r * D + (pch ^ (row & 15)) * 8) * 2u, kl + cb * 512);
-      load_lds16(vt, (uint32_t)(r * D + (pch ^ ((row & 7) << 2)) * 8) * 2u, vl + cb * 512);
-    };
-    if (nrow >= BN) {
-#pragma unroll
-      for (int n = 0; n < LOADS; ++n) kvload(n, false);
-    } else {  // the last, partial tile
-#pragma unroll
-      for (int n = 0; n < LOADS; ++n) kvload(n, true);
-    }
-  };
-
-  float* xch = (float*)(lds + 4 * TILE);  // score exchange: 16 floats per lane per wave
-
-  load_tile(t_first, 0);
-  __builtin_amdgcn_s_waitcnt(0);  // direct loads have landed in LDS
-  __syncthreads();
-
-  const float sl2 = p.sl2;
-  for (int t = t_first; t <= t_last; ++t) {
-    const int cur = (t - t_first) & 1;
-    if (t < t_last) load_tile(t + 1, cur ^ 1);
-
-    const int ts = t * BN, te = ts + BN - 1;
-    // uniform over the pair
-    const bool skip = !wave_active || (p.causal && ts > wp_hi) ||
-                      (p.window > 0 && te < wp_lo - p.window + 1);
-    const uint16_t* kl = lds + cur * (2 * TILE);
-    const uint16_t* vl = kl + TILE;
-
-    // this wave's 32 x 32 score block, S^T = K Q^T over its DQ columns, with
-    // the K operands read PF MFMAs ahead (the scheduling barriers keep it)
-    f32x16_t s[KB];
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-      for (int j = 0; j < 16; ++j) s[kb][j] = 0.f;
-    if (!skip) {
-      constexpr int PF = 4;
-      auto kread = [&](int dc) { return *(const uint4*)(kl + kaddr(dc)); };
-      uint4 a[PF];
-#pragma unroll
-      for (int i = 0; i < PF; ++i) a[i] = kread(i);
-#pragma unroll
-      for (int dc = 0; dc < DC; ++dc) {
-        const uint4 cur_a = a[dc % PF];
-        if (dc + PF < DC) a[dc % PF] = kread(dc + PF);
-        s[0] = Elem<DT>::mfma(cur_a, qf[dc], s[0]);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4)
-        *(float4*)(xch + (wave * 4 + q4) * 256 + lane * 4) =
-            make_float4(s[0][4 * q4 + 0], s[0][4 * q4 + 1], s[0][4 * q4 + 2], s[0][4 * q4 + 3]);
-    }
-    __syncthreads();
-    if (!skip) {
-      const float* px = xch + (wave ^ 1) * 4 * 256 + lane * 4;  // the partner's block
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const float4 x = *(const float4*)(px + q4 * 256);
-        if constexpr (G::kKeySplit) {  // the other key half
-          s[1][4 * q4 + 0] = x.x;
-          s[1][4 * q4 + 1] = x.y;
-          s[1][4 * q4 + 2] = x.z;
-          s[1][4 * q4 + 3] = x.w;
-        } else {  // the other half of the columns
-          s[0][4 * q4 + 0] += x.x;
-          s[0][4 * q4 + 1] += x.y;
-          s[0][4 * q4 + 2] += x.z;
-          s[0][4 * q4 + 3] += x.w;
-        }
-      }
-
-      const bool full = (te < p.kL) && (!p.causal || te <= wp_lo) &&
-                        (p.window == 0 || ts >= wp_hi - p.window + 1);
-      if (!full) {
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-          for (int j = 0; j < 16; ++j) {
-            const int key = ts + 32 * (kb ^ hk) + 8 * (j >> 2) + 4 * lg + (j & 3);
-            const bool vis = key < p.kL && (!p.causal || key <= pos) &&
-                             (p.window == 0 || pos - key < p.window);
-            s[kb][j] = vis ? s[kb][j] : -INFINITY;
-          }
-      }
-      float mx = -INFINITY;
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-        for (int j = 0; j < 16; ++j) mx = fmaxf(mx, s[kb][j]);
-      mx = pair_max(mx);
-      // move the reference max only when this tile's max is far above it
-      const bool upd = mx * sl2 > m_ref * sl2 + kRescaleLog2;
-      const float alpha =
-          upd ? ((m_ref == -INFINITY) ? 0.f : fast_exp2((m_ref - mx) * sl2)) : 1.f;
-      m_ref = upd ? mx : m_ref;
-      const float msc = (m_ref == -INFINITY) ? 0.f : m_ref * sl2;
-      // per-block sums, added last: the pair holds the blocks in opposite
-      // order and a + b == b + a, so both get the same total
-      float ps[KB];
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
-        ps[kb] = 0.f;
-#pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          const float e = fast_exp2(s[kb][j] * sl2 - msc);
-          s[kb][j] = e;
-          ps[kb] += e;
-        }
-      }
-      float psum = ps[0];
-      if constexpr (KB == 2) psum = ps[0] + ps[1];
-      l_run = l_run * alpha + psum;
-      // x * 1 == x: skip the rescale when no row of the wave moved its reference
-      if (__any(alpha != 1.f)) {
-#pragma unroll
-        for (int db = 0; db < DB; ++db)
-#pragma unroll
-          for (int j = 0; j < 16; ++j) o[db][j] *= alpha;
-      }
-
-      // O^T += V^T P^T over this wave's output columns: KB * 2 key halves x
-      // DB column blocks, V^T operands read PF MFMAs ahead
-      uint4 pb[KB * 2];
-#pragma unroll
-      for (int kh = 0; kh < KB * 2; ++kh) {
-        const int kb = kh >> 1, e = kh & 1;
-        pb[kh].x = Elem<DT>::pack2(s[kb][8 * e + 0], s[kb][8 * e + 1]);
-        pb[kh].y = Elem<DT>::pack2(s[kb][8 * e + 2], s[kb][8 * e + 3]);
-        pb[kh].z = Elem<DT>::pack2(s[kb][8 * e + 4], s[kb][8 * e + 5]);
-        pb[kh].w = Elem<DT>::pack2(s[kb][8 * e + 6], s[kb][8 * e + 7]);
-      }
-      constexpr int NPV = KB * 2 * DB, PF = 4;
-      auto vread = [&](int n) {
-        const uint16_t* va = vl + vaddr(n / DB, n % DB);
-        const uint2 lo = read_tr(va), hi = read_tr(va + 8 * D);
-        return make_uint4(lo.x, lo.y, hi.x, hi.y);
-      };
-      uint4 bv[PF];
-#pragma unroll
-      for (int i = 0; i < PF; ++i) bv[i] = vread(i);
-#pragma unroll
-      for (int n = 0; n < NPV; ++n) {
-        const uint4 cur_b = bv[n % PF];
-        if (n + PF < NPV) bv[n % PF] = vread(n + PF);
-        o[n % DB] = Elem<DT>::mfma(cur_b, pb[n / DB], o[n % DB]);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    }
-
-    __builtin_amdgcn_s_waitcnt(0);  // direct loads of the next tile have landed
-    __syncthreads();
-  }
-
-  // ---- epilogue ---------------------------------------------------------
-  const float lsum = pair_sum(l_run);
-  if (!valid) return;
-  const size_t orow = (size_t)(b * p.Hq + hq) * p.qL + qi;
-  if (!p.partials) {
-    const float inv = 1.0f / lsum;
-    uint16_t* dst = p.out + orow * D + od0;
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const int d = db * 32 + 8 * q4 + 4 * lg;
-        uint2 w;
-        w.x = Elem<DT>::pack2(o[db][4 * q4 + 0] * inv, o[db][4 * q4 + 1] * inv);
-        w.y = Elem<DT>::pack2(o[db][4 * q4 + 2] * inv, o[db][4 * q4 + 3] * inv);
-        *(uint2*)(dst + d) = w;
-      }
-  } else {
-    const size_t prow = orow * p.nsplit + split;
-    float* dst = p.part_o + prow * D + od0;
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const int d = db * 32 + 8 * q4 + 4 * lg;
-        *(float4*)(dst + d) =
-            make_float4(o[db][4 * q4 + 0], o[db][4 * q4 + 1], o[db][4 * q4 + 2], o[db][4 * q4 + 3]);
-      }
-    if (lg == 0 && h == 0) {
-      p.part_ml[prow * 2 + 0] = (m_ref == -INFINITY) ? -INFINITY : m_ref * sl2;
-      p.part_ml[prow * 2 + 1] = lsum;
-    }
-  }
-}
-
-// ---------------------------------------------------------------------------
-// D = 256: one wave per SIMD, 32 rows x all 256 columns per wave, software
-// pipelined over tiles.  While the MFMAs of S(t+1) = K(t+1) Q^T run, the same
-// wave computes exp / sum / pack of tile t; while the MFMAs of O += P(t) V(t)
-// run, it masks and takes the row max of S(t+1).  MFMAs and the vector work
-// between them are independent, so the matrix unit keeps busy through the
-// softmax.  K and V have separate double buffers, V one tile behind K:
-// iteration t reads K(t+1) and V(t) and loads K(t+2) and V(t+1).
-// ---------------------------------------------------------------------------
-template <int DT>
-__device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* lds) {
-  constexpr int D = 256, NW = 4, BM = 128, BN = 64, KB = 2, DC = 16, DB = 8;
-  constexpr int ROWCH = D / 8, TILE = BN * D, LOADS = TILE * 2 / 1024 / NW;
-  static_assert(BM == block_rows(D) && BN == tile_keys(D), "geometry");
-  static_assert(LOADS == 8, "one K and one V load per wave per 1 KiB block");
-
-  const int tid = threadIdx.x;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int lane = tid & 63, lr = lane & 31, lg = lane >> 5;
-
-  const int nheads = p.B * p.Hkv;
-  const int head = blockIdx.x % nheads;
-  const int mbr = blockIdx.x / nheads;
-  const int mb = p.causal ? (p.mblocks - 1 - mbr) : mbr;
-  const int split = blockIdx.y;
-  const int b = head / p.Hkv, hkv = head % p.Hkv;
-
-  const int row0 = mb * BM;
-  const int rows_end = min(p.rows, row0 + BM);
-  const int wrow0 = row0 + wave * kRowsPerWave;
   const bool wave_active = wrow0 < rows_end;
   const int my = wrow0 + lr;
   const bool valid = my < rows_end;
@@ -535,7 +202,7 @@ __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* ld
 
   uint4 qf[DC];
   {
-    const uint16_t* qrow = p.q + ((size_t)(b * p.Hq + hq) * p.qL + qi) * D;
+    const uint16_t* qrow = p.q + ((size_t)(b * p.Hq + hq) * p.qL + qi) * D + qd0;
 #pragma unroll
     for (int dc = 0; dc < DC; ++dc)
       qf[dc] = valid ? *(const uint4*)(qrow + dc * 16 + lg * 8) : make_uint4(0, 0, 0, 0);
@@ -550,22 +217,23 @@ __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* ld
   float l_run = 0.f;
   const float sl2 = p.sl2;
 
-  // LDS operand offsets.  K (key row 32 kb + lr, chunk 2 dc + lg, stored at
-  // chunk position (2 dc + lg) ^ (lr & 15)): the swizzle flips bits 3-6 of
-  // the element offset, which nothing else occupies, so one per-lane base
-  // and an XOR with 16 (dc & 7) cover every dc.
-  const int kbase = lr * D + 8 * (lg ^ (lr & 1)) + 16 * ((lr & 15) >> 1);
+  // LDS operand offsets.  K (key row 32 kb + lr, chunk qd0 / 8 + 2 dc + lg,
+  // stored at chunk position (qd0 / 8 + 2 dc + lg) ^ (lr & 15)): the swizzle
+  // flips bits 3-6 of the element offset, which nothing else occupies, so
+  // one per-lane base and an XOR with 16 (dc & 7) cover every dc.
+  const int kbase = lr * D + qd0 + 8 * (lg ^ (lr & 1)) + 16 * ((lr & 15) >> 1);
   auto kaddr = [&](int kb, int dc) { return (kbase ^ (16 * (dc & 7))) + 16 * (dc & 8) + kb * 32 * D; };
   int vlane;
   {
     const int g = lane >> 4, kq = 4 * (g >> 1) + ((lane >> 2) & 3);
-    vlane = kq * D + 32 * kq + 16 * (g & 1) + 4 * (lane & 3);
+    vlane = kq * D + (od0 ^ (32 * kq)) + 16 * (g & 1) + 4 * (lane & 3);
   }
   // K(t) lives in K buffer (t - t_first) & 1, V(t) in V buffer (t - t_first)
   // & 1: the steps come in pairs, so inside a step every buffer offset is a
   // compile-time immediate of the LDS instructions
   uint16_t* const kbuf0 = lds;
   uint16_t* const vbuf0 = lds + 2 * TILE;
+  float* const xch = (float*)(lds + 4 * TILE);  // pair score exchange (D = 512)
 
   // direct loads of one K or V tile (swizzles as in the paired kernel)
   auto load_tile = [&](const uint16_t* g, int t, uint16_t* buf, bool is_v) {
@@ -692,8 +360,8 @@ __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* ld
   // the direct loads of K(tk) into kdst and V(tv) into vdst
   auto qk_weights = [&](f32x16_t (&sn)[KB], const uint16_t* kl, f32x16_t (&sc)[KB],
                         uint4 (&pb)[KB * 2], int tk, uint16_t* kdst, int tv, uint16_t* vdst) {
-    constexpr int NQK = KB * DC, PF = 4;
-    static_assert(NQK == KB * 16, "one score element per slot");
+    constexpr int NQK = KB * DC, PF = 4, LS = NQK / LOADS;
+    static_assert(NQK == KB * 16 && LS >= 2 && LS % 2 == 0, "slot pattern");
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
@@ -721,12 +389,12 @@ __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* ld
       if (n + PF < NQK) a[n % PF] = kread(n + PF, x_next);
       sn[n % KB] = Elem<DT>::mfma(cur_a, qf[n / KB], sn[n % KB]);
       if (n + PF + 1 < NQK) x_next = kx(n + PF + 1);
-      // loads: K block n / 4 at slot n % 4 == 0, V block n / 4 at n % 4 == 2,
-      // each with its lane offset formed in the slot before
-      if (n % 4 == 0) load_issue(kg, tk, kdst, n / 4, loff);
-      if (n % 4 == 2) load_issue(vg, tv, vdst, n / 4, loff);
-      if (n % 4 == 1) loff = load_off(tv, true, n / 4);
-      if (n % 4 == 3 && n + 1 < NQK) loff = load_off(tk, false, (n + 1) / 4);
+      // loads: K block i at slot i LS, V block i at slot i LS + LS / 2, each
+      // with its lane offset formed in the slot before
+      if (n % LS == 0) load_issue(kg, tk, kdst, n / LS, loff);
+      if (n % LS == LS / 2) load_issue(vg, tv, vdst, n / LS, loff);
+      if ((n + 1) % LS == LS / 2) loff = load_off(tv, true, (n + 1) / LS);
+      else if ((n + 1) % LS == 0 && n + 1 < NQK) loff = load_off(tk, false, (n + 1) / LS);
       // weights: fma of element n + 2, exp of n + 1, sum and pack of n
       if (n + 2 < NQK) set(n + 2, get(n + 2) * sl2 - msc);
       if (n + 1 < NQK) set(n + 1, fast_exp2(get(n + 1)));
@@ -796,6 +464,31 @@ __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* ld
     return alpha;
   };
 
+  // D = 512: complete this wave's partial scores with the partner's (every
+  // wave of the workgroup passes the barrier; waves without rows only wait)
+  auto exchange = [&](f32x16_t (&s)[KB], bool active) {
+    if constexpr (PAIR) {
+      if (active) {
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4)
+          *(float4*)(xch + (wave * 4 + q4) * 256 + lane * 4) =
+              make_float4(s[0][4 * q4 + 0], s[0][4 * q4 + 1], s[0][4 * q4 + 2], s[0][4 * q4 + 3]);
+      }
+      __syncthreads();
+      if (active) {
+        const float* px = xch + (wave ^ 1) * 4 * 256 + lane * 4;
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const float4 x = *(const float4*)(px + q4 * 256);
+          s[0][4 * q4 + 0] += x.x;
+          s[0][4 * q4 + 1] += x.y;
+          s[0][4 * q4 + 2] += x.z;
+          s[0][4 * q4 + 3] += x.w;
+        }
+      }
+    }
+  };
+
   // ---- prologue: K(t0), V(t0), K(t0 + 1); S(t0) and its row max ------------
   load_k(t_first);
   load_v(t_first);
@@ -805,8 +498,9 @@ __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* ld
 
   f32x16_t sA[KB], sB[KB];
   float alpha_cur = 1.f;
+  if (wave_active) qk(sA, kbuf0);
+  exchange(sA, wave_active);
   if (wave_active) {
-    qk(sA, kbuf0);
     if (!full_tile(t_first)) mask(sA, t_first);
     alpha_cur = row_max(sA);
   }
@@ -831,6 +525,7 @@ __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* ld
     rescale(alpha_cur);
     const float psum = qk_weights(sn, kbuf0 + (1 - P) * TILE, sc, pb, tk, kbuf0 + P * TILE, tv,
                                   vbuf0 + (1 - P) * TILE);
+    exchange(sn, true);
     l_run = l_run * alpha_cur + psum;
     // the mask is applied to every tile (a few vector ops per MFMA slot,
     // hidden under the MFMA): one copy of the region, no branch
@@ -848,6 +543,7 @@ __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* ld
     for (int t = t_first; t <= t_last; ++t) {
       if (t + 2 <= t_last) load_k(t + 2);
       if (t < t_last) load_v(t + 1);
+      exchange(sA, false);
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
     }
@@ -859,7 +555,7 @@ __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* ld
   const size_t orow = (size_t)(b * p.Hq + hq) * p.qL + qi;
   if (!p.partials) {
     const float inv = 1.0f / lsum;
-    uint16_t* dst = p.out + orow * D;
+    uint16_t* dst = p.out + orow * D + od0;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -872,7 +568,7 @@ __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* ld
       }
   } else {
     const size_t prow = orow * p.nsplit + split;
-    float* dst = p.part_o + prow * D;
+    float* dst = p.part_o + prow * D + od0;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -881,7 +577,7 @@ __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* ld
         *(float4*)(dst + d) =
             make_float4(o[db][4 * q4 + 0], o[db][4 * q4 + 1], o[db][4 * q4 + 2], o[db][4 * q4 + 3]);
       }
-    if (lg == 0) {
+    if (lg == 0 && h == 0) {
       p.part_ml[prow * 2 + 0] = (m_ref == -INFINITY) ? -INFINITY : m_ref * sl2;
       p.part_ml[prow * 2 + 1] = lsum;
     }
@@ -892,13 +588,14 @@ template <int DT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void attn_tile_kernel_d256(AttnParams p) {
   __shared__ __attribute__((aligned(16))) uint16_t lds[4 * 64 * 256];  // 2 K + 2 V tiles
-  attn_pipe_body<DT>(p, lds);
+  attn_pipe_body<DT, 256>(p, lds);
 }
 template <int DT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void attn_tile_kernel_d512(AttnParams p) {
-  __shared__ __attribute__((aligned(16))) uint16_t lds[4 * Geom<512>::TILE + 2 * Geom<512>::XCH];
-  attn_tile_body<DT, 512>(p, lds);
+  // 2 K + 2 V tiles of 32 x 512, then the pair score exchange (4 waves x 4 KiB)
+  __shared__ __attribute__((aligned(16))) uint16_t lds[4 * 32 * 512 + 2 * 4 * 64 * 16];
+  attn_pipe_body<DT, 512>(p, lds);
 }
 
 // Merge of the per-split partials of each output row.  One workgroup of nw =
@@ -992,7 +689,7 @@ hipError_t launch_attention_t(const AttnParams& p, hipStream_t stream) {
   if constexpr (D == 256)
     hipLaunchKernelGGL((attn_tile_kernel_d256<DT>), grid, dim3(256), 0, stream, p);
   else
-    hipLaunchKernelGGL((attn_tile_kernel_d512<DT>), grid, dim3(Geom<512>::NT), 0, stream, p);
+    hipLaunchKernelGGL((attn_tile_kernel_d512<DT>), grid, dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 
