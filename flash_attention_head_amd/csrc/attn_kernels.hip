@@ -107,6 +107,24 @@ __device__ __forceinline__ void load_lds16(const void* sbase, uint32_t voff, voi
       : "v"(voff), "s"(sa), "s"(base));
 }
 
+// (m & x) | (~m & y) bit by bit, one v_bfi_b32 (the compiler does not form
+// it from the and/or expression).
+__device__ __forceinline__ float bit_select(int m, float x, uint32_t y) {
+  float r;
+  asm("v_bfi_b32 %0, %1, %2, %3" : "=v"(r) : "v"(m), "v"(x), "s"(y));
+  return r;
+}
+
+// max(a, b, c) in one v_max3_f32.  fmaxf on values the compiler cannot prove
+// canonical gets extra self-max ops to quiet signalling NaNs; the scores
+// here are finite or -inf (garbage only in the discarded step after the
+// last tile), so they need none.
+__device__ __forceinline__ float max3(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
 // Max and sum over the two lanes (l, l ^ 32) that share a query row.
 __device__ __forceinline__ float pair_max(float v) {
   const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(int, v),
@@ -429,9 +447,20 @@ __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* ld
       const uint2 lo = read_tr(va), hi = read_tr(va + 8 * D);
       return make_uint4(lo.x, lo.y, hi.x, hi.y);
     };
+    // visibility of the tile's elements as a 64-bit mask over c (the
+    // element's key minus ts + 4 lg): bit c set iff lo4 <= c <= hi4
     int lo4, hi4;
     vis_bounds(tn, lo4, hi4);
+    uint32_t vmask[2];
+    {
+      const int lo = min(max(lo4, 0), 64), hi = min(max(hi4 + 1, 0), 64);  // [lo, hi)
+      auto ones = [](int n) { return n >= 32 ? 0xffffffffu : ((1u << n) - 1u); };  // n in [0, 32]
+      vmask[0] = ones(min(hi, 32)) & ~ones(min(lo, 32));
+      vmask[1] = ones(max(hi - 32, 0)) & ~ones(max(lo - 32, 0));
+    }
     auto ce = [](int e) { return 32 * (e / 16) + 8 * ((e % 16) >> 2) + (e & 3); };
+    // 0 or all ones from bit c, then a bit-select between the score and -inf
+    auto keep = [&](int e) { return __builtin_amdgcn_sbfe((int)vmask[ce(e) / 32], ce(e) % 32, 1); };
     auto get = [&](int e) { return sn[e / 16][e % 16]; };
     auto set = [&](int e, float v) { sn[e / 16][e % 16] = v; };
     float mx = -INFINITY;
@@ -439,23 +468,27 @@ __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* ld
 #pragma unroll
     for (int i = 0; i < PF; ++i) bv[i] = vread(i, vx(i));
     int x_next = vx(PF);
-    bool vis = (ce(0) >= lo4) & (ce(0) <= hi4);
-    float xm = -INFINITY;  // masked element of the previous slot
+    int kp = keep(0);
+    const uint32_t ninf_bits = __builtin_amdgcn_readfirstlane(0xff800000u);  // -inf, in an SGPR
+    float x1 = -INFINITY, x2 = -INFINITY;  // masked elements of the last two slots
 #pragma unroll
     for (int n = 0; n < NPV; ++n) {
       const uint4 cur_b = bv[n % PF];
       if (n + PF < NPV) bv[n % PF] = vread(n + PF, x_next);
       o[n % DB] = Elem<DT>::mfma(cur_b, pb[n / DB], o[n % DB]);
+      // the select of element n (its bit came a slot earlier, kept for the
+      // weights), the bit of n + 1, every other slot the max of the two
+      // elements before
+      const float xn = bit_select(kp, get(n), ninf_bits);
+      if (n + 1 < NPV) kp = keep(n + 1);
       if (n + PF + 1 < NPV) x_next = vx(n + PF + 1);
-      // max of element n - 1, select (kept for the weights) of n, compares
-      // of n + 1
-      mx = fmaxf(mx, xm);
-      xm = vis ? get(n) : -INFINITY;
-      set(n, xm);
-      if (n + 1 < NPV) vis = (ce(n + 1) >= lo4) & (ce(n + 1) <= hi4);
+      if (n & 1) mx = max3(mx, x2, x1);
+      set(n, xn);
+      x2 = x1;
+      x1 = xn;
       __builtin_amdgcn_sched_barrier(0);
     }
-    mx = fmaxf(mx, xm);
+    mx = max3(mx, x2, x1);
     mx = pair_max(mx);
     // live == false: the scores were of no tile (the step after the last)
     const bool upd = live && (mx * sl2 > m_ref * sl2 + kRescaleLog2);
