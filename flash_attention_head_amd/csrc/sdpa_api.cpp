@@ -69,17 +69,31 @@ SplitPlan plan_split(int B, int Hq, int Hkv, int qL, int kL, int D) {
     sp.partials = 1;
     return sp;
   }
-  // prefill: split the keys only when the row blocks alone cannot fill the chip
+  // prefill: split the keys only when the row blocks alone cannot fill the
+  // chip (one workgroup per CU at a time).  Among the split counts from the
+  // smallest that fills one round upward, take the first whose last round
+  // of workgroups is at least 90% full (else the fullest): fewer splits mean
+  // less partial traffic for the combine.
   const int64_t rows = (int64_t)(Hq / Hkv) * qL;
   const int64_t wgs = (int64_t)B * Hkv * ceil_div(rows, block_rows(D));
-  const int64_t want = 2 * kPlannedCUs;
+  const int64_t cus = kPlannedCUs;
   const int64_t min_split_keys = 2048;
   sp.nsplit = 1;
   sp.split_len = (int)(ceil_div(kL, 1024) * 1024);
   sp.partials = 0;
-  if (wgs < want && kL >= 2 * min_split_keys) {
-    int64_t n = ceil_div(want, wgs);
+  if (wgs < cus && kL >= 2 * min_split_keys) {
     const int64_t nmax = kL / min_split_keys;
+    const int64_t nmin = ceil_div(cus, wgs);
+    int64_t n = nmin;
+    double best = 0.0;
+    for (int64_t c = nmin; c <= 4 * nmin && c <= nmax; ++c) {
+      const double fill = (double)(wgs * c) / (double)(ceil_div(wgs * c, cus) * cus);
+      if (fill > best + 1e-9) {
+        best = fill;
+        n = c;
+      }
+      if (fill >= 0.9) break;
+    }
     if (n > nmax) n = nmax;
     if (n > 1) {
       const int64_t len = ceil_div(ceil_div(kL, n), 1024) * 1024;
