@@ -63,10 +63,19 @@ bool overlap(const void* a, size_t an, const void* b, size_t bn) {
 SplitPlan plan_split(int B, int Hq, int Hkv, int qL, int kL, int D) {
   SplitPlan sp;
   if (qL <= kDecodeMaxRows) {
-    // decode / verify: always the split path, fixed absolute chunks
-    sp.split_len = kDecodeChunk;
-    sp.nsplit = (int)ceil_div(kL, kDecodeChunk);
+    // decode / verify: always the split path, with chunks at absolute key
+    // positions.  The chunk is kDecodeChunk times a power of two, the
+    // largest that still gives one workgroup per CU for a full round; it
+    // depends on B, Hkv, kL and D only, never on qL, so a verify row gets
+    // the same chunks, and the same bits, as the single-row call.
+    const int64_t heads = (int64_t)B * Hkv;
+    int64_t chunk = kDecodeChunk;
+    while (heads * ceil_div(kL, 2 * chunk) >= kPlannedCUs && 2 * chunk <= (int64_t)INT32_MAX / 2)
+      chunk *= 2;
+    sp.split_len = (int)chunk;
+    sp.nsplit = (int)ceil_div(kL, chunk);
     sp.partials = 1;
+    (void)D;
     return sp;
   }
   // prefill: split the keys only when the row blocks alone cannot fill the

@@ -19,9 +19,10 @@ constexpr int block_rows(int D) { return kWaves / d_split(D) * kRowsPerWave; }
 // Keys per LDS tile, by head dimension.
 constexpr int tile_keys(int D) { return D == 512 ? 32 : 64; }
 
-// Key chunk of the split path used by every call with qL <= kDecodeMaxRows.
-// It is a fixed constant, so chunk boundaries sit at absolute key positions
-// (multiples of kDecodeChunk) whatever kL and qL are.
+// Smallest key chunk of the split path used by every call with
+// qL <= kDecodeMaxRows.  The chunk actually used is this times a power of
+// two chosen from the shape without qL, so chunk boundaries sit at absolute
+// key positions and do not depend on how many query rows a call has.
 constexpr int kDecodeChunk = 1024;
 constexpr int kDecodeMaxRows = 4;
 

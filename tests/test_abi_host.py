@@ -112,14 +112,41 @@ def test_workspace_is_zero_without_a_split(lib):
     assert fa.sdpa_workspace_bytes(1, 2, 1, 128, 128, 256) == 0
 
 
+def decode_chunks(ws, B, Hq, qL, D):
+    """Key chunks of a decode/verify call, read off its workspace size."""
+    per = B * Hq * qL * (D + 2) * 4  # one fp32 (m, l, O[D]) partial per row and chunk
+    assert ws % per == 0
+    return ws // per
+
+
+def test_decode_chunks_depend_on_the_shape_not_on_qL(lib):
+    # verify rows must see exactly the chunks a single-row call sees
+    for (B, Hq, Hkv, kL, D) in [(1, 16, 8, 131072, 256), (1, 32, 4, 32768, 512), (2, 8, 2, 5000, 256),
+                                (1, 16, 8, 1000, 256), (4, 64, 8, 65536, 256)]:
+        n = {qL: decode_chunks(fa.sdpa_workspace_bytes(B, Hq, Hkv, qL, kL, D), B, Hq, qL, D)
+             for qL in (1, 2, 3, 4)}
+        assert len(set(n.values())) == 1, n
+
+
+def test_decode_chunk_is_the_largest_that_fills_the_chip(lib):
+    # chunk = 1024 * 2^k at absolute key positions: the largest for which the
+    # (b, kv head) x chunk workgroups still make one full round of 256
+    for (B, Hq, Hkv, kL) in [(1, 16, 8, 131072), (1, 16, 8, 4096), (1, 8, 8, 1 << 20), (2, 32, 16, 65536)]:
+        n = decode_chunks(fa.sdpa_workspace_bytes(B, Hq, Hkv, 4, kL, 256), B, Hq, 4, 256)
+        chunk = next(c for c in (1024 << k for k in range(20)) if -(-kL // c) == n)
+        heads = B * Hkv
+        assert chunk == 1024 or heads * n >= 256
+        assert heads * -(-kL // (2 * chunk)) < 256
+    # the verify workload: 8 KV heads x 32 chunks of 4096 keys = 256 workgroups
+    assert decode_chunks(fa.sdpa_workspace_bytes(1, 16, 8, 4, 131072, 256), 1, 16, 4, 256) == 32
+
+
 def test_workspace_is_linear_in_key_chunks_not_quadratic(lib):
-    # decode/verify: one fp32 (m, l, O[D]) partial per row and 1024-key chunk
     for qL in (1, 2, 4):
         prev = None
-        for kL in (1000, 1024, 1025, 4096, 65536, 131072):
+        for kL in (1000, 1024, 1025, 4096, 65536, 131072, 1 << 20):
             ws = fa.sdpa_workspace_bytes(1, 16, 8, qL, kL, 256)
-            chunks = -(-kL // 1024)
-            assert ws == 16 * qL * chunks * (256 + 2) * 4
+            assert ws <= 16 * qL * (-(-kL // 1024)) * (256 + 2) * 4
             if prev is not None:
                 assert ws >= prev
             prev = ws
