@@ -52,6 +52,10 @@ struct Elem<0> {  // IEEE binary16
     // one v_cvt_pk_f16_f32, round to nearest even
     return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){lo, hi}, f16x2_t));
   }
+  // acc + lo + hi of a packed pair, in fp32 (one v_dot2_f32_f16 against 1, 1)
+  static __device__ __forceinline__ float sum2(uint32_t w, float acc) {
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, w), (f16x2_t){1.0f16, 1.0f16}, acc, false);
+  }
 };
 
 template <>
@@ -63,6 +67,10 @@ struct Elem<1> {  // bfloat16
   static __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
     // one v_cvt_pk_bf16_f32, round to nearest even
     return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){lo, hi}, bf16x2_t));
+  }
+  // acc + lo + hi of a packed pair, in fp32 (one v_dot2_f32_bf16 against 1, 1)
+  static __device__ __forceinline__ float sum2(uint32_t w, float acc) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w), (bf16x2_t){1.0f, 1.0f}, acc, false);
   }
 };
 
@@ -81,30 +89,57 @@ __device__ __forceinline__ uint2 read_tr(const uint16_t* p) {
   return __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4_t*)p));
 }
 
-// One 16-byte-per-lane direct global->LDS load from sbase + voff bytes
-// (sbase uniform, voff per lane): lane l's 16 bytes land at lds + 16 l.
-// Issued through inline assembly so that the compiler does not treat it as a
-// pending LDS write and wait for it before every later LDS access; the kernel
-// waits for these loads itself, before the barrier that publishes the tile
-// they fill.  M0 (the LDS base of the instruction) is restored afterwards;
-// writing M0 needs one wait state before the load.
-__device__ __forceinline__ void load_lds16(const void* sbase, uint32_t voff, void* lds) {
-  const unsigned base = __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)lds);
-  // the 64-bit base, moved to scalar registers half by half; readfirstlane
-  // returns int, so each half goes through uint32_t (no sign extension)
-  const uint64_t a = (uint64_t)(uintptr_t)sbase;
+// One 16-byte-per-lane direct load into LDS through a buffer descriptor:
+// lane l reads the 16 bytes at base + voff and writes them to lds + 16 l.
+// base, nbytes and lds are uniform.  A lane whose voff is nbytes or more is
+// out of the descriptor's range: the hardware reads zeros for it instead of
+// touching memory, so rows past the end of a K/V slab arrive as zeros with
+// no per-lane clamp.  Issued through inline assembly so that the compiler
+// does not treat it as a pending LDS write and wait for it before every
+// later LDS access; the kernel waits for these loads itself, before the
+// barrier that publishes the tile they fill.  M0 (the LDS base of the
+// instruction) is restored afterwards; writing M0 needs one wait state
+// before the load.
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+// descriptor word 3 for untyped loads on gfx9-family GPUs: data format 32,
+// no index stride, no swizzle
+constexpr int kRsrcWord3 = 0x00020000;
+
+// The 64-bit address of a uniform pointer in scalar registers (readfirstlane
+// returns int, so each half goes through uint32_t: no sign extension).
+__device__ __forceinline__ uint64_t uniform_addr(const void* ptr) {
+  const uint64_t a = (uint64_t)(uintptr_t)ptr;
   const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((unsigned)a);
   const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((unsigned)(a >> 32));
-  const uint64_t sa = ((uint64_t)hi << 32) | (uint64_t)lo;
-  unsigned saved;
+  return ((uint64_t)hi << 32) | lo;
+}
+
+// Descriptor of `bytes` bytes from `base` (a uniform_addr value); word 1
+// holds address bits 32..47 and a zero stride.
+__device__ __forceinline__ i32x4_t tile_rsrc(uint64_t base, int bytes) {
+  return i32x4_t{(int)(uint32_t)base, (int)((uint32_t)(base >> 32) & 0xffffu), bytes, kRsrcWord3};
+}
+
+// M0 holds the LDS base of a direct load.  No code the compiler generates
+// for these kernels reads or writes M0 (a host test checks the generated
+// assembly), so a run of loads saves M0 once, sets it per load and restores
+// it after the last one.
+__device__ __forceinline__ unsigned m0_save() {
+  unsigned s;
+  asm volatile("s_mov_b32 %0, m0" : "=s"(s));
+  return s;
+}
+__device__ __forceinline__ void m0_restore(unsigned s) { asm volatile("s_mov_b32 m0, %0" ::"s"(s)); }
+
+// Call between m0_save and m0_restore.  Writing M0 needs one wait state
+// before the load.
+__device__ __forceinline__ void load_lds16(i32x4_t rsrc, uint32_t voff, void* lds) {
+  const unsigned m0v = __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)lds);
   asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %3\n\t"
+      "s_mov_b32 m0, %2\n\t"
       "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %1, %2\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "v"(voff), "s"(sa), "s"(base));
+      "buffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff),
+      "s"(rsrc), "s"(m0v));
 }
 
 // (m & x) | (~m & y) bit by bit, one v_bfi_b32 (the compiler does not form
@@ -196,8 +231,10 @@ __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* ld
   const int qi = valid ? my / p.G : 0;
   const int hq = hkv * p.G + (valid ? my % p.G : 0);
   const int pos = p.q_offset + qi;
-  const int wp_lo = p.q_offset + wrow0 / p.G;
-  const int wp_hi = p.q_offset + (min(rows_end, wrow0 + kRowsPerWave) - 1) / p.G;
+  // first and last query position of the wave's rows (uniform; scalar
+  // registers, so that tile tests on them are scalar branches)
+  const int wp_lo = __builtin_amdgcn_readfirstlane(p.q_offset + wrow0 / p.G);
+  const int wp_hi = __builtin_amdgcn_readfirstlane(p.q_offset + (min(rows_end, wrow0 + kRowsPerWave) - 1) / p.G);
 
   int kbeg = 0, kend = p.kL;
   {
@@ -253,45 +290,43 @@ __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* ld
   uint16_t* const vbuf0 = lds + 2 * TILE;
   float* const xch = (float*)(lds + 4 * TILE);  // pair score exchange (D = 512)
 
-  // direct loads of one K or V tile (swizzles as in the paired kernel)
+  // Direct loads of one K or V tile: LOADS blocks of 1 KiB (RPB key rows
+  // each) per wave, the n-th at block b = wave + NW n.  Lane l reads row
+  // l / ROWCH of the block at chunk (l % ROWCH) ^ swizzle(row) and lands at
+  // LDS position l, which puts chunk c of key row r at c ^ (r & 15) (K) or
+  // c ^ ((r & 7) << 2) (V).  The lane offsets from the tile start are
+  // loop-invariant registers; the tile start and its bytes before key kL
+  // form the buffer descriptor, so rows past kL read zeros.
+  constexpr int RPB = 1024 / (2 * D);  // key rows per 1 KiB block
+  static_assert(RPB * ROWCH == 64, "block geometry");
+  auto lane_off = [&](bool is_v, int n) {
+    const int r = (wave + NW * n) * RPB + lane / ROWCH;  // key row in the tile
+    const int pch = lane % ROWCH;
+    const int c = is_v ? (pch ^ ((r & 7) << 2)) : (pch ^ (r & 15));
+    return (uint32_t)(r * 2 * D + 16 * c);
+  };
+  uint32_t koff[LOADS], voff[LOADS];
+#pragma unroll
+  for (int n = 0; n < LOADS; ++n) {
+    koff[n] = lane_off(false, n);
+    voff[n] = lane_off(true, n);
+  }
+  auto tile_src = [&](const uint16_t* g, int t) {
+    const int ts = __builtin_amdgcn_readfirstlane(t * BN);
+    return tile_rsrc(uniform_addr(g + (size_t)ts * D), __builtin_amdgcn_readfirstlane(min(p.kL - ts, BN) * 2 * D));
+  };
+  auto load_blk = [&](i32x4_t src, uint16_t* buf, int n, bool is_v) {
+    load_lds16(src, is_v ? voff[n] : koff[n], buf + (wave + NW * n) * 512);
+  };
   auto load_tile = [&](const uint16_t* g, int t, uint16_t* buf, bool is_v) {
-    const int ts = t * BN;
-    const uint16_t* gt = g + (size_t)ts * D;
-    const int nrow = p.kL - ts;
-    auto one = [&](int n, bool clamp) {
-      const int cb = wave * LOADS + n;
-      const int row = cb * (64 / ROWCH) + lane / ROWCH;
-      const int pch = lane % ROWCH;
-      const int r = clamp ? min(row, nrow - 1) : row;
-      const int c = is_v ? (pch ^ ((row & 7) << 2)) : (pch ^ (row & 15));
-      load_lds16(gt, (uint32_t)(r * D + c * 8) * 2u, buf + cb * 512);
-    };
-    if (nrow >= BN) {
+    const i32x4_t src = tile_src(g, t);
+    const unsigned m0 = m0_save();
 #pragma unroll
-      for (int n = 0; n < LOADS; ++n) one(n, false);
-    } else {
-#pragma unroll
-      for (int n = 0; n < LOADS; ++n) one(n, true);
-    }
+    for (int n = 0; n < LOADS; ++n) load_blk(src, buf, n, is_v);
+    m0_restore(m0);
   };
   auto load_k = [&](int t) { load_tile(kg, t, kbuf0 + ((t - t_first) & 1) * TILE, false); };
   auto load_v = [&](int t) { load_tile(vg, t, vbuf0 + ((t - t_first) & 1) * TILE, true); };
-  // one of the LOADS direct loads of a tile, rows clamped branch-free (only
-  // the last tile has rows past kL; their keys are masked), for issuing
-  // inside the MFMA regions: a burst of loads stalls the wave on the memory
-  // pipeline, while one load every few MFMAs keeps it busy in the background.
-  // Split in two so that the lane offset can be formed a slot ahead.
-  auto load_off = [&](int t, bool is_v, int n) {
-    const int cb = wave * LOADS + n;
-    const int row = cb * (64 / ROWCH) + lane / ROWCH;
-    const int pch = lane % ROWCH;
-    const int r = min(row, p.kL - 1 - t * BN);
-    const int c = is_v ? (pch ^ ((row & 7) << 2)) : (pch ^ (row & 15));
-    return (uint32_t)(r * D + c * 8) * 2u;
-  };
-  auto load_issue = [&](const uint16_t* g, int t, uint16_t* buf, int n, uint32_t off) {
-    load_lds16(g + (size_t)(t * BN) * D, off, buf + (wave * LOADS + n) * 512);
-  };
 
   // the keys row `pos` sees form one interval [key_lo, key_hi] (empty if
   // key_hi < key_lo)
@@ -328,21 +363,23 @@ __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* ld
   };
   // keys of tile t a row may not see -> -inf.  Score element (kb, j) holds
   // key ts + 4 lg + c with c = 32 kb + 8 (j / 4) + j % 4 a compile-time
-  // constant, so it is visible iff lo4 <= c <= hi4 for two per-tile values.
-  auto vis_bounds = [&](int t, int& lo4, int& hi4) {
-    lo4 = key_lo - t * BN - 4 * lg;
-    hi4 = key_hi - t * BN - 4 * lg;
-  };
-  auto mask_elem = [](float x, int c, int lo4, int hi4) {
-    return ((c >= lo4) & (c <= hi4)) ? x : -INFINITY;
-  };
+  // constant, so it is visible iff lo4 <= c <= hi4 for two per-tile values:
+  // the tile's visibility is a 64-bit mask over c, and each element takes a
+  // bit extract and a bit-field insert of -inf.  Only tiles that are not
+  // wholly visible to the wave's rows come here (a uniform branch).
   auto mask = [&](f32x16_t (&s)[KB], int t) {
-    int lo4, hi4;
-    vis_bounds(t, lo4, hi4);
+    const int lo4 = key_lo - t * BN - 4 * lg, hi4 = key_hi - t * BN - 4 * lg;
+    const int lo = min(max(lo4, 0), 64), hi = min(max(hi4 + 1, 0), 64);  // visible c in [lo, hi)
+    auto ones = [](int n) { return n >= 32 ? 0xffffffffu : ((1u << n) - 1u); };  // n in [0, 32]
+    const uint32_t vmask[2] = {ones(min(hi, 32)) & ~ones(min(lo, 32)), ones(max(hi - 32, 0)) & ~ones(max(lo - 32, 0))};
+    const uint32_t ninf_bits = __builtin_amdgcn_readfirstlane(0xff800000u);  // -inf, in an SGPR
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-      for (int j = 0; j < 16; ++j) s[kb][j] = mask_elem(s[kb][j], 32 * kb + 8 * (j >> 2) + (j & 3), lo4, hi4);
+      for (int j = 0; j < 16; ++j) {
+        const int c = 32 * kb + 8 * (j >> 2) + (j & 3);
+        s[kb][j] = bit_select(__builtin_amdgcn_sbfe((int)vmask[c / 32], c % 32, 1), s[kb][j], ninf_bits);
+      }
   };
   // row max of S(t) -> reference update; returns the factor the running
   // output and sum take before tile t is added
@@ -372,12 +409,12 @@ __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* ld
   //      barriers keep that order.  With one wave per SIMD, instructions
   //      issue in order, so a vector op that needs the result of the op just
   //      before it stalls the MFMA stream: every dependency chain (address ->
-  //      LDS read, fma -> exp -> sum, compare -> select -> max, offset ->
-  //      load) is spread over consecutive slots instead.
+  //      LDS read, fma -> exp -> sum, compare -> select -> max) is spread
+  //      over consecutive slots instead.
   // S(t+1) = K(t+1) Q^T  ||  weights, sum and packing of tile t; also issues
   // the direct loads of K(tk) into kdst and V(tv) into vdst
   auto qk_weights = [&](f32x16_t (&sn)[KB], const uint16_t* kl, f32x16_t (&sc)[KB],
-                        uint4 (&pb)[KB * 2], int tk, uint16_t* kdst, int tv, uint16_t* vdst) {
+                        uint4 (&pb)[KB * 2], i32x4_t ksrc, uint16_t* kdst, i32x4_t vsrc, uint16_t* vdst) {
     constexpr int NQK = KB * DC, PF = 4, LS = NQK / LOADS;
     static_assert(NQK == KB * 16 && LS >= 2 && LS % 2 == 0, "slot pattern");
 #pragma unroll
@@ -394,11 +431,12 @@ __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* ld
     auto get = [&](int e) { return sc[e / 16][e % 16]; };
     auto set = [&](int e, float v) { sc[e / 16][e % 16] = v; };
     float psum = 0.f;
+    uint32_t wlast = 0;
     uint4 a[PF];
 #pragma unroll
     for (int i = 0; i < PF; ++i) a[i] = kread(i, kx(i));
     int x_next = kx(PF);
-    uint32_t loff = load_off(tk, false, 0);
+    const unsigned m0 = m0_save();
     set(0, fast_exp2(get(0) * sl2 - msc));
     set(1, get(1) * sl2 - msc);
 #pragma unroll
@@ -407,18 +445,18 @@ __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* ld
       if (n + PF < NQK) a[n % PF] = kread(n + PF, x_next);
       sn[n % KB] = Elem<DT>::mfma(cur_a, qf[n / KB], sn[n % KB]);
       if (n + PF + 1 < NQK) x_next = kx(n + PF + 1);
-      // loads: K block i at slot i LS, V block i at slot i LS + LS / 2, each
-      // with its lane offset formed in the slot before
-      if (n % LS == 0) load_issue(kg, tk, kdst, n / LS, loff);
-      if (n % LS == LS / 2) load_issue(vg, tv, vdst, n / LS, loff);
-      if ((n + 1) % LS == LS / 2) loff = load_off(tv, true, (n + 1) / LS);
-      else if ((n + 1) % LS == 0 && n + 1 < NQK) loff = load_off(tk, false, (n + 1) / LS);
+      // loads: K block group i at slot i LS, V block group i at slot i LS + LS / 2
+      if (n % LS == 0) load_blk(ksrc, kdst, n / LS, false);
+      if (n % LS == LS / 2) load_blk(vsrc, vdst, n / LS, true);
       // weights: fma of element n + 2, exp of n + 1, sum and pack of n
       if (n + 2 < NQK) set(n + 2, get(n + 2) * sl2 - msc);
       if (n + 1 < NQK) set(n + 1, fast_exp2(get(n + 1)));
-      psum += get(n);
+      // the row sum adds the rounded weights the P V product uses, a pair
+      // per dot2, one slot after the pair is packed
+      if (!(n & 1) && n > 0) psum = Elem<DT>::sum2(wlast, psum);
       if (n & 1) {  // pack the pair (n - 1, n): P half kh = n / 8
         const uint32_t w = Elem<DT>::pack2(get(n - 1), get(n));
+        wlast = w;
         uint4& q = pb[n / 8];
         switch ((n % 8) / 2) {
           case 0: q.x = w; break;
@@ -429,14 +467,15 @@ __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* ld
       }
       __builtin_amdgcn_sched_barrier(0);
     }
+    psum = Elem<DT>::sum2(wlast, psum);
+    m0_restore(m0);
     // an empty volatile use: the sum is formed here, slot by slot, not sunk
     // past the next region as a serial chain
     asm volatile("" ::"v"(psum));
     return psum;
   };
-  // O += P(t) V(t)  ||  mask and row max of S(t+1)
-  auto pv_max = [&](const uint4 (&pb)[KB * 2], const uint16_t* vl, f32x16_t (&sn)[KB], int tn,
-                    bool live) {
+  // O += P(t) V(t)  ||  row max of S(t+1) (already masked)
+  auto pv_max = [&](const uint4 (&pb)[KB * 2], const uint16_t* vl, f32x16_t (&sn)[KB], bool live) {
     constexpr int NPV = KB * 2 * DB, PF = 4;
     static_assert(NPV == KB * 16, "one score element per slot");
     // V^T operand of MFMA n: key half n / DB, column block n % DB; the XOR
@@ -447,48 +486,21 @@ __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* ld
       const uint2 lo = read_tr(va), hi = read_tr(va + 8 * D);
       return make_uint4(lo.x, lo.y, hi.x, hi.y);
     };
-    // visibility of the tile's elements as a 64-bit mask over c (the
-    // element's key minus ts + 4 lg): bit c set iff lo4 <= c <= hi4
-    int lo4, hi4;
-    vis_bounds(tn, lo4, hi4);
-    uint32_t vmask[2];
-    {
-      const int lo = min(max(lo4, 0), 64), hi = min(max(hi4 + 1, 0), 64);  // [lo, hi)
-      auto ones = [](int n) { return n >= 32 ? 0xffffffffu : ((1u << n) - 1u); };  // n in [0, 32]
-      vmask[0] = ones(min(hi, 32)) & ~ones(min(lo, 32));
-      vmask[1] = ones(max(hi - 32, 0)) & ~ones(max(lo - 32, 0));
-    }
-    auto ce = [](int e) { return 32 * (e / 16) + 8 * ((e % 16) >> 2) + (e & 3); };
-    // 0 or all ones from bit c, then a bit-select between the score and -inf
-    auto keep = [&](int e) { return __builtin_amdgcn_sbfe((int)vmask[ce(e) / 32], ce(e) % 32, 1); };
     auto get = [&](int e) { return sn[e / 16][e % 16]; };
-    auto set = [&](int e, float v) { sn[e / 16][e % 16] = v; };
     float mx = -INFINITY;
     uint4 bv[PF];
 #pragma unroll
     for (int i = 0; i < PF; ++i) bv[i] = vread(i, vx(i));
     int x_next = vx(PF);
-    int kp = keep(0);
-    const uint32_t ninf_bits = __builtin_amdgcn_readfirstlane(0xff800000u);  // -inf, in an SGPR
-    float x1 = -INFINITY, x2 = -INFINITY;  // masked elements of the last two slots
 #pragma unroll
     for (int n = 0; n < NPV; ++n) {
       const uint4 cur_b = bv[n % PF];
       if (n + PF < NPV) bv[n % PF] = vread(n + PF, x_next);
       o[n % DB] = Elem<DT>::mfma(cur_b, pb[n / DB], o[n % DB]);
-      // the select of element n (its bit came a slot earlier, kept for the
-      // weights), the bit of n + 1, every other slot the max of the two
-      // elements before
-      const float xn = bit_select(kp, get(n), ninf_bits);
-      if (n + 1 < NPV) kp = keep(n + 1);
       if (n + PF + 1 < NPV) x_next = vx(n + PF + 1);
-      if (n & 1) mx = max3(mx, x2, x1);
-      set(n, xn);
-      x2 = x1;
-      x1 = xn;
+      if (n & 1) mx = max3(mx, get(n - 1), get(n));
       __builtin_amdgcn_sched_barrier(0);
     }
-    mx = max3(mx, x2, x1);
     mx = pair_max(mx);
     // live == false: the scores were of no tile (the step after the last)
     const bool upd = live && (mx * sl2 > m_ref * sl2 + kRescaleLog2);
@@ -523,6 +535,16 @@ __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* ld
   };
 
   // ---- prologue: K(t0), V(t0), K(t0 + 1); S(t0) and its row max ------------
+  // Rows past kL are out of the loads' range.  When this workgroup's last
+  // tile has such rows, the V buffers start as zeros, so that those rows of
+  // a V tile never hold uninitialised LDS (a zero weight times a NaN bit
+  // pattern would still be NaN); K rows past kL need nothing, their scores
+  // are masked to -inf.
+  if ((t_last + 1) * BN > p.kL) {
+    uint4* vz = (uint4*)vbuf0;
+    for (int i = tid; i < 2 * TILE / 8; i += NW * 64) vz[i] = make_uint4(0, 0, 0, 0);
+    __syncthreads();
+  }
   load_k(t_first);
   load_v(t_first);
   if (t_first < t_last) load_k(t_first + 1);
@@ -556,13 +578,12 @@ __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* ld
     // the rescale for tile t first (its factor is known since the last
     // step), so that the interleaved regions are straight-line code
     rescale(alpha_cur);
-    const float psum = qk_weights(sn, kbuf0 + (1 - P) * TILE, sc, pb, tk, kbuf0 + P * TILE, tv,
-                                  vbuf0 + (1 - P) * TILE);
+    const float psum = qk_weights(sn, kbuf0 + (1 - P) * TILE, sc, pb, tile_src(kg, tk), kbuf0 + P * TILE,
+                                  tile_src(vg, tv), vbuf0 + (1 - P) * TILE);
     exchange(sn, true);
     l_run = l_run * alpha_cur + psum;
-    // the mask is applied to every tile (a few vector ops per MFMA slot,
-    // hidden under the MFMA): one copy of the region, no branch
-    alpha_cur = pv_max(pb, vbuf0 + P * TILE, sn, t + 1, has_next);
+    if (!full_tile(t + 1)) mask(sn, t + 1);
+    alpha_cur = pv_max(pb, vbuf0 + P * TILE, sn, has_next);
     __builtin_amdgcn_s_waitcnt(0);  // K(t+2), V(t+1) have landed
     __syncthreads();
   };
