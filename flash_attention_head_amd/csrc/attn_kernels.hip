@@ -131,15 +131,17 @@ __device__ __forceinline__ unsigned m0_save() {
 }
 __device__ __forceinline__ void m0_restore(unsigned s) { asm volatile("s_mov_b32 m0, %0" ::"s"(s)); }
 
-// Call between m0_save and m0_restore.  Writing M0 needs one wait state
-// before the load.
-__device__ __forceinline__ void load_lds16(i32x4_t rsrc, uint32_t voff, void* lds) {
+// Call between m0_save and m0_restore.  Lane l reads base + soff + voff
+// (soff uniform) and is out of range when soff + voff reaches the
+// descriptor's byte count.  Writing M0 needs one wait state before the
+// load.
+__device__ __forceinline__ void load_lds16(i32x4_t rsrc, uint32_t voff, uint32_t soff, void* lds) {
   const unsigned m0v = __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)lds);
   asm volatile(
-      "s_mov_b32 m0, %2\n\t"
+      "s_mov_b32 m0, %3\n\t"
       "s_nop 0\n\t"
-      "buffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff),
-      "s"(rsrc), "s"(m0v));
+      "buffer_load_dwordx4 %0, %1, %2 offen lds" ::"v"(voff),
+      "s"(rsrc), "s"(__builtin_amdgcn_readfirstlane(soff)), "s"(m0v));
 }
 
 // (m & x) | (~m & y) bit by bit, one v_bfi_b32 (the compiler does not form
@@ -294,29 +296,31 @@ __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* ld
   // each) per wave, the n-th at block b = wave + NW n.  Lane l reads row
   // l / ROWCH of the block at chunk (l % ROWCH) ^ swizzle(row) and lands at
   // LDS position l, which puts chunk c of key row r at c ^ (r & 15) (K) or
-  // c ^ ((r & 7) << 2) (V).  The lane offsets from the tile start are
-  // loop-invariant registers; the tile start and its bytes before key kL
-  // form the buffer descriptor, so rows past kL read zeros.
+  // c ^ ((r & 7) << 2) (V).  Block b starts at byte 1024 b of the tile, so
+  // the n-th load's lane offset is a pattern that repeats every KPAT (K) or
+  // VPAT (V) loads plus n NW 1024, which goes into the scalar offset.  The
+  // tile start and its bytes before key kL form the buffer descriptor, so
+  // rows past kL read zeros (the range check covers the scalar offset too).
   constexpr int RPB = 1024 / (2 * D);  // key rows per 1 KiB block
-  static_assert(RPB * ROWCH == 64, "block geometry");
-  auto lane_off = [&](bool is_v, int n) {
+  constexpr int KPAT = 16 / (NW * RPB), VPAT = 8 / (NW * RPB) > 1 ? 8 / (NW * RPB) : 1;
+  static_assert(RPB * ROWCH == 64 && LOADS % KPAT == 0 && LOADS % VPAT == 0, "block geometry");
+  auto lane_off = [&](bool is_v, int n) {  // offset of the n-th load from its block group
     const int r = (wave + NW * n) * RPB + lane / ROWCH;  // key row in the tile
     const int pch = lane % ROWCH;
     const int c = is_v ? (pch ^ ((r & 7) << 2)) : (pch ^ (r & 15));
-    return (uint32_t)(r * 2 * D + 16 * c);
+    return (uint32_t)(r * 2 * D + 16 * c - n * NW * 1024);
   };
-  uint32_t koff[LOADS], voff[LOADS];
+  uint32_t koff[KPAT], voff[VPAT];
 #pragma unroll
-  for (int n = 0; n < LOADS; ++n) {
-    koff[n] = lane_off(false, n);
-    voff[n] = lane_off(true, n);
-  }
+  for (int i = 0; i < KPAT; ++i) koff[i] = lane_off(false, i);
+#pragma unroll
+  for (int i = 0; i < VPAT; ++i) voff[i] = lane_off(true, i);
   auto tile_src = [&](const uint16_t* g, int t) {
     const int ts = __builtin_amdgcn_readfirstlane(t * BN);
     return tile_rsrc(uniform_addr(g + (size_t)ts * D), __builtin_amdgcn_readfirstlane(min(p.kL - ts, BN) * 2 * D));
   };
   auto load_blk = [&](i32x4_t src, uint16_t* buf, int n, bool is_v) {
-    load_lds16(src, is_v ? voff[n] : koff[n], buf + (wave + NW * n) * 512);
+    load_lds16(src, is_v ? voff[n % VPAT] : koff[n % KPAT], (uint32_t)(n * NW * 1024), buf + (wave + NW * n) * 512);
   };
   auto load_tile = [&](const uint16_t* g, int t, uint16_t* buf, bool is_v) {
     const i32x4_t src = tile_src(g, t);

@@ -1,0 +1,67 @@
+"""Properties of the generated gfx950 code that the kernel source relies on.
+
+The direct K/V loads set M0 (the LDS base of an LDS-destination load) from
+inline assembly, saving it once per run of loads instead of once per load.
+That is only sound while no compiler-generated instruction of these kernels
+reads or writes M0, so the assembly is checked for exactly that.  The
+kernels are also meant to run without scratch memory (no register spills).
+Compiles the kernel source with the library's own flags; no GPU needed.
+"""
+
+import os
+import re
+import subprocess
+
+import pytest
+
+from flash_attention_head_amd import build as B
+
+KERNELS = ("attn_tile_kernel_d256", "attn_tile_kernel_d512", "combine_kernel")
+
+
+@pytest.fixture(scope="module")
+def asm(tmp_path_factory):
+    out = str(tmp_path_factory.mktemp("asm") / "attn_kernels.s")
+    flags = [f for f in B.FLAGS if f not in ("-shared", "-fPIC", "-fvisibility=hidden")]
+    cmd = [B.HIPCC, *flags, "--cuda-device-only", "-S", B.SOURCES[0], "-o", out]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr[-2000:]
+    return open(out).read()
+
+
+def _functions(text):
+    """name -> body lines of every kernel in the assembly listing."""
+    funcs = {}
+    for m in re.finditer(r"^(_Z\S+):", text, re.M):
+        name = m.group(1)
+        if not any(k in name for k in KERNELS):
+            continue
+        end = text.index("s_endpgm", m.end())
+        funcs[name] = text[m.end():end].splitlines()
+    return funcs
+
+
+def test_every_kernel_instance_is_present(asm):
+    names = list(_functions(asm))
+    for k in KERNELS:
+        assert sum(k in n for n in names) >= 2, (k, names)  # fp16 and bf16 instances
+
+
+def test_m0_is_touched_only_by_the_inline_assembly(asm):
+    for name, lines in _functions(asm).items():
+        inside = False
+        for ln in lines:
+            if ";;#ASMSTART" in ln:
+                inside = True
+            elif ";;#ASMEND" in ln:
+                inside = False
+            else:
+                code = ln.split(";")[0]
+                assert inside or not re.search(r"\bm0\b", code), (name, ln)
+
+
+def test_no_scratch_memory(asm):
+    sizes = re.findall(r"\.private_segment_fixed_size:\s+(\d+)", asm)
+    spills = re.findall(r"\.vgpr_spill_count:\s+(\d+)", asm) + re.findall(r"\.sgpr_spill_count:\s+(\d+)", asm)
+    assert sizes and all(int(s) == 0 for s in sizes), sizes
+    assert all(int(s) == 0 for s in spills), spills
