@@ -44,13 +44,23 @@ def time_workload(wl, steps, warmup):
 
     q, k, v = (t.cuda() for t in W.draw(wl))
     out = torch.empty_like(q)
-    need = fa.sdpa_workspace_bytes(wl.B, wl.Hq, wl.Hkv, wl.qL, wl.kL, wl.D)
+    # decode / verify steps (qL <= 4) run as they do in a generation loop:
+    # over a KV cache, here a full one of kL rows per head
+    cache = wl.qL <= 4
+    if cache:
+        need = fa.sdpa_workspace_bytes_kv_view(wl.B, wl.Hq, wl.Hkv, wl.qL, wl.kL, wl.kL, wl.D)
+    else:
+        need = fa.sdpa_workspace_bytes(wl.B, wl.Hq, wl.Hkv, wl.qL, wl.kL, wl.D)
     ws = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
     stream = torch.cuda.current_stream()
 
     def call():
-        fa.sdpa(q, k, v, scale=wl.scale, causal=wl.causal, window=wl.window,
-                q_offset=wl.q_offset, out=out, workspace=ws, stream=stream)
+        if cache:
+            fa.sdpa_kv_cache(q, k, v, wl.kL, scale=wl.scale, causal=wl.causal, window=wl.window,
+                             q_offset=wl.q_offset, out=out, workspace=ws, stream=stream)
+        else:
+            fa.sdpa(q, k, v, scale=wl.scale, causal=wl.causal, window=wl.window,
+                    q_offset=wl.q_offset, out=out, workspace=ws, stream=stream)
 
     for _ in range(warmup):
         call()
@@ -69,7 +79,8 @@ def time_workload(wl, steps, warmup):
     del q, k, v, out, ws
     torch.cuda.empty_cache()
     return {"wall_ms": wall_ms, "event_ms_mean": mean, "event_ms_min": per[0],
-            "event_ms_median": per[len(per) // 2], "workspace_bytes": need}
+            "event_ms_median": per[len(per) // 2], "workspace_bytes": need,
+            "entry": "sdpa_forward_kv_view" if cache else "sdpa_forward"}
 
 
 def summarize(wl, t):
@@ -82,7 +93,7 @@ def summarize(wl, t):
          "tflops": round(fl / (ms * 1e-3) / 1e12, 2),
          "mfma_frac": round(fl / (ms * 1e-3) / 1e12 / PEAK_MFMA_TFLOPS, 4),
          "hbm_gbs": round(io / (ms * 1e-3) / 1e9, 1),
-         "hbm_frac": round(io / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+         "hbm_frac": round(io / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4), "entry": t["entry"]}
     return r
 
 

@@ -7,8 +7,10 @@ used for device memory and streams.  There is no fallback: if the library is
 missing or cannot be loaded, every call raises.
 
 Raw entry points (same names and arguments as the C functions, pointers as
-integers): ``sdpa_forward``, ``sdpa_workspace_bytes``, ``sdpa_last_error``,
-``sdpa_version``.  Convenience wrapper on torch tensors: ``sdpa``.
+integers): ``sdpa_forward``, ``sdpa_workspace_bytes``, ``sdpa_forward_kv_view``,
+``sdpa_workspace_bytes_kv_view``, ``sdpa_last_error``, ``sdpa_version``.
+Convenience wrappers on torch tensors: ``sdpa`` (contiguous K/V) and
+``sdpa_kv_cache`` (K/V in a cache, possibly a wrapped ring).
 """
 
 from __future__ import annotations
@@ -20,8 +22,8 @@ import os
 __all__ = [
     "SDPA_OK", "SDPA_INVALID_ARG", "SDPA_UNSUPPORTED", "SDPA_WORKSPACE_TOO_SMALL",
     "SDPA_HIP_ERROR", "SDPA_FP16", "SDPA_BF16", "SdpaError", "library_path", "load_library",
-    "sdpa_forward", "sdpa_workspace_bytes", "sdpa_last_error", "sdpa_version", "sdpa",
-    "EXPORTED_SYMBOLS",
+    "sdpa_forward", "sdpa_workspace_bytes", "sdpa_forward_kv_view", "sdpa_workspace_bytes_kv_view",
+    "sdpa_last_error", "sdpa_version", "sdpa", "sdpa_kv_cache", "EXPORTED_SYMBOLS",
 ]
 
 SDPA_OK = 0
@@ -32,7 +34,8 @@ SDPA_HIP_ERROR = 4
 SDPA_FP16 = 0
 SDPA_BF16 = 1
 
-EXPORTED_SYMBOLS = ("sdpa_forward", "sdpa_workspace_bytes", "sdpa_last_error", "sdpa_version")
+EXPORTED_SYMBOLS = ("sdpa_forward", "sdpa_workspace_bytes", "sdpa_forward_kv_view",
+                    "sdpa_workspace_bytes_kv_view", "sdpa_last_error", "sdpa_version")
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _lib = None
@@ -65,6 +68,10 @@ def load_library():
     lib.sdpa_forward.restype = ci
     lib.sdpa_workspace_bytes.argtypes = [ci] * 6
     lib.sdpa_workspace_bytes.restype = sz
+    lib.sdpa_forward_kv_view.argtypes = [vp, vp, vp, vp] + [ci] * 8 + [ctypes.c_float] + [ci] * 4 + [vp, sz, vp]
+    lib.sdpa_forward_kv_view.restype = ci
+    lib.sdpa_workspace_bytes_kv_view.argtypes = [ci] * 7
+    lib.sdpa_workspace_bytes_kv_view.restype = sz
     lib.sdpa_last_error.argtypes = []
     lib.sdpa_last_error.restype = ctypes.c_char_p
     lib.sdpa_version.argtypes = []
@@ -86,6 +93,19 @@ def sdpa_workspace_bytes(B, Hq, Hkv, qL, kL, D) -> int:
     return load_library().sdpa_workspace_bytes(B, Hq, Hkv, qL, kL, D)
 
 
+def sdpa_forward_kv_view(q, k, v, out, B, Hq, Hkv, qL, kL, kv_capacity, ring_start, D, scale, causal,
+                         window, q_offset, dtype, workspace, workspace_bytes, stream) -> int:
+    """``int sdpa_forward_kv_view(...)`` of the C ABI; pointer arguments are integers."""
+    return load_library().sdpa_forward_kv_view(q, k, v, out, B, Hq, Hkv, qL, kL, kv_capacity,
+                                               ring_start, D, scale, causal, window, q_offset,
+                                               dtype, workspace, workspace_bytes, stream)
+
+
+def sdpa_workspace_bytes_kv_view(B, Hq, Hkv, qL, kL, kv_capacity, D) -> int:
+    """``size_t sdpa_workspace_bytes_kv_view(...)``; (size_t)-1 for rejected arguments."""
+    return load_library().sdpa_workspace_bytes_kv_view(B, Hq, Hkv, qL, kL, kv_capacity, D)
+
+
 def sdpa_last_error() -> str:
     return load_library().sdpa_last_error().decode()
 
@@ -94,18 +114,8 @@ def sdpa_version() -> int:
     return load_library().sdpa_version()
 
 
-# --------------------------------------------------------- torch tensor wrapper
-def sdpa(q, k, v, *, scale: float | None = None, causal: bool = False, window: int = 0,
-         q_offset: int | None = None, out=None, workspace=None, stream=None):
-    """softmax(scale * q k^T + mask) v on device tensors.
-
-    q: [B, Hq, qL, D], k and v: [B, Hkv, kL, D], contiguous fp16 or bf16 tensors on
-    one GPU; D in {256, 512}; Hq a multiple of Hkv.  scale defaults to 1/sqrt(D)
-    (as fp32).  With causal, query row i sits at key position q_offset + i;
-    q_offset defaults to kL - qL (queries aligned to the end of the keys).
-    window > 0 limits each row to its last `window` keys (requires causal).
-    Runs on `stream` (default: torch's current stream) without synchronising.
-    """
+# --------------------------------------------------------- torch tensor wrappers
+def _check_tensors(q, k, v):
     import torch
 
     if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
@@ -117,19 +127,19 @@ def sdpa(q, k, v, *, scale: float | None = None, causal: bool = False, window: i
     if not (q.is_contiguous() and k.is_contiguous() and v.is_contiguous()):
         raise ValueError("q, k, v must be contiguous")
     B, Hq, qL, D = q.shape
-    Bk, Hkv, kL, Dk = k.shape
+    Bk, Hkv, L, Dk = k.shape
     if tuple(v.shape) != tuple(k.shape) or Bk != B or Dk != D:
         raise ValueError(f"shape mismatch: q {tuple(q.shape)}, k {tuple(k.shape)}, v {tuple(v.shape)}")
-    dtype = SDPA_FP16 if q.dtype == torch.float16 else SDPA_BF16
-    if scale is None:
-        scale = 1.0 / math.sqrt(D)
-    if q_offset is None:
-        q_offset = kL - qL if causal else 0
+    return B, Hq, Hkv, qL, L, D, (SDPA_FP16 if q.dtype == torch.float16 else SDPA_BF16)
+
+
+def _prepare(q, need, D, out, workspace, stream):
+    import torch
+
     if out is None:
         out = torch.empty_like(q)
     elif out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous():
         raise ValueError("out must be a contiguous tensor shaped and typed like q")
-    need = sdpa_workspace_bytes(B, Hq, Hkv, qL, kL, D)
     if need == ctypes.c_size_t(-1).value:
         raise SdpaError(SDPA_UNSUPPORTED if D not in (256, 512) else SDPA_INVALID_ARG,
                         sdpa_last_error())
@@ -140,9 +150,59 @@ def sdpa(q, k, v, *, scale: float | None = None, causal: bool = False, window: i
         ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
+    return out, ws_ptr, ws_bytes, stream
+
+
+def sdpa(q, k, v, *, scale: float | None = None, causal: bool = False, window: int = 0,
+         q_offset: int | None = None, out=None, workspace=None, stream=None):
+    """softmax(scale * q k^T + mask) v on device tensors.
+
+    q: [B, Hq, qL, D], k and v: [B, Hkv, kL, D], contiguous fp16 or bf16 tensors on
+    one GPU; D in {256, 512}; Hq a multiple of Hkv.  scale defaults to 1/sqrt(D)
+    (as fp32).  With causal, query row i sits at key position q_offset + i;
+    q_offset defaults to kL - qL (queries aligned to the end of the keys).
+    window > 0 limits each row to its last `window` keys (requires causal).
+    Runs on `stream` (default: torch's current stream) without synchronising.
+    """
+    B, Hq, Hkv, qL, kL, D, dtype = _check_tensors(q, k, v)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if q_offset is None:
+        q_offset = kL - qL if causal else 0
+    need = sdpa_workspace_bytes(B, Hq, Hkv, qL, kL, D)
+    out, ws_ptr, ws_bytes, stream = _prepare(q, need, D, out, workspace, stream)
     rc = sdpa_forward(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, Hq, Hkv, qL, kL,
                       D, float(scale), int(bool(causal)), int(window), int(q_offset), dtype, ws_ptr,
                       ws_bytes, stream.cuda_stream)
+    if rc != SDPA_OK:
+        raise SdpaError(rc, sdpa_last_error())
+    return out
+
+
+def sdpa_kv_cache(q, k_cache, v_cache, kv_len: int, *, ring_start: int = 0,
+                  scale: float | None = None, causal: bool = False, window: int = 0,
+                  q_offset: int | None = None, out=None, workspace=None, stream=None):
+    """``sdpa`` over keys and values held in a KV cache.
+
+    k_cache and v_cache: [B, Hkv, capacity, D]; kv_len live keys, logical key j
+    in row (ring_start + j) % capacity of its head (a wrapped ring when
+    ring_start + kv_len > capacity).  Positions and masks refer to logical key
+    indices; q_offset defaults to kv_len - qL.  Decode and verify calls
+    (qL <= 4) over one cache use key chunks fixed by (B, Hkv, capacity), so a
+    verify row and the single-row call over its trimmed prefix agree byte for
+    byte.
+    """
+    B, Hq, Hkv, qL, cap, D, dtype = _check_tensors(q, k_cache, v_cache)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if q_offset is None:
+        q_offset = kv_len - qL if causal else 0
+    need = sdpa_workspace_bytes_kv_view(B, Hq, Hkv, qL, int(kv_len), cap, D)
+    out, ws_ptr, ws_bytes, stream = _prepare(q, need, D, out, workspace, stream)
+    rc = sdpa_forward_kv_view(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), out.data_ptr(), B,
+                              Hq, Hkv, qL, int(kv_len), cap, int(ring_start), D, float(scale),
+                              int(bool(causal)), int(window), int(q_offset), dtype, ws_ptr, ws_bytes,
+                              stream.cuda_stream)
     if rc != SDPA_OK:
         raise SdpaError(rc, sdpa_last_error())
     return out

@@ -114,6 +114,13 @@ __device__ __forceinline__ uint64_t uniform_addr(const void* ptr) {
   return ((uint64_t)hi << 32) | lo;
 }
 
+// A uniform 64-bit value in a scalar register pair.
+__device__ __forceinline__ uint64_t uniform64(uint64_t x) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((unsigned)x);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((unsigned)(x >> 32));
+  return ((uint64_t)hi << 32) | lo;
+}
+
 // Descriptor of `bytes` bytes from `base` (a uniform_addr value); word 1
 // holds address bits 32..47 and a zero stride.
 __device__ __forceinline__ i32x4_t tile_rsrc(uint64_t base, int bytes) {
@@ -142,6 +149,29 @@ __device__ __forceinline__ void load_lds16(i32x4_t rsrc, uint32_t voff, uint32_t
       "s_nop 0\n\t"
       "buffer_load_dwordx4 %0, %1, %2 offen lds" ::"v"(voff),
       "s"(rsrc), "s"(__builtin_amdgcn_readfirstlane(soff)), "s"(m0v));
+}
+
+// The same for a block whose rows lie on both sides of the end of a ring of
+// cache rows: the lanes in exec_a read through ra, the lanes in exec_b
+// (the complement) through rb.  A lane outside the exec mask of a load
+// neither reads memory nor writes LDS in it, so each lane is served by
+// exactly one of the two loads.  EXEC is restored before the block ends.
+__device__ __forceinline__ void load_lds16_2(i32x4_t ra, i32x4_t rb, uint64_t exec_a, uint64_t exec_b,
+                                             uint32_t voff, uint32_t soff, uint32_t m0v) {
+  uint64_t saved;
+  asm volatile(
+      "s_mov_b64 %0, exec\n\t"
+      "s_mov_b32 m0, %7\n\t"
+      "s_mov_b64 exec, %3\n\t"
+      "s_nop 1\n\t"
+      "buffer_load_dwordx4 %1, %2, %6 offen lds\n\t"
+      "s_mov_b64 exec, %4\n\t"
+      "s_nop 1\n\t"
+      "buffer_load_dwordx4 %1, %5, %6 offen lds\n\t"
+      "s_mov_b64 exec, %0"
+      : "=&s"(saved)
+      : "v"(voff), "s"(ra), "s"(exec_a), "s"(exec_b), "s"(rb), "s"(__builtin_amdgcn_readfirstlane(soff)),
+        "s"(m0v));
 }
 
 // (m & x) | (~m & y) bit by bit, one v_bfi_b32 (the compiler does not form
@@ -191,7 +221,7 @@ constexpr float kRescaleLog2 = 8.f;
 // busy through the softmax.  K and V have separate double buffers, V one
 // tile behind K: step t reads K(t+1) and V(t) and loads K(t+2) and V(t+1).
 // ---------------------------------------------------------------------------
-template <int DT, int D>
+template <int DT, int D, bool RING>
 __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* lds) {
   // D = 256: a wave owns 32 rows and all 256 columns.  D = 512: the two
   // waves of a pair own the same 32 rows; wave h multiplies Q columns
@@ -253,7 +283,10 @@ __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* ld
   const int t_first = __builtin_amdgcn_readfirstlane(kbeg / BN);
   const int t_last = __builtin_amdgcn_readfirstlane((kend - 1) / BN);
 
-  const size_t kv_off = (size_t)(b * p.Hkv + hkv) * (size_t)p.kL * D;
+  // K/V rows of a head are kv_cap apart; logical key j is physical row
+  // (ring_start + j) % kv_cap.  Without a wrap the live keys are one run of
+  // rows from ring_start; with one (RING) the tile loads split at the wrap.
+  const size_t kv_off = (size_t)(b * p.Hkv + hkv) * (size_t)p.kv_cap * D + (RING ? 0 : (size_t)p.ring_start * D);
   const uint16_t* __restrict__ kg = p.k + kv_off;
   const uint16_t* __restrict__ vg = p.v + kv_off;
 
@@ -315,15 +348,53 @@ __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* ld
   for (int i = 0; i < KPAT; ++i) koff[i] = lane_off(false, i);
 #pragma unroll
   for (int i = 0; i < VPAT; ++i) voff[i] = lane_off(true, i);
+  // A tile's source.  Without RING: one descriptor from the tile's first
+  // row.  With RING the tile's rows r < r0 are physical rows bp + r (bp the
+  // physical row of its first key) and rows r >= r0 wrap to physical r - r0:
+  // descriptor a from row bp, descriptor b from r0 rows before the head's
+  // first row (only lanes with r >= r0 read through it).
+  struct TileSrc {
+    i32x4_t a, b;
+    int r0;  // rows of the tile before the ring wraps (BN: none)
+  };
   auto tile_src = [&](const uint16_t* g, int t) {
     const int ts = __builtin_amdgcn_readfirstlane(t * BN);
-    return tile_rsrc(uniform_addr(g + (size_t)ts * D), __builtin_amdgcn_readfirstlane(min(p.kL - ts, BN) * 2 * D));
+    const int bytes = __builtin_amdgcn_readfirstlane(min(p.kL - ts, BN) * 2 * D);
+    TileSrc src;
+    if constexpr (!RING) {
+      src.a = tile_rsrc(uniform_addr(g + (size_t)ts * D), bytes);
+      src.b = src.a;
+      src.r0 = BN;
+    } else {
+      int bp = p.ring_start + ts;  // < 2 kv_cap: ring_start < kv_cap, ts < kL <= kv_cap
+      if (bp >= p.kv_cap) bp -= p.kv_cap;
+      bp = __builtin_amdgcn_readfirstlane(bp);
+      const int r0 = __builtin_amdgcn_readfirstlane(min(p.kv_cap - bp, BN));
+      const uint64_t head = uniform_addr(g);
+      src.a = tile_rsrc(head + (uint64_t)bp * 2 * D, min(r0 * 2 * D, bytes));
+      src.b = tile_rsrc(head - (uint64_t)r0 * 2 * D, bytes);
+      src.r0 = r0;
+    }
+    return src;
   };
-  auto load_blk = [&](i32x4_t src, uint16_t* buf, int n, bool is_v) {
-    load_lds16(src, is_v ? voff[n % VPAT] : koff[n % KPAT], (uint32_t)(n * NW * 1024), buf + (wave + NW * n) * 512);
+  auto load_blk = [&](const TileSrc& src, uint16_t* buf, int n, bool is_v) {
+    const uint32_t vo = is_v ? voff[n % VPAT] : koff[n % KPAT];
+    uint16_t* dst = buf + (wave + NW * n) * 512;
+    if constexpr (!RING) {
+      load_lds16(src.a, vo, (uint32_t)(n * NW * 1024), dst);
+    } else {
+      // lanes of rows before the wrap: lanes [0, 32) hold the block's first
+      // row and [32, 64) its second (RPB = 2), or all 64 its one row
+      const int rb0 = (wave + NW * n) * RPB;
+      const uint64_t ea = RPB == 2 ? ((rb0 < src.r0 ? 0xffffffffull : 0ull) |
+                                      (rb0 + 1 < src.r0 ? 0xffffffff00000000ull : 0ull))
+                                   : (rb0 < src.r0 ? ~0ull : 0ull);
+      load_lds16_2(src.a, src.b, uniform64(ea), uniform64(~ea), vo, (uint32_t)(n * NW * 1024),
+                   __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)dst));
+    }
   };
   auto load_tile = [&](const uint16_t* g, int t, uint16_t* buf, bool is_v) {
-    const i32x4_t src = tile_src(g, t);
+    const TileSrc src = tile_src(g, t);
     const unsigned m0 = m0_save();
 #pragma unroll
     for (int n = 0; n < LOADS; ++n) load_blk(src, buf, n, is_v);
@@ -418,7 +489,8 @@ __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* ld
   // S(t+1) = K(t+1) Q^T  ||  weights, sum and packing of tile t; also issues
   // the direct loads of K(tk) into kdst and V(tv) into vdst
   auto qk_weights = [&](f32x16_t (&sn)[KB], const uint16_t* kl, f32x16_t (&sc)[KB],
-                        uint4 (&pb)[KB * 2], i32x4_t ksrc, uint16_t* kdst, i32x4_t vsrc, uint16_t* vdst) {
+                        uint4 (&pb)[KB * 2], const TileSrc& ksrc, uint16_t* kdst, const TileSrc& vsrc,
+                        uint16_t* vdst) {
     constexpr int NQK = KB * DC, PF = 4, LS = NQK / LOADS;
     static_assert(NQK == KB * 16 && LS >= 2 && LS % 2 == 0, "slot pattern");
 #pragma unroll
@@ -642,18 +714,18 @@ __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* ld
   }
 }
 
-template <int DT>
+template <int DT, bool RING>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void attn_tile_kernel_d256(AttnParams p) {
   __shared__ __attribute__((aligned(16))) uint16_t lds[4 * 64 * 256];  // 2 K + 2 V tiles
-  attn_pipe_body<DT, 256>(p, lds);
+  attn_pipe_body<DT, 256, RING>(p, lds);
 }
-template <int DT>
+template <int DT, bool RING>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void attn_tile_kernel_d512(AttnParams p) {
   // 2 K + 2 V tiles of 32 x 512, then the pair score exchange (4 waves x 4 KiB)
   __shared__ __attribute__((aligned(16))) uint16_t lds[4 * 32 * 512 + 2 * 4 * 64 * 16];
-  attn_pipe_body<DT, 512>(p, lds);
+  attn_pipe_body<DT, 512, RING>(p, lds);
 }
 
 // Merge of the per-split partials of each output row.  One workgroup of nw =
@@ -741,13 +813,13 @@ __global__ __launch_bounds__(64 * kCombineWaves) void combine_kernel(AttnParams 
   }
 }
 
-template <int DT, int D>
+template <int DT, int D, bool RING>
 hipError_t launch_attention_t(const AttnParams& p, hipStream_t stream) {
   const dim3 grid((unsigned)(p.B * p.Hkv * p.mblocks), (unsigned)p.nsplit, 1);
   if constexpr (D == 256)
-    hipLaunchKernelGGL((attn_tile_kernel_d256<DT>), grid, dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((attn_tile_kernel_d256<DT, RING>), grid, dim3(256), 0, stream, p);
   else
-    hipLaunchKernelGGL((attn_tile_kernel_d512<DT>), grid, dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((attn_tile_kernel_d512<DT, RING>), grid, dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 
@@ -761,9 +833,14 @@ hipError_t launch_combine_t(const AttnParams& p, hipStream_t stream) {
 
 }  // namespace
 
-hipError_t launch_attention(const AttnParams& p, int D, int dtype, hipStream_t stream) {
-  if (D == 256) return dtype == 0 ? launch_attention_t<0, 256>(p, stream) : launch_attention_t<1, 256>(p, stream);
-  return dtype == 0 ? launch_attention_t<0, 512>(p, stream) : launch_attention_t<1, 512>(p, stream);
+template <int D, bool RING>
+hipError_t launch_attention_d(const AttnParams& p, int dtype, hipStream_t stream) {
+  return dtype == 0 ? launch_attention_t<0, D, RING>(p, stream) : launch_attention_t<1, D, RING>(p, stream);
+}
+
+hipError_t launch_attention(const AttnParams& p, int D, int dtype, bool ring, hipStream_t stream) {
+  if (D == 256) return ring ? launch_attention_d<256, true>(p, dtype, stream) : launch_attention_d<256, false>(p, dtype, stream);
+  return ring ? launch_attention_d<512, true>(p, dtype, stream) : launch_attention_d<512, false>(p, dtype, stream);
 }
 
 hipError_t launch_combine(const AttnParams& p, int D, int dtype, hipStream_t stream) {

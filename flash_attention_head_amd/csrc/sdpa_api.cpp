@@ -60,18 +60,23 @@ bool overlap(const void* a, size_t an, const void* b, size_t bn) {
 
 }  // namespace
 
-SplitPlan plan_split(int B, int Hq, int Hkv, int qL, int kL, int D) {
+SplitPlan plan_split(int B, int Hq, int Hkv, int qL, int kL, int D, int kv_capacity) {
   SplitPlan sp;
   if (qL <= kDecodeMaxRows) {
     // decode / verify: always the split path, with chunks at absolute key
-    // positions.  The chunk is kDecodeChunk times a power of two, the
-    // largest that still gives one workgroup per CU for a full round; it
-    // depends on B, Hkv, kL and D only, never on qL, so a verify row gets
-    // the same chunks, and the same bits, as the single-row call.
-    const int64_t heads = (int64_t)B * Hkv;
+    // positions.  A verify row must get the same chunks, and so the same
+    // bits, as the single-row call over its own trimmed key prefix, whose kL
+    // is smaller: the chunk may depend on neither qL nor kL.  Without a
+    // cache capacity it is kDecodeChunk.  With one it is kDecodeChunk times
+    // a power of two, the largest for which the (b, KV head) x chunk
+    // workgroups of a full cache still fill one round of the CUs: a pure
+    // function of (B, Hkv, capacity), which every call over that cache shares.
     int64_t chunk = kDecodeChunk;
-    while (heads * ceil_div(kL, 2 * chunk) >= kPlannedCUs && 2 * chunk <= (int64_t)INT32_MAX / 2)
-      chunk *= 2;
+    if (kv_capacity > 0) {
+      const int64_t heads = (int64_t)B * Hkv;
+      while (heads * ceil_div(kv_capacity, 2 * chunk) >= kPlannedCUs && 2 * chunk <= (int64_t)INT32_MAX / 2)
+        chunk *= 2;
+    }
     sp.split_len = (int)chunk;
     sp.nsplit = (int)ceil_div(kL, chunk);
     sp.partials = 1;
@@ -116,24 +121,28 @@ SplitPlan plan_split(int B, int Hq, int Hkv, int qL, int kL, int D) {
 
 }  // namespace sdpa
 
-using namespace sdpa;
+namespace sdpa {
+namespace {
 
-SDPA_API size_t sdpa_workspace_bytes(int B, int Hq, int Hkv, int qL, int kL, int D) {
-  if (check_shape(B, Hq, Hkv, qL, kL, D) != SDPA_OK) return (size_t)-1;
-  return workspace_for(plan_split(B, Hq, Hkv, qL, kL, D), B, Hq, qL, D);
+// KV-cache view checks (sdpa_forward_kv_view and its workspace query).
+int check_view(int kL, int kv_capacity, int ring_start) {
+  if (kv_capacity < kL)
+    return fail(SDPA_INVALID_ARG, "kv_capacity (%d) must be >= kL (%d)", kv_capacity, kL);
+  if (ring_start < 0 || ring_start >= kv_capacity)
+    return fail(SDPA_INVALID_ARG, "ring_start must lie in [0, kv_capacity) = [0, %d) (got %d)",
+                kv_capacity, ring_start);
+  return SDPA_OK;
 }
 
-SDPA_API const char* sdpa_last_error(void) { return g_last_error; }
-
-SDPA_API int sdpa_version(void) { return 100; }
-
-SDPA_API int sdpa_forward(const void* q, const void* k, const void* v, void* out, int B, int Hq,
-                          int Hkv, int qL, int kL, int D, float scale, int causal, int window,
-                          int q_offset, int dtype, void* workspace, size_t workspace_bytes,
-                          void* stream) {
-  g_last_error[0] = '\0';
+// Both forward entry points: K/V rows of a head are kv_cap apart, logical
+// key j is physical row (ring_start + j) % kv_cap; chunk_cap is the cache
+// capacity the decode chunks are sized from (0: none).
+int forward_impl(const void* q, const void* k, const void* v, void* out, int B, int Hq, int Hkv,
+                 int qL, int kL, int kv_cap, int ring_start, int chunk_cap, int D, float scale,
+                 int causal, int window, int q_offset, int dtype, void* workspace,
+                 size_t workspace_bytes, void* stream) {
   if (!q || !k || !v || !out) return fail(SDPA_INVALID_ARG, "q, k, v and out must be non-null");
-  int rc = check_shape(B, Hq, Hkv, qL, kL, D);
+  int rc = check_shape(B, Hq, Hkv, qL, kv_cap, D);
   if (rc != SDPA_OK) return rc;
   if (dtype != SDPA_FP16 && dtype != SDPA_BF16)
     return fail(SDPA_UNSUPPORTED, "dtype %d is not supported (0 = fp16, 1 = bf16)", dtype);
@@ -148,16 +157,17 @@ SDPA_API int sdpa_forward(const void* q, const void* k, const void* v, void* out
                 "(got %d)",
                 kL - qL, q_offset);
   const size_t qbytes = (size_t)B * Hq * qL * D * 2;
-  const size_t kvbytes = (size_t)B * Hkv * kL * D * 2;
+  const size_t kvbytes = (size_t)B * Hkv * kv_cap * D * 2;
   if (overlap(out, qbytes, q, qbytes) || overlap(out, qbytes, k, kvbytes) ||
       overlap(out, qbytes, v, kvbytes))
     return fail(SDPA_INVALID_ARG, "out must not overlap q, k or v");
 
-  const SplitPlan sp = plan_split(B, Hq, Hkv, qL, kL, D);
+  const SplitPlan sp = plan_split(B, Hq, Hkv, qL, kL, D, chunk_cap);
   const size_t need = workspace_for(sp, B, Hq, qL, D);
   if (need > 0 && (!workspace || workspace_bytes < need))
     return fail(SDPA_WORKSPACE_TOO_SMALL, "workspace of %zu bytes needed, %zu given", need,
                 workspace ? workspace_bytes : (size_t)0);
+  if (sp.nsplit > 65535) return fail(SDPA_INVALID_ARG, "too many key splits (%d)", sp.nsplit);
 
   AttnParams p;
   p.q = (const uint16_t*)q;
@@ -170,6 +180,8 @@ SDPA_API int sdpa_forward(const void* q, const void* k, const void* v, void* out
   p.G = Hq / Hkv;
   p.qL = qL;
   p.kL = kL;
+  p.kv_cap = kv_cap;
+  p.ring_start = ring_start;
   p.causal = causal;
   p.window = window;
   p.q_offset = causal ? q_offset : 0;
@@ -187,11 +199,58 @@ SDPA_API int sdpa_forward(const void* q, const void* k, const void* v, void* out
     p.part_o = nullptr;
     p.part_ml = nullptr;
   }
-  if (sp.nsplit > 65535) return fail(SDPA_INVALID_ARG, "too many key splits (%d)", sp.nsplit);
+  // the rows of some tile wrap around the end of the cache rows only if the
+  // live keys do
+  const bool ring = (int64_t)ring_start + kL > kv_cap;
 
   hipStream_t s = (hipStream_t)stream;
-  hipError_t e = launch_attention(p, D, dtype, s);
+  hipError_t e = launch_attention(p, D, dtype, ring, s);
   if (e == hipSuccess && sp.partials) e = launch_combine(p, D, dtype, s);
   if (e != hipSuccess) return fail(SDPA_HIP_ERROR, "kernel launch failed: %s", hipGetErrorString(e));
   return SDPA_OK;
+}
+
+}  // namespace
+}  // namespace sdpa
+
+using namespace sdpa;
+
+SDPA_API size_t sdpa_workspace_bytes(int B, int Hq, int Hkv, int qL, int kL, int D) {
+  if (check_shape(B, Hq, Hkv, qL, kL, D) != SDPA_OK) return (size_t)-1;
+  return workspace_for(plan_split(B, Hq, Hkv, qL, kL, D, 0), B, Hq, qL, D);
+}
+
+SDPA_API size_t sdpa_workspace_bytes_kv_view(int B, int Hq, int Hkv, int qL, int kL,
+                                             int kv_capacity, int D) {
+  if (check_shape(B, Hq, Hkv, qL, kL, D) != SDPA_OK || check_view(kL, kv_capacity, 0) != SDPA_OK ||
+      check_shape(B, Hq, Hkv, qL, kv_capacity, D) != SDPA_OK)
+    return (size_t)-1;
+  return workspace_for(plan_split(B, Hq, Hkv, qL, kL, D, kv_capacity), B, Hq, qL, D);
+}
+
+SDPA_API const char* sdpa_last_error(void) { return g_last_error; }
+
+SDPA_API int sdpa_version(void) { return 200; }
+
+SDPA_API int sdpa_forward(const void* q, const void* k, const void* v, void* out, int B, int Hq,
+                          int Hkv, int qL, int kL, int D, float scale, int causal, int window,
+                          int q_offset, int dtype, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+  g_last_error[0] = '\0';
+  return forward_impl(q, k, v, out, B, Hq, Hkv, qL, kL, kL, 0, 0, D, scale, causal, window,
+                      q_offset, dtype, workspace, workspace_bytes, stream);
+}
+
+SDPA_API int sdpa_forward_kv_view(const void* q, const void* k, const void* v, void* out, int B,
+                                  int Hq, int Hkv, int qL, int kL, int kv_capacity, int ring_start,
+                                  int D, float scale, int causal, int window, int q_offset,
+                                  int dtype, void* workspace, size_t workspace_bytes,
+                                  void* stream) {
+  g_last_error[0] = '\0';
+  int rc = check_shape(B, Hq, Hkv, qL, kL, D);
+  if (rc != SDPA_OK) return rc;
+  rc = check_view(kL, kv_capacity, ring_start);
+  if (rc != SDPA_OK) return rc;
+  return forward_impl(q, k, v, out, B, Hq, Hkv, qL, kL, kv_capacity, ring_start, kv_capacity, D,
+                      scale, causal, window, q_offset, dtype, workspace, workspace_bytes, stream);
 }

@@ -19,10 +19,12 @@ constexpr int block_rows(int D) { return kWaves / d_split(D) * kRowsPerWave; }
 // Keys per LDS tile, by head dimension.
 constexpr int tile_keys(int D) { return D == 512 ? 32 : 64; }
 
-// Smallest key chunk of the split path used by every call with
-// qL <= kDecodeMaxRows.  The chunk actually used is this times a power of
-// two chosen from the shape without qL, so chunk boundaries sit at absolute
-// key positions and do not depend on how many query rows a call has.
+// Key chunk of the split path used by every call with qL <= kDecodeMaxRows
+// when no KV-cache capacity is given.  With a capacity the chunk is this
+// times a power of two chosen from (B, Hkv, capacity).  Either way chunk
+// boundaries sit at absolute key positions and depend neither on qL nor on
+// the number of live keys, so a row gets the same chunks, and the same bits,
+// in a verify block and in a single-row call over its own key prefix.
 constexpr int kDecodeChunk = 1024;
 constexpr int kDecodeMaxRows = 4;
 
@@ -37,6 +39,8 @@ struct AttnParams {
   float* part_o;      // [rows_total, nsplit, D] unnormalised fp32 accumulators
   float* part_ml;     // [rows_total, nsplit, 2]: running max (log2 units), sum
   int B, Hq, Hkv, G, qL, kL;
+  int kv_cap;         // rows per KV head in k and v (head stride kv_cap * D), >= kL
+  int ring_start;     // physical row of logical key 0; key j is row (ring_start + j) % kv_cap
   int causal, window, q_offset;
   float sl2;          // scale * log2(e)
   int rows;           // G * qL packed rows per (b, kv head)
@@ -47,15 +51,17 @@ struct AttnParams {
 };
 
 // Split plan for a shape: how many key splits, how long each, and whether
-// the partial/combine path is used.  Pure function of the shape.
+// the partial/combine path is used.  Pure function of the shape and of the
+// KV-cache capacity (0: none given).
 struct SplitPlan {
   int nsplit;
   int split_len;
   int partials;
 };
-SplitPlan plan_split(int B, int Hq, int Hkv, int qL, int kL, int D);
+SplitPlan plan_split(int B, int Hq, int Hkv, int qL, int kL, int D, int kv_capacity);
 
-hipError_t launch_attention(const AttnParams& p, int D, int dtype, hipStream_t stream);
+// ring: some tile's keys wrap around the end of the cache rows
+hipError_t launch_attention(const AttnParams& p, int D, int dtype, bool ring, hipStream_t stream);
 hipError_t launch_combine(const AttnParams& p, int D, int dtype, hipStream_t stream);
 
 }  // namespace sdpa

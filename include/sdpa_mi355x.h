@@ -34,8 +34,11 @@
  *
  * Calls with qL <= 4 (decode and verify) run a split-key path whose result
  * for a row is bit-identical to a qL = 1 call over that row's visible key
- * prefix, whatever qL is (the byte-for-byte verify-vs-decode requirement of
- * mlxcel issue #2160, Acceptance Criteria).
+ * prefix, whatever qL is and whatever kL that prefix has (the byte-for-byte
+ * verify-vs-decode requirement of mlxcel issue #2160, Acceptance Criteria).
+ * The keys are split into chunks of a size that depends on neither: 1024
+ * keys for sdpa_forward, and a size fixed by the cache's shape for
+ * sdpa_forward_kv_view.
  *
  * Errors are returned as status codes; nothing is thrown across this
  * boundary, nothing aborts, nothing is printed.  The library allocates no
@@ -102,6 +105,43 @@ int sdpa_forward(const void* q, const void* k, const void* v, void* out, int B, 
  * SDPA_INVALID_ARG or SDPA_UNSUPPORTED.
  */
 size_t sdpa_workspace_bytes(int B, int Hq, int Hkv, int qL, int kL, int D);
+
+/*
+ * sdpa_forward over keys and values held in a KV cache: the decode and verify
+ * calls of mlxcel issue #2160 run over such caches, including sliding-window
+ * layers kept as a ring buffer with a cursor (Current Behavior, the 12B and
+ * 31B geometries; Proposed Solution step 2) and "strided, sliced keys" (the
+ * #1935 divergence class named under Current Behavior, 31B).
+ *
+ *   k, v         device pointers to caches [B, Hkv, kv_capacity, D] (row
+ *                major, contiguous); read only.
+ *   kL           live keys, 1 <= kL <= kv_capacity.
+ *   kv_capacity  rows per head in the caches.
+ *   ring_start   physical row of logical key 0, 0 <= ring_start < kv_capacity:
+ *                logical key j is row (ring_start + j) % kv_capacity of its
+ *                head.  0 for a cache filled from row 0; the ring's oldest
+ *                row for a wrapped ring.  Rows outside the kL live keys are
+ *                never read (they may hold anything, NaN included).
+ *   Everything else, including positions, masks and q_offset, is as in
+ *   sdpa_forward with key j meaning logical key j.
+ *
+ * The keys are accumulated in logical order, so a row's result depends on
+ * the live keys' values in logical order and not on where in the cache they
+ * sit.  With qL <= 4 the key chunks are sized from (B, Hkv, kv_capacity)
+ * alone, so every call over one cache -- a verify block and the single-row
+ * calls over each row's trimmed prefix -- uses the same chunk boundaries and
+ * gives each row the same bytes.  The workspace is
+ * sdpa_workspace_bytes_kv_view(...).  Status codes as sdpa_forward, plus
+ * SDPA_INVALID_ARG for kv_capacity < kL or ring_start out of range.
+ */
+int sdpa_forward_kv_view(const void* q, const void* k, const void* v, void* out, int B, int Hq,
+                         int Hkv, int qL, int kL, int kv_capacity, int ring_start, int D,
+                         float scale, int causal, int window, int q_offset, int dtype,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes of sdpa_forward_kv_view; (size_t)-1 for arguments it rejects. */
+size_t sdpa_workspace_bytes_kv_view(int B, int Hq, int Hkv, int qL, int kL, int kv_capacity,
+                                    int D);
 
 /* Message for the last non-zero status returned on the calling thread ("" if none). */
 const char* sdpa_last_error(void);

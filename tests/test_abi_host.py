@@ -126,19 +126,53 @@ def test_decode_chunks_depend_on_the_shape_not_on_qL(lib):
         n = {qL: decode_chunks(fa.sdpa_workspace_bytes(B, Hq, Hkv, qL, kL, D), B, Hq, qL, D)
              for qL in (1, 2, 3, 4)}
         assert len(set(n.values())) == 1, n
+        nv = {qL: decode_chunks(fa.sdpa_workspace_bytes_kv_view(B, Hq, Hkv, qL, kL, 2 * kL, D), B, Hq, qL, D)
+              for qL in (1, 2, 3, 4)}
+        assert len(set(nv.values())) == 1, nv
 
 
-def test_decode_chunk_is_the_largest_that_fills_the_chip(lib):
+def test_plain_decode_chunks_are_1024_keys_whatever_kL(lib):
+    # a verify block over kL keys and the single-row calls over each row's
+    # trimmed prefix (kL - 3 .. kL keys) must share chunk boundaries: with no
+    # cache capacity given the chunk cannot depend on kL at all
+    for (B, Hq, Hkv) in [(1, 16, 8), (1, 32, 4), (4, 64, 8)]:
+        for kL in (1, 1023, 1024, 1025, 126976, 126977, 131072, 1 << 20):
+            n = decode_chunks(fa.sdpa_workspace_bytes(B, Hq, Hkv, 4, kL, 256), B, Hq, 4, 256)
+            assert n == -(-kL // 1024), (B, Hkv, kL, n)
+
+
+def kv_view_chunk(B, Hq, Hkv, kL, cap, D=256):
+    n = decode_chunks(fa.sdpa_workspace_bytes_kv_view(B, Hq, Hkv, 4, kL, cap, D), B, Hq, 4, D)
+    return next(c for c in (1024 << k for k in range(21)) if -(-kL // c) == n)
+
+
+def test_cache_decode_chunk_depends_on_the_capacity_not_on_kL(lib):
+    # every call over one cache (any live key count) gets the same chunk size
+    for (B, Hq, Hkv, cap) in [(1, 16, 8, 131072), (1, 16, 8, 200000), (1, 32, 4, 65536), (2, 8, 2, 1 << 20)]:
+        sizes = {kv_view_chunk(B, Hq, Hkv, kL, cap) for kL in (cap, cap - 1, cap - 3, cap // 2 + 5)}
+        assert len(sizes) == 1, (B, Hkv, cap, sizes)
+
+
+def test_cache_decode_chunk_is_the_largest_that_fills_the_chip(lib):
     # chunk = 1024 * 2^k at absolute key positions: the largest for which the
-    # (b, kv head) x chunk workgroups still make one full round of 256
-    for (B, Hq, Hkv, kL) in [(1, 16, 8, 131072), (1, 16, 8, 4096), (1, 8, 8, 1 << 20), (2, 32, 16, 65536)]:
-        n = decode_chunks(fa.sdpa_workspace_bytes(B, Hq, Hkv, 4, kL, 256), B, Hq, 4, 256)
-        chunk = next(c for c in (1024 << k for k in range(20)) if -(-kL // c) == n)
-        heads = B * Hkv
+    # (b, kv head) x chunk workgroups of a full cache still make one full
+    # round of 256
+    for (B, Hq, Hkv, cap) in [(1, 16, 8, 131072), (1, 16, 8, 4096), (1, 8, 8, 1 << 20), (2, 32, 16, 65536)]:
+        chunk = kv_view_chunk(B, Hq, Hkv, cap, cap)
+        heads, n = B * Hkv, -(-cap // chunk)
         assert chunk == 1024 or heads * n >= 256
-        assert heads * -(-kL // (2 * chunk)) < 256
+        assert heads * -(-cap // (2 * chunk)) < 256
     # the verify workload: 8 KV heads x 32 chunks of 4096 keys = 256 workgroups
-    assert decode_chunks(fa.sdpa_workspace_bytes(1, 16, 8, 4, 131072, 256), 1, 16, 4, 256) == 32
+    assert kv_view_chunk(1, 16, 8, 131072, 131072) == 4096
+
+
+def test_kv_view_rejects_bad_views(lib):
+    for (kL, cap, ring) in [(10, 9, 0), (10, 10, 10), (10, 10, -1), (10, 20, 20)]:
+        rc = lib.sdpa_forward_kv_view(1, 1, 1, 1, 1, 2, 1, 1, kL, cap, ring, 256, ctypes.c_float(0.0625), 1, 0,
+                                      kL - 1, 0, None, 0, None)
+        assert rc == fa.SDPA_INVALID_ARG, (kL, cap, ring, rc)
+        assert "kv_capacity" in fa.sdpa_last_error() or "ring_start" in fa.sdpa_last_error()
+    assert fa.sdpa_workspace_bytes_kv_view(1, 2, 1, 1, 10, 9, 256) == ctypes.c_size_t(-1).value
 
 
 def test_workspace_is_linear_in_key_chunks_not_quadratic(lib):

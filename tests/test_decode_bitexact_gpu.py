@@ -84,3 +84,12 @@ def test_rows_straddling_a_chunk_boundary(kL):
 def test_bitexact_with_fp16_and_group_of_eight():
     q, k, v = W.random_qkv(70, 2, 16, 2, 4, 5000, 256, FP16)
     _check_rows(q, k, v, window=700, what="fp16 G8 B2")
+
+
+@pytest.mark.timeout(600)
+def test_rows_whose_prefixes_straddle_a_power_of_two_of_chunks():
+    # 8 KV heads and 126978 keys: the rows' prefixes hold 126975..126978 keys,
+    # on both sides of 124 * 1024 = 126976, where a chunk sized from the key
+    # count to fill 256 workgroups would step from 2048 to 4096 keys
+    q, k, v = W.random_qkv(73, 1, 16, 8, 4, 126978, 256, BF16)
+    _check_rows(q, k, v, window=0, what="126978 keys")
