@@ -141,7 +141,7 @@ def _prepare(q, need, D, out, workspace, stream):
     elif out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous():
         raise ValueError("out must be a contiguous tensor shaped and typed like q")
     if need == ctypes.c_size_t(-1).value:
-        raise SdpaError(SDPA_UNSUPPORTED if D not in (256, 512) else SDPA_INVALID_ARG,
+        raise SdpaError(SDPA_UNSUPPORTED if D not in (128, 256, 512) else SDPA_INVALID_ARG,
                         sdpa_last_error())
     ws_ptr, ws_bytes = 0, 0
     if need > 0:
@@ -158,7 +158,7 @@ def sdpa(q, k, v, *, scale: float | None = None, causal: bool = False, window: i
     """softmax(scale * q k^T + mask) v on device tensors.
 
     q: [B, Hq, qL, D], k and v: [B, Hkv, kL, D], contiguous fp16 or bf16 tensors on
-    one GPU; D in {256, 512}; Hq a multiple of Hkv.  scale defaults to 1/sqrt(D)
+    one GPU; D in {128, 256, 512}; Hq a multiple of Hkv.  scale defaults to 1/sqrt(D)
     (as fp32).  With causal, query row i sits at key position q_offset + i;
     q_offset defaults to kL - qL (queries aligned to the end of the keys).
     window > 0 limits each row to its last `window` keys (requires causal).

@@ -223,21 +223,26 @@ constexpr float kRescaleLog2 = 8.f;
 // ---------------------------------------------------------------------------
 template <int DT, int D, bool RING>
 __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* lds) {
-  // D = 256: a wave owns 32 rows and all 256 columns.  D = 512: the two
-  // waves of a pair own the same 32 rows; wave h multiplies Q columns
+  // D = 128 or 256: a wave owns 32 rows and all D columns.  D = 512: the
+  // two waves of a pair own the same 32 rows; wave h multiplies Q columns
   // [256 h, 256 h + 256) into partial scores, the pair swaps them through LDS
   // and adds them (a + b == b + a: both hold bitwise identical scores and run
   // identical softmax arithmetic), and wave h accumulates output columns
-  // [256 h, 256 h + 256).  Either way 32 x 256 fp32 accumulators per wave.
+  // [256 h, 256 h + 256).  Up to 32 x 256 fp32 accumulators per wave.
   constexpr bool PAIR = (D == 512);
   constexpr int NW = 4, RBW = PAIR ? 2 : 4;  // 32-row blocks per workgroup
   constexpr int BM = RBW * kRowsPerWave, BN = tile_keys(D), KB = BN / 32;
-  constexpr int DQ = 256, DO = PAIR ? D / 2 : D;  // Q columns multiplied, output columns owned
+  constexpr int DQ = D < 256 ? D : 256, DO = PAIR ? D / 2 : D;  // Q columns multiplied, output columns owned
   constexpr int DC = DQ / 16, DB = DO / 32;
   constexpr int ROWCH = D / 8, TILE = BN * D, LOADS = TILE * 2 / 1024 / NW;
+  // score elements per lane, and per MFMA slot of the S and P V regions
+  constexpr int NE = KB * 16, EPS = NE / (KB * DC), EPV = NE / (KB * 2 * DB);
+  // V rows of 16 chunks (D = 128) swizzle over 4 rows, wider ones over 8
+  constexpr int VSW = ROWCH >= 32 ? 7 : 3;
   static_assert(BM == block_rows(D), "geometry");
-  static_assert(LOADS == 8, "one K and one V load per wave per 1 KiB block");
-  static_assert(KB * DC == KB * 16 && KB * 2 * DB == KB * 16, "one score element per MFMA slot");
+  static_assert(LOADS == 4 || LOADS == 8, "K and V loads of 1 KiB blocks per wave");
+  static_assert((EPS == 1 || EPS == 2) && EPS * KB * DC == NE && (EPV == 1 || EPV == 2) && EPV * KB * 2 * DB == NE,
+                "one or two score elements per MFMA slot");
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -316,7 +321,7 @@ __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* ld
   int vlane;
   {
     const int g = lane >> 4, kq = 4 * (g >> 1) + ((lane >> 2) & 3);
-    vlane = kq * D + (od0 ^ (32 * kq)) + 16 * (g & 1) + 4 * (lane & 3);
+    vlane = kq * D + (od0 ^ (32 * (kq & VSW))) + 16 * (g & 1) + 4 * (lane & 3);
   }
   // K(t) lives in K buffer (t - t_first) & 1, V(t) in V buffer (t - t_first)
   // & 1: the steps come in pairs, so inside a step every buffer offset is a
@@ -329,18 +334,19 @@ __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* ld
   // each) per wave, the n-th at block b = wave + NW n.  Lane l reads row
   // l / ROWCH of the block at chunk (l % ROWCH) ^ swizzle(row) and lands at
   // LDS position l, which puts chunk c of key row r at c ^ (r & 15) (K) or
-  // c ^ ((r & 7) << 2) (V).  Block b starts at byte 1024 b of the tile, so
+  // c ^ ((r & VSW) << 2) (V).  Block b starts at byte 1024 b of the tile, so
   // the n-th load's lane offset is a pattern that repeats every KPAT (K) or
   // VPAT (V) loads plus n NW 1024, which goes into the scalar offset.  The
   // tile start and its bytes before key kL form the buffer descriptor, so
   // rows past kL read zeros (the range check covers the scalar offset too).
   constexpr int RPB = 1024 / (2 * D);  // key rows per 1 KiB block
-  constexpr int KPAT = 16 / (NW * RPB), VPAT = 8 / (NW * RPB) > 1 ? 8 / (NW * RPB) : 1;
+  constexpr int KPAT = 16 / (NW * RPB) > 1 ? 16 / (NW * RPB) : 1;
+  constexpr int VPAT = (VSW + 1) / (NW * RPB) > 1 ? (VSW + 1) / (NW * RPB) : 1;
   static_assert(RPB * ROWCH == 64 && LOADS % KPAT == 0 && LOADS % VPAT == 0, "block geometry");
   auto lane_off = [&](bool is_v, int n) {  // offset of the n-th load from its block group
     const int r = (wave + NW * n) * RPB + lane / ROWCH;  // key row in the tile
     const int pch = lane % ROWCH;
-    const int c = is_v ? (pch ^ ((r & 7) << 2)) : (pch ^ (r & 15));
+    const int c = is_v ? (pch ^ ((r & VSW) << 2)) : (pch ^ (r & 15));
     return (uint32_t)(r * 2 * D + 16 * c - n * NW * 1024);
   };
   uint32_t koff[KPAT], voff[VPAT];
@@ -383,12 +389,14 @@ __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* ld
     if constexpr (!RING) {
       load_lds16(src.a, vo, (uint32_t)(n * NW * 1024), dst);
     } else {
-      // lanes of rows before the wrap: lanes [0, 32) hold the block's first
-      // row and [32, 64) its second (RPB = 2), or all 64 its one row
+      // lanes of rows before the wrap: lanes [LPR i, LPR (i + 1)) hold row
+      // i of the block's RPB rows
+      constexpr int LPR = 64 / RPB;
       const int rb0 = (wave + NW * n) * RPB;
-      const uint64_t ea = RPB == 2 ? ((rb0 < src.r0 ? 0xffffffffull : 0ull) |
-                                      (rb0 + 1 < src.r0 ? 0xffffffff00000000ull : 0ull))
-                                   : (rb0 < src.r0 ? ~0ull : 0ull);
+      uint64_t ea = 0;
+#pragma unroll
+      for (int i = 0; i < RPB; ++i)
+        if (rb0 + i < src.r0) ea |= (LPR == 64 ? ~0ull : ((1ull << LPR) - 1ull) << (LPR * i));
       load_lds16_2(src.a, src.b, uniform64(ea), uniform64(~ea), vo, (uint32_t)(n * NW * 1024),
                    __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)dst));
     }
@@ -492,7 +500,7 @@ __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* ld
                         uint4 (&pb)[KB * 2], const TileSrc& ksrc, uint16_t* kdst, const TileSrc& vsrc,
                         uint16_t* vdst) {
     constexpr int NQK = KB * DC, PF = 4, LS = NQK / LOADS;
-    static_assert(NQK == KB * 16 && LS >= 2 && LS % 2 == 0, "slot pattern");
+    static_assert(LS >= 2 && LS % 2 == 0, "slot pattern");
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
@@ -513,8 +521,15 @@ __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* ld
     for (int i = 0; i < PF; ++i) a[i] = kread(i, kx(i));
     int x_next = kx(PF);
     const unsigned m0 = m0_save();
-    set(0, fast_exp2(get(0) * sl2 - msc));
-    set(1, get(1) * sl2 - msc);
+    // weights in slot n: fma of elements EPS (n + 2) .., exp of EPS (n + 1) ..,
+    // sum and pack of EPS n .. (EPS elements each)
+#pragma unroll
+    for (int i = 0; i < EPS; ++i) {
+      set(i, fast_exp2(get(i) * sl2 - msc));
+      set(EPS + i, get(EPS + i) * sl2 - msc);
+    }
+    // slot m packs a pair iff one of its elements is odd
+    auto packs = [](int m) { return EPS == 2 || (m & 1); };
 #pragma unroll
     for (int n = 0; n < NQK; ++n) {
       const uint4 cur_a = a[n % PF];
@@ -524,21 +539,28 @@ __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* ld
       // loads: K block group i at slot i LS, V block group i at slot i LS + LS / 2
       if (n % LS == 0) load_blk(ksrc, kdst, n / LS, false);
       if (n % LS == LS / 2) load_blk(vsrc, vdst, n / LS, true);
-      // weights: fma of element n + 2, exp of n + 1, sum and pack of n
-      if (n + 2 < NQK) set(n + 2, get(n + 2) * sl2 - msc);
-      if (n + 1 < NQK) set(n + 1, fast_exp2(get(n + 1)));
+#pragma unroll
+      for (int i = 0; i < EPS; ++i) {
+        const int ef = EPS * (n + 2) + i, ex = EPS * (n + 1) + i;
+        if (ef < NE) set(ef, get(ef) * sl2 - msc);
+        if (ex < NE) set(ex, fast_exp2(get(ex)));
+      }
       // the row sum adds the rounded weights the P V product uses, a pair
       // per dot2, one slot after the pair is packed
-      if (!(n & 1) && n > 0) psum = Elem<DT>::sum2(wlast, psum);
-      if (n & 1) {  // pack the pair (n - 1, n): P half kh = n / 8
-        const uint32_t w = Elem<DT>::pack2(get(n - 1), get(n));
-        wlast = w;
-        uint4& q = pb[n / 8];
-        switch ((n % 8) / 2) {
-          case 0: q.x = w; break;
-          case 1: q.y = w; break;
-          case 2: q.z = w; break;
-          default: q.w = w; break;
+      if (n > 0 && packs(n - 1)) psum = Elem<DT>::sum2(wlast, psum);
+#pragma unroll
+      for (int i = 0; i < EPS; ++i) {
+        const int e = EPS * n + i;
+        if (e & 1) {  // pack the pair (e - 1, e): P half kh = e / 8
+          const uint32_t w = Elem<DT>::pack2(get(e - 1), get(e));
+          wlast = w;
+          uint4& q = pb[e / 8];
+          switch ((e % 8) / 2) {
+            case 0: q.x = w; break;
+            case 1: q.y = w; break;
+            case 2: q.z = w; break;
+            default: q.w = w; break;
+          }
         }
       }
       __builtin_amdgcn_sched_barrier(0);
@@ -553,7 +575,6 @@ __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* ld
   // O += P(t) V(t)  ||  row max of S(t+1) (already masked)
   auto pv_max = [&](const uint4 (&pb)[KB * 2], const uint16_t* vl, f32x16_t (&sn)[KB], bool live) {
     constexpr int NPV = KB * 2 * DB, PF = 4;
-    static_assert(NPV == KB * 16, "one score element per slot");
     // V^T operand of MFMA n: key half n / DB, column block n % DB; the XOR
     // part of the address is a register, the rest an immediate
     auto vx = [&](int n) { return vlane ^ (32 * (n % DB)); };
@@ -574,7 +595,8 @@ __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* ld
       if (n + PF < NPV) bv[n % PF] = vread(n + PF, x_next);
       o[n % DB] = Elem<DT>::mfma(cur_b, pb[n / DB], o[n % DB]);
       if (n + PF + 1 < NPV) x_next = vx(n + PF + 1);
-      if (n & 1) mx = max3(mx, get(n - 1), get(n));
+      if (EPV == 2) mx = max3(mx, get(2 * n), get(2 * n + 1));  // this slot's pair of elements
+      else if (n & 1) mx = max3(mx, get(n - 1), get(n));         // every other slot, the last pair
       __builtin_amdgcn_sched_barrier(0);
     }
     mx = pair_max(mx);
@@ -716,6 +738,12 @@ __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* ld
 
 template <int DT, bool RING>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void attn_tile_kernel_d128(AttnParams p) {
+  __shared__ __attribute__((aligned(16))) uint16_t lds[4 * 64 * 128];  // 2 K + 2 V tiles
+  attn_pipe_body<DT, 128, RING>(p, lds);
+}
+template <int DT, bool RING>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void attn_tile_kernel_d256(AttnParams p) {
   __shared__ __attribute__((aligned(16))) uint16_t lds[4 * 64 * 256];  // 2 K + 2 V tiles
   attn_pipe_body<DT, 256, RING>(p, lds);
@@ -738,13 +766,16 @@ constexpr int kCombineWaves = 16;
 
 template <int DT, int D>
 __global__ __launch_bounds__(64 * kCombineWaves) void combine_kernel(AttnParams p) {
-  constexpr int PER = D / 64;  // columns per lane
+  // columns per lane, at least 4 (one float4); at D = 128 only lanes
+  // [0, 32) own columns, the others take part in the reductions only
+  constexpr int PER = D / 64 >= 4 ? D / 64 : 4;
   constexpr int NW = kCombineWaves;
   const int nw = blockDim.x >> 6;  // waves in this launch, <= NW
   __shared__ float red[NW];
   __shared__ __attribute__((aligned(16))) float part[NW][D];
   __shared__ float lpart[NW];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const bool cols = lane * PER < D;
   const size_t row = blockIdx.x;
   const int qi = (int)(row % (size_t)p.qL);
   const int pos = p.q_offset + qi;
@@ -774,6 +805,7 @@ __global__ __launch_bounds__(64 * kCombineWaves) void combine_kernel(AttnParams 
       const float w = (mc == -INFINITY) ? 0.f : fast_exp2(mc - M);
       L += ml[2 * c + 1] * w;
       const float* src = po + (size_t)c * D;
+      if (!cols) continue;
 #pragma unroll
       for (int e = 0; e < PER; e += 4) {
         const float4 x = *(const float4*)(src + e);
@@ -784,14 +816,16 @@ __global__ __launch_bounds__(64 * kCombineWaves) void combine_kernel(AttnParams 
       }
     }
   }
+  if (cols) {
 #pragma unroll
-  for (int e = 0; e < PER; e += 4)
-    *(float4*)(&part[wave][lane * PER + e]) = make_float4(acc[e], acc[e + 1], acc[e + 2], acc[e + 3]);
+    for (int e = 0; e < PER; e += 4)
+      *(float4*)(&part[wave][lane * PER + e]) = make_float4(acc[e], acc[e + 1], acc[e + 2], acc[e + 3]);
+  }
   if (lane == 0) lpart[wave] = L;
   __syncthreads();
 
   // wave 0: the wave partials in wave order, normalise, round
-  if (wave != 0) return;
+  if (wave != 0 || !cols) return;
   float Lt = 0.f;
   for (int w = 0; w < nw; ++w) Lt += lpart[w];
   const float inv = (Lt > 0.f) ? 1.0f / Lt : 0.f;
@@ -816,7 +850,9 @@ __global__ __launch_bounds__(64 * kCombineWaves) void combine_kernel(AttnParams 
 template <int DT, int D, bool RING>
 hipError_t launch_attention_t(const AttnParams& p, hipStream_t stream) {
   const dim3 grid((unsigned)(p.B * p.Hkv * p.mblocks), (unsigned)p.nsplit, 1);
-  if constexpr (D == 256)
+  if constexpr (D == 128)
+    hipLaunchKernelGGL((attn_tile_kernel_d128<DT, RING>), grid, dim3(256), 0, stream, p);
+  else if constexpr (D == 256)
     hipLaunchKernelGGL((attn_tile_kernel_d256<DT, RING>), grid, dim3(256), 0, stream, p);
   else
     hipLaunchKernelGGL((attn_tile_kernel_d512<DT, RING>), grid, dim3(256), 0, stream, p);
@@ -839,11 +875,13 @@ hipError_t launch_attention_d(const AttnParams& p, int dtype, hipStream_t stream
 }
 
 hipError_t launch_attention(const AttnParams& p, int D, int dtype, bool ring, hipStream_t stream) {
+  if (D == 128) return ring ? launch_attention_d<128, true>(p, dtype, stream) : launch_attention_d<128, false>(p, dtype, stream);
   if (D == 256) return ring ? launch_attention_d<256, true>(p, dtype, stream) : launch_attention_d<256, false>(p, dtype, stream);
   return ring ? launch_attention_d<512, true>(p, dtype, stream) : launch_attention_d<512, false>(p, dtype, stream);
 }
 
 hipError_t launch_combine(const AttnParams& p, int D, int dtype, hipStream_t stream) {
+  if (D == 128) return dtype == 0 ? launch_combine_t<0, 128>(p, stream) : launch_combine_t<1, 128>(p, stream);
   if (D == 256) return dtype == 0 ? launch_combine_t<0, 256>(p, stream) : launch_combine_t<1, 256>(p, stream);
   return dtype == 0 ? launch_combine_t<0, 512>(p, stream) : launch_combine_t<1, 512>(p, stream);
 }

@@ -33,8 +33,8 @@ int check_shape(int B, int Hq, int Hkv, int qL, int kL, int D) {
                 Hkv, qL, kL);
   if (Hq % Hkv != 0)
     return fail(SDPA_INVALID_ARG, "Hq (%d) must be a multiple of Hkv (%d)", Hq, Hkv);
-  if (D != 256 && D != 512)
-    return fail(SDPA_UNSUPPORTED, "head_dim %d is not supported (256 or 512)", D);
+  if (D != 128 && D != 256 && D != 512)
+    return fail(SDPA_UNSUPPORTED, "head_dim %d is not supported (128, 256 or 512)", D);
   // index arithmetic inside the kernels: packed rows per KV head and the
   // launch grid stay in 32-bit range; byte offsets are 64-bit
   const int64_t rows = (int64_t)(Hq / Hkv) * qL;

@@ -72,6 +72,8 @@ WORKLOADS = {
                        "Gemma-4-31B-like sliding layer, B1 Hq32 Hkv16 D256 L32768 bf16 window 1024"),
     "global_d512_32k": _wl("global_d512_32k", 1, 32, 4, 32768, 32768, 512, BF16, True, 0, 0, 42,
                            "Gemma-4-31B-like global layer, B1 Hq32 Hkv4 D512 L32768 bf16 causal"),
+    "causal_d128_16k": _wl("causal_d128_16k", 1, 32, 8, 16384, 16384, 128, BF16, True, 0, 0, 6,
+                           "head_dim 128 causal self-attention, B1 Hq32 Hkv8 D128 L16384 bf16"),
     "decode_q4_128k": _wl("decode_q4_128k", 1, 16, 8, 4, 131072, 256, BF16, True, 0, 131072 - 4, 5,
                           "verify block, B1 Hq16 Hkv8 D256 qL4 kL131072 bf16 causal bottom-right"),
     "decode_q1_128k": _wl("decode_q1_128k", 1, 16, 8, 1, 131072, 256, BF16, True, 0, 131072 - 1, 5,

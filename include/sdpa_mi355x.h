@@ -58,7 +58,7 @@ extern "C" {
 /* Status codes. */
 #define SDPA_OK 0
 #define SDPA_INVALID_ARG 1          /* a pointer, size, flag or offset is out of range */
-#define SDPA_UNSUPPORTED 2          /* head_dim not 256/512, or an unknown dtype */
+#define SDPA_UNSUPPORTED 2          /* head_dim not 128/256/512, or an unknown dtype */
 #define SDPA_WORKSPACE_TOO_SMALL 3  /* workspace_bytes < sdpa_workspace_bytes(...) */
 #define SDPA_HIP_ERROR 4            /* the kernel launch reported a HIP error */
 
@@ -73,7 +73,7 @@ extern "C" {
  *   q, k, v   device pointers, layouts above, element type `dtype`; read only.
  *   out       device pointer, [B, Hq, qL, D]; written.  Must not overlap q/k/v.
  *   B, Hq, Hkv, qL, kL  sizes, all >= 1; Hq must be a multiple of Hkv.
- *   D         head dimension: 256 or 512 (else SDPA_UNSUPPORTED).
+ *   D         head dimension: 128, 256 or 512 (else SDPA_UNSUPPORTED).
  *   scale     finite fp32 factor > 0 applied to q.k (1/sqrt(D) is the usual one).
  *   causal    0 or 1.
  *   window    0 (none) or >= 1; a window requires causal = 1.

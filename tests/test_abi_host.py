@@ -66,7 +66,7 @@ BAD = [
     (dict(B=0), fa.SDPA_INVALID_ARG, ">= 1"),
     (dict(kL=-3), fa.SDPA_INVALID_ARG, ">= 1"),
     (dict(Hq=3), fa.SDPA_INVALID_ARG, "multiple"),
-    (dict(D=128), fa.SDPA_UNSUPPORTED, "head_dim"),
+    (dict(D=64), fa.SDPA_UNSUPPORTED, "head_dim"),
     (dict(D=192), fa.SDPA_UNSUPPORTED, "head_dim"),
     (dict(dtype=2), fa.SDPA_UNSUPPORTED, "dtype"),
     (dict(scale=float("nan")), fa.SDPA_INVALID_ARG, "scale"),
@@ -190,7 +190,7 @@ def test_workspace_is_linear_in_key_chunks_not_quadratic(lib):
 
 
 def test_workspace_of_rejected_shapes_is_size_max(lib):
-    assert fa.sdpa_workspace_bytes(1, 4, 2, 8, 64, 128) == SIZE_MAX
+    assert fa.sdpa_workspace_bytes(1, 4, 2, 8, 64, 192) == SIZE_MAX
     assert fa.sdpa_workspace_bytes(1, 3, 2, 8, 64, 256) == SIZE_MAX
     assert fa.sdpa_workspace_bytes(0, 4, 2, 8, 64, 256) == SIZE_MAX
 

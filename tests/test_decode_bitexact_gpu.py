@@ -67,6 +67,12 @@ def test_verify_block_at_head_dim_512_global_geometry():
     _check_rows(q, k, v, window=0, what="D512 32/4")
 
 
+@pytest.mark.timeout(600)
+def test_verify_block_at_head_dim_128():
+    q, k, v = W.random_qkv(54, 1, 32, 8, 4, 20000, 128, BF16)
+    _check_rows(q, k, v, window=0, what="D128 32/8")
+
+
 @pytest.mark.parametrize("qL", [2, 3])
 def test_verify_blocks_of_two_and_three(qL):
     q, k, v = W.random_qkv(52 + qL, 1, 16, 8, qL, 20000, 256, BF16)

@@ -44,6 +44,11 @@ SMALL = [
     (1, 4, 2, 3, 2500, 256, BF16, True, 100, 2497),    # verify block with a window
     (1, 8, 2, 4, 1500, 512, BF16, True, 0, 1496),      # verify block at head_dim 512
     (2, 2, 1, 2, 700, 256, FP16, False, 0, 0),         # unmasked decode
+    (2, 4, 2, 333, 333, 128, FP16, True, 0, 0),        # head_dim 128: ragged tiles and row blocks
+    (1, 4, 2, 100, 1000, 128, BF16, True, 77, 900),    # head_dim 128, window over a prefix
+    (1, 2, 1, 300, 9000, 128, FP16, True, 0, 8700),    # head_dim 128 with key split
+    (1, 4, 2, 4, 2500, 128, BF16, True, 0, 2496),      # head_dim 128 verify block
+    (1, 2, 2, 65, 190, 128, BF16, False, 0, 0),        # head_dim 128, no mask
 ]
 
 
@@ -72,7 +77,7 @@ def test_tiny_causal_workload_every_row():
 
 
 FULL = [("chunked_prefill_32k", 160), ("causal_h64_16k", 160), ("sliding_32k", 200),
-        ("global_d512_32k", 64), ("decode_q4_128k", 32), ("decode_q1_128k", 16)]
+        ("global_d512_32k", 64), ("causal_d128_16k", 96), ("decode_q4_128k", 32), ("decode_q1_128k", 16)]
 
 
 @pytest.mark.timeout(600)
