@@ -74,6 +74,11 @@ def load(path: str = _LIB):
         [u16p, u16p, u16p, f64p] + [ci] * 6 + [ctypes.c_float] + [ci] * 4 + [i64p, ctypes.c_int64, ci]
     )
     lib.oracle_sdpa_rows_f64.restype = ci
+    i64 = ctypes.c_int64
+    lib.oracle_sdpa_bias_f64.argtypes = (
+        [u16p, u16p, u16p, u16p, i64, i64, i64, f64p] + [ci] * 6 + [ctypes.c_float] + [ci] * 4 + [i64p, i64, ci]
+    )
+    lib.oracle_sdpa_bias_f64.restype = ci
     lib.oracle_widen.argtypes = [u16p, f64p, ctypes.c_int64, ci]
     lib.oracle_widen.restype = None
     if path == _LIB:
@@ -156,4 +161,39 @@ def widen(bits, dtype: int, lib=None) -> np.ndarray:
     b = _bits(bits)
     out = np.empty(b.shape, dtype=np.float64)
     lib.oracle_widen(_ptr(b, ctypes.c_uint16), _ptr(out, ctypes.c_double), b.size, int(dtype))
+    return out
+
+
+def sdpa_bias_f64(q, k, v, bias, *, scale: float, causal: bool = False, window: int = 0,
+                  q_offset: int = 0, dtype: int = FP16, rows=None, threads: int | None = None,
+                  lib=None) -> np.ndarray:
+    """Output rows with an additive mask array added to the scaled scores.
+
+    bias: uint16 bit patterns (the input dtype), shape [Bb, Hb, qL, kL] with Bb in
+    {1, B} and Hb in {1, Hq} (1 broadcasts).  rows=None: every row, [B, Hq, qL, D];
+    else the flat rows (b*Hq + hq)*qL + i, [len(rows), D].
+    """
+    lib = lib or load()
+    q, k, v, bias = _bits(q), _bits(k), _bits(v), _bits(bias)
+    B, Hq, Hkv, qL, kL, D = _check_shapes(q, k, v)
+    if bias.ndim != 4 or bias.shape[2:] != (qL, kL) or bias.shape[0] not in (1, B) or bias.shape[1] not in (1, Hq):
+        raise ValueError(f"bias shape {bias.shape} does not broadcast to {(B, Hq, qL, kL)}")
+    sq = kL
+    sh = 0 if bias.shape[1] == 1 else qL * kL
+    sb = 0 if bias.shape[0] == 1 else bias.shape[1] * qL * kL
+    if rows is None:
+        out = np.empty((B, Hq, qL, D), dtype=np.float64)
+        rptr, nrows = None, 0
+    else:
+        rows = np.ascontiguousarray(rows, dtype=np.int64)
+        out = np.empty((rows.size, D), dtype=np.float64)
+        rptr, nrows = _ptr(rows, ctypes.c_int64), rows.size
+    rc = lib.oracle_sdpa_bias_f64(
+        _ptr(q, ctypes.c_uint16), _ptr(k, ctypes.c_uint16), _ptr(v, ctypes.c_uint16),
+        _ptr(bias, ctypes.c_uint16), sb, sh, sq, _ptr(out, ctypes.c_double), B, Hq, Hkv, qL, kL, D,
+        float(np.float32(scale)), int(bool(causal)), int(window), int(q_offset), int(dtype), rptr, nrows,
+        int(threads or default_threads()),
+    )
+    if rc != 0:
+        raise RuntimeError(f"oracle_sdpa_bias_f64 failed ({rc})")
     return out

@@ -40,7 +40,15 @@
  *   - a masked key is excluded outright (weight exactly zero), never given a
  *     large finite negative score;
  *   - inputs are the exact fp16/bf16 bit patterns, widened exactly; scale is
- *     the fp32 value the caller passes, widened exactly.
+ *     the fp32 value the caller passes, widened exactly;
+ *   - an optional additive mask array ("bias") is added to the scaled score,
+ *     s_j = scale * <q, k_j> + bias[b, hq, i, j] (the array mask that
+ *     lablup/mlxcel issue #672, Root cause, hands to SDPA and that the cuDNN
+ *     path takes as a bias); it has the input dtype, and keys are contiguous
+ *     within a bias row, its batch, head and row strides are given (0 for a
+ *     broadcast dimension).  A key whose biased score is -inf is excluded
+ *     like a masked key; a row with no finite score is a zero row.  The
+ *     causal and window rules still apply on top.
  */
 #include <math.h>
 #include <pthread.h>
@@ -80,6 +88,8 @@ static double widen(uint16_t h, int dtype) {
 
 typedef struct {
   const uint16_t *q, *k, *v;
+  const uint16_t *bias; /* NULL: none */
+  int64_t bias_sb, bias_sh, bias_sq;
   int B, Hq, Hkv, qL, kL, D;
   double scale;
   int causal, window, q_offset, dtype;
@@ -112,8 +122,10 @@ static void attend_row(const problem_t *pr, long row, double *s, double *o) {
 
   double *qd = o; /* widen q into the output buffer; it is overwritten later */
   for (long d = 0; d < D; ++d) qd[d] = widen(qrow[d], pr->dtype);
+  const uint16_t *brow = pr->bias ? pr->bias + b * pr->bias_sb + hq * pr->bias_sh + i * pr->bias_sq : NULL;
 
-  /* pass 1: scores of the visible keys, and their maximum */
+  /* pass 1: scores of the visible keys (plus the bias), and their maximum;
+   * a key whose score is -inf takes no part from here on */
   int any = 0;
   double m = -INFINITY;
   for (long j = 0; j < pr->kL; ++j) {
@@ -122,23 +134,25 @@ static void attend_row(const problem_t *pr, long row, double *s, double *o) {
     double dot = 0.0;
     for (long d = 0; d < D; ++d) dot += qd[d] * widen(krow[d], pr->dtype);
     s[j] = pr->scale * dot;
+    if (brow) s[j] += widen(brow[j], pr->dtype);
+    if (s[j] == -INFINITY) continue;
     if (!any || s[j] > m) m = s[j];
     any = 1;
   }
   for (long d = 0; d < D; ++d) o[d] = 0.0;
-  if (!any) return; /* no visible key: defined as a zero row */
+  if (!any) return; /* no visible key with a finite score: defined as a zero row */
 
   /* pass 2: exponentials relative to the maximum, and their sum */
   double l = 0.0;
   for (long j = 0; j < pr->kL; ++j) {
-    if (!key_visible(pr, p, j)) continue;
+    if (!key_visible(pr, p, j) || s[j] == -INFINITY) continue;
     s[j] = exp(s[j] - m);
     l += s[j];
   }
 
   /* pass 3: weighted sum of value rows, then normalise */
   for (long j = 0; j < pr->kL; ++j) {
-    if (!key_visible(pr, p, j)) continue;
+    if (!key_visible(pr, p, j) || s[j] == -INFINITY) continue;
     const uint16_t *vrow = vbase + j * D;
     for (long d = 0; d < D; ++d) o[d] += s[j] * widen(vrow[d], pr->dtype);
   }
@@ -208,6 +222,8 @@ static int make_problem(problem_t *pr, const uint16_t *q, const uint16_t *k, con
   pr->q = q;
   pr->k = k;
   pr->v = v;
+  pr->bias = NULL;
+  pr->bias_sb = pr->bias_sh = pr->bias_sq = 0;
   pr->B = B;
   pr->Hq = Hq;
   pr->Hkv = Hkv;
@@ -250,6 +266,32 @@ int oracle_sdpa_rows_f64(const uint16_t *q, const uint16_t *k, const uint16_t *v
   for (int64_t n = 0; n < nrows; ++n)
     if (rows[n] < 0 || rows[n] >= total) return -1;
   if (nrows == 0) return 0;
+  return run(&pr, rows, nrows, out, nthreads);
+}
+
+/*
+ * The same with an additive mask array: bias row (b, hq, i) starts at element
+ * b * bias_sb + hq * bias_sh + i * bias_sq of `bias` and holds kL keys.
+ * rows == NULL: every row, out [B, Hq, qL, D]; else out is [nrows, D].
+ */
+int oracle_sdpa_bias_f64(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                         const uint16_t *bias, int64_t bias_sb, int64_t bias_sh, int64_t bias_sq,
+                         double *out, int B, int Hq, int Hkv, int qL, int kL, int D, float scale,
+                         int causal, int window, int q_offset, int dtype, const int64_t *rows,
+                         int64_t nrows, int nthreads) {
+  problem_t pr;
+  if (!out || !bias || bias_sb < 0 || bias_sh < 0 || bias_sq < 0 ||
+      make_problem(&pr, q, k, v, B, Hq, Hkv, qL, kL, D, scale, causal, window, q_offset, dtype))
+    return -1;
+  pr.bias = bias;
+  pr.bias_sb = bias_sb;
+  pr.bias_sh = bias_sh;
+  pr.bias_sq = bias_sq;
+  if (!rows) return run(&pr, NULL, (int64_t)B * Hq * qL, out, nthreads);
+  const int64_t total = (int64_t)B * Hq * qL;
+  for (int64_t n = 0; n < nrows; ++n)
+    if (rows[n] < 0 || rows[n] >= total) return -1;
+  if (nrows <= 0) return nrows == 0 ? 0 : -1;
   return run(&pr, rows, nrows, out, nthreads);
 }
 

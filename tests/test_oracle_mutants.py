@@ -34,8 +34,13 @@ MUTANTS = {
     "bf16_widened_as_fp16": ("return dtype == ORACLE_BF16 ? widen_bf16(h) : widen_fp16(h);",
                              "return widen_fp16(h);"),
     "max_over_first_key_only": ("if (!any || s[j] > m) m = s[j];", "if (!any) m = s[j];"),
-    "last_visible_key_skipped": ("for (long j = 0; j < pr->kL; ++j) {\n    if (!key_visible(pr, p, j)) continue;\n    const uint16_t *vrow",
-                                 "for (long j = 0; j < pr->kL; ++j) {\n    if (!key_visible(pr, p, j) || !key_visible(pr, p, j + 1)) continue;\n    const uint16_t *vrow"),
+    "last_visible_key_skipped": ("    if (!key_visible(pr, p, j) || s[j] == -INFINITY) continue;\n    const uint16_t *vrow",
+                                 "    if (!key_visible(pr, p, j) || s[j] == -INFINITY || !key_visible(pr, p, j + 1)) continue;\n    const uint16_t *vrow"),
+    "bias_ignored": ("if (brow) s[j] += widen(brow[j], pr->dtype);", "(void)brow;"),
+    "bias_subtracted": ("if (brow) s[j] += widen(brow[j], pr->dtype);", "if (brow) s[j] -= widen(brow[j], pr->dtype);"),
+    "bias_head_stride_dropped": ("hq * pr->bias_sh", "0 * pr->bias_sh"),
+    "bias_row_stride_dropped": ("i * pr->bias_sq", "0 * pr->bias_sq"),
+    "minus_inf_bias_not_excluded": ("    if (s[j] == -INFINITY) continue;\n    if (!any", "    if (!any"),
 }
 
 

@@ -259,3 +259,106 @@ def test_thread_count_does_not_change_results(oracle_lib):
     a = oracle.sdpa_f64(q, k, v, threads=1, **kw)
     b = oracle.sdpa_f64(q, k, v, threads=7, **kw)
     assert np.array_equal(a, b)
+
+
+# ------------------------------------------- additive mask array ("bias") --
+def _bias_bits(rng, shape, dtype, ninf_frac=0.0):
+    """Random N(0, 2) bias rounded to dtype, with a fraction of -inf entries (never
+    a whole row), as bit patterns."""
+    b = rng.normal(0.0, 2.0, size=shape).astype(np.float32)
+    if ninf_frac > 0:
+        drop = rng.random(shape) < ninf_frac
+        drop[..., 0] = False  # every row keeps at least key 0
+        b[drop] = -np.inf
+    return _np_bits(b, dtype)
+
+
+def _torch_ref_bias(q, k, v, bias, scale, causal, window, q_offset, dtype):
+    qd = torch.from_numpy(_widened(q, dtype))
+    kd = torch.from_numpy(_widened(k, dtype))
+    vd = torch.from_numpy(_widened(v, dtype))
+    add = torch.from_numpy(_widened(bias, dtype))
+    mask = torch.from_numpy(_mask(q.shape[2], k.shape[2], causal, window, q_offset))
+    add = torch.where(mask, add, torch.tensor(float("-inf"), dtype=torch.float64))
+    return F.scaled_dot_product_attention(qd, kd, vd, attn_mask=add, scale=float(np.float32(scale)),
+                                          enable_gqa=True).numpy()
+
+
+@pytest.mark.parametrize("bshape", ["11", "B1", "1H", "BH"])
+@pytest.mark.parametrize("causal,window", [(False, 0), (True, 0), (True, 3)])
+def test_bias_matches_torch_float64_sdpa_with_a_float_mask(oracle_lib, bshape, causal, window):
+    rng = np.random.default_rng(7)
+    for (Hq, Hkv), qL, kL, dtype, D in [((2, 1), 3, 9, FP16, 8), ((4, 2), 9, 9, BF16, 5), ((1, 1), 1, 4, BF16, 8)]:
+        B = 2
+        q_offset = kL - qL if causal else 0
+        q, k, v = (W.bits(t) for t in W.random_qkv(300 + qL + kL, B, Hq, Hkv, qL, kL, D, dtype))
+        shape = (B if bshape[0] == "B" else 1, Hq if bshape[1] == "H" else 1, qL, kL)
+        bias = _bias_bits(rng, shape, dtype, ninf_frac=0.2 if not causal else 0.0)
+        got = oracle.sdpa_bias_f64(q, k, v, bias, scale=0.37, causal=causal, window=window,
+                                   q_offset=q_offset, dtype=dtype, threads=2)
+        ref = _torch_ref_bias(q, k, v, bias, 0.37, causal, window, q_offset, dtype)
+        np.testing.assert_allclose(got, ref, rtol=0, atol=1e-12)
+
+
+def test_zero_bias_is_the_unbiased_call_bitwise(oracle_lib):
+    q, k, v = (W.bits(t) for t in W.random_qkv(401, 2, 4, 2, 5, 11, 8, BF16))
+    zero = np.zeros((1, 1, 5, 11), dtype=np.uint16)
+    a = oracle.sdpa_bias_f64(q, k, v, zero, scale=0.5, causal=True, q_offset=6, dtype=BF16, threads=2)
+    b = oracle.sdpa_f64(q, k, v, scale=0.5, causal=True, q_offset=6, dtype=BF16, threads=2)
+    assert np.array_equal(a, b)
+
+
+def test_minus_inf_bias_drops_exactly_those_keys(oracle_lib):
+    # a row whose bias is 0 on a key subset and -inf elsewhere equals the
+    # unbiased single-row call over that subset of keys
+    rng = np.random.default_rng(11)
+    qL, kL, D = 4, 13, 8
+    q, k, v = (W.bits(t) for t in W.random_qkv(402, 1, 2, 1, qL, kL, D, FP16))
+    keep = rng.random((1, 2, qL, kL)) < 0.5
+    keep[..., 3] = True
+    bias = np.where(keep, np.uint16(0), _np_bits(np.array([-np.inf], dtype=np.float32), FP16)[0])
+    got = oracle.sdpa_bias_f64(q, k, v, bias.astype(np.uint16), scale=0.3, dtype=FP16, threads=2)
+    for h in range(2):
+        for i in range(qL):
+            idx = np.nonzero(keep[0, h, i])[0]
+            one = oracle.sdpa_f64(q[:, h:h + 1, i:i + 1], k[:, :, idx], v[:, :, idx], scale=0.3, dtype=FP16,
+                                  threads=1)
+            assert np.array_equal(got[0, h, i], one[0, 0, 0]), (h, i)
+
+
+def test_a_constant_bias_per_row_changes_only_rounding(oracle_lib):
+    q, k, v = (W.bits(t) for t in W.random_qkv(403, 1, 2, 2, 6, 10, 8, BF16))
+    row_const = np.repeat(np.linspace(-3.0, 5.0, 6, dtype=np.float32)[:, None], 10, axis=1)
+    bias = _np_bits(row_const[None, None], BF16)
+    a = oracle.sdpa_bias_f64(q, k, v, bias, scale=0.4, causal=True, q_offset=4, dtype=BF16, threads=2)
+    b = oracle.sdpa_f64(q, k, v, scale=0.4, causal=True, q_offset=4, dtype=BF16, threads=2)
+    np.testing.assert_allclose(a, b, rtol=0, atol=1e-12)
+
+
+def test_head_broadcast_bias_equals_an_explicit_repeat(oracle_lib):
+    rng = np.random.default_rng(12)
+    q, k, v = (W.bits(t) for t in W.random_qkv(404, 2, 4, 2, 3, 7, 8, FP16))
+    b1 = _bias_bits(rng, (2, 1, 3, 7), FP16)
+    a = oracle.sdpa_bias_f64(q, k, v, b1, scale=0.3, dtype=FP16, threads=2)
+    b = oracle.sdpa_bias_f64(q, k, v, np.repeat(b1, 4, axis=1), scale=0.3, dtype=FP16, threads=2)
+    assert np.array_equal(a, b)
+
+
+def test_a_row_with_no_finite_biased_score_is_a_zero_row(oracle_lib):
+    q, k, v = (W.bits(t) for t in W.random_qkv(405, 1, 1, 1, 2, 5, 8, BF16))
+    f = np.zeros((1, 1, 2, 5), dtype=np.float32)
+    f[0, 0, 1, :] = -np.inf
+    got = oracle.sdpa_bias_f64(q, k, v, _np_bits(f, BF16), scale=0.3, dtype=BF16, threads=1)
+    assert np.array_equal(got[0, 0, 1], np.zeros(8)) and np.isfinite(got).all()
+    assert np.abs(got[0, 0, 0]).sum() > 0
+
+
+def test_bias_row_selection_equals_the_full_call(oracle_lib):
+    rng = np.random.default_rng(13)
+    q, k, v = (W.bits(t) for t in W.random_qkv(406, 2, 4, 2, 5, 9, 8, BF16))
+    bias = _bias_bits(rng, (2, 4, 5, 9), BF16)
+    full = oracle.sdpa_bias_f64(q, k, v, bias, scale=0.3, causal=True, q_offset=4, dtype=BF16, threads=2)
+    rows = np.array([0, 7, 19, 33, 39], dtype=np.int64)
+    sel = oracle.sdpa_bias_f64(q, k, v, bias, scale=0.3, causal=True, q_offset=4, dtype=BF16, rows=rows,
+                               threads=2)
+    assert np.array_equal(sel, full.reshape(-1, 8)[rows])
