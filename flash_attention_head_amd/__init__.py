@@ -8,9 +8,10 @@ missing or cannot be loaded, every call raises.
 
 Raw entry points (same names and arguments as the C functions, pointers as
 integers): ``sdpa_forward``, ``sdpa_workspace_bytes``, ``sdpa_forward_kv_view``,
-``sdpa_workspace_bytes_kv_view``, ``sdpa_last_error``, ``sdpa_version``.
-Convenience wrappers on torch tensors: ``sdpa`` (contiguous K/V) and
-``sdpa_kv_cache`` (K/V in a cache, possibly a wrapped ring).
+``sdpa_workspace_bytes_kv_view``, ``sdpa_forward_bias``, ``sdpa_last_error``,
+``sdpa_version``.  Convenience wrappers on torch tensors: ``sdpa`` (contiguous
+K/V, optionally an additive mask array) and ``sdpa_kv_cache`` (K/V in a cache,
+possibly a wrapped ring).
 """
 
 from __future__ import annotations
@@ -23,6 +24,7 @@ __all__ = [
     "SDPA_OK", "SDPA_INVALID_ARG", "SDPA_UNSUPPORTED", "SDPA_WORKSPACE_TOO_SMALL",
     "SDPA_HIP_ERROR", "SDPA_FP16", "SDPA_BF16", "SdpaError", "library_path", "load_library",
     "sdpa_forward", "sdpa_workspace_bytes", "sdpa_forward_kv_view", "sdpa_workspace_bytes_kv_view",
+    "sdpa_forward_bias",
     "sdpa_last_error", "sdpa_version", "sdpa", "sdpa_kv_cache", "EXPORTED_SYMBOLS",
 ]
 
@@ -35,7 +37,8 @@ SDPA_FP16 = 0
 SDPA_BF16 = 1
 
 EXPORTED_SYMBOLS = ("sdpa_forward", "sdpa_workspace_bytes", "sdpa_forward_kv_view",
-                    "sdpa_workspace_bytes_kv_view", "sdpa_last_error", "sdpa_version")
+                    "sdpa_workspace_bytes_kv_view", "sdpa_forward_bias", "sdpa_last_error",
+                    "sdpa_version")
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _lib = None
@@ -72,6 +75,9 @@ def load_library():
     lib.sdpa_forward_kv_view.restype = ci
     lib.sdpa_workspace_bytes_kv_view.argtypes = [ci] * 7
     lib.sdpa_workspace_bytes_kv_view.restype = sz
+    ll = ctypes.c_longlong
+    lib.sdpa_forward_bias.argtypes = [vp, vp, vp, vp, ll, ll, ll, vp] + [ci] * 6 + [ctypes.c_float] + [ci] * 4 + [vp, sz, vp]
+    lib.sdpa_forward_bias.restype = ci
     lib.sdpa_last_error.argtypes = []
     lib.sdpa_last_error.restype = ctypes.c_char_p
     lib.sdpa_version.argtypes = []
@@ -104,6 +110,14 @@ def sdpa_forward_kv_view(q, k, v, out, B, Hq, Hkv, qL, kL, kv_capacity, ring_sta
 def sdpa_workspace_bytes_kv_view(B, Hq, Hkv, qL, kL, kv_capacity, D) -> int:
     """``size_t sdpa_workspace_bytes_kv_view(...)``; (size_t)-1 for rejected arguments."""
     return load_library().sdpa_workspace_bytes_kv_view(B, Hq, Hkv, qL, kL, kv_capacity, D)
+
+
+def sdpa_forward_bias(q, k, v, bias, bias_stride_b, bias_stride_h, bias_stride_q, out, B, Hq, Hkv, qL, kL,
+                      D, scale, causal, window, q_offset, dtype, workspace, workspace_bytes, stream) -> int:
+    """``int sdpa_forward_bias(...)`` of the C ABI; pointer arguments are integers."""
+    return load_library().sdpa_forward_bias(q, k, v, bias, bias_stride_b, bias_stride_h, bias_stride_q, out,
+                                            B, Hq, Hkv, qL, kL, D, scale, causal, window, q_offset, dtype,
+                                            workspace, workspace_bytes, stream)
 
 
 def sdpa_last_error() -> str:
@@ -154,7 +168,7 @@ def _prepare(q, need, D, out, workspace, stream):
 
 
 def sdpa(q, k, v, *, scale: float | None = None, causal: bool = False, window: int = 0,
-         q_offset: int | None = None, out=None, workspace=None, stream=None):
+         q_offset: int | None = None, bias=None, out=None, workspace=None, stream=None):
     """softmax(scale * q k^T + mask) v on device tensors.
 
     q: [B, Hq, qL, D], k and v: [B, Hkv, kL, D], contiguous fp16 or bf16 tensors on
@@ -162,6 +176,8 @@ def sdpa(q, k, v, *, scale: float | None = None, causal: bool = False, window: i
     (as fp32).  With causal, query row i sits at key position q_offset + i;
     q_offset defaults to kL - qL (queries aligned to the end of the keys).
     window > 0 limits each row to its last `window` keys (requires causal).
+    bias: an optional additive mask array of q's dtype, a tensor that broadcasts to
+    [B, Hq, qL, kL] with contiguous keys (size-1 or stride-0 dimensions broadcast).
     Runs on `stream` (default: torch's current stream) without synchronising.
     """
     B, Hq, Hkv, qL, kL, D, dtype = _check_tensors(q, k, v)
@@ -171,9 +187,22 @@ def sdpa(q, k, v, *, scale: float | None = None, causal: bool = False, window: i
         q_offset = kL - qL if causal else 0
     need = sdpa_workspace_bytes(B, Hq, Hkv, qL, kL, D)
     out, ws_ptr, ws_bytes, stream = _prepare(q, need, D, out, workspace, stream)
-    rc = sdpa_forward(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, Hq, Hkv, qL, kL,
-                      D, float(scale), int(bool(causal)), int(window), int(q_offset), dtype, ws_ptr,
-                      ws_bytes, stream.cuda_stream)
+    if bias is None:
+        rc = sdpa_forward(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, Hq, Hkv, qL, kL,
+                          D, float(scale), int(bool(causal)), int(window), int(q_offset), dtype, ws_ptr,
+                          ws_bytes, stream.cuda_stream)
+    else:
+        if bias.dtype != q.dtype or not bias.is_cuda or bias.dim() != 4:
+            raise ValueError("bias must be a 4-D GPU tensor of q's dtype")
+        bshape = tuple(bias.shape)
+        if bshape[2:] != (qL, kL) or bshape[0] not in (1, B) or bshape[1] not in (1, Hq):
+            raise ValueError(f"bias {bshape} does not broadcast to {(B, Hq, qL, kL)}")
+        if kL > 1 and bias.stride(3) != 1:
+            raise ValueError("bias keys must be contiguous")
+        sb, sh, sq = (0 if bshape[i] == 1 else bias.stride(i) for i in range(3))
+        rc = sdpa_forward_bias(q.data_ptr(), k.data_ptr(), v.data_ptr(), bias.data_ptr(), sb, sh, sq,
+                               out.data_ptr(), B, Hq, Hkv, qL, kL, D, float(scale), int(bool(causal)),
+                               int(window), int(q_offset), dtype, ws_ptr, ws_bytes, stream.cuda_stream)
     if rc != SDPA_OK:
         raise SdpaError(rc, sdpa_last_error())
     return out

@@ -221,7 +221,7 @@ constexpr float kRescaleLog2 = 8.f;
 // busy through the softmax.  K and V have separate double buffers, V one
 // tile behind K: step t reads K(t+1) and V(t) and loads K(t+2) and V(t+1).
 // ---------------------------------------------------------------------------
-template <int DT, int D, bool RING>
+template <int DT, int D, bool RING, bool BIAS>
 __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* lds) {
   // D = 128 or 256: a wave owns 32 rows and all D columns.  D = 512: the
   // two waves of a pair own the same 32 rows; wave h multiplies Q columns
@@ -409,6 +409,73 @@ __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* ld
     m0_restore(m0);
   };
   auto load_k = [&](int t) { load_tile(kg, t, kbuf0 + ((t - t_first) & 1) * TILE, false); };
+
+  // Additive mask array (BIAS).  A bias tile holds this workgroup's BM
+  // packed rows x BN keys for one K/V tile, in LDS after K, V (and the pair
+  // exchange), double-buffered like K: bias(t) is in bias buffer
+  // (t - t_first) & 1 and is loaded with K(t).  Chunk c (8 keys) of tile row
+  // r sits at chunk position c ^ (r & (BCPR - 1)), so the 32 rows a read
+  // touches spread over the banks.  A lane's load offsets are loop-invariant
+  // (its row's (query head, position) and its chunk); rows past the
+  // workgroup's last row point out of the descriptor's range and read zeros,
+  // keys past kL read the next row's entries, whose scores are masked.
+  constexpr int BTILE = BM * BN, BCPR = BN * 2 / 16, BRPB = 64 / BCPR;
+  constexpr int BLOADS = BIAS ? BTILE * 2 / 1024 / NW : 0;
+  static_assert(!BIAS || (BLOADS >= 1 && BRPB * BCPR == 64 && !RING), "bias tile geometry");
+  uint16_t* const bbuf0 = lds + 4 * TILE + (PAIR ? 2 * 4 * 64 * 16 : 0);
+  uint32_t boff[BLOADS > 0 ? BLOADS : 1];
+  int bbase = 0;
+  int64_t bias_extent = 0;
+  const uint16_t* bias_b = nullptr;
+  if constexpr (BIAS) {
+#pragma unroll
+    for (int n = 0; n < BLOADS; ++n) {
+      const int r = (wave + NW * n) * BRPB + lane / BCPR;  // bias tile row
+      const int c = (lane % BCPR) ^ (r & (BCPR - 1));
+      const int prow = row0 + r;
+      const int pq = prow / p.G, ph = hkv * p.G + prow % p.G;
+      boff[n] = prow < rows_end ? (uint32_t)((ph * p.bias_sh + pq * p.bias_sq + 8 * c) * 2) : 0xfffffff0u;
+    }
+    bias_b = p.bias + b * p.bias_sb;
+    bias_extent = (int64_t)(p.Hq - 1) * p.bias_sh + (int64_t)(p.qL - 1) * p.bias_sq + p.kL;
+    const int r = rb * kRowsPerWave + lr;  // this lane's row in the bias tile
+    bbase = r * BN + 8 * (r & (BCPR - 1)) + 4 * lg;
+  }
+  // batch b's bias from key t BN to the end of its extent.  The range check
+  // is per 4-byte word, so the range is rounded up to a whole word: a word
+  // that holds the extent's last element and the 2 bytes after it must not
+  // read as zero (those 2 bytes share its aligned 4-byte granule, so they
+  // are mapped; their value only reaches keys past kL, which are masked)
+  auto bias_src = [&](int t) {
+    const int ts = __builtin_amdgcn_readfirstlane(t * BN);
+    return tile_rsrc(uniform_addr(bias_b + ts), __builtin_amdgcn_readfirstlane((int)(((bias_extent - ts) * 2 + 3) & ~3ll)));
+  };
+  auto load_bblk = [&](const i32x4_t& src, uint16_t* buf, int n) {
+    load_lds16(src, boff[n], 0u, buf + (wave + NW * n) * 512);
+  };
+  auto load_b = [&](int t) {
+    if constexpr (BIAS) {
+      const i32x4_t src = bias_src(t);
+      const unsigned m0 = m0_save();
+#pragma unroll
+      for (int n = 0; n < BLOADS; ++n) load_bblk(src, bbuf0 + ((t - t_first) & 1) * BTILE, n);
+      m0_restore(m0);
+    }
+  };
+  // the 4-key groups of bias a lane needs for one tile (group g holds the
+  // keys of score elements 4 g .. 4 g + 3), and one element's value in the
+  // units of the raw q.k scores the kernel keeps (bias / scale: the softmax
+  // takes exp2(s scale log2 e), so s + bias / scale gives scale s + bias)
+  const float inv_scale = p.inv_scale;
+  auto bias_read = [&](const uint16_t* bl, int g) { return *(const uint2*)(bl + (bbase ^ (8 * g))); };
+  auto bias_val = [&](const uint2 (&bw)[KB * 4], int e) {
+    const uint32_t w = (e % 4) < 2 ? bw[e / 4].x : bw[e / 4].y;
+    const uint32_t h = (e & 1) ? (w >> 16) : (w & 0xffffu);
+    float x;
+    if constexpr (DT == 1) x = __builtin_bit_cast(float, h << 16);
+    else x = (float)__builtin_bit_cast(_Float16, (uint16_t)h);
+    return x * inv_scale;
+  };
   auto load_v = [&](int t) { load_tile(vg, t, vbuf0 + ((t - t_first) & 1) * TILE, true); };
 
   // the keys row `pos` sees form one interval [key_lo, key_hi] (empty if
@@ -498,7 +565,8 @@ __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* ld
   // the direct loads of K(tk) into kdst and V(tv) into vdst
   auto qk_weights = [&](f32x16_t (&sn)[KB], const uint16_t* kl, f32x16_t (&sc)[KB],
                         uint4 (&pb)[KB * 2], const TileSrc& ksrc, uint16_t* kdst, const TileSrc& vsrc,
-                        uint16_t* vdst) {
+                        uint16_t* vdst, const i32x4_t& bsrc, uint16_t* bdst, const uint16_t* bl,
+                        uint2 (&bw)[KB * 4]) {
     constexpr int NQK = KB * DC, PF = 4, LS = NQK / LOADS;
     static_assert(LS >= 2 && LS % 2 == 0, "slot pattern");
 #pragma unroll
@@ -539,6 +607,12 @@ __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* ld
       // loads: K block group i at slot i LS, V block group i at slot i LS + LS / 2
       if (n % LS == 0) load_blk(ksrc, kdst, n / LS, false);
       if (n % LS == LS / 2) load_blk(vsrc, vdst, n / LS, true);
+      if constexpr (BIAS) {
+        // the bias tile that goes with K(tk), and in the last slots the bias
+        // of S(t + 1) for the P V region (its reads are in flight by then)
+        if (n % LS == 1 && n / LS < BLOADS) load_bblk(bsrc, bdst, n / LS);
+        if (n >= NQK - KB * 4) bw[n - (NQK - KB * 4)] = bias_read(bl, n - (NQK - KB * 4));
+      }
 #pragma unroll
       for (int i = 0; i < EPS; ++i) {
         const int ef = EPS * (n + 2) + i, ex = EPS * (n + 1) + i;
@@ -573,7 +647,8 @@ __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* ld
     return psum;
   };
   // O += P(t) V(t)  ||  row max of S(t+1) (already masked)
-  auto pv_max = [&](const uint4 (&pb)[KB * 2], const uint16_t* vl, f32x16_t (&sn)[KB], bool live) {
+  auto pv_max = [&](const uint4 (&pb)[KB * 2], const uint16_t* vl, f32x16_t (&sn)[KB], bool live,
+                    const uint2 (&bw)[KB * 4]) {
     constexpr int NPV = KB * 2 * DB, PF = 4;
     // V^T operand of MFMA n: key half n / DB, column block n % DB; the XOR
     // part of the address is a register, the rest an immediate
@@ -585,6 +660,17 @@ __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* ld
     };
     auto get = [&](int e) { return sn[e / 16][e % 16]; };
     float mx = -INFINITY;
+    // BIAS: the elements a slot's max takes get their bias one slot before
+    auto add_bias = [&](int slot) {
+      if constexpr (BIAS) {
+#pragma unroll
+        for (int i = 0; i < EPV; ++i) {
+          const int e = EPV * slot + i;
+          if (e < NE) sn[e / 16][e % 16] = get(e) + bias_val(bw, e);
+        }
+      }
+    };
+    add_bias(0);
     uint4 bv[PF];
 #pragma unroll
     for (int i = 0; i < PF; ++i) bv[i] = vread(i, vx(i));
@@ -597,6 +683,7 @@ __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* ld
       if (n + PF + 1 < NPV) x_next = vx(n + PF + 1);
       if (EPV == 2) mx = max3(mx, get(2 * n), get(2 * n + 1));  // this slot's pair of elements
       else if (n & 1) mx = max3(mx, get(n - 1), get(n));         // every other slot, the last pair
+      add_bias(n + 1);
       __builtin_amdgcn_sched_barrier(0);
     }
     mx = pair_max(mx);
@@ -644,8 +731,12 @@ __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* ld
     __syncthreads();
   }
   load_k(t_first);
+  load_b(t_first);
   load_v(t_first);
-  if (t_first < t_last) load_k(t_first + 1);
+  if (t_first < t_last) {
+    load_k(t_first + 1);
+    load_b(t_first + 1);
+  }
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
@@ -654,6 +745,13 @@ __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* ld
   if (wave_active) qk(sA, kbuf0);
   exchange(sA, wave_active);
   if (wave_active) {
+    if constexpr (BIAS) {
+      uint2 bw0[KB * 4];
+#pragma unroll
+      for (int g = 0; g < KB * 4; ++g) bw0[g] = bias_read(bbuf0, g);
+#pragma unroll
+      for (int e = 0; e < NE; ++e) sA[e / 16][e % 16] += bias_val(bw0, e);
+    }
     if (!full_tile(t_first)) mask(sA, t_first);
     alpha_cur = row_max(sA);
   }
@@ -676,12 +774,14 @@ __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* ld
     // the rescale for tile t first (its factor is known since the last
     // step), so that the interleaved regions are straight-line code
     rescale(alpha_cur);
+    uint2 bw[KB * 4];
     const float psum = qk_weights(sn, kbuf0 + (1 - P) * TILE, sc, pb, tile_src(kg, tk), kbuf0 + P * TILE,
-                                  tile_src(vg, tv), vbuf0 + (1 - P) * TILE);
+                                  tile_src(vg, tv), vbuf0 + (1 - P) * TILE, BIAS ? bias_src(tk) : i32x4_t{},
+                                  bbuf0 + P * BTILE, bbuf0 + (1 - P) * BTILE, bw);
     exchange(sn, true);
     l_run = l_run * alpha_cur + psum;
     if (!full_tile(t + 1)) mask(sn, t + 1);
-    alpha_cur = pv_max(pb, vbuf0 + P * TILE, sn, has_next);
+    alpha_cur = pv_max(pb, vbuf0 + P * TILE, sn, has_next, bw);
     __builtin_amdgcn_s_waitcnt(0);  // K(t+2), V(t+1) have landed
     __syncthreads();
   };
@@ -693,7 +793,10 @@ __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* ld
     }
   } else {  // no rows: this wave only loads its share of every tile
     for (int t = t_first; t <= t_last; ++t) {
-      if (t + 2 <= t_last) load_k(t + 2);
+      if (t + 2 <= t_last) {
+        load_k(t + 2);
+        load_b(t + 2);
+      }
       if (t < t_last) load_v(t + 1);
       exchange(sA, false);
       __builtin_amdgcn_s_waitcnt(0);
@@ -706,7 +809,7 @@ __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* ld
   if (!valid) return;
   const size_t orow = (size_t)(b * p.Hq + hq) * p.qL + qi;
   if (!p.partials) {
-    const float inv = 1.0f / lsum;
+    const float inv = lsum > 0.f ? 1.0f / lsum : 0.f;  // a row with no finite score: zeros
     uint16_t* dst = p.out + orow * D + od0;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
@@ -736,24 +839,25 @@ __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* ld
   }
 }
 
-template <int DT, bool RING>
+// LDS per workgroup: 2 K + 2 V tiles (+ the pair score exchange at D = 512,
+// 4 waves x 4 KiB) (+ 2 bias tiles of the workgroup's rows x the tile's keys)
+template <int DT, bool RING, bool BIAS>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void attn_tile_kernel_d128(AttnParams p) {
-  __shared__ __attribute__((aligned(16))) uint16_t lds[4 * 64 * 128];  // 2 K + 2 V tiles
-  attn_pipe_body<DT, 128, RING>(p, lds);
+  __shared__ __attribute__((aligned(16))) uint16_t lds[4 * 64 * 128 + (BIAS ? 2 * 128 * 64 : 0)];
+  attn_pipe_body<DT, 128, RING, BIAS>(p, lds);
 }
-template <int DT, bool RING>
+template <int DT, bool RING, bool BIAS>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void attn_tile_kernel_d256(AttnParams p) {
-  __shared__ __attribute__((aligned(16))) uint16_t lds[4 * 64 * 256];  // 2 K + 2 V tiles
-  attn_pipe_body<DT, 256, RING>(p, lds);
+  __shared__ __attribute__((aligned(16))) uint16_t lds[4 * 64 * 256 + (BIAS ? 2 * 128 * 64 : 0)];
+  attn_pipe_body<DT, 256, RING, BIAS>(p, lds);
 }
-template <int DT, bool RING>
+template <int DT, bool RING, bool BIAS>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void attn_tile_kernel_d512(AttnParams p) {
-  // 2 K + 2 V tiles of 32 x 512, then the pair score exchange (4 waves x 4 KiB)
-  __shared__ __attribute__((aligned(16))) uint16_t lds[4 * 32 * 512 + 2 * 4 * 64 * 16];
-  attn_pipe_body<DT, 512, RING>(p, lds);
+  __shared__ __attribute__((aligned(16))) uint16_t lds[4 * 32 * 512 + 2 * 4 * 64 * 16 + (BIAS ? 2 * 64 * 32 : 0)];
+  attn_pipe_body<DT, 512, RING, BIAS>(p, lds);
 }
 
 // Merge of the per-split partials of each output row.  One workgroup of nw =
@@ -847,15 +951,15 @@ __global__ __launch_bounds__(64 * kCombineWaves) void combine_kernel(AttnParams 
   }
 }
 
-template <int DT, int D, bool RING>
+template <int DT, int D, bool RING, bool BIAS>
 hipError_t launch_attention_t(const AttnParams& p, hipStream_t stream) {
   const dim3 grid((unsigned)(p.B * p.Hkv * p.mblocks), (unsigned)p.nsplit, 1);
   if constexpr (D == 128)
-    hipLaunchKernelGGL((attn_tile_kernel_d128<DT, RING>), grid, dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((attn_tile_kernel_d128<DT, RING, BIAS>), grid, dim3(256), 0, stream, p);
   else if constexpr (D == 256)
-    hipLaunchKernelGGL((attn_tile_kernel_d256<DT, RING>), grid, dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((attn_tile_kernel_d256<DT, RING, BIAS>), grid, dim3(256), 0, stream, p);
   else
-    hipLaunchKernelGGL((attn_tile_kernel_d512<DT, RING>), grid, dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((attn_tile_kernel_d512<DT, RING, BIAS>), grid, dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 
@@ -869,15 +973,21 @@ hipError_t launch_combine_t(const AttnParams& p, hipStream_t stream) {
 
 }  // namespace
 
-template <int D, bool RING>
+template <int D, bool RING, bool BIAS>
 hipError_t launch_attention_d(const AttnParams& p, int dtype, hipStream_t stream) {
-  return dtype == 0 ? launch_attention_t<0, D, RING>(p, stream) : launch_attention_t<1, D, RING>(p, stream);
+  return dtype == 0 ? launch_attention_t<0, D, RING, BIAS>(p, stream) : launch_attention_t<1, D, RING, BIAS>(p, stream);
+}
+
+template <int D>
+hipError_t launch_attention_dd(const AttnParams& p, int dtype, bool ring, hipStream_t stream) {
+  if (p.bias) return launch_attention_d<D, false, true>(p, dtype, stream);  // the host never sets both
+  return ring ? launch_attention_d<D, true, false>(p, dtype, stream) : launch_attention_d<D, false, false>(p, dtype, stream);
 }
 
 hipError_t launch_attention(const AttnParams& p, int D, int dtype, bool ring, hipStream_t stream) {
-  if (D == 128) return ring ? launch_attention_d<128, true>(p, dtype, stream) : launch_attention_d<128, false>(p, dtype, stream);
-  if (D == 256) return ring ? launch_attention_d<256, true>(p, dtype, stream) : launch_attention_d<256, false>(p, dtype, stream);
-  return ring ? launch_attention_d<512, true>(p, dtype, stream) : launch_attention_d<512, false>(p, dtype, stream);
+  if (D == 128) return launch_attention_dd<128>(p, dtype, ring, stream);
+  if (D == 256) return launch_attention_dd<256>(p, dtype, ring, stream);
+  return launch_attention_dd<512>(p, dtype, ring, stream);
 }
 
 hipError_t launch_combine(const AttnParams& p, int D, int dtype, hipStream_t stream) {

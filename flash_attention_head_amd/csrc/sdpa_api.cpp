@@ -137,10 +137,11 @@ int check_view(int kL, int kv_capacity, int ring_start) {
 // Both forward entry points: K/V rows of a head are kv_cap apart, logical
 // key j is physical row (ring_start + j) % kv_cap; chunk_cap is the cache
 // capacity the decode chunks are sized from (0: none).
-int forward_impl(const void* q, const void* k, const void* v, void* out, int B, int Hq, int Hkv,
-                 int qL, int kL, int kv_cap, int ring_start, int chunk_cap, int D, float scale,
-                 int causal, int window, int q_offset, int dtype, void* workspace,
-                 size_t workspace_bytes, void* stream) {
+int forward_impl(const void* q, const void* k, const void* v, const void* bias, int64_t bias_sb,
+                 int64_t bias_sh, int64_t bias_sq, void* out, int B, int Hq, int Hkv, int qL, int kL,
+                 int kv_cap, int ring_start, int chunk_cap, int D, float scale, int causal,
+                 int window, int q_offset, int dtype, void* workspace, size_t workspace_bytes,
+                 void* stream) {
   if (!q || !k || !v || !out) return fail(SDPA_INVALID_ARG, "q, k, v and out must be non-null");
   int rc = check_shape(B, Hq, Hkv, qL, kv_cap, D);
   if (rc != SDPA_OK) return rc;
@@ -182,10 +183,15 @@ int forward_impl(const void* q, const void* k, const void* v, void* out, int B, 
   p.kL = kL;
   p.kv_cap = kv_cap;
   p.ring_start = ring_start;
+  p.bias = (const uint16_t*)bias;
+  p.bias_sb = bias_sb;
+  p.bias_sh = bias_sh;
+  p.bias_sq = bias_sq;
   p.causal = causal;
   p.window = window;
   p.q_offset = causal ? q_offset : 0;
   p.sl2 = scale * 1.4426950408889634f;
+  p.inv_scale = 1.0f / scale;
   p.rows = p.G * qL;
   p.mblocks = (int)ceil_div(p.rows, block_rows(D));
   p.nsplit = sp.nsplit;
@@ -237,8 +243,30 @@ SDPA_API int sdpa_forward(const void* q, const void* k, const void* v, void* out
                           int q_offset, int dtype, void* workspace, size_t workspace_bytes,
                           void* stream) {
   g_last_error[0] = '\0';
-  return forward_impl(q, k, v, out, B, Hq, Hkv, qL, kL, kL, 0, 0, D, scale, causal, window,
-                      q_offset, dtype, workspace, workspace_bytes, stream);
+  return forward_impl(q, k, v, nullptr, 0, 0, 0, out, B, Hq, Hkv, qL, kL, kL, 0, 0, D, scale, causal,
+                      window, q_offset, dtype, workspace, workspace_bytes, stream);
+}
+
+SDPA_API int sdpa_forward_bias(const void* q, const void* k, const void* v, const void* bias,
+                               long long bias_stride_b, long long bias_stride_h,
+                               long long bias_stride_q, void* out, int B, int Hq, int Hkv, int qL,
+                               int kL, int D, float scale, int causal, int window, int q_offset,
+                               int dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  g_last_error[0] = '\0';
+  int rc = check_shape(B, Hq, Hkv, qL, kL, D);
+  if (rc != SDPA_OK) return rc;
+  if (!bias) return fail(SDPA_INVALID_ARG, "bias must be non-null");
+  if (bias_stride_b < 0 || bias_stride_h < 0 || bias_stride_q < 0)
+    return fail(SDPA_INVALID_ARG, "bias strides must be >= 0");
+  // the kernels address one batch's bias rows with 32-bit byte offsets
+  const int64_t extent = (int64_t)(Hq - 1) * bias_stride_h + (int64_t)(qL - 1) * bias_stride_q + kL;
+  if (bias_stride_h > (int64_t)1 << 30 || bias_stride_q > (int64_t)1 << 30 || extent > ((int64_t)1 << 30))
+    return fail(SDPA_UNSUPPORTED, "one batch of the bias spans %lld elements (at most 2^30)", (long long)extent);
+  const size_t qbytes = (size_t)B * Hq * qL * D * 2;
+  const size_t bbytes = (size_t)(((int64_t)(B - 1) * bias_stride_b + extent) * 2);
+  if (overlap(out, qbytes, bias, bbytes)) return fail(SDPA_INVALID_ARG, "out must not overlap the bias");
+  return forward_impl(q, k, v, bias, bias_stride_b, bias_stride_h, bias_stride_q, out, B, Hq, Hkv, qL, kL,
+                      kL, 0, 0, D, scale, causal, window, q_offset, dtype, workspace, workspace_bytes, stream);
 }
 
 SDPA_API int sdpa_forward_kv_view(const void* q, const void* k, const void* v, void* out, int B,
@@ -251,6 +279,7 @@ SDPA_API int sdpa_forward_kv_view(const void* q, const void* k, const void* v, v
   if (rc != SDPA_OK) return rc;
   rc = check_view(kL, kv_capacity, ring_start);
   if (rc != SDPA_OK) return rc;
-  return forward_impl(q, k, v, out, B, Hq, Hkv, qL, kL, kv_capacity, ring_start, kv_capacity, D,
-                      scale, causal, window, q_offset, dtype, workspace, workspace_bytes, stream);
+  return forward_impl(q, k, v, nullptr, 0, 0, 0, out, B, Hq, Hkv, qL, kL, kv_capacity, ring_start,
+                      kv_capacity, D, scale, causal, window, q_offset, dtype, workspace, workspace_bytes,
+                      stream);
 }

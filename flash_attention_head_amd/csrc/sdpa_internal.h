@@ -39,10 +39,13 @@ struct AttnParams {
   float* part_o;      // [rows_total, nsplit, D] unnormalised fp32 accumulators
   float* part_ml;     // [rows_total, nsplit, 2]: running max (log2 units), sum
   int B, Hq, Hkv, G, qL, kL;
+  const uint16_t* bias;  // additive mask array or nullptr; keys contiguous within a row
+  int64_t bias_sb, bias_sh, bias_sq;  // its batch, query-head and query-row strides (elements)
   int kv_cap;         // rows per KV head in k and v (head stride kv_cap * D), >= kL
   int ring_start;     // physical row of logical key 0; key j is row (ring_start + j) % kv_cap
   int causal, window, q_offset;
   float sl2;          // scale * log2(e)
+  float inv_scale;    // 1 / scale: the kernels keep raw q.k scores, so a bias enters as bias / scale
   int rows;           // G * qL packed rows per (b, kv head)
   int mblocks;        // ceil(rows / block_rows(D))
   int nsplit;         // key splits
@@ -60,7 +63,8 @@ struct SplitPlan {
 };
 SplitPlan plan_split(int B, int Hq, int Hkv, int qL, int kL, int D, int kv_capacity);
 
-// ring: some tile's keys wrap around the end of the cache rows
+// ring: some tile's keys wrap around the end of the cache rows; p.bias set:
+// the instances that add the mask array (never together with ring)
 hipError_t launch_attention(const AttnParams& p, int D, int dtype, bool ring, hipStream_t stream);
 hipError_t launch_combine(const AttnParams& p, int D, int dtype, hipStream_t stream);
 

@@ -143,6 +143,31 @@ int sdpa_forward_kv_view(const void* q, const void* k, const void* v, void* out,
 size_t sdpa_workspace_bytes_kv_view(int B, int Hq, int Hkv, int qL, int kL, int kv_capacity,
                                     int D);
 
+/*
+ * sdpa_forward with an additive mask array ("bias") added to the scaled
+ * scores: s = scale * q.k + bias[b, hq, i, j], then the causal / window rules
+ * and softmax as in sdpa_forward.  This is the array mask that lablup/mlxcel
+ * issue #672 hands to SDPA and that cuDNN takes as a bias ("Root cause"),
+ * and that CUDA's fused decode kernel rejects (mlxcel issue #2160, Current
+ * Behavior, 12B).
+ *
+ *   bias     device pointer, element type `dtype`; row (b, hq, i) starts at
+ *            element b * bias_stride_b + hq * bias_stride_h + i *
+ *            bias_stride_q and holds kL contiguous keys.  A zero stride
+ *            broadcasts that dimension.  Read only; must not overlap out.
+ *            One batch's rows must lie within 2^30 elements
+ *            (SDPA_UNSUPPORTED otherwise).  Entries are finite or -inf.
+ *   A key whose biased score is -inf is excluded like a masked key; a row
+ *   with no finite biased score comes out as zeros.
+ *   The workspace is sdpa_workspace_bytes(B, Hq, Hkv, qL, kL, D), and qL <= 4
+ *   keeps the bit-exactness of sdpa_forward (1024-key chunks).
+ */
+int sdpa_forward_bias(const void* q, const void* k, const void* v, const void* bias,
+                      long long bias_stride_b, long long bias_stride_h, long long bias_stride_q,
+                      void* out, int B, int Hq, int Hkv, int qL, int kL, int D, float scale,
+                      int causal, int window, int q_offset, int dtype, void* workspace,
+                      size_t workspace_bytes, void* stream);
+
 /* Message for the last non-zero status returned on the calling thread ("" if none). */
 const char* sdpa_last_error(void);
 

@@ -206,3 +206,18 @@ def test_binding_fails_loudly_without_the_library(tmp_path, monkeypatch):
     finally:
         monkeypatch.delenv("SDPA_MI355X_LIB")
         importlib.reload(fa)
+
+
+def test_bias_entry_point_rejects_bad_bias_arguments(lib):
+    f = ctypes.c_float(0.0625)
+    base = dict(q=0x1000, k=0x100000, v=0x200000, bias=0x400000, sb=0, sh=0, sq=64, out=0x300000)
+
+    def call(**kw):
+        a = dict(base, **kw)
+        return lib.sdpa_forward_bias(a["q"], a["k"], a["v"], a["bias"], a["sb"], a["sh"], a["sq"], a["out"],
+                                     1, 4, 2, 8, 64, 256, f, 1, 0, 56, 0, None, 0, None)
+
+    assert call(bias=None) == fa.SDPA_INVALID_ARG and "bias" in fa.sdpa_last_error()
+    assert call(sq=-1) == fa.SDPA_INVALID_ARG and "stride" in fa.sdpa_last_error()
+    assert call(sh=1 << 31) == fa.SDPA_UNSUPPORTED and "2^30" in fa.sdpa_last_error()
+    assert call(bias=0x300000 - 64) == fa.SDPA_INVALID_ARG and "overlap" in fa.sdpa_last_error()

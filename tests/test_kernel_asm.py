@@ -72,8 +72,8 @@ def _metadata(text):
 
 def test_no_scratch_memory(asm):
     """No kernel touches scratch memory or spills vector registers.  Only the
-    wrapped-ring instances (template flag true, "Lb1") may park scalar
-    registers in vector-register lanes, which is no memory traffic."""
+    wrapped-ring and bias instances (a template flag true, "Lb1") may park
+    scalar registers in vector-register lanes, which is no memory traffic."""
     meta = _metadata(asm)
     assert len(meta) >= 18, sorted(meta)
     for name, f in meta.items():
