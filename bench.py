@@ -27,8 +27,8 @@ if ROOT not in sys.path:
 PEAK_MFMA_TFLOPS = 2516.6
 PEAK_HBM_GBS = 8000.0
 HEADLINE = "chunked_prefill_32k"
-EXTRA = ["causal_h64_16k", "sliding_32k", "global_d512_32k", "causal_d128_16k", "decode_q4_128k",
-         "decode_q1_128k", "tiny_causal"]
+EXTRA = ["causal_h64_16k", "sliding_32k", "global_d512_32k", "causal_d128_16k", "chunked_prefill_32k_bias",
+         "decode_q4_128k", "decode_q1_128k", "tiny_causal"]
 
 
 def log(msg):
@@ -43,6 +43,8 @@ def time_workload(wl, steps, warmup):
     from flash_attention_head_amd import workloads as W
 
     q, k, v = (t.cuda() for t in W.draw(wl))
+    bias = W.draw_bias(wl)
+    bias = bias.cuda() if bias is not None else None
     out = torch.empty_like(q)
     # decode / verify steps (qL <= 4) run as they do in a generation loop:
     # over a KV cache, here a full one of kL rows per head
@@ -60,7 +62,7 @@ def time_workload(wl, steps, warmup):
                              q_offset=wl.q_offset, out=out, workspace=ws, stream=stream)
         else:
             fa.sdpa(q, k, v, scale=wl.scale, causal=wl.causal, window=wl.window,
-                    q_offset=wl.q_offset, out=out, workspace=ws, stream=stream)
+                    q_offset=wl.q_offset, bias=bias, out=out, workspace=ws, stream=stream)
 
     for _ in range(warmup):
         call()
@@ -80,7 +82,7 @@ def time_workload(wl, steps, warmup):
     torch.cuda.empty_cache()
     return {"wall_ms": wall_ms, "event_ms_mean": mean, "event_ms_min": per[0],
             "event_ms_median": per[len(per) // 2], "workspace_bytes": need,
-            "entry": "sdpa_forward_kv_view" if cache else "sdpa_forward"}
+            "entry": "sdpa_forward_kv_view" if cache else ("sdpa_forward_bias" if bias is not None else "sdpa_forward")}
 
 
 def summarize(wl, t):

@@ -74,11 +74,29 @@ WORKLOADS = {
                            "Gemma-4-31B-like global layer, B1 Hq32 Hkv4 D512 L32768 bf16 causal"),
     "causal_d128_16k": _wl("causal_d128_16k", 1, 32, 8, 16384, 16384, 128, BF16, True, 0, 0, 6,
                            "head_dim 128 causal self-attention, B1 Hq32 Hkv8 D128 L16384 bf16"),
+    "chunked_prefill_32k_bias": _wl("chunked_prefill_32k_bias", 1, 16, 8, 1024, 32768, 256, FP16, True, 0,
+                                    32768 - 1024, 2,
+                                    "chunked_prefill_32k plus one additive mask array [1, 1, 1024, 32768] "
+                                    "shared by every head, N(0, 1) fp16 (seed 7)"),
     "decode_q4_128k": _wl("decode_q4_128k", 1, 16, 8, 4, 131072, 256, BF16, True, 0, 131072 - 4, 5,
                           "verify block, B1 Hq16 Hkv8 D256 qL4 kL131072 bf16 causal bottom-right"),
     "decode_q1_128k": _wl("decode_q1_128k", 1, 16, 8, 1, 131072, 256, BF16, True, 0, 131072 - 1, 5,
                           "decode, B1 Hq16 Hkv8 D256 qL1 kL131072 bf16 (row 3 of the qL=4 draw)"),
 }
+
+
+# workloads that also pass an additive mask array: name -> (bias batch dim, bias head dim, seed)
+BIAS = {"chunked_prefill_32k_bias": (1, 1, 7)}
+
+
+def draw_bias(wl: Workload) -> "torch.Tensor | None":
+    """The seeded additive mask array of a workload in BIAS (None for the others)."""
+    if wl.name not in BIAS:
+        return None
+    bb, bh, seed = BIAS[wl.name]
+    g = torch.Generator(device="cpu")
+    g.manual_seed(seed)
+    return torch.randn((bb, bh, wl.qL, wl.kL), generator=g, dtype=torch.float32).to(TORCH_DTYPES[wl.dtype])
 
 
 def draw(wl: Workload, device: str = "cpu"):

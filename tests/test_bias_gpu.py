@@ -113,3 +113,21 @@ def test_verify_rows_with_bias_match_single_row_calls():
                       bias=bias[:, :, r:r + 1, :n], causal=True, q_offset=n - 1)
         torch.cuda.synchronize()
         assert torch.equal(block[:, :, r:r + 1].contiguous().view(torch.int16), one.view(torch.int16)), r
+
+
+@pytest.mark.timeout(600)
+def test_full_size_bias_workload_on_sampled_rows():
+    wl = W.WORKLOADS["chunked_prefill_32k_bias"]
+    q, k, v = W.draw(wl)
+    bias = W.draw_bias(wl)
+    note(f"{wl.name} full size")
+    got = fa.sdpa(q.cuda(), k.cuda(), v.cuda(), bias=bias.cuda(), causal=wl.causal, q_offset=wl.q_offset)
+    torch.cuda.synchronize()
+    got = got.cpu()
+    assert torch.isfinite(got.float()).all()
+    rng = np.random.default_rng(wl.seed)
+    nrows = wl.B * wl.Hq * wl.qL
+    rows = np.unique(np.concatenate([np.arange(16), np.arange(nrows - 16, nrows), rng.integers(0, nrows, 64)]))
+    ref = oracle.sdpa_bias_f64(W.bits(q), W.bits(k), W.bits(v), W.bits(bias), scale=wl.scale, causal=wl.causal,
+                               q_offset=wl.q_offset, dtype=wl.dtype, rows=rows, threads=ORACLE_THREADS)
+    check_close(f64(got.reshape(-1, wl.D)[torch.from_numpy(rows)]), ref, wl.dtype, f"{wl.name} ({rows.size} rows)")
