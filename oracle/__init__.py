@@ -79,6 +79,10 @@ def load(path: str = _LIB):
         [u16p, u16p, u16p, u16p, i64, i64, i64, f64p] + [ci] * 6 + [ctypes.c_float] + [ci] * 4 + [i64p, i64, ci]
     )
     lib.oracle_sdpa_bias_f64.restype = ci
+    lib.oracle_sdpa_dv_f64.argtypes = (
+        [u16p, u16p, u16p, f64p] + [ci] * 7 + [ctypes.c_float] + [ci] * 4 + [i64p, i64, ci]
+    )
+    lib.oracle_sdpa_dv_f64.restype = ci
     lib.oracle_widen.argtypes = [u16p, f64p, ctypes.c_int64, ci]
     lib.oracle_widen.restype = None
     if path == _LIB:
@@ -196,4 +200,39 @@ def sdpa_bias_f64(q, k, v, bias, *, scale: float, causal: bool = False, window: 
     )
     if rc != 0:
         raise RuntimeError(f"oracle_sdpa_bias_f64 failed ({rc})")
+    return out
+
+
+def sdpa_dv_f64(q, k, v, *, scale: float, causal: bool = False, window: int = 0, q_offset: int = 0,
+                dtype: int = FP16, rows=None, threads: int | None = None, lib=None) -> np.ndarray:
+    """Output rows when v's head dim Dv may differ from q's and k's D.
+
+    q [B, Hq, qL, D], k [B, Hkv, kL, D], v [B, Hkv, kL, Dv] (uint16 bit patterns).
+    rows=None: every row, [B, Hq, qL, Dv]; else the flat rows (b*Hq + hq)*qL + i,
+    [len(rows), Dv].
+    """
+    lib = lib or load()
+    q, k, v = _bits(q), _bits(k), _bits(v)
+    if q.ndim != 4 or k.ndim != 4 or v.ndim != 4:
+        raise ValueError("q, k, v must be [B, H, L, D]")
+    B, Hq, qL, D = q.shape
+    Bk, Hkv, kL, Dk = k.shape
+    if v.shape[:3] != k.shape[:3] or Bk != B or Dk != D:
+        raise ValueError("shape mismatch between q, k, v")
+    Dv = v.shape[3]
+    if rows is None:
+        out = np.empty((B, Hq, qL, Dv), dtype=np.float64)
+        rptr, nrows = None, 0
+    else:
+        rows = np.ascontiguousarray(rows, dtype=np.int64)
+        out = np.empty((rows.size, Dv), dtype=np.float64)
+        rptr, nrows = _ptr(rows, ctypes.c_int64), rows.size
+    rc = lib.oracle_sdpa_dv_f64(
+        _ptr(q, ctypes.c_uint16), _ptr(k, ctypes.c_uint16), _ptr(v, ctypes.c_uint16),
+        _ptr(out, ctypes.c_double), B, Hq, Hkv, qL, kL, D, Dv, float(np.float32(scale)),
+        int(bool(causal)), int(window), int(q_offset), int(dtype), rptr, nrows,
+        int(threads or default_threads()),
+    )
+    if rc != 0:
+        raise RuntimeError(f"oracle_sdpa_dv_f64 failed ({rc})")
     return out

@@ -48,7 +48,12 @@
  *     within a bias row, its batch, head and row strides are given (0 for a
  *     broadcast dimension).  A key whose biased score is -inf is excluded
  *     like a masked key; a row with no finite score is a zero row.  The
- *     causal and window rules still apply on top.
+ *     causal and window rules still apply on top;
+ *   - the value rows may be longer than the query/key rows (Dv != D: the
+ *     Q=192/K=192/V=256 heads named in the review discussion of mlx PR
+ *     #3293): the scores take the D-long dot products, the output row is the
+ *     weighted sum of the Dv-long value rows, V is [B, Hkv, kL, Dv] and the
+ *     output [B, Hq, qL, Dv].
  */
 #include <math.h>
 #include <pthread.h>
@@ -90,7 +95,7 @@ typedef struct {
   const uint16_t *q, *k, *v;
   const uint16_t *bias; /* NULL: none */
   int64_t bias_sb, bias_sh, bias_sq;
-  int B, Hq, Hkv, qL, kL, D;
+  int B, Hq, Hkv, qL, kL, D, Dv; /* D: q and k rows; Dv: v and output rows */
   double scale;
   int causal, window, q_offset, dtype;
 } problem_t;
@@ -104,10 +109,10 @@ static int key_visible(const problem_t *pr, long p, long j) {
 
 /*
  * One output row.  `row` is the flat index (b * Hq + hq) * qL + i.
- * `s` is caller scratch of kL doubles.  Writes D doubles to `o`.
+ * `s` is caller scratch of kL + D doubles.  Writes Dv doubles to `o`.
  */
 static void attend_row(const problem_t *pr, long row, double *s, double *o) {
-  const long D = pr->D;
+  const long D = pr->D, Dv = pr->Dv;
   const long i = row % pr->qL;
   const long bh = row / pr->qL;
   const long hq = bh % pr->Hq;
@@ -118,9 +123,9 @@ static void attend_row(const problem_t *pr, long row, double *s, double *o) {
 
   const uint16_t *qrow = pr->q + row * D;
   const uint16_t *kbase = pr->k + (b * pr->Hkv + hk) * (long)pr->kL * D;
-  const uint16_t *vbase = pr->v + (b * pr->Hkv + hk) * (long)pr->kL * D;
+  const uint16_t *vbase = pr->v + (b * pr->Hkv + hk) * (long)pr->kL * Dv;
 
-  double *qd = o; /* widen q into the output buffer; it is overwritten later */
+  double *qd = s + pr->kL; /* the widened query row */
   for (long d = 0; d < D; ++d) qd[d] = widen(qrow[d], pr->dtype);
   const uint16_t *brow = pr->bias ? pr->bias + b * pr->bias_sb + hq * pr->bias_sh + i * pr->bias_sq : NULL;
 
@@ -139,7 +144,7 @@ static void attend_row(const problem_t *pr, long row, double *s, double *o) {
     if (!any || s[j] > m) m = s[j];
     any = 1;
   }
-  for (long d = 0; d < D; ++d) o[d] = 0.0;
+  for (long d = 0; d < Dv; ++d) o[d] = 0.0;
   if (!any) return; /* no visible key with a finite score: defined as a zero row */
 
   /* pass 2: exponentials relative to the maximum, and their sum */
@@ -153,10 +158,10 @@ static void attend_row(const problem_t *pr, long row, double *s, double *o) {
   /* pass 3: weighted sum of value rows, then normalise */
   for (long j = 0; j < pr->kL; ++j) {
     if (!key_visible(pr, p, j) || s[j] == -INFINITY) continue;
-    const uint16_t *vrow = vbase + j * D;
-    for (long d = 0; d < D; ++d) o[d] += s[j] * widen(vrow[d], pr->dtype);
+    const uint16_t *vrow = vbase + j * Dv;
+    for (long d = 0; d < Dv; ++d) o[d] += s[j] * widen(vrow[d], pr->dtype);
   }
-  for (long d = 0; d < D; ++d) o[d] /= l;
+  for (long d = 0; d < Dv; ++d) o[d] /= l;
 }
 
 typedef struct {
@@ -170,14 +175,14 @@ typedef struct {
 
 static void *worker(void *arg) {
   work_t *w = (work_t *)arg;
-  double *s = (double *)malloc(sizeof(double) * (size_t)(w->pr->kL > 0 ? w->pr->kL : 1));
+  double *s = (double *)malloc(sizeof(double) * ((size_t)w->pr->kL + (size_t)w->pr->D));
   if (!s) {
     w->failed = 1;
     return NULL;
   }
   for (int64_t n = w->first; n < w->nrows; n += w->stride) {
     long row = w->rows ? (long)w->rows[n] : (long)n;
-    attend_row(w->pr, row, s, w->out + n * (int64_t)w->pr->D);
+    attend_row(w->pr, row, s, w->out + n * (int64_t)w->pr->Dv);
   }
   free(s);
   return NULL;
@@ -230,6 +235,7 @@ static int make_problem(problem_t *pr, const uint16_t *q, const uint16_t *k, con
   pr->qL = qL;
   pr->kL = kL;
   pr->D = D;
+  pr->Dv = D;
   pr->scale = (double)scale;
   pr->causal = causal;
   pr->window = window;
@@ -287,6 +293,27 @@ int oracle_sdpa_bias_f64(const uint16_t *q, const uint16_t *k, const uint16_t *v
   pr.bias_sb = bias_sb;
   pr.bias_sh = bias_sh;
   pr.bias_sq = bias_sq;
+  if (!rows) return run(&pr, NULL, (int64_t)B * Hq * qL, out, nthreads);
+  const int64_t total = (int64_t)B * Hq * qL;
+  for (int64_t n = 0; n < nrows; ++n)
+    if (rows[n] < 0 || rows[n] >= total) return -1;
+  if (nrows <= 0) return nrows == 0 ? 0 : -1;
+  return run(&pr, rows, nrows, out, nthreads);
+}
+
+/*
+ * A value head dim Dv that may differ from D: v is [B, Hkv, kL, Dv].
+ * rows == NULL: every row, out [B, Hq, qL, Dv]; else out is [nrows, Dv].
+ */
+int oracle_sdpa_dv_f64(const uint16_t *q, const uint16_t *k, const uint16_t *v, double *out,
+                       int B, int Hq, int Hkv, int qL, int kL, int D, int Dv, float scale,
+                       int causal, int window, int q_offset, int dtype, const int64_t *rows,
+                       int64_t nrows, int nthreads) {
+  problem_t pr;
+  if (!out || Dv < 1 ||
+      make_problem(&pr, q, k, v, B, Hq, Hkv, qL, kL, D, scale, causal, window, q_offset, dtype))
+    return -1;
+  pr.Dv = Dv;
   if (!rows) return run(&pr, NULL, (int64_t)B * Hq * qL, out, nthreads);
   const int64_t total = (int64_t)B * Hq * qL;
   for (int64_t n = 0; n < nrows; ++n)

@@ -24,12 +24,12 @@ MUTANTS = {
     "gqa_modulo_mapping": ("const long hk = hq / group;", "const long hk = hq % pr->Hkv;"),
     "scale_dropped": ("s[j] = pr->scale * dot;", "s[j] = dot;"),
     "exp_sign_flipped": ("s[j] = exp(s[j] - m);", "s[j] = exp(m - s[j]);"),
-    "no_normalisation": ("for (long d = 0; d < D; ++d) o[d] /= l;", "(void)l;"),
+    "no_normalisation": ("for (long d = 0; d < Dv; ++d) o[d] /= l;", "(void)l;"),
     "q_offset_ignored": ("const long p = (long)pr->q_offset + i;", "const long p = i;"),
     "k_and_v_swapped_in_scores": ("const uint16_t *krow = kbase + j * D;",
                                   "const uint16_t *krow = vbase + j * D;"),
-    "v_batch_offset_dropped": ("const uint16_t *vbase = pr->v + (b * pr->Hkv + hk) * (long)pr->kL * D;",
-                               "const uint16_t *vbase = pr->v + (hk) * (long)pr->kL * D;"),
+    "v_batch_offset_dropped": ("const uint16_t *vbase = pr->v + (b * pr->Hkv + hk) * (long)pr->kL * Dv;",
+                               "const uint16_t *vbase = pr->v + (hk) * (long)pr->kL * Dv;"),
     "fp16_exponent_bias": ("expo - 25", "expo - 24"),
     "bf16_widened_as_fp16": ("return dtype == ORACLE_BF16 ? widen_bf16(h) : widen_fp16(h);",
                              "return widen_fp16(h);"),
@@ -40,6 +40,9 @@ MUTANTS = {
     "bias_subtracted": ("if (brow) s[j] += widen(brow[j], pr->dtype);", "if (brow) s[j] -= widen(brow[j], pr->dtype);"),
     "bias_head_stride_dropped": ("hq * pr->bias_sh", "0 * pr->bias_sh"),
     "bias_row_stride_dropped": ("i * pr->bias_sq", "0 * pr->bias_sq"),
+    "v_head_stride_uses_d": ("(b * pr->Hkv + hk) * (long)pr->kL * Dv;", "(b * pr->Hkv + hk) * (long)pr->kL * D;"),
+    "v_row_stride_uses_d": ("const uint16_t *vrow = vbase + j * Dv;", "const uint16_t *vrow = vbase + j * D;"),
+    "value_columns_cut_at_d": ("for (long d = 0; d < Dv; ++d) o[d] += s[j]", "for (long d = 0; d < D; ++d) o[d] += s[j]"),
     "minus_inf_bias_not_excluded": ("    if (s[j] == -INFINITY) continue;\n    if (!any", "    if (!any"),
 }
 

@@ -362,3 +362,61 @@ def test_bias_row_selection_equals_the_full_call(oracle_lib):
     sel = oracle.sdpa_bias_f64(q, k, v, bias, scale=0.3, causal=True, q_offset=4, dtype=BF16, rows=rows,
                                threads=2)
     assert np.array_equal(sel, full.reshape(-1, 8)[rows])
+
+
+# ------------------------------------------------------- value head dim Dv --
+# v rows longer than the q/k rows (the Q=192/K=192/V=256 heads named in the
+# review discussion of ml-explore/mlx PR #3293): scores from D-long dot
+# products, output rows the weighted sums of Dv-long value rows.
+def _torch_ref_dv(q, k, v, scale, causal, window, q_offset, dtype):
+    qd, kd, vd = (torch.from_numpy(_widened(x, dtype)) for x in (q, k, v))
+    mask = torch.from_numpy(_mask(q.shape[2], k.shape[2], causal, window, q_offset))
+    return F.scaled_dot_product_attention(qd, kd, vd, attn_mask=mask, scale=float(np.float32(scale)),
+                                          enable_gqa=True).numpy()
+
+
+@pytest.mark.parametrize("causal,window", [(False, 0), (True, 0), (True, 3)])
+def test_value_dim_matches_torch_float64_sdpa(oracle_lib, causal, window):
+    for (Hq, Hkv), qL, kL, D, Dv, dtype in [((2, 1), 3, 9, 6, 8, FP16), ((4, 2), 9, 9, 5, 11, BF16),
+                                             ((1, 1), 1, 4, 8, 3, FP16)]:
+        B = 2
+        q_offset = kL - qL if causal else 0
+        q, k, _ = (W.bits(t) for t in W.random_qkv(500 + Dv, B, Hq, Hkv, qL, kL, D, dtype))
+        v = W.bits(W.random_qkv(600 + Dv, B, Hkv, Hkv, 1, kL, Dv, dtype)[2])
+        got = oracle.sdpa_dv_f64(q, k, v, scale=0.37, causal=causal, window=window, q_offset=q_offset,
+                                 dtype=dtype, threads=2)
+        assert got.shape == (B, Hq, qL, Dv)
+        ref = _torch_ref_dv(q, k, v, 0.37, causal, window, q_offset, dtype)
+        np.testing.assert_allclose(got, ref, rtol=0, atol=1e-12)
+
+
+def test_value_columns_equal_equal_dim_calls_bitwise(oracle_lib):
+    # output column c depends on value column c alone, through the same
+    # weights: the leading D and the trailing D columns of a Dv-wide result are
+    # the equal-dim calls over those value columns, bit for bit
+    D, Dv = 6, 10
+    q, k, _ = (W.bits(t) for t in W.random_qkv(610, 2, 4, 2, 5, 12, D, BF16))
+    v = W.bits(W.random_qkv(611, 2, 2, 2, 1, 12, Dv, BF16)[2])
+    got = oracle.sdpa_dv_f64(q, k, v, scale=0.45, causal=True, window=4, q_offset=7, dtype=BF16, threads=2)
+    lead = oracle.sdpa_f64(q, k, np.ascontiguousarray(v[..., :D]), scale=0.45, causal=True, window=4,
+                           q_offset=7, dtype=BF16, threads=2)
+    trail = oracle.sdpa_f64(q, k, np.ascontiguousarray(v[..., Dv - D:]), scale=0.45, causal=True, window=4,
+                            q_offset=7, dtype=BF16, threads=2)
+    assert np.array_equal(got[..., :D], lead)
+    assert np.array_equal(got[..., Dv - D:], trail)
+
+
+def test_value_dim_equal_to_d_is_the_plain_call_bitwise(oracle_lib):
+    q, k, v = (W.bits(t) for t in W.random_qkv(612, 1, 4, 1, 6, 9, 8, FP16))
+    a = oracle.sdpa_dv_f64(q, k, v, scale=0.3, causal=True, q_offset=3, dtype=FP16, threads=2)
+    b = oracle.sdpa_f64(q, k, v, scale=0.3, causal=True, q_offset=3, dtype=FP16, threads=2)
+    assert np.array_equal(a, b)
+
+
+def test_value_dim_row_selection_equals_the_full_call(oracle_lib):
+    q, k, _ = (W.bits(t) for t in W.random_qkv(613, 2, 4, 2, 5, 9, 6, BF16))
+    v = W.bits(W.random_qkv(614, 2, 2, 2, 1, 9, 9, BF16)[2])
+    full = oracle.sdpa_dv_f64(q, k, v, scale=0.3, causal=True, q_offset=4, dtype=BF16, threads=2)
+    rows = np.array([0, 7, 19, 33, 39], dtype=np.int64)
+    sel = oracle.sdpa_dv_f64(q, k, v, scale=0.3, causal=True, q_offset=4, dtype=BF16, rows=rows, threads=2)
+    assert np.array_equal(sel, full.reshape(-1, 9)[rows])
