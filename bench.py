@@ -27,8 +27,8 @@ if ROOT not in sys.path:
 PEAK_MFMA_TFLOPS = 2516.6
 PEAK_HBM_GBS = 8000.0
 HEADLINE = "chunked_prefill_32k"
-EXTRA = ["causal_h64_16k", "sliding_32k", "global_d512_32k", "causal_d128_16k", "chunked_prefill_32k_bias",
-         "decode_q4_128k", "decode_q1_128k", "tiny_causal"]
+EXTRA = ["causal_h64_16k", "sliding_32k", "global_d512_32k", "causal_d128_16k", "causal_d192_16k",
+         "causal_dk192_dv256_16k", "chunked_prefill_32k_bias", "decode_q4_128k", "decode_q1_128k", "tiny_causal"]
 
 
 def log(msg):
@@ -45,14 +45,14 @@ def time_workload(wl, steps, warmup):
     q, k, v = (t.cuda() for t in W.draw(wl))
     bias = W.draw_bias(wl)
     bias = bias.cuda() if bias is not None else None
-    out = torch.empty_like(q)
+    out = torch.empty(tuple(q.shape[:3]) + (wl.dv,), dtype=q.dtype, device=q.device)
     # decode / verify steps (qL <= 4) run as they do in a generation loop:
     # over a KV cache, here a full one of kL rows per head
     cache = wl.qL <= 4
     if cache:
         need = fa.sdpa_workspace_bytes_kv_view(wl.B, wl.Hq, wl.Hkv, wl.qL, wl.kL, wl.kL, wl.D)
     else:
-        need = fa.sdpa_workspace_bytes(wl.B, wl.Hq, wl.Hkv, wl.qL, wl.kL, wl.D)
+        need = fa.sdpa_workspace_bytes_dv(wl.B, wl.Hq, wl.Hkv, wl.qL, wl.kL, wl.D, wl.dv)
     ws = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
     stream = torch.cuda.current_stream()
 
@@ -82,14 +82,15 @@ def time_workload(wl, steps, warmup):
     torch.cuda.empty_cache()
     return {"wall_ms": wall_ms, "event_ms_mean": mean, "event_ms_min": per[0],
             "event_ms_median": per[len(per) // 2], "workspace_bytes": need,
-            "entry": "sdpa_forward_kv_view" if cache else ("sdpa_forward_bias" if bias is not None else "sdpa_forward")}
+            "entry": "sdpa_forward_kv_view" if cache else ("sdpa_forward_bias" if bias is not None else
+                                                           "sdpa_forward_dv" if wl.dv != wl.D else "sdpa_forward")}
 
 
 def summarize(wl, t):
     from flash_attention_head_amd import workloads as W
 
     fl = W.flops(wl)
-    io = W.io_bytes(wl.B, wl.Hq, wl.Hkv, wl.qL, wl.kL, wl.D)["total"]
+    io = W.io_bytes(wl.B, wl.Hq, wl.Hkv, wl.qL, wl.kL, wl.D, Dv=wl.dv)["total"]
     ms = t["event_ms_mean"]
     r = {"ms": round(ms, 4), "ms_min": round(t["event_ms_min"], 4),
          "tflops": round(fl / (ms * 1e-3) / 1e12, 2),

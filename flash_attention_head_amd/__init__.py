@@ -8,10 +8,11 @@ missing or cannot be loaded, every call raises.
 
 Raw entry points (same names and arguments as the C functions, pointers as
 integers): ``sdpa_forward``, ``sdpa_workspace_bytes``, ``sdpa_forward_kv_view``,
-``sdpa_workspace_bytes_kv_view``, ``sdpa_forward_bias``, ``sdpa_last_error``,
-``sdpa_version``.  Convenience wrappers on torch tensors: ``sdpa`` (contiguous
-K/V, optionally an additive mask array) and ``sdpa_kv_cache`` (K/V in a cache,
-possibly a wrapped ring).
+``sdpa_workspace_bytes_kv_view``, ``sdpa_forward_bias``, ``sdpa_forward_dv``,
+``sdpa_workspace_bytes_dv``, ``sdpa_last_error``, ``sdpa_version``.
+Convenience wrappers on torch tensors: ``sdpa`` (contiguous K/V, optionally an
+additive mask array, optionally a value head dim other than q's) and
+``sdpa_kv_cache`` (K/V in a cache, possibly a wrapped ring).
 """
 
 from __future__ import annotations
@@ -24,7 +25,7 @@ __all__ = [
     "SDPA_OK", "SDPA_INVALID_ARG", "SDPA_UNSUPPORTED", "SDPA_WORKSPACE_TOO_SMALL",
     "SDPA_HIP_ERROR", "SDPA_FP16", "SDPA_BF16", "SdpaError", "library_path", "load_library",
     "sdpa_forward", "sdpa_workspace_bytes", "sdpa_forward_kv_view", "sdpa_workspace_bytes_kv_view",
-    "sdpa_forward_bias",
+    "sdpa_forward_bias", "sdpa_forward_dv", "sdpa_workspace_bytes_dv",
     "sdpa_last_error", "sdpa_version", "sdpa", "sdpa_kv_cache", "EXPORTED_SYMBOLS",
 ]
 
@@ -37,8 +38,11 @@ SDPA_FP16 = 0
 SDPA_BF16 = 1
 
 EXPORTED_SYMBOLS = ("sdpa_forward", "sdpa_workspace_bytes", "sdpa_forward_kv_view",
-                    "sdpa_workspace_bytes_kv_view", "sdpa_forward_bias", "sdpa_last_error",
-                    "sdpa_version")
+                    "sdpa_workspace_bytes_kv_view", "sdpa_forward_bias", "sdpa_forward_dv",
+                    "sdpa_workspace_bytes_dv", "sdpa_last_error", "sdpa_version")
+
+# (q/k head dim, v head dim) pairs the library takes
+HEAD_DIMS = ((128, 128), (192, 192), (256, 256), (512, 512), (192, 256))
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _lib = None
@@ -78,6 +82,10 @@ def load_library():
     ll = ctypes.c_longlong
     lib.sdpa_forward_bias.argtypes = [vp, vp, vp, vp, ll, ll, ll, vp] + [ci] * 6 + [ctypes.c_float] + [ci] * 4 + [vp, sz, vp]
     lib.sdpa_forward_bias.restype = ci
+    lib.sdpa_forward_dv.argtypes = [vp, vp, vp, vp] + [ci] * 7 + [ctypes.c_float] + [ci] * 4 + [vp, sz, vp]
+    lib.sdpa_forward_dv.restype = ci
+    lib.sdpa_workspace_bytes_dv.argtypes = [ci] * 7
+    lib.sdpa_workspace_bytes_dv.restype = sz
     lib.sdpa_last_error.argtypes = []
     lib.sdpa_last_error.restype = ctypes.c_char_p
     lib.sdpa_version.argtypes = []
@@ -120,6 +128,18 @@ def sdpa_forward_bias(q, k, v, bias, bias_stride_b, bias_stride_h, bias_stride_q
                                             workspace, workspace_bytes, stream)
 
 
+def sdpa_forward_dv(q, k, v, out, B, Hq, Hkv, qL, kL, D, Dv, scale, causal, window, q_offset, dtype,
+                    workspace, workspace_bytes, stream) -> int:
+    """``int sdpa_forward_dv(...)`` of the C ABI; pointer arguments are integers."""
+    return load_library().sdpa_forward_dv(q, k, v, out, B, Hq, Hkv, qL, kL, D, Dv, scale, causal, window,
+                                          q_offset, dtype, workspace, workspace_bytes, stream)
+
+
+def sdpa_workspace_bytes_dv(B, Hq, Hkv, qL, kL, D, Dv) -> int:
+    """``size_t sdpa_workspace_bytes_dv(...)``; (size_t)-1 for rejected shapes."""
+    return load_library().sdpa_workspace_bytes_dv(B, Hq, Hkv, qL, kL, D, Dv)
+
+
 def sdpa_last_error() -> str:
     return load_library().sdpa_last_error().decode()
 
@@ -129,7 +149,9 @@ def sdpa_version() -> int:
 
 
 # --------------------------------------------------------- torch tensor wrappers
-def _check_tensors(q, k, v):
+def _check_tensors(q, k, v, value_dim=False):
+    """Sizes and dtype code; with value_dim, v's last size may differ from q's
+    (it is then returned as an eighth value)."""
     import torch
 
     if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
@@ -142,20 +164,24 @@ def _check_tensors(q, k, v):
         raise ValueError("q, k, v must be contiguous")
     B, Hq, qL, D = q.shape
     Bk, Hkv, L, Dk = k.shape
-    if tuple(v.shape) != tuple(k.shape) or Bk != B or Dk != D:
+    same = tuple(v.shape) == tuple(k.shape) or (value_dim and tuple(v.shape[:3]) == tuple(k.shape[:3]))
+    if not same or Bk != B or Dk != D:
         raise ValueError(f"shape mismatch: q {tuple(q.shape)}, k {tuple(k.shape)}, v {tuple(v.shape)}")
-    return B, Hq, Hkv, qL, L, D, (SDPA_FP16 if q.dtype == torch.float16 else SDPA_BF16)
+    sizes = (B, Hq, Hkv, qL, L, D, (SDPA_FP16 if q.dtype == torch.float16 else SDPA_BF16))
+    return sizes + (v.shape[3],) if value_dim else sizes
 
 
-def _prepare(q, need, D, out, workspace, stream):
+def _prepare(q, need, D, out, workspace, stream, Dv=None):
     import torch
 
+    Dv = D if Dv is None else Dv
+    oshape = tuple(q.shape[:3]) + (Dv,)
     if out is None:
-        out = torch.empty_like(q)
-    elif out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous():
-        raise ValueError("out must be a contiguous tensor shaped and typed like q")
+        out = torch.empty(oshape, dtype=q.dtype, device=q.device)
+    elif tuple(out.shape) != oshape or out.dtype != q.dtype or not out.is_contiguous():
+        raise ValueError(f"out must be a contiguous {oshape} tensor of q's dtype")
     if need == ctypes.c_size_t(-1).value:
-        raise SdpaError(SDPA_UNSUPPORTED if D not in (128, 256, 512) else SDPA_INVALID_ARG,
+        raise SdpaError(SDPA_UNSUPPORTED if (D, Dv) not in HEAD_DIMS else SDPA_INVALID_ARG,
                         sdpa_last_error())
     ws_ptr, ws_bytes = 0, 0
     if need > 0:
@@ -171,20 +197,32 @@ def sdpa(q, k, v, *, scale: float | None = None, causal: bool = False, window: i
          q_offset: int | None = None, bias=None, out=None, workspace=None, stream=None):
     """softmax(scale * q k^T + mask) v on device tensors.
 
-    q: [B, Hq, qL, D], k and v: [B, Hkv, kL, D], contiguous fp16 or bf16 tensors on
-    one GPU; D in {128, 256, 512}; Hq a multiple of Hkv.  scale defaults to 1/sqrt(D)
-    (as fp32).  With causal, query row i sits at key position q_offset + i;
+    q: [B, Hq, qL, D], k: [B, Hkv, kL, D], v: [B, Hkv, kL, Dv], contiguous fp16 or
+    bf16 tensors on one GPU; D = Dv in {128, 192, 256, 512}, or D = 192 with
+    Dv = 256 (sdpa_forward_dv, no bias); Hq a multiple of Hkv.  The result is
+    [B, Hq, qL, Dv].  scale defaults to 1/sqrt(D) (as fp32).  With causal, query row i sits at key position q_offset + i;
     q_offset defaults to kL - qL (queries aligned to the end of the keys).
     window > 0 limits each row to its last `window` keys (requires causal).
     bias: an optional additive mask array of q's dtype, a tensor that broadcasts to
     [B, Hq, qL, kL] with contiguous keys (size-1 or stride-0 dimensions broadcast).
     Runs on `stream` (default: torch's current stream) without synchronising.
     """
-    B, Hq, Hkv, qL, kL, D, dtype = _check_tensors(q, k, v)
+    B, Hq, Hkv, qL, kL, D, dtype, Dv = _check_tensors(q, k, v, value_dim=True)
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     if q_offset is None:
         q_offset = kL - qL if causal else 0
+    if Dv != D:
+        if bias is not None:
+            raise ValueError("a bias is not supported with a value head dim other than q's")
+        need = sdpa_workspace_bytes_dv(B, Hq, Hkv, qL, kL, D, Dv)
+        out, ws_ptr, ws_bytes, stream = _prepare(q, need, D, out, workspace, stream, Dv)
+        rc = sdpa_forward_dv(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, Hq, Hkv, qL, kL,
+                             D, Dv, float(scale), int(bool(causal)), int(window), int(q_offset), dtype, ws_ptr,
+                             ws_bytes, stream.cuda_stream)
+        if rc != SDPA_OK:
+            raise SdpaError(rc, sdpa_last_error())
+        return out
     need = sdpa_workspace_bytes(B, Hq, Hkv, qL, kL, D)
     out, ws_ptr, ws_bytes, stream = _prepare(q, need, D, out, workspace, stream)
     if bias is None:

@@ -221,28 +221,38 @@ constexpr float kRescaleLog2 = 8.f;
 // busy through the softmax.  K and V have separate double buffers, V one
 // tile behind K: step t reads K(t+1) and V(t) and loads K(t+2) and V(t+1).
 // ---------------------------------------------------------------------------
-template <int DT, int D, bool RING, bool BIAS>
+template <int DT, int DK, int DV, bool RING, bool BIAS>
 __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* lds) {
-  // D = 128 or 256: a wave owns 32 rows and all D columns.  D = 512: the
-  // two waves of a pair own the same 32 rows; wave h multiplies Q columns
-  // [256 h, 256 h + 256) into partial scores, the pair swaps them through LDS
-  // and adds them (a + b == b + a: both hold bitwise identical scores and run
-  // identical softmax arithmetic), and wave h accumulates output columns
-  // [256 h, 256 h + 256).  Up to 32 x 256 fp32 accumulators per wave.
-  constexpr bool PAIR = (D == 512);
+  // DK: head dim of q and k; DV: head dim of v and the output.
+  // DK <= 256: a wave owns 32 rows and all DV output columns.  DK = DV =
+  // 512: the two waves of a pair own the same 32 rows; wave h multiplies Q
+  // columns [256 h, 256 h + 256) into partial scores, the pair swaps them
+  // through LDS and adds them (a + b == b + a: both hold bitwise identical
+  // scores and run identical softmax arithmetic), and wave h accumulates
+  // output columns [256 h, 256 h + 256).  Up to 32 x 256 fp32 accumulators
+  // per wave.
+  constexpr bool PAIR = (DK == 512);
+  static_assert(PAIR == (DV == 512), "head dim 512 only with DK == DV");
   constexpr int NW = 4, RBW = PAIR ? 2 : 4;  // 32-row blocks per workgroup
-  constexpr int BM = RBW * kRowsPerWave, BN = tile_keys(D), KB = BN / 32;
-  constexpr int DQ = D < 256 ? D : 256, DO = PAIR ? D / 2 : D;  // Q columns multiplied, output columns owned
+  constexpr int BM = RBW * kRowsPerWave, BN = tile_keys(DK), KB = BN / 32;
+  constexpr int DQ = DK < 256 ? DK : 256, DO = PAIR ? DV / 2 : DV;  // Q columns multiplied, output columns owned
   constexpr int DC = DQ / 16, DB = DO / 32;
-  constexpr int ROWCH = D / 8, TILE = BN * D, LOADS = TILE * 2 / 1024 / NW;
-  // score elements per lane, and per MFMA slot of the S and P V regions
-  constexpr int NE = KB * 16, EPS = NE / (KB * DC), EPV = NE / (KB * 2 * DB);
-  // V rows of 16 chunks (D = 128) swizzle over 4 rows, wider ones over 8
+  // K and V tiles sit in LDS as BN rows of LD elements; a head dim below LD
+  // (192) leaves the end of each row unused, so that 192-wide rows take the
+  // 256-wide layout and its swizzles unchanged
+  constexpr int LD = lds_row(DK, DV);
+  constexpr int ROWCH = LD / 8, TILE = BN * LD, LOADS = TILE * 2 / 1024 / NW;
+  // score elements per lane; the S region has NQK MFMA slots and the P V
+  // region NPV, each taking one or two of the elements' vector work
+  constexpr int NE = KB * 16, NQK = KB * DC, NPV = KB * 2 * DB;
+  // V rows of 16 chunks (LD = 128) swizzle over 4 rows, wider ones over 8
   constexpr int VSW = ROWCH >= 32 ? 7 : 3;
-  static_assert(BM == block_rows(D), "geometry");
+  static_assert(BM == block_rows(DK), "geometry");
   static_assert(LOADS == 4 || LOADS == 8, "K and V loads of 1 KiB blocks per wave");
-  static_assert((EPS == 1 || EPS == 2) && EPS * KB * DC == NE && (EPV == 1 || EPV == 2) && EPV * KB * 2 * DB == NE,
-                "one or two score elements per MFMA slot");
+  static_assert(NQK <= NE && NE <= 2 * NQK && NPV <= NE && NE <= 2 * NPV, "one or two score elements per MFMA slot");
+  // the first score element of S slot n and of P V slot n (n <= the slot count)
+  auto es = [](int n) { return (n < NQK ? n : NQK) * NE / NQK; };
+  auto ev = [](int n) { return (n < NPV ? n : NPV) * NE / NPV; };
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -291,13 +301,13 @@ __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* ld
   // K/V rows of a head are kv_cap apart; logical key j is physical row
   // (ring_start + j) % kv_cap.  Without a wrap the live keys are one run of
   // rows from ring_start; with one (RING) the tile loads split at the wrap.
-  const size_t kv_off = (size_t)(b * p.Hkv + hkv) * (size_t)p.kv_cap * D + (RING ? 0 : (size_t)p.ring_start * D);
-  const uint16_t* __restrict__ kg = p.k + kv_off;
-  const uint16_t* __restrict__ vg = p.v + kv_off;
+  const size_t kv_row = (size_t)(b * p.Hkv + hkv) * (size_t)p.kv_cap + (RING ? 0 : (size_t)p.ring_start);
+  const uint16_t* __restrict__ kg = p.k + kv_row * DK;
+  const uint16_t* __restrict__ vg = p.v + kv_row * DV;
 
   uint4 qf[DC];
   {
-    const uint16_t* qrow = p.q + ((size_t)(b * p.Hq + hq) * p.qL + qi) * D + qd0;
+    const uint16_t* qrow = p.q + ((size_t)(b * p.Hq + hq) * p.qL + qi) * DK + qd0;
 #pragma unroll
     for (int dc = 0; dc < DC; ++dc)
       qf[dc] = valid ? *(const uint4*)(qrow + dc * 16 + lg * 8) : make_uint4(0, 0, 0, 0);
@@ -316,12 +326,12 @@ __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* ld
   // stored at chunk position (qd0 / 8 + 2 dc + lg) ^ (lr & 15)): the swizzle
   // flips bits 3-6 of the element offset, which nothing else occupies, so
   // one per-lane base and an XOR with 16 (dc & 7) cover every dc.
-  const int kbase = lr * D + qd0 + 8 * (lg ^ (lr & 1)) + 16 * ((lr & 15) >> 1);
-  auto kaddr = [&](int kb, int dc) { return (kbase ^ (16 * (dc & 7))) + 16 * (dc & 8) + kb * 32 * D; };
+  const int kbase = lr * LD + qd0 + 8 * (lg ^ (lr & 1)) + 16 * ((lr & 15) >> 1);
+  auto kaddr = [&](int kb, int dc) { return (kbase ^ (16 * (dc & 7))) + 16 * (dc & 8) + kb * 32 * LD; };
   int vlane;
   {
     const int g = lane >> 4, kq = 4 * (g >> 1) + ((lane >> 2) & 3);
-    vlane = kq * D + (od0 ^ (32 * (kq & VSW))) + 16 * (g & 1) + 4 * (lane & 3);
+    vlane = kq * LD + (od0 ^ (32 * (kq & VSW))) + 16 * (g & 1) + 4 * (lane & 3);
   }
   // K(t) lives in K buffer (t - t_first) & 1, V(t) in V buffer (t - t_first)
   // & 1: the steps come in pairs, so inside a step every buffer offset is a
@@ -330,24 +340,30 @@ __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* ld
   uint16_t* const vbuf0 = lds + 2 * TILE;
   float* const xch = (float*)(lds + 4 * TILE);  // pair score exchange (D = 512)
 
-  // Direct loads of one K or V tile: LOADS blocks of 1 KiB (RPB key rows
-  // each) per wave, the n-th at block b = wave + NW n.  Lane l reads row
-  // l / ROWCH of the block at chunk (l % ROWCH) ^ swizzle(row) and lands at
-  // LDS position l, which puts chunk c of key row r at c ^ (r & 15) (K) or
-  // c ^ ((r & VSW) << 2) (V).  Block b starts at byte 1024 b of the tile, so
-  // the n-th load's lane offset is a pattern that repeats every KPAT (K) or
-  // VPAT (V) loads plus n NW 1024, which goes into the scalar offset.  The
-  // tile start and its bytes before key kL form the buffer descriptor, so
-  // rows past kL read zeros (the range check covers the scalar offset too).
-  constexpr int RPB = 1024 / (2 * D);  // key rows per 1 KiB block
+  // Direct loads of one K or V tile: LOADS blocks of 1 KiB of LDS (RPB key
+  // rows each) per wave, the n-th at block b = wave + NW n.  Lane l reads
+  // key row l / ROWCH of the block at chunk (l % ROWCH) ^ swizzle(row) and
+  // lands at LDS position l, which puts chunk c of key row r at c ^ (r & 15)
+  // (K) or c ^ ((r & VSW) << 2) (V).  A lane whose chunk lies past the head
+  // dim (LD > DK or DV) gets an offset outside every tile's range and writes
+  // zeros.  Block b starts at key row RPB b, so the n-th load's lane offset
+  // is a pattern that repeats every KPAT (K) or VPAT (V) loads plus n NW RPB
+  // rows, which goes into the scalar offset.  The tile start and its bytes
+  // before key kL form the buffer descriptor, so rows past kL read zeros
+  // (the range check covers the scalar offset too).
+  constexpr int RPB = 1024 / (2 * LD);  // key rows per 1 KiB block
   constexpr int KPAT = 16 / (NW * RPB) > 1 ? 16 / (NW * RPB) : 1;
   constexpr int VPAT = (VSW + 1) / (NW * RPB) > 1 ? (VSW + 1) / (NW * RPB) : 1;
   static_assert(RPB * ROWCH == 64 && LOADS % KPAT == 0 && LOADS % VPAT == 0, "block geometry");
+  // above any tile's bytes, and far enough below 2^32 that adding a scalar
+  // offset cannot wrap it
+  constexpr uint32_t kPastRange = 0x40000000u;
+  auto row_bytes = [](bool is_v) { return 2 * (is_v ? DV : DK); };
   auto lane_off = [&](bool is_v, int n) {  // offset of the n-th load from its block group
     const int r = (wave + NW * n) * RPB + lane / ROWCH;  // key row in the tile
     const int pch = lane % ROWCH;
     const int c = is_v ? (pch ^ ((r & VSW) << 2)) : (pch ^ (r & 15));
-    return (uint32_t)(r * 2 * D + 16 * c - n * NW * 1024);
+    return 16 * c < row_bytes(is_v) ? (uint32_t)((r - n * NW * RPB) * row_bytes(is_v) + 16 * c) : kPastRange;
   };
   uint32_t koff[KPAT], voff[VPAT];
 #pragma unroll
@@ -363,12 +379,13 @@ __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* ld
     i32x4_t a, b;
     int r0;  // rows of the tile before the ring wraps (BN: none)
   };
-  auto tile_src = [&](const uint16_t* g, int t) {
+  auto tile_src = [&](const uint16_t* g, int t, bool is_v) {
+    const int rowb = row_bytes(is_v);
     const int ts = __builtin_amdgcn_readfirstlane(t * BN);
-    const int bytes = __builtin_amdgcn_readfirstlane(min(p.kL - ts, BN) * 2 * D);
+    const int bytes = __builtin_amdgcn_readfirstlane(min(p.kL - ts, BN) * rowb);
     TileSrc src;
     if constexpr (!RING) {
-      src.a = tile_rsrc(uniform_addr(g + (size_t)ts * D), bytes);
+      src.a = tile_rsrc(uniform_addr(g + (size_t)ts * (rowb / 2)), bytes);
       src.b = src.a;
       src.r0 = BN;
     } else {
@@ -377,8 +394,8 @@ __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* ld
       bp = __builtin_amdgcn_readfirstlane(bp);
       const int r0 = __builtin_amdgcn_readfirstlane(min(p.kv_cap - bp, BN));
       const uint64_t head = uniform_addr(g);
-      src.a = tile_rsrc(head + (uint64_t)bp * 2 * D, min(r0 * 2 * D, bytes));
-      src.b = tile_rsrc(head - (uint64_t)r0 * 2 * D, bytes);
+      src.a = tile_rsrc(head + (uint64_t)bp * rowb, min(r0 * rowb, bytes));
+      src.b = tile_rsrc(head - (uint64_t)r0 * rowb, bytes);
       src.r0 = r0;
     }
     return src;
@@ -386,8 +403,9 @@ __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* ld
   auto load_blk = [&](const TileSrc& src, uint16_t* buf, int n, bool is_v) {
     const uint32_t vo = is_v ? voff[n % VPAT] : koff[n % KPAT];
     uint16_t* dst = buf + (wave + NW * n) * 512;
+    const uint32_t so = (uint32_t)(n * NW * RPB * row_bytes(is_v));
     if constexpr (!RING) {
-      load_lds16(src.a, vo, (uint32_t)(n * NW * 1024), dst);
+      load_lds16(src.a, vo, so, dst);
     } else {
       // lanes of rows before the wrap: lanes [LPR i, LPR (i + 1)) hold row
       // i of the block's RPB rows
@@ -397,12 +415,12 @@ __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* ld
 #pragma unroll
       for (int i = 0; i < RPB; ++i)
         if (rb0 + i < src.r0) ea |= (LPR == 64 ? ~0ull : ((1ull << LPR) - 1ull) << (LPR * i));
-      load_lds16_2(src.a, src.b, uniform64(ea), uniform64(~ea), vo, (uint32_t)(n * NW * 1024),
+      load_lds16_2(src.a, src.b, uniform64(ea), uniform64(~ea), vo, so,
                    __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)dst));
     }
   };
   auto load_tile = [&](const uint16_t* g, int t, uint16_t* buf, bool is_v) {
-    const TileSrc src = tile_src(g, t);
+    const TileSrc src = tile_src(g, t, is_v);
     const unsigned m0 = m0_save();
 #pragma unroll
     for (int n = 0; n < LOADS; ++n) load_blk(src, buf, n, is_v);
@@ -492,7 +510,7 @@ __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* ld
   // S^T = K(t) Q^T, K operands read PF MFMAs ahead; the two key-block chains
   // alternate
   auto qk = [&](f32x16_t (&s)[KB], const uint16_t* kl) {
-    constexpr int NQK = KB * DC, PF = 4;
+    constexpr int PF = 4;
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
@@ -567,8 +585,10 @@ __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* ld
                         uint4 (&pb)[KB * 2], const TileSrc& ksrc, uint16_t* kdst, const TileSrc& vsrc,
                         uint16_t* vdst, const i32x4_t& bsrc, uint16_t* bdst, const uint16_t* bl,
                         uint2 (&bw)[KB * 4]) {
-    constexpr int NQK = KB * DC, PF = 4, LS = NQK / LOADS;
-    static_assert(LS >= 2 && LS % 2 == 0, "slot pattern");
+    constexpr int PF = 4, LS = NQK / LOADS;
+    // the slot of a run of LS that issues the bias load (apart from K's and V's)
+    constexpr int BSLOT = LS == 3 ? 2 : 1;
+    static_assert(LS >= 2 && LS * LOADS == NQK, "slot pattern");
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
@@ -577,7 +597,7 @@ __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* ld
     // its address is a register, the rest an immediate
     auto kx = [&](int n) { return kbase ^ (16 * ((n / KB) & 7)); };
     auto kread = [&](int n, int x) {
-      return *(const uint4*)(kl + x + 16 * ((n / KB) & 8) + (n % KB) * 32 * D);
+      return *(const uint4*)(kl + x + 16 * ((n / KB) & 8) + (n % KB) * 32 * LD);
     };
     const float msc = (m_ref == -INFINITY) ? 0.f : m_ref * sl2;
     auto get = [&](int e) { return sc[e / 16][e % 16]; };
@@ -589,15 +609,15 @@ __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* ld
     for (int i = 0; i < PF; ++i) a[i] = kread(i, kx(i));
     int x_next = kx(PF);
     const unsigned m0 = m0_save();
-    // weights in slot n: fma of elements EPS (n + 2) .., exp of EPS (n + 1) ..,
-    // sum and pack of EPS n .. (EPS elements each)
+    // weights in slot n: fma of the elements of slot n + 2, exp of those of
+    // slot n + 1, sum and pack of its own (elements [es(m), es(m + 1)) are
+    // slot m's)
 #pragma unroll
-    for (int i = 0; i < EPS; ++i) {
-      set(i, fast_exp2(get(i) * sl2 - msc));
-      set(EPS + i, get(EPS + i) * sl2 - msc);
-    }
-    // slot m packs a pair iff one of its elements is odd
-    auto packs = [](int m) { return EPS == 2 || (m & 1); };
+    for (int e = es(0); e < es(1); ++e) set(e, fast_exp2(get(e) * sl2 - msc));
+#pragma unroll
+    for (int e = es(1); e < es(2); ++e) set(e, get(e) * sl2 - msc);
+    // slot m packs a pair iff one of its (one or two) elements is odd
+    auto packs = [&](int m) { return es(m + 1) - es(m) == 2 || (es(m) & 1); };
 #pragma unroll
     for (int n = 0; n < NQK; ++n) {
       const uint4 cur_a = a[n % PF];
@@ -610,21 +630,20 @@ __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* ld
       if constexpr (BIAS) {
         // the bias tile that goes with K(tk), and in the last slots the bias
         // of S(t + 1) for the P V region (its reads are in flight by then)
-        if (n % LS == 1 && n / LS < BLOADS) load_bblk(bsrc, bdst, n / LS);
+        if (n % LS == BSLOT && n / LS < BLOADS) load_bblk(bsrc, bdst, n / LS);
         if (n >= NQK - KB * 4) bw[n - (NQK - KB * 4)] = bias_read(bl, n - (NQK - KB * 4));
       }
 #pragma unroll
-      for (int i = 0; i < EPS; ++i) {
-        const int ef = EPS * (n + 2) + i, ex = EPS * (n + 1) + i;
-        if (ef < NE) set(ef, get(ef) * sl2 - msc);
-        if (ex < NE) set(ex, fast_exp2(get(ex)));
+      for (int i = 0; i < 2; ++i) {
+        const int ef = es(n + 2) + i, ex = es(n + 1) + i;
+        if (ef < es(n + 3)) set(ef, get(ef) * sl2 - msc);
+        if (ex < es(n + 2)) set(ex, fast_exp2(get(ex)));
       }
       // the row sum adds the rounded weights the P V product uses, a pair
       // per dot2, one slot after the pair is packed
       if (n > 0 && packs(n - 1)) psum = Elem<DT>::sum2(wlast, psum);
 #pragma unroll
-      for (int i = 0; i < EPS; ++i) {
-        const int e = EPS * n + i;
+      for (int e = es(n); e < es(n + 1); ++e) {
         if (e & 1) {  // pack the pair (e - 1, e): P half kh = e / 8
           const uint32_t w = Elem<DT>::pack2(get(e - 1), get(e));
           wlast = w;
@@ -649,13 +668,13 @@ __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* ld
   // O += P(t) V(t)  ||  row max of S(t+1) (already masked)
   auto pv_max = [&](const uint4 (&pb)[KB * 2], const uint16_t* vl, f32x16_t (&sn)[KB], bool live,
                     const uint2 (&bw)[KB * 4]) {
-    constexpr int NPV = KB * 2 * DB, PF = 4;
+    constexpr int PF = 4;
     // V^T operand of MFMA n: key half n / DB, column block n % DB; the XOR
     // part of the address is a register, the rest an immediate
     auto vx = [&](int n) { return vlane ^ (32 * (n % DB)); };
     auto vread = [&](int n, int x) {
-      const uint16_t* va = vl + x + 16 * (n / DB) * D;
-      const uint2 lo = read_tr(va), hi = read_tr(va + 8 * D);
+      const uint16_t* va = vl + x + 16 * (n / DB) * LD;
+      const uint2 lo = read_tr(va), hi = read_tr(va + 8 * LD);
       return make_uint4(lo.x, lo.y, hi.x, hi.y);
     };
     auto get = [&](int e) { return sn[e / 16][e % 16]; };
@@ -664,10 +683,7 @@ __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* ld
     auto add_bias = [&](int slot) {
       if constexpr (BIAS) {
 #pragma unroll
-        for (int i = 0; i < EPV; ++i) {
-          const int e = EPV * slot + i;
-          if (e < NE) sn[e / 16][e % 16] = get(e) + bias_val(bw, e);
-        }
+        for (int e = ev(slot); e < ev(slot + 1); ++e) sn[e / 16][e % 16] = get(e) + bias_val(bw, e);
       }
     };
     add_bias(0);
@@ -681,8 +697,10 @@ __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* ld
       if (n + PF < NPV) bv[n % PF] = vread(n + PF, x_next);
       o[n % DB] = Elem<DT>::mfma(cur_b, pb[n / DB], o[n % DB]);
       if (n + PF + 1 < NPV) x_next = vx(n + PF + 1);
-      if (EPV == 2) mx = max3(mx, get(2 * n), get(2 * n + 1));  // this slot's pair of elements
-      else if (n & 1) mx = max3(mx, get(n - 1), get(n));         // every other slot, the last pair
+      // the pairs (e - 1, e) whose odd element is one of this slot's
+#pragma unroll
+      for (int e = ev(n); e < ev(n + 1); ++e)
+        if (e & 1) mx = max3(mx, get(e - 1), get(e));
       add_bias(n + 1);
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -775,8 +793,8 @@ __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* ld
     // step), so that the interleaved regions are straight-line code
     rescale(alpha_cur);
     uint2 bw[KB * 4];
-    const float psum = qk_weights(sn, kbuf0 + (1 - P) * TILE, sc, pb, tile_src(kg, tk), kbuf0 + P * TILE,
-                                  tile_src(vg, tv), vbuf0 + (1 - P) * TILE, BIAS ? bias_src(tk) : i32x4_t{},
+    const float psum = qk_weights(sn, kbuf0 + (1 - P) * TILE, sc, pb, tile_src(kg, tk, false), kbuf0 + P * TILE,
+                                  tile_src(vg, tv, true), vbuf0 + (1 - P) * TILE, BIAS ? bias_src(tk) : i32x4_t{},
                                   bbuf0 + P * BTILE, bbuf0 + (1 - P) * BTILE, bw);
     exchange(sn, true);
     l_run = l_run * alpha_cur + psum;
@@ -810,7 +828,7 @@ __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* ld
   const size_t orow = (size_t)(b * p.Hq + hq) * p.qL + qi;
   if (!p.partials) {
     const float inv = lsum > 0.f ? 1.0f / lsum : 0.f;  // a row with no finite score: zeros
-    uint16_t* dst = p.out + orow * D + od0;
+    uint16_t* dst = p.out + orow * DV + od0;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -823,7 +841,7 @@ __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* ld
       }
   } else {
     const size_t prow = orow * p.nsplit + split;
-    float* dst = p.part_o + prow * D + od0;
+    float* dst = p.part_o + prow * DV + od0;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -839,25 +857,39 @@ __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* ld
   }
 }
 
-// LDS per workgroup: 2 K + 2 V tiles (+ the pair score exchange at D = 512,
-// 4 waves x 4 KiB) (+ 2 bias tiles of the workgroup's rows x the tile's keys)
+// LDS per workgroup: 2 K + 2 V tiles of 64 (32 at D = 512) rows of
+// lds_row(DK, DV) elements (+ the pair score exchange at D = 512, 4 waves x
+// 4 KiB) (+ 2 bias tiles of the workgroup's rows x the tile's keys)
 template <int DT, bool RING, bool BIAS>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void attn_tile_kernel_d128(AttnParams p) {
   __shared__ __attribute__((aligned(16))) uint16_t lds[4 * 64 * 128 + (BIAS ? 2 * 128 * 64 : 0)];
-  attn_pipe_body<DT, 128, RING, BIAS>(p, lds);
+  attn_pipe_body<DT, 128, 128, RING, BIAS>(p, lds);
+}
+template <int DT, bool RING, bool BIAS>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void attn_tile_kernel_d192(AttnParams p) {
+  __shared__ __attribute__((aligned(16))) uint16_t lds[4 * 64 * 256 + (BIAS ? 2 * 128 * 64 : 0)];
+  attn_pipe_body<DT, 192, 192, RING, BIAS>(p, lds);
+}
+// q and k of head dim 192, v and out of 256 (no ring or bias instances)
+template <int DT>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void attn_tile_kernel_dk192_dv256(AttnParams p) {
+  __shared__ __attribute__((aligned(16))) uint16_t lds[4 * 64 * 256];
+  attn_pipe_body<DT, 192, 256, false, false>(p, lds);
 }
 template <int DT, bool RING, bool BIAS>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void attn_tile_kernel_d256(AttnParams p) {
   __shared__ __attribute__((aligned(16))) uint16_t lds[4 * 64 * 256 + (BIAS ? 2 * 128 * 64 : 0)];
-  attn_pipe_body<DT, 256, RING, BIAS>(p, lds);
+  attn_pipe_body<DT, 256, 256, RING, BIAS>(p, lds);
 }
 template <int DT, bool RING, bool BIAS>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void attn_tile_kernel_d512(AttnParams p) {
   __shared__ __attribute__((aligned(16))) uint16_t lds[4 * 32 * 512 + 2 * 4 * 64 * 16 + (BIAS ? 2 * 64 * 32 : 0)];
-  attn_pipe_body<DT, 512, RING, BIAS>(p, lds);
+  attn_pipe_body<DT, 512, 512, RING, BIAS>(p, lds);
 }
 
 // Merge of the per-split partials of each output row.  One workgroup of nw =
@@ -956,6 +988,8 @@ hipError_t launch_attention_t(const AttnParams& p, hipStream_t stream) {
   const dim3 grid((unsigned)(p.B * p.Hkv * p.mblocks), (unsigned)p.nsplit, 1);
   if constexpr (D == 128)
     hipLaunchKernelGGL((attn_tile_kernel_d128<DT, RING, BIAS>), grid, dim3(256), 0, stream, p);
+  else if constexpr (D == 192)
+    hipLaunchKernelGGL((attn_tile_kernel_d192<DT, RING, BIAS>), grid, dim3(256), 0, stream, p);
   else if constexpr (D == 256)
     hipLaunchKernelGGL((attn_tile_kernel_d256<DT, RING, BIAS>), grid, dim3(256), 0, stream, p);
   else
@@ -984,14 +1018,23 @@ hipError_t launch_attention_dd(const AttnParams& p, int dtype, bool ring, hipStr
   return ring ? launch_attention_d<D, true, false>(p, dtype, stream) : launch_attention_d<D, false, false>(p, dtype, stream);
 }
 
-hipError_t launch_attention(const AttnParams& p, int D, int dtype, bool ring, hipStream_t stream) {
+hipError_t launch_attention(const AttnParams& p, int D, int Dv, int dtype, bool ring, hipStream_t stream) {
+  if (D != Dv) {  // 192 with 256: the host passes neither a ring nor a bias
+    if (ring || p.bias || D != 192 || Dv != 256) return hipErrorInvalidValue;
+    const dim3 grid((unsigned)(p.B * p.Hkv * p.mblocks), (unsigned)p.nsplit, 1);
+    if (dtype == 0) hipLaunchKernelGGL((attn_tile_kernel_dk192_dv256<0>), grid, dim3(256), 0, stream, p);
+    else hipLaunchKernelGGL((attn_tile_kernel_dk192_dv256<1>), grid, dim3(256), 0, stream, p);
+    return hipGetLastError();
+  }
   if (D == 128) return launch_attention_dd<128>(p, dtype, ring, stream);
+  if (D == 192) return launch_attention_dd<192>(p, dtype, ring, stream);
   if (D == 256) return launch_attention_dd<256>(p, dtype, ring, stream);
   return launch_attention_dd<512>(p, dtype, ring, stream);
 }
 
 hipError_t launch_combine(const AttnParams& p, int D, int dtype, hipStream_t stream) {
   if (D == 128) return dtype == 0 ? launch_combine_t<0, 128>(p, stream) : launch_combine_t<1, 128>(p, stream);
+  if (D == 192) return dtype == 0 ? launch_combine_t<0, 192>(p, stream) : launch_combine_t<1, 192>(p, stream);
   if (D == 256) return dtype == 0 ? launch_combine_t<0, 256>(p, stream) : launch_combine_t<1, 256>(p, stream);
   return dtype == 0 ? launch_combine_t<0, 512>(p, stream) : launch_combine_t<1, 512>(p, stream);
 }

@@ -26,15 +26,19 @@ int fail(int status, const char* fmt, ...) {
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-// Shape checks shared by sdpa_forward and sdpa_workspace_bytes.
-int check_shape(int B, int Hq, int Hkv, int qL, int kL, int D) {
+// Shape checks shared by every entry point and workspace query.  D is the
+// head dim of q and k, Dv that of v and out: equal, one of 128, 192, 256 or
+// 512, or the pair D = 192, Dv = 256.
+int check_shape(int B, int Hq, int Hkv, int qL, int kL, int D, int Dv) {
   if (B < 1 || Hq < 1 || Hkv < 1 || qL < 1 || kL < 1)
     return fail(SDPA_INVALID_ARG, "sizes must be >= 1 (B=%d Hq=%d Hkv=%d qL=%d kL=%d)", B, Hq,
                 Hkv, qL, kL);
   if (Hq % Hkv != 0)
     return fail(SDPA_INVALID_ARG, "Hq (%d) must be a multiple of Hkv (%d)", Hq, Hkv);
-  if (D != 128 && D != 256 && D != 512)
-    return fail(SDPA_UNSUPPORTED, "head_dim %d is not supported (128, 256 or 512)", D);
+  if (D != Dv && !(D == 192 && Dv == 256))
+    return fail(SDPA_UNSUPPORTED, "head dims q/k %d with v %d are not supported (equal, or 192 with 256)", D, Dv);
+  if (D != 128 && D != 192 && D != 256 && D != 512)
+    return fail(SDPA_UNSUPPORTED, "head_dim %d is not supported (128, 192, 256 or 512)", D);
   // index arithmetic inside the kernels: packed rows per KV head and the
   // launch grid stay in 32-bit range; byte offsets are 64-bit
   const int64_t rows = (int64_t)(Hq / Hkv) * qL;
@@ -42,7 +46,7 @@ int check_shape(int B, int Hq, int Hkv, int qL, int kL, int D) {
   if (rows > INT32_MAX / 2 || flat_rows > INT32_MAX / 2 ||
       (int64_t)B * Hkv * ceil_div(rows, block_rows(D)) > INT32_MAX / 2)
     return fail(SDPA_INVALID_ARG, "problem too large for one call");
-  if ((int64_t)B * Hq * qL * D > INT64_MAX / 4 || (int64_t)B * Hkv * kL * D > INT64_MAX / 4)
+  if ((int64_t)B * Hq * qL * Dv > INT64_MAX / 4 || (int64_t)B * Hkv * kL * Dv > INT64_MAX / 4)
     return fail(SDPA_INVALID_ARG, "element count overflows");
   return SDPA_OK;
 }
@@ -139,11 +143,11 @@ int check_view(int kL, int kv_capacity, int ring_start) {
 // capacity the decode chunks are sized from (0: none).
 int forward_impl(const void* q, const void* k, const void* v, const void* bias, int64_t bias_sb,
                  int64_t bias_sh, int64_t bias_sq, void* out, int B, int Hq, int Hkv, int qL, int kL,
-                 int kv_cap, int ring_start, int chunk_cap, int D, float scale, int causal,
+                 int kv_cap, int ring_start, int chunk_cap, int D, int Dv, float scale, int causal,
                  int window, int q_offset, int dtype, void* workspace, size_t workspace_bytes,
                  void* stream) {
   if (!q || !k || !v || !out) return fail(SDPA_INVALID_ARG, "q, k, v and out must be non-null");
-  int rc = check_shape(B, Hq, Hkv, qL, kv_cap, D);
+  int rc = check_shape(B, Hq, Hkv, qL, kv_cap, D, Dv);
   if (rc != SDPA_OK) return rc;
   if (dtype != SDPA_FP16 && dtype != SDPA_BF16)
     return fail(SDPA_UNSUPPORTED, "dtype %d is not supported (0 = fp16, 1 = bf16)", dtype);
@@ -157,14 +161,14 @@ int forward_impl(const void* q, const void* k, const void* v, const void* bias, 
                 "causal q_offset must lie in [0, kL - qL] = [0, %d] so every row sees a key "
                 "(got %d)",
                 kL - qL, q_offset);
-  const size_t qbytes = (size_t)B * Hq * qL * D * 2;
-  const size_t kvbytes = (size_t)B * Hkv * kv_cap * D * 2;
-  if (overlap(out, qbytes, q, qbytes) || overlap(out, qbytes, k, kvbytes) ||
-      overlap(out, qbytes, v, kvbytes))
+  const size_t qbytes = (size_t)B * Hq * qL * D * 2, obytes = (size_t)B * Hq * qL * Dv * 2;
+  const size_t kbytes = (size_t)B * Hkv * kv_cap * D * 2, vbytes = (size_t)B * Hkv * kv_cap * Dv * 2;
+  if (overlap(out, obytes, q, qbytes) || overlap(out, obytes, k, kbytes) ||
+      overlap(out, obytes, v, vbytes))
     return fail(SDPA_INVALID_ARG, "out must not overlap q, k or v");
 
   const SplitPlan sp = plan_split(B, Hq, Hkv, qL, kL, D, chunk_cap);
-  const size_t need = workspace_for(sp, B, Hq, qL, D);
+  const size_t need = workspace_for(sp, B, Hq, qL, Dv);
   if (need > 0 && (!workspace || workspace_bytes < need))
     return fail(SDPA_WORKSPACE_TOO_SMALL, "workspace of %zu bytes needed, %zu given", need,
                 workspace ? workspace_bytes : (size_t)0);
@@ -200,7 +204,7 @@ int forward_impl(const void* q, const void* k, const void* v, const void* bias, 
   if (sp.partials) {
     const size_t prow = (size_t)B * Hq * qL * (size_t)sp.nsplit;
     p.part_o = (float*)workspace;
-    p.part_ml = (float*)((char*)workspace + prow * (size_t)D * sizeof(float));
+    p.part_ml = (float*)((char*)workspace + prow * (size_t)Dv * sizeof(float));
   } else {
     p.part_o = nullptr;
     p.part_ml = nullptr;
@@ -210,8 +214,8 @@ int forward_impl(const void* q, const void* k, const void* v, const void* bias, 
   const bool ring = (int64_t)ring_start + kL > kv_cap;
 
   hipStream_t s = (hipStream_t)stream;
-  hipError_t e = launch_attention(p, D, dtype, ring, s);
-  if (e == hipSuccess && sp.partials) e = launch_combine(p, D, dtype, s);
+  hipError_t e = launch_attention(p, D, Dv, dtype, ring, s);
+  if (e == hipSuccess && sp.partials) e = launch_combine(p, Dv, dtype, s);
   if (e != hipSuccess) return fail(SDPA_HIP_ERROR, "kernel launch failed: %s", hipGetErrorString(e));
   return SDPA_OK;
 }
@@ -222,28 +226,42 @@ int forward_impl(const void* q, const void* k, const void* v, const void* bias, 
 using namespace sdpa;
 
 SDPA_API size_t sdpa_workspace_bytes(int B, int Hq, int Hkv, int qL, int kL, int D) {
-  if (check_shape(B, Hq, Hkv, qL, kL, D) != SDPA_OK) return (size_t)-1;
+  if (check_shape(B, Hq, Hkv, qL, kL, D, D) != SDPA_OK) return (size_t)-1;
   return workspace_for(plan_split(B, Hq, Hkv, qL, kL, D, 0), B, Hq, qL, D);
+}
+
+SDPA_API size_t sdpa_workspace_bytes_dv(int B, int Hq, int Hkv, int qL, int kL, int D, int Dv) {
+  if (check_shape(B, Hq, Hkv, qL, kL, D, Dv) != SDPA_OK) return (size_t)-1;
+  return workspace_for(plan_split(B, Hq, Hkv, qL, kL, D, 0), B, Hq, qL, Dv);
 }
 
 SDPA_API size_t sdpa_workspace_bytes_kv_view(int B, int Hq, int Hkv, int qL, int kL,
                                              int kv_capacity, int D) {
-  if (check_shape(B, Hq, Hkv, qL, kL, D) != SDPA_OK || check_view(kL, kv_capacity, 0) != SDPA_OK ||
-      check_shape(B, Hq, Hkv, qL, kv_capacity, D) != SDPA_OK)
+  if (check_shape(B, Hq, Hkv, qL, kL, D, D) != SDPA_OK || check_view(kL, kv_capacity, 0) != SDPA_OK ||
+      check_shape(B, Hq, Hkv, qL, kv_capacity, D, D) != SDPA_OK)
     return (size_t)-1;
   return workspace_for(plan_split(B, Hq, Hkv, qL, kL, D, kv_capacity), B, Hq, qL, D);
 }
 
 SDPA_API const char* sdpa_last_error(void) { return g_last_error; }
 
-SDPA_API int sdpa_version(void) { return 200; }
+SDPA_API int sdpa_version(void) { return 300; }
 
 SDPA_API int sdpa_forward(const void* q, const void* k, const void* v, void* out, int B, int Hq,
                           int Hkv, int qL, int kL, int D, float scale, int causal, int window,
                           int q_offset, int dtype, void* workspace, size_t workspace_bytes,
                           void* stream) {
   g_last_error[0] = '\0';
-  return forward_impl(q, k, v, nullptr, 0, 0, 0, out, B, Hq, Hkv, qL, kL, kL, 0, 0, D, scale, causal,
+  return forward_impl(q, k, v, nullptr, 0, 0, 0, out, B, Hq, Hkv, qL, kL, kL, 0, 0, D, D, scale, causal,
+                      window, q_offset, dtype, workspace, workspace_bytes, stream);
+}
+
+SDPA_API int sdpa_forward_dv(const void* q, const void* k, const void* v, void* out, int B, int Hq,
+                             int Hkv, int qL, int kL, int D, int Dv, float scale, int causal,
+                             int window, int q_offset, int dtype, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  g_last_error[0] = '\0';
+  return forward_impl(q, k, v, nullptr, 0, 0, 0, out, B, Hq, Hkv, qL, kL, kL, 0, 0, D, Dv, scale, causal,
                       window, q_offset, dtype, workspace, workspace_bytes, stream);
 }
 
@@ -253,7 +271,7 @@ SDPA_API int sdpa_forward_bias(const void* q, const void* k, const void* v, cons
                                int kL, int D, float scale, int causal, int window, int q_offset,
                                int dtype, void* workspace, size_t workspace_bytes, void* stream) {
   g_last_error[0] = '\0';
-  int rc = check_shape(B, Hq, Hkv, qL, kL, D);
+  int rc = check_shape(B, Hq, Hkv, qL, kL, D, D);
   if (rc != SDPA_OK) return rc;
   if (!bias) return fail(SDPA_INVALID_ARG, "bias must be non-null");
   if (bias_stride_b < 0 || bias_stride_h < 0 || bias_stride_q < 0)
@@ -266,7 +284,7 @@ SDPA_API int sdpa_forward_bias(const void* q, const void* k, const void* v, cons
   const size_t bbytes = (size_t)(((int64_t)(B - 1) * bias_stride_b + extent) * 2);
   if (overlap(out, qbytes, bias, bbytes)) return fail(SDPA_INVALID_ARG, "out must not overlap the bias");
   return forward_impl(q, k, v, bias, bias_stride_b, bias_stride_h, bias_stride_q, out, B, Hq, Hkv, qL, kL,
-                      kL, 0, 0, D, scale, causal, window, q_offset, dtype, workspace, workspace_bytes, stream);
+                      kL, 0, 0, D, D, scale, causal, window, q_offset, dtype, workspace, workspace_bytes, stream);
 }
 
 SDPA_API int sdpa_forward_kv_view(const void* q, const void* k, const void* v, void* out, int B,
@@ -275,11 +293,11 @@ SDPA_API int sdpa_forward_kv_view(const void* q, const void* k, const void* v, v
                                   int dtype, void* workspace, size_t workspace_bytes,
                                   void* stream) {
   g_last_error[0] = '\0';
-  int rc = check_shape(B, Hq, Hkv, qL, kL, D);
+  int rc = check_shape(B, Hq, Hkv, qL, kL, D, D);
   if (rc != SDPA_OK) return rc;
   rc = check_view(kL, kv_capacity, ring_start);
   if (rc != SDPA_OK) return rc;
   return forward_impl(q, k, v, nullptr, 0, 0, 0, out, B, Hq, Hkv, qL, kL, kv_capacity, ring_start,
-                      kv_capacity, D, scale, causal, window, q_offset, dtype, workspace, workspace_bytes,
+                      kv_capacity, D, D, scale, causal, window, q_offset, dtype, workspace, workspace_bytes,
                       stream);
 }

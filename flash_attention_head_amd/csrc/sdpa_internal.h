@@ -19,6 +19,12 @@ constexpr int block_rows(int D) { return kWaves / d_split(D) * kRowsPerWave; }
 // Keys per LDS tile, by head dimension.
 constexpr int tile_keys(int D) { return D == 512 ? 32 : 64; }
 
+// Elements per K / V row in LDS: the head dims rounded up to 128, 256 or 512
+// (a 192-wide row takes a 256-wide slot).
+constexpr int lds_row(int dk, int dv) {
+  return (dk > dv ? dk : dv) <= 128 ? 128 : (dk > dv ? dk : dv) <= 256 ? 256 : 512;
+}
+
 // Key chunk of the split path used by every call with qL <= kDecodeMaxRows
 // when no KV-cache capacity is given.  With a capacity the chunk is this
 // times a power of two chosen from (B, Hkv, capacity).  Either way chunk
@@ -36,12 +42,12 @@ struct AttnParams {
   const uint16_t* k;
   const uint16_t* v;
   uint16_t* out;      // direct output (nsplit == 1 and !partials)
-  float* part_o;      // [rows_total, nsplit, D] unnormalised fp32 accumulators
+  float* part_o;      // [rows_total, nsplit, Dv] unnormalised fp32 accumulators
   float* part_ml;     // [rows_total, nsplit, 2]: running max (log2 units), sum
   int B, Hq, Hkv, G, qL, kL;
   const uint16_t* bias;  // additive mask array or nullptr; keys contiguous within a row
   int64_t bias_sb, bias_sh, bias_sq;  // its batch, query-head and query-row strides (elements)
-  int kv_cap;         // rows per KV head in k and v (head stride kv_cap * D), >= kL
+  int kv_cap;         // rows per KV head in k and v (head strides kv_cap * D, kv_cap * Dv), >= kL
   int ring_start;     // physical row of logical key 0; key j is row (ring_start + j) % kv_cap
   int causal, window, q_offset;
   float sl2;          // scale * log2(e)
@@ -63,9 +69,11 @@ struct SplitPlan {
 };
 SplitPlan plan_split(int B, int Hq, int Hkv, int qL, int kL, int D, int kv_capacity);
 
+// D: head dim of q and k; Dv: of v and out (D, or 256 with D = 192).
 // ring: some tile's keys wrap around the end of the cache rows; p.bias set:
-// the instances that add the mask array (never together with ring)
-hipError_t launch_attention(const AttnParams& p, int D, int dtype, bool ring, hipStream_t stream);
-hipError_t launch_combine(const AttnParams& p, int D, int dtype, hipStream_t stream);
+// the instances that add the mask array (never together with ring, and
+// neither with D != Dv)
+hipError_t launch_attention(const AttnParams& p, int D, int Dv, int dtype, bool ring, hipStream_t stream);
+hipError_t launch_combine(const AttnParams& p, int Dv, int dtype, hipStream_t stream);
 
 }  // namespace sdpa

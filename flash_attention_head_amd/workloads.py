@@ -42,6 +42,11 @@ class Workload:
     q_offset: int
     seed: int
     what: str
+    Dv: int = 0  # head dim of v and the output; 0: D
+
+    @property
+    def dv(self) -> int:
+        return self.Dv or self.D
 
     @property
     def scale(self) -> float:
@@ -51,8 +56,8 @@ class Workload:
         return dataclasses.replace(self, **kw)
 
 
-def _wl(name, B, Hq, Hkv, qL, kL, D, dtype, causal, window, q_offset, seed, what):
-    return Workload(name, B, Hq, Hkv, qL, kL, D, dtype, causal, window, q_offset, seed, what)
+def _wl(name, B, Hq, Hkv, qL, kL, D, dtype, causal, window, q_offset, seed, what, Dv=0):
+    return Workload(name, B, Hq, Hkv, qL, kL, D, dtype, causal, window, q_offset, seed, what, Dv)
 
 
 # The five workloads the library is measured and checked on.  Shapes follow the
@@ -74,6 +79,11 @@ WORKLOADS = {
                            "Gemma-4-31B-like global layer, B1 Hq32 Hkv4 D512 L32768 bf16 causal"),
     "causal_d128_16k": _wl("causal_d128_16k", 1, 32, 8, 16384, 16384, 128, BF16, True, 0, 0, 6,
                            "head_dim 128 causal self-attention, B1 Hq32 Hkv8 D128 L16384 bf16"),
+    "causal_d192_16k": _wl("causal_d192_16k", 1, 32, 8, 16384, 16384, 192, BF16, True, 0, 0, 8,
+                           "head_dim 192 causal self-attention, B1 Hq32 Hkv8 D192 L16384 bf16"),
+    "causal_dk192_dv256_16k": _wl("causal_dk192_dv256_16k", 1, 32, 8, 16384, 16384, 192, BF16, True, 0, 0, 9,
+                                  "q/k head dim 192 with v head dim 256, causal, B1 Hq32 Hkv8 L16384 bf16",
+                                  Dv=256),
     "chunked_prefill_32k_bias": _wl("chunked_prefill_32k_bias", 1, 16, 8, 1024, 32768, 256, FP16, True, 0,
                                     32768 - 1024, 2,
                                     "chunked_prefill_32k plus one additive mask array [1, 1, 1024, 32768] "
@@ -112,19 +122,20 @@ def draw(wl: Workload, device: str = "cpu"):
     dt = TORCH_DTYPES[wl.dtype]
     q = torch.randn((wl.B, wl.Hq, wl.qL, wl.D), generator=g, dtype=torch.float32).to(dt)
     k = torch.randn((wl.B, wl.Hkv, wl.kL, wl.D), generator=g, dtype=torch.float32).to(dt)
-    v = torch.randn((wl.B, wl.Hkv, wl.kL, wl.D), generator=g, dtype=torch.float32).to(dt)
+    v = torch.randn((wl.B, wl.Hkv, wl.kL, wl.dv), generator=g, dtype=torch.float32).to(dt)
     return q, k, v
 
 
 def random_qkv(seed: int, B: int, Hq: int, Hkv: int, qL: int, kL: int, D: int, dtype: int,
-               std: float = 1.0):
-    """Seeded Q, K, V of an arbitrary shape, same recipe as ``draw``."""
+               std: float = 1.0, Dv: int = 0):
+    """Seeded Q, K, V of an arbitrary shape, same recipe as ``draw`` (v's head
+    dim is Dv when given, else D)."""
     g = torch.Generator(device="cpu")
     g.manual_seed(seed)
     dt = TORCH_DTYPES[dtype]
     q = (torch.randn((B, Hq, qL, D), generator=g, dtype=torch.float32) * std).to(dt)
     k = (torch.randn((B, Hkv, kL, D), generator=g, dtype=torch.float32) * std).to(dt)
-    v = (torch.randn((B, Hkv, kL, D), generator=g, dtype=torch.float32) * std).to(dt)
+    v = (torch.randn((B, Hkv, kL, Dv or D), generator=g, dtype=torch.float32) * std).to(dt)
     return q, k, v
 
 
@@ -142,13 +153,17 @@ def visible_keys(qL: int, kL: int, causal: bool, window: int, q_offset: int) -> 
 
 
 def flops(wl: Workload) -> float:
-    """Algorithmic FLOP: 4 * B * Hq * D * (visible query-key pairs per head)."""
+    """Algorithmic FLOP: 2 * B * Hq * (D + Dv) * (visible query-key pairs per head),
+    i.e. 4 * B * Hq * D * pairs when Dv = D."""
     pairs = int(visible_keys(wl.qL, wl.kL, wl.causal, wl.window, wl.q_offset).sum())
-    return 4.0 * wl.B * wl.Hq * wl.D * pairs
+    return 2.0 * wl.B * wl.Hq * (wl.D + wl.dv) * pairs
 
 
-def io_bytes(B, Hq, Hkv, qL, kL, D, elem_bytes=2) -> dict:
-    """Bytes of the inputs and the output, each read or written once."""
+def io_bytes(B, Hq, Hkv, qL, kL, D, elem_bytes=2, Dv=0) -> dict:
+    """Bytes of the inputs and the output, each read or written once (v and
+    the output have head dim Dv when given, else D)."""
+    Dv = Dv or D
     q = B * Hq * qL * D * elem_bytes
-    kv = 2 * B * Hkv * kL * D * elem_bytes
-    return {"q": q, "kv": kv, "out": q, "inputs": q + kv, "total": 2 * q + kv}
+    kv = B * Hkv * kL * (D + Dv) * elem_bytes
+    out = B * Hq * qL * Dv * elem_bytes
+    return {"q": q, "kv": kv, "out": out, "inputs": q + kv, "total": q + kv + out}

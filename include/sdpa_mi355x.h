@@ -11,8 +11,11 @@
  * fused SDPA full attention kernel") and PR #3660 ("Fused SDPA
  * full-attention for head_dim=192/256") add to MLX for head_dim 192/256.
  * Its result equals the unfused matmul + softmax + matmul path (mlx PR
- * #3660, Microbenchmarks: "max abs err 0.0"; mlx PR #3293, Benchmark) up to
- * floating-point rounding.
+ * #3660, Microbenchmarks, where the fused and unfused outputs agree exactly;
+ * mlx PR #3293, Benchmark) up to floating-point rounding.  Head dims: 128,
+ * 192 (the dim mlx PR #3293 also routes to the fused kernel, in its review
+ * discussion), 256 and 512, and through sdpa_forward_dv q/k of 192 with v of
+ * 256 (the GLM4-MoE-Lite heads named in that same discussion).
  *
  * Tensor layout (all row-major and contiguous, as the (B, H, L, D) arrays of
  * the M3 Ultra test script in mlx PR #3293):
@@ -58,7 +61,7 @@ extern "C" {
 /* Status codes. */
 #define SDPA_OK 0
 #define SDPA_INVALID_ARG 1          /* a pointer, size, flag or offset is out of range */
-#define SDPA_UNSUPPORTED 2          /* head_dim not 128/256/512, or an unknown dtype */
+#define SDPA_UNSUPPORTED 2          /* head_dim not 128/192/256/512, or an unknown dtype */
 #define SDPA_WORKSPACE_TOO_SMALL 3  /* workspace_bytes < sdpa_workspace_bytes(...) */
 #define SDPA_HIP_ERROR 4            /* the kernel launch reported a HIP error */
 
@@ -73,7 +76,7 @@ extern "C" {
  *   q, k, v   device pointers, layouts above, element type `dtype`; read only.
  *   out       device pointer, [B, Hq, qL, D]; written.  Must not overlap q/k/v.
  *   B, Hq, Hkv, qL, kL  sizes, all >= 1; Hq must be a multiple of Hkv.
- *   D         head dimension: 128, 256 or 512 (else SDPA_UNSUPPORTED).
+ *   D         head dimension: 128, 192, 256 or 512 (else SDPA_UNSUPPORTED).
  *   scale     finite fp32 factor > 0 applied to q.k (1/sqrt(D) is the usual one).
  *   causal    0 or 1.
  *   window    0 (none) or >= 1; a window requires causal = 1.
@@ -167,6 +170,25 @@ int sdpa_forward_bias(const void* q, const void* k, const void* v, const void* b
                       void* out, int B, int Hq, int Hkv, int qL, int kL, int D, float scale,
                       int causal, int window, int q_offset, int dtype, void* workspace,
                       size_t workspace_bytes, void* stream);
+
+/*
+ * sdpa_forward with a value head dim Dv that may differ from the query/key
+ * head dim D: q and k are [B, Hq, qL, D] and [B, Hkv, kL, D], v is
+ * [B, Hkv, kL, Dv] and out [B, Hq, qL, Dv].  Scores take the D-long dot
+ * products; the output is the weighted sum of the Dv-long value rows.  The
+ * pairs supported are D == Dv (any head dim sdpa_forward takes; the call is
+ * then sdpa_forward) and D = 192 with Dv = 256, the Q=192/K=192/V=256 heads
+ * that the review discussion of ml-explore/mlx PR #3293 says its
+ * query_head_dim == value_head_dim gate keeps off the fused path.  Other
+ * pairs: SDPA_UNSUPPORTED.  Everything else, qL <= 4 bit-exactness included,
+ * is as in sdpa_forward; the workspace is sdpa_workspace_bytes_dv(...).
+ */
+int sdpa_forward_dv(const void* q, const void* k, const void* v, void* out, int B, int Hq, int Hkv,
+                    int qL, int kL, int D, int Dv, float scale, int causal, int window,
+                    int q_offset, int dtype, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes of sdpa_forward_dv; (size_t)-1 for arguments it rejects. */
+size_t sdpa_workspace_bytes_dv(int B, int Hq, int Hkv, int qL, int kL, int D, int Dv);
 
 /* Message for the last non-zero status returned on the calling thread ("" if none). */
 const char* sdpa_last_error(void);

@@ -67,7 +67,7 @@ BAD = [
     (dict(kL=-3), fa.SDPA_INVALID_ARG, ">= 1"),
     (dict(Hq=3), fa.SDPA_INVALID_ARG, "multiple"),
     (dict(D=64), fa.SDPA_UNSUPPORTED, "head_dim"),
-    (dict(D=192), fa.SDPA_UNSUPPORTED, "head_dim"),
+    (dict(D=160), fa.SDPA_UNSUPPORTED, "head_dim"),
     (dict(dtype=2), fa.SDPA_UNSUPPORTED, "dtype"),
     (dict(scale=float("nan")), fa.SDPA_INVALID_ARG, "scale"),
     (dict(scale=float("inf")), fa.SDPA_INVALID_ARG, "scale"),
@@ -190,7 +190,7 @@ def test_workspace_is_linear_in_key_chunks_not_quadratic(lib):
 
 
 def test_workspace_of_rejected_shapes_is_size_max(lib):
-    assert fa.sdpa_workspace_bytes(1, 4, 2, 8, 64, 192) == SIZE_MAX
+    assert fa.sdpa_workspace_bytes(1, 4, 2, 8, 64, 160) == SIZE_MAX
     assert fa.sdpa_workspace_bytes(1, 3, 2, 8, 64, 256) == SIZE_MAX
     assert fa.sdpa_workspace_bytes(0, 4, 2, 8, 64, 256) == SIZE_MAX
 
@@ -221,3 +221,38 @@ def test_bias_entry_point_rejects_bad_bias_arguments(lib):
     assert call(sq=-1) == fa.SDPA_INVALID_ARG and "stride" in fa.sdpa_last_error()
     assert call(sh=1 << 31) == fa.SDPA_UNSUPPORTED and "2^30" in fa.sdpa_last_error()
     assert call(bias=0x300000 - 64) == fa.SDPA_INVALID_ARG and "overlap" in fa.sdpa_last_error()
+
+
+# sdpa_forward_dv: q/k head dim D, v and out head dim Dv
+DV_ORDER = ["q", "k", "v", "out", "B", "Hq", "Hkv", "qL", "kL", "D", "Dv", "scale", "causal", "window",
+            "q_offset", "dtype", "workspace", "workspace_bytes", "stream"]
+
+
+def _call_dv(**kw):
+    args = {**GOOD, "D": 192, "Dv": 256, **kw}
+    return fa.sdpa_forward_dv(*[args[n] for n in DV_ORDER])
+
+
+@pytest.mark.parametrize("D,Dv", [(256, 192), (128, 256), (192, 512), (256, 512), (64, 64), (192, 128)])
+def test_value_dim_pairs_outside_the_supported_set_are_rejected(lib, D, Dv):
+    assert _call_dv(D=D, Dv=Dv) == fa.SDPA_UNSUPPORTED
+    assert "head" in fa.sdpa_last_error()
+    assert fa.sdpa_workspace_bytes_dv(1, 4, 2, 2, 5000, D, Dv) == SIZE_MAX
+
+
+def test_value_dim_entry_checks_the_other_arguments_like_sdpa_forward(lib):
+    assert _call_dv(B=0) == fa.SDPA_INVALID_ARG and ">= 1" in fa.sdpa_last_error()
+    assert _call_dv(q_offset=57) == fa.SDPA_INVALID_ARG and "q_offset" in fa.sdpa_last_error()
+    # out is [B, Hq, qL, 256]: 16 KiB here, so from 8 KiB below k it reaches into k
+    assert _call_dv(out=0x100000 - 8192) == fa.SDPA_INVALID_ARG and "overlap" in fa.sdpa_last_error()
+    # v is [B, Hkv, kL, 256] (64 KiB): out just past its 48 KiB of a D = 192 view still overlaps
+    assert _call_dv(out=0x200000 + 49152) == fa.SDPA_INVALID_ARG and "overlap" in fa.sdpa_last_error()
+    assert _call_dv(qL=2, q_offset=62, workspace_bytes=16) == fa.SDPA_WORKSPACE_TOO_SMALL
+
+
+def test_value_dim_workspace_counts_value_columns(lib):
+    # decode: one (m, l, O[Dv]) fp32 partial per row and 1024-key chunk
+    ws = fa.sdpa_workspace_bytes_dv(1, 16, 8, 4, 5000, 192, 256)
+    assert ws == 16 * 4 * 5 * (256 + 2) * 4
+    assert fa.sdpa_workspace_bytes_dv(1, 16, 8, 4, 5000, 192, 192) == fa.sdpa_workspace_bytes(1, 16, 8, 4, 5000, 192)
+    assert fa.sdpa_workspace_bytes_dv(1, 64, 64, 16384, 16384, 192, 256) == 0

@@ -73,6 +73,20 @@ def test_verify_block_at_head_dim_128():
     _check_rows(q, k, v, window=0, what="D128 32/8")
 
 
+@pytest.mark.timeout(600)
+def test_verify_block_at_head_dim_192():
+    q, k, v = W.random_qkv(55, 1, 32, 8, 4, 20000, 192, BF16)
+    _check_rows(q, k, v, window=0, what="D192 32/8")
+
+
+@pytest.mark.timeout(600)
+def test_verify_block_with_value_head_dim_256():
+    # q/k head dim 192, v head dim 256 (sdpa_forward_dv)
+    q, k, v = W.random_qkv(56, 1, 16, 16, 4, 20000, 192, FP16, Dv=256)
+    _check_rows(q, k, v, window=0, what="D192 Dv256")
+    _check_rows(q, k, v, window=700, what="D192 Dv256 window 700")
+
+
 @pytest.mark.parametrize("qL", [2, 3])
 def test_verify_blocks_of_two_and_three(qL):
     q, k, v = W.random_qkv(52 + qL, 1, 16, 8, qL, 20000, 256, BF16)

@@ -65,6 +65,8 @@ CASES = [
     (1, 2, 1, 4, 600, 640, 17, 512, BF16, True, 0, 596),          # head_dim 512, offset, no wrap
     (1, 4, 2, 4, 1000, 1000, 963, 128, BF16, True, 0, 996),       # head_dim 128, wrapped ring
     (1, 4, 2, 200, 3000, 3000, 1501, 128, FP16, True, 0, 2800),   # head_dim 128 prefill, wrapped
+    (1, 4, 2, 4, 1000, 1000, 963, 192, FP16, True, 0, 996),       # head_dim 192, wrapped ring
+    (1, 4, 2, 200, 3000, 3200, 2901, 192, BF16, True, 0, 2800),   # head_dim 192 prefill, wrapped
 ]
 
 
@@ -84,7 +86,7 @@ def test_cache_views_match_the_oracle(case):
 @pytest.mark.parametrize("qL,kL,cap,rs,D", [(4, 3000, 3000, 1234, 256), (4, 3000, 3500, 3301, 256),
                                             (130, 5000, 5000, 2047, 256), (4, 1500, 1500, 1499, 512),
                                             (70, 1500, 1600, 900, 512), (4, 1000, 1000, 962, 128),
-                                            (70, 1000, 1000, 961, 128)])
+                                            (70, 1000, 1000, 961, 128), (4, 1000, 1000, 962, 192)])
 def test_ring_view_equals_the_same_keys_from_row_zero(qL, kL, cap, rs, D):
     q, k, v = W.random_qkv(4000 + rs, 1, 8, 2, qL, kL, D, BF16)
     note(f"ring vs row-0 cache q{qL} k{kL} cap{cap} r{rs} D{D}")
