@@ -27,7 +27,8 @@ if ROOT not in sys.path:
 PEAK_MFMA_TFLOPS = 2516.6
 PEAK_HBM_GBS = 8000.0
 HEADLINE = "chunked_prefill_32k"
-EXTRA = ["causal_h64_16k", "sliding_32k", "global_d512_32k", "causal_d128_16k", "causal_d192_16k",
+EXTRA = ["causal_h64_16k", "sliding_32k", "global_d512_32k", "causal_d64_16k", "causal_d80_16k",
+         "causal_d128_16k", "causal_d192_16k",
          "causal_dk192_dv256_16k", "chunked_prefill_32k_bias", "decode_q4_128k", "decode_q1_128k", "tiny_causal"]
 
 

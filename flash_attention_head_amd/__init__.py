@@ -42,7 +42,7 @@ EXPORTED_SYMBOLS = ("sdpa_forward", "sdpa_workspace_bytes", "sdpa_forward_kv_vie
                     "sdpa_workspace_bytes_dv", "sdpa_last_error", "sdpa_version")
 
 # (q/k head dim, v head dim) pairs the library takes
-HEAD_DIMS = ((128, 128), (192, 192), (256, 256), (512, 512), (192, 256))
+HEAD_DIMS = ((64, 64), (80, 80), (128, 128), (192, 192), (256, 256), (512, 512), (192, 256))
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _lib = None
@@ -198,7 +198,7 @@ def sdpa(q, k, v, *, scale: float | None = None, causal: bool = False, window: i
     """softmax(scale * q k^T + mask) v on device tensors.
 
     q: [B, Hq, qL, D], k: [B, Hkv, kL, D], v: [B, Hkv, kL, Dv], contiguous fp16 or
-    bf16 tensors on one GPU; D = Dv in {128, 192, 256, 512}, or D = 192 with
+    bf16 tensors on one GPU; D = Dv in {64, 80, 128, 192, 256, 512}, or D = 192 with
     Dv = 256 (sdpa_forward_dv, no bias); Hq a multiple of Hkv.  The result is
     [B, Hq, qL, Dv].  scale defaults to 1/sqrt(D) (as fp32).  With causal, query row i sits at key position q_offset + i;
     q_offset defaults to kL - qL (queries aligned to the end of the keys).

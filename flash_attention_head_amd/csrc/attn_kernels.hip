@@ -236,7 +236,11 @@ __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* ld
   constexpr int NW = 4, RBW = PAIR ? 2 : 4;  // 32-row blocks per workgroup
   constexpr int BM = RBW * kRowsPerWave, BN = tile_keys(DK), KB = BN / 32;
   constexpr int DQ = DK < 256 ? DK : 256, DO = PAIR ? DV / 2 : DV;  // Q columns multiplied, output columns owned
-  constexpr int DC = DQ / 16, DB = DO / 32;
+  // output column blocks of 32: a head dim of 80 takes three, the last one
+  // half beyond the value rows (their LDS columns read zeros, and the
+  // epilogue writes only columns below DV)
+  constexpr int DC = DQ / 16, DB = (DO + 31) / 32;
+  static_assert(DQ % 16 == 0 && DO % 16 == 0, "head dims are multiples of 16");
   // K and V tiles sit in LDS as BN rows of LD elements; a head dim below LD
   // (192) leaves the end of each row unused, so that 192-wide rows take the
   // 256-wide layout and its swizzles unchanged
@@ -249,7 +253,7 @@ __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* ld
   constexpr int VSW = ROWCH >= 32 ? 7 : 3;
   static_assert(BM == block_rows(DK), "geometry");
   static_assert(LOADS == 4 || LOADS == 8, "K and V loads of 1 KiB blocks per wave");
-  static_assert(NQK <= NE && NE <= 2 * NQK && NPV <= NE && NE <= 2 * NPV, "one or two score elements per MFMA slot");
+  static_assert(NQK <= NE && NE <= 4 * NQK && NPV <= NE && NE <= 4 * NPV, "one to four score elements per MFMA slot");
   // the first score element of S slot n and of P V slot n (n <= the slot count)
   auto es = [](int n) { return (n < NQK ? n : NQK) * NE / NQK; };
   auto ev = [](int n) { return (n < NPV ? n : NPV) * NE / NPV; };
@@ -585,10 +589,17 @@ __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* ld
                         uint4 (&pb)[KB * 2], const TileSrc& ksrc, uint16_t* kdst, const TileSrc& vsrc,
                         uint16_t* vdst, const i32x4_t& bsrc, uint16_t* bdst, const uint16_t* bl,
                         uint2 (&bw)[KB * 4]) {
-    constexpr int PF = 4, LS = NQK / LOADS;
-    // the slot of a run of LS that issues the bias load (apart from K's and V's)
-    constexpr int BSLOT = LS == 3 ? 2 : 1;
-    static_assert(LS >= 2 && LS * LOADS == NQK, "slot pattern");
+    constexpr int PF = 4;
+    // the slots of K block group i, V block group i and bias block group i:
+    // spread evenly over the region, V half a spacing after K, bias one slot
+    // after K (two when runs are three slots long, so as not to share V's).
+    // When the slots divide evenly the tests are written as runs of LS slots
+    // (the form the compiler schedules best); otherwise slot by slot.
+    static_assert(NQK >= 2 * LOADS, "slot pattern");
+    constexpr bool EVEN = NQK % LOADS == 0;
+    constexpr int LS = NQK / LOADS, BSLOT = LS == 3 ? 2 : 1;
+    auto kslot = [](int i) { return i * NQK / LOADS; };
+    auto vslot = [](int i) { return (2 * i + 1) * NQK / (2 * LOADS); };
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
@@ -603,7 +614,6 @@ __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* ld
     auto get = [&](int e) { return sc[e / 16][e % 16]; };
     auto set = [&](int e, float v) { sc[e / 16][e % 16] = v; };
     float psum = 0.f;
-    uint32_t wlast = 0;
     uint4 a[PF];
 #pragma unroll
     for (int i = 0; i < PF; ++i) a[i] = kread(i, kx(i));
@@ -616,37 +626,59 @@ __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* ld
     for (int e = es(0); e < es(1); ++e) set(e, fast_exp2(get(e) * sl2 - msc));
 #pragma unroll
     for (int e = es(1); e < es(2); ++e) set(e, get(e) * sl2 - msc);
-    // slot m packs a pair iff one of its (one or two) elements is odd
-    auto packs = [&](int m) { return es(m + 1) - es(m) == 2 || (es(m) & 1); };
+    // the pairs slot m packs: its odd elements e, pair (e - 1, e); at most two
+    auto npacks = [&](int m) {
+      int c = 0;
+      for (int e = es(m); e < es(m + 1); ++e) c += e & 1;
+      return c;
+    };
+    uint32_t wlast[2] = {0, 0};  // the words the last slot packed
 #pragma unroll
     for (int n = 0; n < NQK; ++n) {
       const uint4 cur_a = a[n % PF];
       if (n + PF < NQK) a[n % PF] = kread(n + PF, x_next);
       sn[n % KB] = Elem<DT>::mfma(cur_a, qf[n / KB], sn[n % KB]);
       if (n + PF + 1 < NQK) x_next = kx(n + PF + 1);
-      // loads: K block group i at slot i LS, V block group i at slot i LS + LS / 2
-      if (n % LS == 0) load_blk(ksrc, kdst, n / LS, false);
-      if (n % LS == LS / 2) load_blk(vsrc, vdst, n / LS, true);
+      // loads: K, V and bias block group i at slots kslot(i), vslot(i), bslot(i)
+      if constexpr (EVEN) {
+        if (n % LS == 0) load_blk(ksrc, kdst, n / LS, false);
+        if (n % LS == LS / 2) load_blk(vsrc, vdst, n / LS, true);
+      } else {
+#pragma unroll
+        for (int i = 0; i < LOADS; ++i) {
+          if (n == kslot(i)) load_blk(ksrc, kdst, i, false);
+          if (n == vslot(i)) load_blk(vsrc, vdst, i, true);
+        }
+      }
       if constexpr (BIAS) {
         // the bias tile that goes with K(tk), and in the last slots the bias
         // of S(t + 1) for the P V region (its reads are in flight by then)
-        if (n % LS == BSLOT && n / LS < BLOADS) load_bblk(bsrc, bdst, n / LS);
+        if constexpr (EVEN) {
+          if (n % LS == BSLOT && n / LS < BLOADS) load_bblk(bsrc, bdst, n / LS);
+        } else {
+#pragma unroll
+          for (int i = 0; i < BLOADS; ++i)
+            if (n == kslot(i) + 1) load_bblk(bsrc, bdst, i);
+        }
         if (n >= NQK - KB * 4) bw[n - (NQK - KB * 4)] = bias_read(bl, n - (NQK - KB * 4));
       }
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
+      for (int i = 0; i < 4; ++i) {
         const int ef = es(n + 2) + i, ex = es(n + 1) + i;
         if (ef < es(n + 3)) set(ef, get(ef) * sl2 - msc);
         if (ex < es(n + 2)) set(ex, fast_exp2(get(ex)));
       }
       // the row sum adds the rounded weights the P V product uses, a pair
       // per dot2, one slot after the pair is packed
-      if (n > 0 && packs(n - 1)) psum = Elem<DT>::sum2(wlast, psum);
+      if (n > 0) {
+#pragma unroll
+        for (int i = 0; i < npacks(n - 1); ++i) psum = Elem<DT>::sum2(wlast[i], psum);
+      }
 #pragma unroll
       for (int e = es(n); e < es(n + 1); ++e) {
         if (e & 1) {  // pack the pair (e - 1, e): P half kh = e / 8
           const uint32_t w = Elem<DT>::pack2(get(e - 1), get(e));
-          wlast = w;
+          wlast[e - es(n) > 1 ? 1 : 0] = w;
           uint4& q = pb[e / 8];
           switch ((e % 8) / 2) {
             case 0: q.x = w; break;
@@ -658,7 +690,8 @@ __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* ld
       }
       __builtin_amdgcn_sched_barrier(0);
     }
-    psum = Elem<DT>::sum2(wlast, psum);
+#pragma unroll
+    for (int i = 0; i < npacks(NQK - 1); ++i) psum = Elem<DT>::sum2(wlast[i], psum);
     m0_restore(m0);
     // an empty volatile use: the sum is formed here, slot by slot, not sunk
     // past the next region as a serial chain
@@ -833,6 +866,7 @@ __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* ld
     for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
+        if (db * 32 + 8 * q4 >= DO) continue;  // columns past the value rows
         const int d = db * 32 + 8 * q4 + 4 * lg;
         uint2 w;
         w.x = Elem<DT>::pack2(o[db][4 * q4 + 0] * inv, o[db][4 * q4 + 1] * inv);
@@ -846,6 +880,7 @@ __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* ld
     for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
+        if (db * 32 + 8 * q4 >= DO) continue;  // columns past the value rows
         const int d = db * 32 + 8 * q4 + 4 * lg;
         *(float4*)(dst + d) =
             make_float4(o[db][4 * q4 + 0], o[db][4 * q4 + 1], o[db][4 * q4 + 2], o[db][4 * q4 + 3]);
@@ -860,6 +895,18 @@ __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* ld
 // LDS per workgroup: 2 K + 2 V tiles of 64 (32 at D = 512) rows of
 // lds_row(DK, DV) elements (+ the pair score exchange at D = 512, 4 waves x
 // 4 KiB) (+ 2 bias tiles of the workgroup's rows x the tile's keys)
+template <int DT, bool RING, bool BIAS>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void attn_tile_kernel_d64(AttnParams p) {
+  __shared__ __attribute__((aligned(16))) uint16_t lds[4 * 64 * 128 + (BIAS ? 2 * 128 * 64 : 0)];
+  attn_pipe_body<DT, 64, 64, RING, BIAS>(p, lds);
+}
+template <int DT, bool RING, bool BIAS>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void attn_tile_kernel_d80(AttnParams p) {
+  __shared__ __attribute__((aligned(16))) uint16_t lds[4 * 64 * 128 + (BIAS ? 2 * 128 * 64 : 0)];
+  attn_pipe_body<DT, 80, 80, RING, BIAS>(p, lds);
+}
 template <int DT, bool RING, bool BIAS>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void attn_tile_kernel_d128(AttnParams p) {
@@ -902,8 +949,8 @@ constexpr int kCombineWaves = 16;
 
 template <int DT, int D>
 __global__ __launch_bounds__(64 * kCombineWaves) void combine_kernel(AttnParams p) {
-  // columns per lane, at least 4 (one float4); at D = 128 only lanes
-  // [0, 32) own columns, the others take part in the reductions only
+  // columns per lane, at least 4 (one float4); below D = 256 only lanes
+  // [0, D / 4) own columns, the others take part in the reductions only
   constexpr int PER = D / 64 >= 4 ? D / 64 : 4;
   constexpr int NW = kCombineWaves;
   const int nw = blockDim.x >> 6;  // waves in this launch, <= NW
@@ -986,7 +1033,11 @@ __global__ __launch_bounds__(64 * kCombineWaves) void combine_kernel(AttnParams 
 template <int DT, int D, bool RING, bool BIAS>
 hipError_t launch_attention_t(const AttnParams& p, hipStream_t stream) {
   const dim3 grid((unsigned)(p.B * p.Hkv * p.mblocks), (unsigned)p.nsplit, 1);
-  if constexpr (D == 128)
+  if constexpr (D == 64)
+    hipLaunchKernelGGL((attn_tile_kernel_d64<DT, RING, BIAS>), grid, dim3(256), 0, stream, p);
+  else if constexpr (D == 80)
+    hipLaunchKernelGGL((attn_tile_kernel_d80<DT, RING, BIAS>), grid, dim3(256), 0, stream, p);
+  else if constexpr (D == 128)
     hipLaunchKernelGGL((attn_tile_kernel_d128<DT, RING, BIAS>), grid, dim3(256), 0, stream, p);
   else if constexpr (D == 192)
     hipLaunchKernelGGL((attn_tile_kernel_d192<DT, RING, BIAS>), grid, dim3(256), 0, stream, p);
@@ -1026,6 +1077,8 @@ hipError_t launch_attention(const AttnParams& p, int D, int Dv, int dtype, bool 
     else hipLaunchKernelGGL((attn_tile_kernel_dk192_dv256<1>), grid, dim3(256), 0, stream, p);
     return hipGetLastError();
   }
+  if (D == 64) return launch_attention_dd<64>(p, dtype, ring, stream);
+  if (D == 80) return launch_attention_dd<80>(p, dtype, ring, stream);
   if (D == 128) return launch_attention_dd<128>(p, dtype, ring, stream);
   if (D == 192) return launch_attention_dd<192>(p, dtype, ring, stream);
   if (D == 256) return launch_attention_dd<256>(p, dtype, ring, stream);
@@ -1033,6 +1086,8 @@ hipError_t launch_attention(const AttnParams& p, int D, int Dv, int dtype, bool 
 }
 
 hipError_t launch_combine(const AttnParams& p, int D, int dtype, hipStream_t stream) {
+  if (D == 64) return dtype == 0 ? launch_combine_t<0, 64>(p, stream) : launch_combine_t<1, 64>(p, stream);
+  if (D == 80) return dtype == 0 ? launch_combine_t<0, 80>(p, stream) : launch_combine_t<1, 80>(p, stream);
   if (D == 128) return dtype == 0 ? launch_combine_t<0, 128>(p, stream) : launch_combine_t<1, 128>(p, stream);
   if (D == 192) return dtype == 0 ? launch_combine_t<0, 192>(p, stream) : launch_combine_t<1, 192>(p, stream);
   if (D == 256) return dtype == 0 ? launch_combine_t<0, 256>(p, stream) : launch_combine_t<1, 256>(p, stream);

@@ -37,8 +37,8 @@ int check_shape(int B, int Hq, int Hkv, int qL, int kL, int D, int Dv) {
     return fail(SDPA_INVALID_ARG, "Hq (%d) must be a multiple of Hkv (%d)", Hq, Hkv);
   if (D != Dv && !(D == 192 && Dv == 256))
     return fail(SDPA_UNSUPPORTED, "head dims q/k %d with v %d are not supported (equal, or 192 with 256)", D, Dv);
-  if (D != 128 && D != 192 && D != 256 && D != 512)
-    return fail(SDPA_UNSUPPORTED, "head_dim %d is not supported (128, 192, 256 or 512)", D);
+  if (D != 64 && D != 80 && D != 128 && D != 192 && D != 256 && D != 512)
+    return fail(SDPA_UNSUPPORTED, "head_dim %d is not supported (64, 80, 128, 192, 256 or 512)", D);
   // index arithmetic inside the kernels: packed rows per KV head and the
   // launch grid stay in 32-bit range; byte offsets are 64-bit
   const int64_t rows = (int64_t)(Hq / Hkv) * qL;

@@ -79,6 +79,10 @@ WORKLOADS = {
                            "Gemma-4-31B-like global layer, B1 Hq32 Hkv4 D512 L32768 bf16 causal"),
     "causal_d128_16k": _wl("causal_d128_16k", 1, 32, 8, 16384, 16384, 128, BF16, True, 0, 0, 6,
                            "head_dim 128 causal self-attention, B1 Hq32 Hkv8 D128 L16384 bf16"),
+    "causal_d64_16k": _wl("causal_d64_16k", 1, 32, 8, 16384, 16384, 64, BF16, True, 0, 0, 10,
+                          "head_dim 64 causal self-attention, B1 Hq32 Hkv8 D64 L16384 bf16"),
+    "causal_d80_16k": _wl("causal_d80_16k", 1, 32, 8, 16384, 16384, 80, BF16, True, 0, 0, 11,
+                          "head_dim 80 causal self-attention, B1 Hq32 Hkv8 D80 L16384 bf16"),
     "causal_d192_16k": _wl("causal_d192_16k", 1, 32, 8, 16384, 16384, 192, BF16, True, 0, 0, 8,
                            "head_dim 192 causal self-attention, B1 Hq32 Hkv8 D192 L16384 bf16"),
     "causal_dk192_dv256_16k": _wl("causal_dk192_dv256_16k", 1, 32, 8, 16384, 16384, 192, BF16, True, 0, 0, 9,

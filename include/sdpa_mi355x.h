@@ -12,10 +12,11 @@
  * full-attention for head_dim=192/256") add to MLX for head_dim 192/256.
  * Its result equals the unfused matmul + softmax + matmul path (mlx PR
  * #3660, Microbenchmarks, where the fused and unfused outputs agree exactly;
- * mlx PR #3293, Benchmark) up to floating-point rounding.  Head dims: 128,
- * 192 (the dim mlx PR #3293 also routes to the fused kernel, in its review
- * discussion), 256 and 512, and through sdpa_forward_dv q/k of 192 with v of
- * 256 (the GLM4-MoE-Lite heads named in that same discussion).
+ * mlx PR #3293, Benchmark) up to floating-point rounding.  Head dims: 64,
+ * 80 and 128 (the dims MLX's fused kernel already took, per the routing
+ * code in mlx PR #3293), 192 (which that PR's review discussion adds), 256
+ * and 512, and through sdpa_forward_dv q/k of 192 with v of 256 (the
+ * GLM4-MoE-Lite heads named in that same discussion).
  *
  * Tensor layout (all row-major and contiguous, as the (B, H, L, D) arrays of
  * the M3 Ultra test script in mlx PR #3293):
@@ -61,7 +62,7 @@ extern "C" {
 /* Status codes. */
 #define SDPA_OK 0
 #define SDPA_INVALID_ARG 1          /* a pointer, size, flag or offset is out of range */
-#define SDPA_UNSUPPORTED 2          /* head_dim not 128/192/256/512, or an unknown dtype */
+#define SDPA_UNSUPPORTED 2          /* head_dim not 64/80/128/192/256/512, or an unknown dtype */
 #define SDPA_WORKSPACE_TOO_SMALL 3  /* workspace_bytes < sdpa_workspace_bytes(...) */
 #define SDPA_HIP_ERROR 4            /* the kernel launch reported a HIP error */
 
@@ -76,7 +77,7 @@ extern "C" {
  *   q, k, v   device pointers, layouts above, element type `dtype`; read only.
  *   out       device pointer, [B, Hq, qL, D]; written.  Must not overlap q/k/v.
  *   B, Hq, Hkv, qL, kL  sizes, all >= 1; Hq must be a multiple of Hkv.
- *   D         head dimension: 128, 192, 256 or 512 (else SDPA_UNSUPPORTED).
+ *   D         head dimension: 64, 80, 128, 192, 256 or 512 (else SDPA_UNSUPPORTED).
  *   scale     finite fp32 factor > 0 applied to q.k (1/sqrt(D) is the usual one).
  *   causal    0 or 1.
  *   window    0 (none) or >= 1; a window requires causal = 1.

@@ -66,7 +66,7 @@ BAD = [
     (dict(B=0), fa.SDPA_INVALID_ARG, ">= 1"),
     (dict(kL=-3), fa.SDPA_INVALID_ARG, ">= 1"),
     (dict(Hq=3), fa.SDPA_INVALID_ARG, "multiple"),
-    (dict(D=64), fa.SDPA_UNSUPPORTED, "head_dim"),
+    (dict(D=96), fa.SDPA_UNSUPPORTED, "head_dim"),
     (dict(D=160), fa.SDPA_UNSUPPORTED, "head_dim"),
     (dict(dtype=2), fa.SDPA_UNSUPPORTED, "dtype"),
     (dict(scale=float("nan")), fa.SDPA_INVALID_ARG, "scale"),
@@ -233,7 +233,7 @@ def _call_dv(**kw):
     return fa.sdpa_forward_dv(*[args[n] for n in DV_ORDER])
 
 
-@pytest.mark.parametrize("D,Dv", [(256, 192), (128, 256), (192, 512), (256, 512), (64, 64), (192, 128)])
+@pytest.mark.parametrize("D,Dv", [(256, 192), (128, 256), (192, 512), (256, 512), (96, 96), (192, 128), (64, 80)])
 def test_value_dim_pairs_outside_the_supported_set_are_rejected(lib, D, Dv):
     assert _call_dv(D=D, Dv=Dv) == fa.SDPA_UNSUPPORTED
     assert "head" in fa.sdpa_last_error()

@@ -56,6 +56,9 @@ CASES = [
     (1, 4, 2, 4, 3000, 128, BF16, False, 0, 0, False, True),     # head_dim 128 decode, unmasked
     (2, 4, 2, 200, 333, 192, BF16, True, 0, 133, True, True),    # head_dim 192
     (1, 4, 2, 4, 3000, 192, FP16, True, 0, 2996, False, True),   # head_dim 192 verify block
+    (2, 4, 2, 200, 333, 64, FP16, True, 0, 133, True, True),     # head_dim 64
+    (2, 4, 2, 200, 333, 80, BF16, True, 0, 133, True, True),     # head_dim 80
+    (1, 2, 1, 130, 4100, 80, FP16, True, 0, 3970, False, False),  # head_dim 80 with key split
 ]
 
 

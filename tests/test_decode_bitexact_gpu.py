@@ -80,6 +80,13 @@ def test_verify_block_at_head_dim_192():
 
 
 @pytest.mark.timeout(600)
+@pytest.mark.parametrize("D", [64, 80])
+def test_verify_block_at_small_head_dims(D):
+    q, k, v = W.random_qkv(57 + D, 1, 32, 8, 4, 20000, D, FP16)
+    _check_rows(q, k, v, window=0, what=f"D{D} 32/8")
+
+
+@pytest.mark.timeout(600)
 def test_verify_block_with_value_head_dim_256():
     # q/k head dim 192, v head dim 256 (sdpa_forward_dv)
     q, k, v = W.random_qkv(56, 1, 16, 16, 4, 20000, 192, FP16, Dv=256)

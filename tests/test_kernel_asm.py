@@ -16,7 +16,7 @@ import pytest
 
 from flash_attention_head_amd import build as B
 
-KERNELS = ("attn_tile_kernel_d128", "attn_tile_kernel_d192", "attn_tile_kernel_dk192_dv256", "attn_tile_kernel_d256",
+KERNELS = ("attn_tile_kernel_d64", "attn_tile_kernel_d80", "attn_tile_kernel_d128", "attn_tile_kernel_d192", "attn_tile_kernel_dk192_dv256", "attn_tile_kernel_d256",
            "attn_tile_kernel_d512",
            "combine_kernel")
 

@@ -67,6 +67,9 @@ CASES = [
     (1, 4, 2, 200, 3000, 3000, 1501, 128, FP16, True, 0, 2800),   # head_dim 128 prefill, wrapped
     (1, 4, 2, 4, 1000, 1000, 963, 192, FP16, True, 0, 996),       # head_dim 192, wrapped ring
     (1, 4, 2, 200, 3000, 3200, 2901, 192, BF16, True, 0, 2800),   # head_dim 192 prefill, wrapped
+    (1, 4, 2, 4, 1000, 1000, 963, 64, BF16, True, 0, 996),        # head_dim 64, wrapped ring
+    (1, 4, 2, 4, 1000, 1000, 963, 80, FP16, True, 0, 996),        # head_dim 80, wrapped ring
+    (1, 4, 2, 200, 3000, 3000, 1501, 80, BF16, True, 0, 2800),    # head_dim 80 prefill, wrapped
 ]
 
 

@@ -54,6 +54,15 @@ SMALL = [
     (1, 2, 1, 300, 9000, 192, BF16, True, 0, 8700),    # head_dim 192 with key split
     (1, 4, 2, 4, 2500, 192, FP16, True, 0, 2496),      # head_dim 192 verify block
     (1, 2, 2, 65, 190, 192, FP16, False, 0, 0),        # head_dim 192, no mask
+    (2, 4, 2, 333, 333, 64, FP16, True, 0, 0),         # head_dim 64: ragged tiles and row blocks
+    (1, 4, 2, 100, 1000, 64, BF16, True, 77, 900),     # head_dim 64, window over a prefix
+    (1, 2, 1, 300, 9000, 64, FP16, True, 0, 8700),     # head_dim 64 with key split
+    (1, 4, 2, 4, 2500, 64, BF16, True, 0, 2496),       # head_dim 64 verify block
+    (2, 4, 2, 333, 333, 80, BF16, True, 0, 0),         # head_dim 80: ragged tiles and row blocks
+    (1, 4, 2, 100, 1000, 80, FP16, True, 77, 900),     # head_dim 80, window over a prefix
+    (1, 2, 1, 300, 9000, 80, BF16, True, 0, 8700),     # head_dim 80 with key split
+    (1, 4, 2, 4, 2500, 80, FP16, True, 0, 2496),       # head_dim 80 verify block
+    (1, 2, 2, 65, 190, 80, FP16, False, 0, 0),         # head_dim 80, no mask
 ]
 
 
@@ -82,7 +91,8 @@ def test_tiny_causal_workload_every_row():
 
 
 FULL = [("chunked_prefill_32k", 160), ("causal_h64_16k", 160), ("sliding_32k", 200),
-        ("global_d512_32k", 64), ("causal_d128_16k", 96), ("causal_d192_16k", 96), ("decode_q4_128k", 32),
+        ("global_d512_32k", 64), ("causal_d64_16k", 96), ("causal_d80_16k", 96), ("causal_d128_16k", 96),
+        ("causal_d192_16k", 96), ("decode_q4_128k", 32),
         ("decode_q1_128k", 16)]
 
 
@@ -130,7 +140,8 @@ def test_zero_queries_average_visible_values_at_full_size(name):
     assert worst <= TOL[wl.dtype]
 
 
-@pytest.mark.parametrize("D,dtype", [(256, FP16), (256, BF16), (512, BF16), (192, FP16)])
+@pytest.mark.parametrize("D,dtype", [(256, FP16), (256, BF16), (512, BF16), (192, FP16), (80, BF16),
+                                     (64, FP16)])
 def test_first_causal_row_and_unit_window_are_exact(D, dtype):
     # causal row 0 at q_offset 0 sees key 0 only; a window of 1 sees key p only:
     # exp2(0) = 1, every other weight is 0, so the output is the value row bitwise
