@@ -204,6 +204,16 @@ __device__ __forceinline__ float pair_sum(float v) {
   return __builtin_bit_cast(float, (int)r[0]) + __builtin_bit_cast(float, (int)r[1]);
 }
 
+// Wait until at most N vector memory operations of this wave are
+// outstanding (vmcnt only; LDS and export counters untouched).  Loads
+// complete in issue order, so this waits for everything but the N most
+// recent loads.
+template <int N>
+__device__ __forceinline__ void wait_vmem() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
 // Lazy rescaling: a row's reference max moves only when a tile's max exceeds
 // it by more than this many binary orders of magnitude, so exp2 arguments stay
 // <= kRescaleLog2 (weights <= 256, well inside the fp16/bf16 range) and the
@@ -232,6 +242,8 @@ __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* ld
   // output columns [256 h, 256 h + 256).  Up to 32 x 256 fp32 accumulators
   // per wave.
   constexpr bool PAIR = (DK == 512);
+  // V(t+1) loaded in the P V region of step t (see the step below)
+  constexpr bool VLATE = PAIR;
   static_assert(PAIR == (DV == 512), "head dim 512 only with DK == DV");
   constexpr int NW = 4, RBW = PAIR ? 2 : 4;  // 32-row blocks per workgroup
   constexpr int BM = RBW * kRowsPerWave, BN = tile_keys(DK), KB = BN / 32;
@@ -576,6 +588,21 @@ __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* ld
     }
   };
 
+  // K operand of S MFMA n: key block n % KB, d step n / KB; the XOR part of
+  // its address is a register, the rest an immediate
+  auto kx = [&](int n) { return kbase ^ (16 * ((n / KB) & 7)); };
+  auto kread_at = [&](const uint16_t* kl, int n, int x) {
+    return *(const uint4*)(kl + x + 16 * ((n / KB) & 8) + (n % KB) * 32 * LD);
+  };
+  // V^T operand of P V MFMA n: key half n / DB, column block n % DB; the
+  // XOR part of the address is a register, the rest an immediate
+  auto vx = [&](int n) { return vlane ^ (32 * (n % DB)); };
+  auto vread_at = [&](const uint16_t* vl, int n, int x) {
+    const uint16_t* va = vl + x + 16 * (n / DB) * LD;
+    const uint2 lo = read_tr(va), hi = read_tr(va + 8 * LD);
+    return make_uint4(lo.x, lo.y, hi.x, hi.y);
+  };
+
   // ---- interleaved regions: slot n issues MFMA n, the operand read for MFMA
   //      n + PF and a share of the other tile's vector work; the scheduling
   //      barriers keep that order.  With one wave per SIMD, instructions
@@ -584,17 +611,19 @@ __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* ld
   //      LDS read, fma -> exp -> sum, compare -> select -> max) is spread
   //      over consecutive slots instead.
   // S(t+1) = K(t+1) Q^T  ||  weights, sum and packing of tile t; also issues
-  // the direct loads of K(tk) into kdst and V(tv) into vdst
+  // the direct loads of K(tk) (and its bias tile) into kdst (bdst), and
+  // unless VLATE those of V(tv) into vdst
   auto qk_weights = [&](f32x16_t (&sn)[KB], const uint16_t* kl, f32x16_t (&sc)[KB],
                         uint4 (&pb)[KB * 2], const TileSrc& ksrc, uint16_t* kdst, const TileSrc& vsrc,
                         uint16_t* vdst, const i32x4_t& bsrc, uint16_t* bdst, const uint16_t* bl,
-                        uint2 (&bw)[KB * 4]) {
+                        uint2 (&bw)[KB * 4], uint4 (&a)[4]) {
     constexpr int PF = 4;
-    // the slots of K block group i, V block group i and bias block group i:
-    // spread evenly over the region, V half a spacing after K, bias one slot
-    // after K (two when runs are three slots long, so as not to share V's).
-    // When the slots divide evenly the tests are written as runs of LS slots
-    // (the form the compiler schedules best); otherwise slot by slot.
+    // the slots of K block group i, V block group i (unless VLATE) and bias
+    // block group i: spread evenly over the region, V half a spacing after
+    // K, bias one slot after K (two when runs are three slots long, so as
+    // not to share V's).  When the slots divide evenly the tests are written
+    // as runs of LS slots (the form the compiler schedules best); otherwise
+    // slot by slot.
     static_assert(NQK >= 2 * LOADS, "slot pattern");
     constexpr bool EVEN = NQK % LOADS == 0;
     constexpr int LS = NQK / LOADS, BSLOT = LS == 3 ? 2 : 1;
@@ -606,17 +635,11 @@ __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* ld
       for (int j = 0; j < 16; ++j) sn[kb][j] = 0.f;
     // K operand of MFMA n: key block n % KB, d step n / KB; the XOR part of
     // its address is a register, the rest an immediate
-    auto kx = [&](int n) { return kbase ^ (16 * ((n / KB) & 7)); };
-    auto kread = [&](int n, int x) {
-      return *(const uint4*)(kl + x + 16 * ((n / KB) & 8) + (n % KB) * 32 * LD);
-    };
+    auto kread = [&](int n, int x) { return kread_at(kl, n, x); };
     const float msc = (m_ref == -INFINITY) ? 0.f : m_ref * sl2;
     auto get = [&](int e) { return sc[e / 16][e % 16]; };
     auto set = [&](int e, float v) { sc[e / 16][e % 16] = v; };
     float psum = 0.f;
-    uint4 a[PF];
-#pragma unroll
-    for (int i = 0; i < PF; ++i) a[i] = kread(i, kx(i));
     int x_next = kx(PF);
     const unsigned m0 = m0_save();
     // weights in slot n: fma of the elements of slot n + 2, exp of those of
@@ -642,12 +665,12 @@ __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* ld
       // loads: K, V and bias block group i at slots kslot(i), vslot(i), bslot(i)
       if constexpr (EVEN) {
         if (n % LS == 0) load_blk(ksrc, kdst, n / LS, false);
-        if (n % LS == LS / 2) load_blk(vsrc, vdst, n / LS, true);
+        if (!VLATE && n % LS == LS / 2) load_blk(vsrc, vdst, n / LS, true);
       } else {
 #pragma unroll
         for (int i = 0; i < LOADS; ++i) {
           if (n == kslot(i)) load_blk(ksrc, kdst, i, false);
-          if (n == vslot(i)) load_blk(vsrc, vdst, i, true);
+          if (!VLATE && n == vslot(i)) load_blk(vsrc, vdst, i, true);
         }
       }
       if constexpr (BIAS) {
@@ -698,18 +721,17 @@ __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* ld
     asm volatile("" ::"v"(psum));
     return psum;
   };
-  // O += P(t) V(t)  ||  row max of S(t+1) (already masked)
+  // O += P(t) V(t)  ||  row max of S(t+1) (already masked); with VLATE also
+  // issues the direct loads of V(tv) into vdst, one block group every LSV
+  // slots
   auto pv_max = [&](const uint4 (&pb)[KB * 2], const uint16_t* vl, f32x16_t (&sn)[KB], bool live,
-                    const uint2 (&bw)[KB * 4]) {
+                    const uint2 (&bw)[KB * 4], const TileSrc& vsrc, uint16_t* vdst) {
     constexpr int PF = 4;
+    static_assert(NPV % LOADS == 0 && NPV >= LOADS, "V load slot pattern");
+    constexpr int LSV = NPV / LOADS;
     // V^T operand of MFMA n: key half n / DB, column block n % DB; the XOR
     // part of the address is a register, the rest an immediate
-    auto vx = [&](int n) { return vlane ^ (32 * (n % DB)); };
-    auto vread = [&](int n, int x) {
-      const uint16_t* va = vl + x + 16 * (n / DB) * LD;
-      const uint2 lo = read_tr(va), hi = read_tr(va + 8 * LD);
-      return make_uint4(lo.x, lo.y, hi.x, hi.y);
-    };
+    auto vread = [&](int n, int x) { return vread_at(vl, n, x); };
     auto get = [&](int e) { return sn[e / 16][e % 16]; };
     float mx = -INFINITY;
     // BIAS: the elements a slot's max takes get their bias one slot before
@@ -724,12 +746,14 @@ __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* ld
 #pragma unroll
     for (int i = 0; i < PF; ++i) bv[i] = vread(i, vx(i));
     int x_next = vx(PF);
+    const unsigned m0 = VLATE ? m0_save() : 0u;
 #pragma unroll
     for (int n = 0; n < NPV; ++n) {
       const uint4 cur_b = bv[n % PF];
       if (n + PF < NPV) bv[n % PF] = vread(n + PF, x_next);
       o[n % DB] = Elem<DT>::mfma(cur_b, pb[n / DB], o[n % DB]);
       if (n + PF + 1 < NPV) x_next = vx(n + PF + 1);
+      if (VLATE && n % LSV == LSV / 2) load_blk(vsrc, vdst, n / LSV, true);
       // the pairs (e - 1, e) whose odd element is one of this slot's
 #pragma unroll
       for (int e = ev(n); e < ev(n + 1); ++e)
@@ -737,6 +761,7 @@ __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* ld
       add_bias(n + 1);
       __builtin_amdgcn_sched_barrier(0);
     }
+    if constexpr (VLATE) m0_restore(m0);
     mx = pair_max(mx);
     // live == false: the scores were of no tile (the step after the last)
     const bool upd = live && (mx * sl2 > m_ref * sl2 + kRescaleLog2);
@@ -745,8 +770,15 @@ __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* ld
     return alpha;
   };
 
+  // Direct loads a VLATE step issues in its S region (K(t+2) and its bias
+  // tile) and in its P V region (V(t+1)); a wrapped ring issues two loads
+  // per block
+  constexpr int S_LOADS = LOADS * (RING ? 2 : 1) + BLOADS, PV_LOADS = LOADS * (RING ? 2 : 1);
+
   // D = 512: complete this wave's partial scores with the partner's (every
-  // wave of the workgroup passes the barrier; waves without rows only wait)
+  // wave of the workgroup passes the barrier; waves without rows only wait).
+  // The barrier also publishes V(t): each wave first waits for its own V(t)
+  // loads, the ones it issued before its S region's loads.
   auto exchange = [&](f32x16_t (&s)[KB], bool active) {
     if constexpr (PAIR) {
       if (active) {
@@ -755,6 +787,7 @@ __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* ld
           *(float4*)(xch + (wave * 4 + q4) * 256 + lane * 4) =
               make_float4(s[0][4 * q4 + 0], s[0][4 * q4 + 1], s[0][4 * q4 + 2], s[0][4 * q4 + 3]);
       }
+      if constexpr (VLATE) wait_vmem<S_LOADS>();
       __syncthreads();
       if (active) {
         const float* px = xch + (wave ^ 1) * 4 * 256 + lane * 4;
@@ -815,25 +848,38 @@ __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* ld
   // false).  Loads past the last tile reload the last tile into a buffer no
   // later step reads.
   // P = (t - t_first) & 1, a compile-time constant: K(t+1) is in K buffer
-  // 1 - P and V(t) in V buffer P; K(t+2) goes to K buffer P and V(t+1) to
-  // V buffer 1 - P.
+  // 1 - P and V(t) in V buffer P; K(t+2) goes to K buffer P (loaded in the S
+  // region) and V(t+1) to V buffer 1 - P.  Without VLATE V(t+1) is loaded in
+  // the S region too, and the barrier at the end of the step publishes
+  // both.  With VLATE (D = 512, whose steps already have a barrier between
+  // the regions, the pair exchange) V(t+1) is loaded in the P V region, and
+  // the exchange barrier of the next step publishes it: each load has a
+  // whole region to land in, and a tile's loads spread over both regions.
   auto step = [&](int t, f32x16_t (&sc)[KB], f32x16_t (&sn)[KB], auto parity) {
     constexpr int P = decltype(parity)::value;
     const bool has_next = t < t_last;
     const int tk = min(t + 2, t_last), tv = min(t + 1, t_last);
     uint4 pb[KB * 2];
-    // the rescale for tile t first (its factor is known since the last
-    // step), so that the interleaved regions are straight-line code
+    // the first K operands of the S region, then the rescale for tile t (its
+    // factor is known since the last step), so that the interleaved regions
+    // are straight-line code
+    const uint16_t* const kl = kbuf0 + (1 - P) * TILE;
+    uint4 a[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) a[i] = kread_at(kl, i, kx(i));
     rescale(alpha_cur);
     uint2 bw[KB * 4];
-    const float psum = qk_weights(sn, kbuf0 + (1 - P) * TILE, sc, pb, tile_src(kg, tk, false), kbuf0 + P * TILE,
-                                  tile_src(vg, tv, true), vbuf0 + (1 - P) * TILE, BIAS ? bias_src(tk) : i32x4_t{},
-                                  bbuf0 + P * BTILE, bbuf0 + (1 - P) * BTILE, bw);
-    exchange(sn, true);
+    const TileSrc vsrc = tile_src(vg, tv, true);
+    uint16_t* const vdst = vbuf0 + (1 - P) * TILE;
+    const float psum = qk_weights(sn, kl, sc, pb, tile_src(kg, tk, false), kbuf0 + P * TILE,
+                                  vsrc, vdst, BIAS ? bias_src(tk) : i32x4_t{}, bbuf0 + P * BTILE,
+                                  bbuf0 + (1 - P) * BTILE, bw, a);
+    exchange(sn, true);  // with VLATE also the V(t) barrier
     l_run = l_run * alpha_cur + psum;
     if (!full_tile(t + 1)) mask(sn, t + 1);
-    alpha_cur = pv_max(pb, vbuf0 + P * TILE, sn, has_next, bw);
-    __builtin_amdgcn_s_waitcnt(0);  // K(t+2), V(t+1) have landed
+    alpha_cur = pv_max(pb, vbuf0 + P * TILE, sn, has_next, bw, vsrc, vdst);
+    if constexpr (VLATE) wait_vmem<PV_LOADS>();  // K(t+2) (and its bias) have landed; V(t+1) may be in flight
+    else __builtin_amdgcn_s_waitcnt(0);          // K(t+2), V(t+1) have landed
     __syncthreads();
   };
 
@@ -842,18 +888,24 @@ __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* ld
       step(t, sA, sB, std::integral_constant<int, 0>{});
       if (t + 1 <= t_last) step(t + 1, sB, sA, std::integral_constant<int, 1>{});
     }
-  } else {  // no rows: this wave only loads its share of every tile
+  } else {  // no rows: this wave only loads its share of every tile and
+            // meets the same barriers
     for (int t = t_first; t <= t_last; ++t) {
       if (t + 2 <= t_last) {
         load_k(t + 2);
         load_b(t + 2);
       }
-      if (t < t_last) load_v(t + 1);
+      if constexpr (!VLATE)
+        if (t < t_last) load_v(t + 1);
       exchange(sA, false);
+      if constexpr (VLATE)
+        if (t < t_last) load_v(t + 1);
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
     }
   }
+  // no direct load may still be writing this workgroup's LDS when it ends
+  __builtin_amdgcn_s_waitcnt(0);
 
   // ---- epilogue ---------------------------------------------------------
   const float lsum = pair_sum(l_run);
@@ -1030,6 +1082,82 @@ __global__ __launch_bounds__(64 * kCombineWaves) void combine_kernel(AttnParams 
   }
 }
 
+// The same merge for calls of at most kCombineFew splits: one wave per row
+// (four rows per workgroup), every chunk load in flight at once.  The row's
+// chunks are taken in ascending order, and each product is rounded before
+// it is added, starting from +0: those are exactly the sums of
+// combine_kernel when each of its waves holds at most one of the row's
+// chunks, which is always the case when a call with one split more would
+// launch it (min(kCombineWaves, nsplit) waves).  So a row's bytes do not
+// depend on which of the two kernels merges it.
+constexpr int kCombineFew = 4;
+
+template <int DT, int D>
+__global__ __launch_bounds__(256) void combine_few_kernel(AttnParams p, size_t rows) {
+#pragma clang fp contract(off)  // every product rounded on its own, as described above
+  constexpr int PER = D / 64 >= 4 ? D / 64 : 4;
+  const int lane = threadIdx.x & 63;
+  const size_t row = (size_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const bool cols = lane * PER < D;
+  const int qi = (int)(row % (size_t)p.qL);
+  const int pos = p.q_offset + qi;
+  const int key_hi = p.causal ? min(pos, p.kL - 1) : p.kL - 1;
+  const int key_lo = p.window > 0 ? max(0, pos - p.window + 1) : 0;
+  const int c_lo = key_lo / p.split_len, c_hi = key_hi / p.split_len;
+  const float* ml = p.part_ml + row * p.nsplit * 2;
+  const float* po = p.part_o + row * (size_t)p.nsplit * D + lane * PER;
+
+  float mc[kCombineFew], lc[kCombineFew];
+  float4 x[kCombineFew][PER / 4];
+  float M = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < kCombineFew; ++i) {
+    const int c = c_lo + i;
+    mc[i] = -INFINITY;
+    lc[i] = 0.f;
+    if (c <= c_hi) {
+      mc[i] = ml[2 * c];
+      lc[i] = ml[2 * c + 1];
+      M = fmaxf(M, mc[i]);
+      if (cols) {
+#pragma unroll
+        for (int e = 0; e < PER / 4; ++e) x[i][e] = *(const float4*)(po + (size_t)c * D + 4 * e);
+      }
+    }
+  }
+  float acc[PER];
+#pragma unroll
+  for (int e = 0; e < PER; ++e) acc[e] = 0.f;
+  float L = 0.f;
+  if (M != -INFINITY) {
+#pragma unroll
+    for (int i = 0; i < kCombineFew; ++i) {
+      if (c_lo + i > c_hi) break;
+      const float w = (mc[i] == -INFINITY) ? 0.f : fast_exp2(mc[i] - M);
+      L = L + lc[i] * w;
+      if (!cols) continue;
+#pragma unroll
+      for (int e = 0; e < PER / 4; ++e) {
+        acc[4 * e + 0] = acc[4 * e + 0] + x[i][e].x * w;
+        acc[4 * e + 1] = acc[4 * e + 1] + x[i][e].y * w;
+        acc[4 * e + 2] = acc[4 * e + 2] + x[i][e].z * w;
+        acc[4 * e + 3] = acc[4 * e + 3] + x[i][e].w * w;
+      }
+    }
+  }
+  if (!cols) return;
+  const float inv = (L > 0.f) ? 1.0f / L : 0.f;
+  uint16_t* dst = p.out + row * D + lane * PER;
+#pragma unroll
+  for (int e = 0; e < PER; e += 4) {
+    uint2 o2;
+    o2.x = Elem<DT>::pack2(acc[e + 0] * inv, acc[e + 1] * inv);
+    o2.y = Elem<DT>::pack2(acc[e + 2] * inv, acc[e + 3] * inv);
+    *(uint2*)(dst + e) = o2;
+  }
+}
+
 template <int DT, int D, bool RING, bool BIAS>
 hipError_t launch_attention_t(const AttnParams& p, hipStream_t stream) {
   const dim3 grid((unsigned)(p.B * p.Hkv * p.mblocks), (unsigned)p.nsplit, 1);
@@ -1050,7 +1178,13 @@ hipError_t launch_attention_t(const AttnParams& p, hipStream_t stream) {
 
 template <int DT, int D>
 hipError_t launch_combine_t(const AttnParams& p, hipStream_t stream) {
-  const size_t total = (size_t)p.B * p.Hq * p.qL;  // one workgroup per output row
+  const size_t total = (size_t)p.B * p.Hq * p.qL;
+  if (p.nsplit <= kCombineFew) {  // one wave per output row
+    hipLaunchKernelGGL((combine_few_kernel<DT, D>), dim3((unsigned)((total + 3) / 4), 1, 1), dim3(256), 0, stream,
+                       p, total);
+    return hipGetLastError();
+  }
+  // one workgroup per output row
   const int nw = p.nsplit < kCombineWaves ? p.nsplit : kCombineWaves;
   hipLaunchKernelGGL((combine_kernel<DT, D>), dim3((unsigned)total, 1, 1), dim3(64 * nw), 0, stream, p);
   return hipGetLastError();

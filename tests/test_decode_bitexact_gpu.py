@@ -100,9 +100,11 @@ def test_verify_blocks_of_two_and_three(qL):
     _check_rows(q, k, v, window=0, what=f"qL{qL}")
 
 
-@pytest.mark.parametrize("kL", [1024, 1025, 1026, 1027, 2050, 3071, 4])
+@pytest.mark.parametrize("kL", [1024, 1025, 1026, 1027, 2050, 3071, 4, 4097, 4099])
 def test_rows_straddling_a_chunk_boundary(kL):
-    # the block's rows end on both sides of a multiple of the 1024-key chunk
+    # the block's rows end on both sides of a multiple of the 1024-key chunk;
+    # at 4097 and 4099 keys the block has 5 chunks and the first rows' own
+    # calls 4, which the merge takes with its few-split kernel
     q, k, v = W.random_qkv(60 + kL, 1, 4, 2, 4, kL, 256, FP16)
     _check_rows(q, k, v, window=0, what=f"kL{kL}")
     _check_rows(q, k, v, window=3, what=f"kL{kL} window 3")
