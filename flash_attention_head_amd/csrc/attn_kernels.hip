@@ -214,6 +214,11 @@ __device__ __forceinline__ void wait_vmem() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
+// K/V tiles of LDS per workgroup: 2 K + 3 V for the 256-wide LDS rows
+// (head dims 192 and 256) without a bias tile, else 2 + 2 (the narrower
+// rows keep two workgroups per CU within 256 registers)
+constexpr int kv_tiles(bool bias, int dk) { return (!bias && dk > 128 && dk != 512) ? 5 : 4; }
+
 // Lazy rescaling: a row's reference max moves only when a tile's max exceeds
 // it by more than this many binary orders of magnitude, so exp2 arguments stay
 // <= kRescaleLog2 (weights <= 256, well inside the fp16/bf16 range) and the
@@ -242,8 +247,10 @@ __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* ld
   // output columns [256 h, 256 h + 256).  Up to 32 x 256 fp32 accumulators
   // per wave.
   constexpr bool PAIR = (DK == 512);
-  // V(t+1) loaded in the P V region of step t (see the step below)
-  constexpr bool VLATE = PAIR;
+  // V3: a third V buffer; V loaded in the P V region (see the step below)
+  constexpr bool V3 = kv_tiles(BIAS, DK) == 5;
+  constexpr bool VLATE = PAIR || V3;
+  constexpr int NVB = V3 ? 3 : 2;
   static_assert(PAIR == (DV == 512), "head dim 512 only with DK == DV");
   constexpr int NW = 4, RBW = PAIR ? 2 : 4;  // 32-row blocks per workgroup
   constexpr int BM = RBW * kRowsPerWave, BN = tile_keys(DK), KB = BN / 32;
@@ -510,7 +517,7 @@ __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* ld
     else x = (float)__builtin_bit_cast(_Float16, (uint16_t)h);
     return x * inv_scale;
   };
-  auto load_v = [&](int t) { load_tile(vg, t, vbuf0 + ((t - t_first) & 1) * TILE, true); };
+  auto load_v = [&](int t) { load_tile(vg, t, vbuf0 + ((t - t_first) % NVB) * TILE, true); };
 
   // the keys row `pos` sees form one interval [key_lo, key_hi] (empty if
   // key_hi < key_lo)
@@ -787,7 +794,7 @@ __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* ld
           *(float4*)(xch + (wave * 4 + q4) * 256 + lane * 4) =
               make_float4(s[0][4 * q4 + 0], s[0][4 * q4 + 1], s[0][4 * q4 + 2], s[0][4 * q4 + 3]);
       }
-      if constexpr (VLATE) wait_vmem<S_LOADS>();
+      wait_vmem<S_LOADS>();
       __syncthreads();
       if (active) {
         const float* px = xch + (wave ^ 1) * 4 * 256 + lane * 4;
@@ -811,7 +818,7 @@ __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* ld
   // are masked to -inf.
   if ((t_last + 1) * BN > p.kL) {
     uint4* vz = (uint4*)vbuf0;
-    for (int i = tid; i < 2 * TILE / 8; i += NW * 64) vz[i] = make_uint4(0, 0, 0, 0);
+    for (int i = tid; i < NVB * TILE / 8; i += NW * 64) vz[i] = make_uint4(0, 0, 0, 0);
     __syncthreads();
   }
   load_k(t_first);
@@ -820,6 +827,7 @@ __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* ld
   if (t_first < t_last) {
     load_k(t_first + 1);
     load_b(t_first + 1);
+    if constexpr (V3) load_v(t_first + 1);
   }
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
@@ -848,17 +856,25 @@ __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* ld
   // false).  Loads past the last tile reload the last tile into a buffer no
   // later step reads.
   // P = (t - t_first) & 1, a compile-time constant: K(t+1) is in K buffer
-  // 1 - P and V(t) in V buffer P; K(t+2) goes to K buffer P (loaded in the S
-  // region) and V(t+1) to V buffer 1 - P.  Without VLATE V(t+1) is loaded in
-  // the S region too, and the barrier at the end of the step publishes
-  // both.  With VLATE (D = 512, whose steps already have a barrier between
-  // the regions, the pair exchange) V(t+1) is loaded in the P V region, and
-  // the exchange barrier of the next step publishes it: each load has a
-  // whole region to land in, and a tile's loads spread over both regions.
-  auto step = [&](int t, f32x16_t (&sc)[KB], f32x16_t (&sn)[KB], auto parity) {
-    constexpr int P = decltype(parity)::value;
+  // 1 - P; K(t+2) goes to K buffer P, loaded in the S region.  The V loads
+  // take one of three schedules (VLATE: in the P V region, so that each
+  // load has a whole region to land in and a tile's loads spread over both
+  // regions):
+  // - two V buffers (head dims up to 128, and bias instances): V(t) is in
+  //   V buffer P, V(t+1) is loaded into V buffer 1 - P in the S region, and
+  //   the barrier at the end of the step publishes it with K(t+2);
+  // - D = 512 (PAIR, VLATE), whose steps already have a barrier between the
+  //   regions, the pair exchange: V(t+1) is loaded into V buffer 1 - P in
+  //   the P V region, and the next step's exchange barrier publishes it;
+  // - three V buffers (V3, VLATE: D 192 and 256 without a bias): V(t) is in
+  //   V buffer VB = (t - t_first) % 3 (the steps come in sixes, so that it
+  //   is a compile-time constant too), and step t loads V(t+2) in its P V
+  //   region into the buffer V(t-1) held; the barrier at the end of step
+  //   t+1 publishes it, with no barrier between the regions.
+  auto step = [&](int t, f32x16_t (&sc)[KB], f32x16_t (&sn)[KB], auto parity, auto vbuf) {
+    constexpr int P = decltype(parity)::value, VB = decltype(vbuf)::value;
     const bool has_next = t < t_last;
-    const int tk = min(t + 2, t_last), tv = min(t + 1, t_last);
+    const int tk = min(t + 2, t_last), tv = min(t + (V3 ? 2 : 1), t_last);
     uint4 pb[KB * 2];
     // the first K operands of the S region, then the rescale for tile t (its
     // factor is known since the last step), so that the interleaved regions
@@ -870,23 +886,44 @@ __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* ld
     rescale(alpha_cur);
     uint2 bw[KB * 4];
     const TileSrc vsrc = tile_src(vg, tv, true);
-    uint16_t* const vdst = vbuf0 + (1 - P) * TILE;
+    uint16_t* const vdst = vbuf0 + (V3 ? (VB + 2) % 3 : 1 - P) * TILE;
     const float psum = qk_weights(sn, kl, sc, pb, tile_src(kg, tk, false), kbuf0 + P * TILE,
                                   vsrc, vdst, BIAS ? bias_src(tk) : i32x4_t{}, bbuf0 + P * BTILE,
                                   bbuf0 + (1 - P) * BTILE, bw, a);
-    exchange(sn, true);  // with VLATE also the V(t) barrier
+    exchange(sn, true);  // D = 512: also the V(t) barrier
     l_run = l_run * alpha_cur + psum;
     if (!full_tile(t + 1)) mask(sn, t + 1);
-    alpha_cur = pv_max(pb, vbuf0 + P * TILE, sn, has_next, bw, vsrc, vdst);
-    if constexpr (VLATE) wait_vmem<PV_LOADS>();  // K(t+2) (and its bias) have landed; V(t+1) may be in flight
-    else __builtin_amdgcn_s_waitcnt(0);          // K(t+2), V(t+1) have landed
+    alpha_cur = pv_max(pb, vbuf0 + (V3 ? VB : P) * TILE, sn, has_next, bw, vsrc, vdst);
+    // VLATE: K(t+2) (and its bias) have landed, and with V3 V(t+1) too; the
+    // V loads of this step may be in flight.  Otherwise everything has.
+    if constexpr (VLATE) wait_vmem<PV_LOADS>();
+    else __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   };
 
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
   if (wave_active) {
-    for (int t = t_first; t <= t_last; t += 2) {
-      step(t, sA, sB, std::integral_constant<int, 0>{});
-      if (t + 1 <= t_last) step(t + 1, sB, sA, std::integral_constant<int, 1>{});
+    if constexpr (V3) {
+      for (int t = t_first; t <= t_last; t += 6) {
+        step(t, sA, sB, I0{}, I0{});
+        if (t + 1 > t_last) break;
+        step(t + 1, sB, sA, I1{}, I1{});
+        if (t + 2 > t_last) break;
+        step(t + 2, sA, sB, I0{}, I2{});
+        if (t + 3 > t_last) break;
+        step(t + 3, sB, sA, I1{}, I0{});
+        if (t + 4 > t_last) break;
+        step(t + 4, sA, sB, I0{}, I1{});
+        if (t + 5 > t_last) break;
+        step(t + 5, sB, sA, I1{}, I2{});
+      }
+    } else {
+      for (int t = t_first; t <= t_last; t += 2) {
+        step(t, sA, sB, I0{}, I0{});
+        if (t + 1 <= t_last) step(t + 1, sB, sA, I1{}, I0{});
+      }
     }
   } else {  // no rows: this wave only loads its share of every tile and
             // meets the same barriers
@@ -894,11 +931,12 @@ __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* ld
       if (t + 2 <= t_last) {
         load_k(t + 2);
         load_b(t + 2);
+        if constexpr (V3) load_v(t + 2);
       }
       if constexpr (!VLATE)
         if (t < t_last) load_v(t + 1);
       exchange(sA, false);
-      if constexpr (VLATE)
+      if constexpr (PAIR)
         if (t < t_last) load_v(t + 1);
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
@@ -950,38 +988,38 @@ __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* ld
 template <int DT, bool RING, bool BIAS>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void attn_tile_kernel_d64(AttnParams p) {
-  __shared__ __attribute__((aligned(16))) uint16_t lds[4 * 64 * 128 + (BIAS ? 2 * 128 * 64 : 0)];
+  __shared__ __attribute__((aligned(16))) uint16_t lds[kv_tiles(BIAS, 64) * 64 * 128 + (BIAS ? 2 * 128 * 64 : 0)];
   attn_pipe_body<DT, 64, 64, RING, BIAS>(p, lds);
 }
 template <int DT, bool RING, bool BIAS>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void attn_tile_kernel_d80(AttnParams p) {
-  __shared__ __attribute__((aligned(16))) uint16_t lds[4 * 64 * 128 + (BIAS ? 2 * 128 * 64 : 0)];
+  __shared__ __attribute__((aligned(16))) uint16_t lds[kv_tiles(BIAS, 80) * 64 * 128 + (BIAS ? 2 * 128 * 64 : 0)];
   attn_pipe_body<DT, 80, 80, RING, BIAS>(p, lds);
 }
 template <int DT, bool RING, bool BIAS>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void attn_tile_kernel_d128(AttnParams p) {
-  __shared__ __attribute__((aligned(16))) uint16_t lds[4 * 64 * 128 + (BIAS ? 2 * 128 * 64 : 0)];
+  __shared__ __attribute__((aligned(16))) uint16_t lds[kv_tiles(BIAS, 128) * 64 * 128 + (BIAS ? 2 * 128 * 64 : 0)];
   attn_pipe_body<DT, 128, 128, RING, BIAS>(p, lds);
 }
 template <int DT, bool RING, bool BIAS>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void attn_tile_kernel_d192(AttnParams p) {
-  __shared__ __attribute__((aligned(16))) uint16_t lds[4 * 64 * 256 + (BIAS ? 2 * 128 * 64 : 0)];
+  __shared__ __attribute__((aligned(16))) uint16_t lds[kv_tiles(BIAS, 192) * 64 * 256 + (BIAS ? 2 * 128 * 64 : 0)];
   attn_pipe_body<DT, 192, 192, RING, BIAS>(p, lds);
 }
 // q and k of head dim 192, v and out of 256 (no ring or bias instances)
 template <int DT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void attn_tile_kernel_dk192_dv256(AttnParams p) {
-  __shared__ __attribute__((aligned(16))) uint16_t lds[4 * 64 * 256];
+  __shared__ __attribute__((aligned(16))) uint16_t lds[kv_tiles(false, 192) * 64 * 256];
   attn_pipe_body<DT, 192, 256, false, false>(p, lds);
 }
 template <int DT, bool RING, bool BIAS>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void attn_tile_kernel_d256(AttnParams p) {
-  __shared__ __attribute__((aligned(16))) uint16_t lds[4 * 64 * 256 + (BIAS ? 2 * 128 * 64 : 0)];
+  __shared__ __attribute__((aligned(16))) uint16_t lds[kv_tiles(BIAS, 256) * 64 * 256 + (BIAS ? 2 * 128 * 64 : 0)];
   attn_pipe_body<DT, 256, 256, RING, BIAS>(p, lds);
 }
 template <int DT, bool RING, bool BIAS>
