@@ -130,6 +130,38 @@ def measured_traffic(wl_name):
         return None
 
 
+def read_reference(nbytes=1 << 30, steps=10):
+    """Plain streaming kernels over nbytes, the context for the decode lines' HBM rate (the
+    same bytes as their K and V): torch's sum over the buffer as bf16 and as fp32 (reads
+    only), and a device-to-device copy of it (its read and written bytes both counted)."""
+    import torch
+
+    x = torch.ones(nbytes // 2, dtype=torch.bfloat16, device="cuda")
+    y = torch.empty_like(x)
+
+    def rate(fn, moved):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(steps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b) / steps
+        gbs = moved / (ms * 1e-3) / 1e9
+        return {"gbs": round(gbs, 1), "frac": round(gbs / PEAK_HBM_GBS, 4), "ms": round(ms, 4)}
+
+    out = {"sum_bf16": rate(lambda: x.sum(), nbytes),
+           "sum_fp32": rate(lambda: x.view(torch.float32).sum(), nbytes),
+           "copy": rate(lambda: y.copy_(x), 2 * nbytes),
+           "bytes": nbytes}
+    del x, y
+    torch.cuda.empty_cache()
+    return out
+
+
 def cpu_baseline(wl, target_s=15.0):
     """The fp64 oracle on a bounded, seeded sample of the workload's rows."""
     import numpy as np
@@ -220,6 +252,12 @@ def main():
             extra[name] = summarize(w2, t2)
             log(f"[bench] {name}: {extra[name]}")
 
+    read_ref = None
+    if args.extra:
+        log("[bench] plain streaming read (context for the decode lines)")
+        read_ref = read_reference()
+        log(f"[bench] read reference: {read_ref}")
+
     base = None
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (oracle on a row sample)")
@@ -251,6 +289,7 @@ def main():
                                "sdpa_forward call, HIP events on its stream"},
         "cpu_baseline": base,
         "extra": extra,
+        "hbm_read_reference": read_ref,
     }
     print(json.dumps(line), flush=True)
 

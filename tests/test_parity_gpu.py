@@ -66,6 +66,26 @@ SMALL = [
 ]
 
 
+@pytest.mark.parametrize("D", [256, 192])
+@pytest.mark.parametrize("ntile", list(range(1, 14)))
+def test_every_tile_count_of_the_step_loop(D, ntile):
+    # head dims 192 and 256 run their 64-key tiles in steps of six (K buffer
+    # t mod 2, V buffer t mod 3): 1..13 tiles end the loop after every step
+    # position and start every V buffer phase; the last tile is ragged
+    kL = 64 * ntile - 13 if ntile > 1 else 40
+    q, k, v = W.random_qkv(3000 + 20 * ntile + D, 1, 4, 2, 70, kL, D, BF16 if ntile % 2 else FP16)
+    dtype = BF16 if ntile % 2 else FP16
+    scale = float(np.float32(1.0 / np.sqrt(D)))
+    for causal, window in [(False, 0), (True, 100)]:
+        if causal and kL < 70:
+            continue  # a causal block needs as many keys as rows
+        qo = kL - 70 if causal else 0
+        note(f"step loop D{D} tiles {ntile} kL {kL} causal {causal}")
+        got = f64(run_gpu(q, k, v, causal=causal, window=window, q_offset=qo))
+        ref = oracle_full(q, k, v, scale=scale, causal=causal, window=window, q_offset=qo, dtype=dtype)
+        check_close(got, ref, dtype, f"step loop D{D} tiles {ntile} causal {causal}")
+
+
 @pytest.mark.parametrize("case", SMALL, ids=[f"B{c[0]}Hq{c[1]}Hkv{c[2]}q{c[3]}k{c[4]}D{c[5]}"
                                              f"{'bf16' if c[6] else 'f16'}c{int(c[7])}w{c[8]}"
                                              for c in SMALL])
