@@ -143,6 +143,35 @@ def random_qkv(seed: int, B: int, Hq: int, Hkv: int, qL: int, kL: int, D: int, d
     return q, k, v
 
 
+def random_q4kv(seed: int, B: int, Hkv: int, kL: int, D: int, dtype: int):
+    """Seeded 4-bit K and V rows: (kq, ks, kb, vq, vs, vb).
+
+    kq, vq [B, Hkv, kL, D / 8] int32: code words of uniformly random bits (eight
+    4-bit codes each).  ks, vs, kb, vb [B, Hkv, kL, D / 64] in the dtype: a
+    scale drawn from U(0.3, 0.5) and a bias of -7.5 * scale + N(0, 0.1) per
+    group of 64 elements, so that a group spans about [-3, 3], the range of
+    N(0, 1) values quantized 64 at a time.  Holds none of the attention or
+    dequantization arithmetic.
+    """
+    if D % 64:
+        raise ValueError("4-bit rows need D to be a multiple of 64")
+    g = torch.Generator(device="cpu")
+    g.manual_seed(seed)
+    dt = TORCH_DTYPES[dtype]
+    out = []
+    for _ in range(2):
+        words = torch.randint(-(1 << 31), 1 << 31, (B, Hkv, kL, D // 8), generator=g, dtype=torch.int64)
+        sc = torch.rand((B, Hkv, kL, D // 64), generator=g, dtype=torch.float32) * 0.2 + 0.3
+        bi = -7.5 * sc + 0.1 * torch.randn((B, Hkv, kL, D // 64), generator=g, dtype=torch.float32)
+        out += [words.to(torch.int32), sc.to(dt), bi.to(dt)]
+    return tuple(out)
+
+
+def words(t: torch.Tensor) -> np.ndarray:
+    """uint32 views of a CPU int32 tensor of 4-bit code words."""
+    return t.contiguous().numpy().view(np.uint32)
+
+
 def bits(t: torch.Tensor) -> np.ndarray:
     """uint16 bit patterns of a CPU fp16/bf16 tensor (no copy of values)."""
     return t.contiguous().view(torch.int16).numpy().view(np.uint16)

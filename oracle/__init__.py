@@ -85,6 +85,13 @@ def load(path: str = _LIB):
     lib.oracle_sdpa_dv_f64.restype = ci
     lib.oracle_widen.argtypes = [u16p, f64p, ctypes.c_int64, ci]
     lib.oracle_widen.restype = None
+    u32p = ctypes.POINTER(ctypes.c_uint32)
+    lib.oracle_sdpa_q4kv_f64.argtypes = (
+        [u16p, u32p, u16p, u16p, u32p, u16p, u16p, f64p] + [ci] * 6 + [ctypes.c_float] + [ci] * 4 + [i64p, i64, ci]
+    )
+    lib.oracle_sdpa_q4kv_f64.restype = ci
+    lib.oracle_dequant4.argtypes = [u32p, u16p, u16p, f64p, i64, ci, ci]
+    lib.oracle_dequant4.restype = None
     if path == _LIB:
         _lib = lib
     return lib
@@ -235,4 +242,68 @@ def sdpa_dv_f64(q, k, v, *, scale: float, causal: bool = False, window: int = 0,
     )
     if rc != 0:
         raise RuntimeError(f"oracle_sdpa_dv_f64 failed ({rc})")
+    return out
+
+
+def _words(a: np.ndarray) -> np.ndarray:
+    a = np.ascontiguousarray(a)
+    if a.dtype not in (np.uint32, np.int32):
+        raise TypeError("4-bit codes are packed in 32-bit words (uint32 arrays)")
+    return a.view(np.uint32)
+
+
+def dequant4_f64(codes, scales, biases, *, D: int, dtype: int = FP16, lib=None) -> np.ndarray:
+    """The values of 4-bit rows: codes [..., D / 8] words, scales and biases [..., D / 64]
+    (uint16 bit patterns of the dtype); returns [..., D] float64."""
+    lib = lib or load()
+    codes, scales, biases = _words(codes), _bits(scales), _bits(biases)
+    if D % 64 or codes.shape[-1] != D // 8 or scales.shape[-1] != D // 64 or biases.shape != scales.shape:
+        raise ValueError("4-bit rows: codes [..., D/8], scales and biases [..., D/64], D a multiple of 64")
+    n = codes.size // (D // 8)
+    if scales.size != n * (D // 64):
+        raise ValueError("codes and scales describe different row counts")
+    out = np.empty(codes.shape[:-1] + (D,), dtype=np.float64)
+    lib.oracle_dequant4(_ptr(codes, ctypes.c_uint32), _ptr(scales, ctypes.c_uint16), _ptr(biases, ctypes.c_uint16),
+                        _ptr(out, ctypes.c_double), n, D, int(dtype))
+    return out
+
+
+def sdpa_q4kv_f64(q, kq, ks, kb, vq, vs, vb, *, scale: float, causal: bool = False, window: int = 0,
+                  q_offset: int = 0, dtype: int = FP16, rows=None, threads: int | None = None,
+                  lib=None) -> np.ndarray:
+    """Output rows with 4-bit K and V.
+
+    q [B, Hq, qL, D] (uint16 bit patterns); kq, vq [B, Hkv, kL, D / 8] uint32 code words;
+    ks, kb, vs, vb [B, Hkv, kL, D / 64] scales and biases (uint16 bit patterns of the dtype).
+    rows=None: every row, [B, Hq, qL, D]; else the flat rows (b*Hq + hq)*qL + i, [len(rows), D].
+    """
+    lib = lib or load()
+    q = _bits(q)
+    kq, vq = _words(kq), _words(vq)
+    ks, kb, vs, vb = _bits(ks), _bits(kb), _bits(vs), _bits(vb)
+    if q.ndim != 4 or kq.ndim != 4:
+        raise ValueError("q and the code words must be [B, H, L, ...]")
+    B, Hq, qL, D = q.shape
+    Bk, Hkv, kL, W = kq.shape
+    if Bk != B or W * 8 != D or D % 64 or vq.shape != kq.shape:
+        raise ValueError("shape mismatch between q and the 4-bit K/V")
+    for a in (ks, kb, vs, vb):
+        if a.shape != (B, Hkv, kL, D // 64):
+            raise ValueError("scales and biases must be [B, Hkv, kL, D / 64]")
+    if rows is None:
+        out = np.empty((B, Hq, qL, D), dtype=np.float64)
+        rptr, nrows = None, 0
+    else:
+        rows = np.ascontiguousarray(rows, dtype=np.int64)
+        out = np.empty((rows.size, D), dtype=np.float64)
+        rptr, nrows = _ptr(rows, ctypes.c_int64), rows.size
+    rc = lib.oracle_sdpa_q4kv_f64(
+        _ptr(q, ctypes.c_uint16), _ptr(kq, ctypes.c_uint32), _ptr(ks, ctypes.c_uint16), _ptr(kb, ctypes.c_uint16),
+        _ptr(vq, ctypes.c_uint32), _ptr(vs, ctypes.c_uint16), _ptr(vb, ctypes.c_uint16),
+        _ptr(out, ctypes.c_double), B, Hq, Hkv, qL, kL, D, float(np.float32(scale)),
+        int(bool(causal)), int(window), int(q_offset), int(dtype), rptr, nrows,
+        int(threads or default_threads()),
+    )
+    if rc != 0:
+        raise RuntimeError(f"oracle_sdpa_q4kv_f64 failed ({rc})")
     return out

@@ -53,7 +53,17 @@
  *     Q=192/K=192/V=256 heads named in the review discussion of mlx PR
  *     #3293): the scores take the D-long dot products, the output row is the
  *     weighted sum of the Dv-long value rows, V is [B, Hkv, kL, Dv] and the
- *     output [B, Hq, qL, Dv].
+ *     output [B, Hq, qL, Dv];
+ *   - K and V may instead be 4-bit quantized (the prefix KV cache kept 4-bit
+ *     at rest in the End-to-end section of mlx PR #3660; the pages give no
+ *     format, so the affine, group-64 form that mlxcel issue #2160 names for
+ *     its checkpoints is read as the plain one): the head dim of each key and
+ *     value row splits into groups of 64 consecutive elements, each with a
+ *     scale and a bias in the input dtype, and element d of a row is
+ *     scale[d / 64] * c_d + bias[d / 64] with its 4-bit code c_d in 0..15.
+ *     The codes of a row are packed eight to a 32-bit word, element 8w + n
+ *     in bits 4n .. 4n + 3 of word w.  The oracle dequantizes each element in
+ *     double and runs the same three passes on those values.
  */
 #include <math.h>
 #include <pthread.h>
@@ -93,12 +103,36 @@ static double widen(uint16_t h, int dtype) {
 
 typedef struct {
   const uint16_t *q, *k, *v;
+  /* 4-bit K and V (NULL: k and v hold the fp16/bf16 rows): codes [B, Hkv,
+   * kL, D / 8] words, scales and biases [B, Hkv, kL, D / 64] */
+  const uint32_t *kq, *vq;
+  const uint16_t *ks, *kb, *vs, *vb;
   const uint16_t *bias; /* NULL: none */
   int64_t bias_sb, bias_sh, bias_sq;
   int B, Hq, Hkv, qL, kL, D, Dv; /* D: q and k rows; Dv: v and output rows */
   double scale;
   int causal, window, q_offset, dtype;
 } problem_t;
+
+/* Element d of a 4-bit row: its code, times its group's scale, plus the
+ * group's bias.  `row` is the row's index among all [B, Hkv, kL] rows. */
+static double dequant4(const uint32_t *codes, const uint16_t *scales, const uint16_t *biases,
+                       long row, long D, long d, int dtype) {
+  const uint32_t word = codes[row * (D / 8) + d / 8];
+  const unsigned c = (word >> (4 * (d % 8))) & 0xfu;
+  const long g = row * (D / 64) + d / 64;
+  return widen(scales[g], dtype) * (double)c + widen(biases[g], dtype);
+}
+
+/* Element d of key row / value row `row` (an index among all [B, Hkv, kL] rows). */
+static double key_elem(const problem_t *pr, long row, long d) {
+  if (pr->kq) return dequant4(pr->kq, pr->ks, pr->kb, row, pr->D, d, pr->dtype);
+  return widen(pr->k[row * pr->D + d], pr->dtype);
+}
+static double value_elem(const problem_t *pr, long row, long d) {
+  if (pr->vq) return dequant4(pr->vq, pr->vs, pr->vb, row, pr->Dv, d, pr->dtype);
+  return widen(pr->v[row * pr->Dv + d], pr->dtype);
+}
 
 /* Is key j visible from absolute query position p? */
 static int key_visible(const problem_t *pr, long p, long j) {
@@ -122,8 +156,7 @@ static void attend_row(const problem_t *pr, long row, double *s, double *o) {
   const long p = (long)pr->q_offset + i;
 
   const uint16_t *qrow = pr->q + row * D;
-  const uint16_t *kbase = pr->k + (b * pr->Hkv + hk) * (long)pr->kL * D;
-  const uint16_t *vbase = pr->v + (b * pr->Hkv + hk) * (long)pr->kL * Dv;
+  const long kvrow0 = (b * pr->Hkv + hk) * (long)pr->kL; /* the head's first K/V row */
 
   double *qd = s + pr->kL; /* the widened query row */
   for (long d = 0; d < D; ++d) qd[d] = widen(qrow[d], pr->dtype);
@@ -135,9 +168,8 @@ static void attend_row(const problem_t *pr, long row, double *s, double *o) {
   double m = -INFINITY;
   for (long j = 0; j < pr->kL; ++j) {
     if (!key_visible(pr, p, j)) continue;
-    const uint16_t *krow = kbase + j * D;
     double dot = 0.0;
-    for (long d = 0; d < D; ++d) dot += qd[d] * widen(krow[d], pr->dtype);
+    for (long d = 0; d < D; ++d) dot += qd[d] * key_elem(pr, kvrow0 + j, d);
     s[j] = pr->scale * dot;
     if (brow) s[j] += widen(brow[j], pr->dtype);
     if (s[j] == -INFINITY) continue;
@@ -158,8 +190,7 @@ static void attend_row(const problem_t *pr, long row, double *s, double *o) {
   /* pass 3: weighted sum of value rows, then normalise */
   for (long j = 0; j < pr->kL; ++j) {
     if (!key_visible(pr, p, j) || s[j] == -INFINITY) continue;
-    const uint16_t *vrow = vbase + j * Dv;
-    for (long d = 0; d < Dv; ++d) o[d] += s[j] * widen(vrow[d], pr->dtype);
+    for (long d = 0; d < Dv; ++d) o[d] += s[j] * value_elem(pr, kvrow0 + j, d);
   }
   for (long d = 0; d < Dv; ++d) o[d] /= l;
 }
@@ -227,6 +258,8 @@ static int make_problem(problem_t *pr, const uint16_t *q, const uint16_t *k, con
   pr->q = q;
   pr->k = k;
   pr->v = v;
+  pr->kq = pr->vq = NULL;
+  pr->ks = pr->kb = pr->vs = pr->vb = NULL;
   pr->bias = NULL;
   pr->bias_sb = pr->bias_sh = pr->bias_sq = 0;
   pr->B = B;
@@ -320,6 +353,44 @@ int oracle_sdpa_dv_f64(const uint16_t *q, const uint16_t *k, const uint16_t *v, 
     if (rows[n] < 0 || rows[n] >= total) return -1;
   if (nrows <= 0) return nrows == 0 ? 0 : -1;
   return run(&pr, rows, nrows, out, nthreads);
+}
+
+/*
+ * 4-bit K and V: kq/vq hold the codes [B, Hkv, kL, D / 8] (32-bit words),
+ * ks/kb and vs/vb the scales and biases [B, Hkv, kL, D / 64] in the input
+ * dtype; D must be a multiple of 64.
+ * rows == NULL: every row, out [B, Hq, qL, D]; else out is [nrows, D].
+ */
+int oracle_sdpa_q4kv_f64(const uint16_t *q, const uint32_t *kq, const uint16_t *ks,
+                         const uint16_t *kb, const uint32_t *vq, const uint16_t *vs,
+                         const uint16_t *vb, double *out, int B, int Hq, int Hkv, int qL, int kL,
+                         int D, float scale, int causal, int window, int q_offset, int dtype,
+                         const int64_t *rows, int64_t nrows, int nthreads) {
+  problem_t pr;
+  /* k and v are not read: the quantized rows stand for them */
+  if (!out || !kq || !ks || !kb || !vq || !vs || !vb || D % 64 != 0 ||
+      make_problem(&pr, q, ks, vs, B, Hq, Hkv, qL, kL, D, scale, causal, window, q_offset, dtype))
+    return -1;
+  pr.kq = kq;
+  pr.ks = ks;
+  pr.kb = kb;
+  pr.vq = vq;
+  pr.vs = vs;
+  pr.vb = vb;
+  if (!rows) return run(&pr, NULL, (int64_t)B * Hq * qL, out, nthreads);
+  const int64_t total = (int64_t)B * Hq * qL;
+  for (int64_t n = 0; n < nrows; ++n)
+    if (rows[n] < 0 || rows[n] >= total) return -1;
+  if (nrows <= 0) return nrows == 0 ? 0 : -1;
+  return run(&pr, rows, nrows, out, nthreads);
+}
+
+/* The dequantized values of n 4-bit rows of D elements (out [n, D]), for the
+ * tests of the format itself. */
+void oracle_dequant4(const uint32_t *codes, const uint16_t *scales, const uint16_t *biases,
+                     double *out, int64_t n, int D, int dtype) {
+  for (int64_t r = 0; r < n; ++r)
+    for (long d = 0; d < D; ++d) out[r * D + d] = dequant4(codes, scales, biases, (long)r, D, d, dtype);
 }
 
 /* Exact widening exposed for the tests of the input decoding itself. */

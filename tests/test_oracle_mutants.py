@@ -26,24 +26,33 @@ MUTANTS = {
     "exp_sign_flipped": ("s[j] = exp(s[j] - m);", "s[j] = exp(m - s[j]);"),
     "no_normalisation": ("for (long d = 0; d < Dv; ++d) o[d] /= l;", "(void)l;"),
     "q_offset_ignored": ("const long p = (long)pr->q_offset + i;", "const long p = i;"),
-    "k_and_v_swapped_in_scores": ("const uint16_t *krow = kbase + j * D;",
-                                  "const uint16_t *krow = vbase + j * D;"),
-    "v_batch_offset_dropped": ("const uint16_t *vbase = pr->v + (b * pr->Hkv + hk) * (long)pr->kL * Dv;",
-                               "const uint16_t *vbase = pr->v + (hk) * (long)pr->kL * Dv;"),
+    "k_and_v_swapped_in_scores": ("dot += qd[d] * key_elem(pr, kvrow0 + j, d);",
+                                  "dot += qd[d] * value_elem(pr, kvrow0 + j, d);"),
+    "v_batch_offset_dropped": ("return widen(pr->v[row * pr->Dv + d], pr->dtype);",
+                               "return widen(pr->v[(row % ((long)pr->Hkv * pr->kL)) * pr->Dv + d], pr->dtype);"),
     "fp16_exponent_bias": ("expo - 25", "expo - 24"),
     "bf16_widened_as_fp16": ("return dtype == ORACLE_BF16 ? widen_bf16(h) : widen_fp16(h);",
                              "return widen_fp16(h);"),
     "max_over_first_key_only": ("if (!any || s[j] > m) m = s[j];", "if (!any) m = s[j];"),
-    "last_visible_key_skipped": ("    if (!key_visible(pr, p, j) || s[j] == -INFINITY) continue;\n    const uint16_t *vrow",
-                                 "    if (!key_visible(pr, p, j) || s[j] == -INFINITY || !key_visible(pr, p, j + 1)) continue;\n    const uint16_t *vrow"),
+    "last_visible_key_skipped": ("    if (!key_visible(pr, p, j) || s[j] == -INFINITY) continue;\n    for (long d = 0; d < Dv; ++d) o[d] +=",
+                                 "    if (!key_visible(pr, p, j) || s[j] == -INFINITY || !key_visible(pr, p, j + 1)) continue;\n    for (long d = 0; d < Dv; ++d) o[d] +="),
     "bias_ignored": ("if (brow) s[j] += widen(brow[j], pr->dtype);", "(void)brow;"),
     "bias_subtracted": ("if (brow) s[j] += widen(brow[j], pr->dtype);", "if (brow) s[j] -= widen(brow[j], pr->dtype);"),
     "bias_head_stride_dropped": ("hq * pr->bias_sh", "0 * pr->bias_sh"),
     "bias_row_stride_dropped": ("i * pr->bias_sq", "0 * pr->bias_sq"),
-    "v_head_stride_uses_d": ("(b * pr->Hkv + hk) * (long)pr->kL * Dv;", "(b * pr->Hkv + hk) * (long)pr->kL * D;"),
-    "v_row_stride_uses_d": ("const uint16_t *vrow = vbase + j * Dv;", "const uint16_t *vrow = vbase + j * D;"),
+    "v_head_stride_uses_d": ("return widen(pr->v[row * pr->Dv + d], pr->dtype);",
+                             "return widen(pr->v[(row / pr->kL) * pr->kL * pr->D + (row % pr->kL) * pr->Dv + d], pr->dtype);"),
+    "v_row_stride_uses_d": ("return widen(pr->v[row * pr->Dv + d], pr->dtype);",
+                            "return widen(pr->v[row * pr->D + d], pr->dtype);"),
     "value_columns_cut_at_d": ("for (long d = 0; d < Dv; ++d) o[d] += s[j]", "for (long d = 0; d < D; ++d) o[d] += s[j]"),
     "minus_inf_bias_not_excluded": ("    if (s[j] == -INFINITY) continue;\n    if (!any", "    if (!any"),
+    "q4_nibble_order_reversed": ("(word >> (4 * (d % 8)))", "(word >> (4 * (7 - d % 8)))"),
+    "q4_groups_of_32": ("const long g = row * (D / 64) + d / 64;", "const long g = row * (D / 64) + (d / 32) % (D / 64);"),
+    "q4_scale_and_bias_swapped": ("return widen(scales[g], dtype) * (double)c + widen(biases[g], dtype);",
+                                  "return widen(biases[g], dtype) * (double)c + widen(scales[g], dtype);"),
+    "q4_signed_codes": ("widen(scales[g], dtype) * (double)c", "widen(scales[g], dtype) * ((double)c - 8.0)"),
+    "q4_v_takes_k_scales": ("dequant4(pr->vq, pr->vs, pr->vb,", "dequant4(pr->vq, pr->ks, pr->kb,"),
+    "q4_word_ignores_the_row": ("codes[row * (D / 8) + d / 8]", "codes[d / 8]"),
 }
 
 

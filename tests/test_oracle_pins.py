@@ -420,3 +420,101 @@ def test_value_dim_row_selection_equals_the_full_call(oracle_lib):
     rows = np.array([0, 7, 19, 33, 39], dtype=np.int64)
     sel = oracle.sdpa_dv_f64(q, k, v, scale=0.3, causal=True, q_offset=4, dtype=BF16, rows=rows, threads=2)
     assert np.array_equal(sel, full.reshape(-1, 9)[rows])
+
+
+# ------------------------------------------------------------ 4-bit K / V --
+# Affine 4-bit rows (the reading of the 4-bit-at-rest prefix KV cache of
+# ml-explore/mlx PR #3660, End-to-end section, in the affine group-64 form
+# that lablup/mlxcel issue #2160 names): element d of a row is
+# scale[d // 64] * code_d + bias[d // 64]; the codes are packed eight to a
+# 32-bit word, element 8w + n in bits 4n .. 4n + 3 of word w.  The expected
+# values below are worked out by hand from that definition.
+
+def _u16(values, dtype):
+    return _np_bits(np.asarray(values, dtype=np.float32), dtype)
+
+
+def test_dequant4_golden_words(oracle_lib):
+    # one group of 64: scale 0.5, bias -1, so code c gives c / 2 - 1
+    words = np.array([[0x76543210, 0xFEDCBA98, 0x00000000, 0xFFFFFFFF,
+                       0x0000000F, 0xF0000000, 0x12345678, 0x89ABCDEF]], dtype=np.uint32)
+    got = oracle.dequant4_f64(words, _u16([0.5], BF16), _u16([-1.0], BF16), D=64, dtype=BF16)
+    expect = ([-1.0, -0.5, 0.0, 0.5, 1.0, 1.5, 2.0, 2.5]
+              + [3.0, 3.5, 4.0, 4.5, 5.0, 5.5, 6.0, 6.5]
+              + [-1.0] * 8
+              + [6.5] * 8
+              + [6.5] + [-1.0] * 7
+              + [-1.0] * 7 + [6.5]
+              + [3.0, 2.5, 2.0, 1.5, 1.0, 0.5, 0.0, -0.5]
+              + [6.5, 6.0, 5.5, 5.0, 4.5, 4.0, 3.5, 3.0])
+    assert got.tolist() == [expect]
+
+
+def test_dequant4_two_groups_and_two_rows(oracle_lib):
+    # D = 128: row 0 has groups (scale 1, bias 0) and (scale 2, bias 3);
+    # row 1 has (scale 0.25, bias -2) and (scale 4, bias 0.5)
+    words = np.full((2, 16), 0x76543210, dtype=np.uint32)
+    scales = _u16([[1.0, 2.0], [0.25, 4.0]], FP16)
+    biases = _u16([[0.0, 3.0], [-2.0, 0.5]], FP16)
+    got = oracle.dequant4_f64(words, scales, biases, D=128, dtype=FP16)
+    r0 = [0, 1, 2, 3, 4, 5, 6, 7] * 8 + [3, 5, 7, 9, 11, 13, 15, 17] * 8
+    r1 = [-2.0, -1.75, -1.5, -1.25, -1.0, -0.75, -0.5, -0.25] * 8 + [0.5, 4.5, 8.5, 12.5, 16.5, 20.5, 24.5, 28.5] * 8
+    assert got.tolist() == [r0, r1]
+
+
+def _codes_as_values(words: np.ndarray, D: int) -> np.ndarray:
+    """The 4-bit codes of packed rows as integers [..., D] (the packing order only)."""
+    shifts = 4 * np.arange(8, dtype=np.uint32)
+    c = (words[..., :, None] >> shifts) & 0xF
+    return c.reshape(words.shape[:-1] + (D,)).astype(np.float64)
+
+
+@pytest.mark.parametrize("dtype", [FP16, BF16])
+def test_q4kv_with_unit_groups_is_the_plain_call_on_the_codes_bitwise(oracle_lib, dtype):
+    # scale 1 and bias 0: every value is its code, exactly representable, so
+    # the quantized call must be the plain (pinned) call on those values, bit
+    # for bit
+    B, Hq, Hkv, qL, kL, D = 2, 4, 2, 5, 9, 128
+    q = W.bits(W.random_qkv(710, B, Hq, Hkv, qL, kL, D, dtype)[0])
+    kq, _, _, vq, _, _ = W.random_q4kv(711, B, Hkv, kL, D, dtype)
+    ones, zeros = _u16(np.ones((B, Hkv, kL, D // 64)), dtype), _u16(np.zeros((B, Hkv, kL, D // 64)), dtype)
+    k = _u16(_codes_as_values(W.words(kq), D), dtype)
+    v = _u16(_codes_as_values(W.words(vq), D), dtype)
+    for causal, window in [(False, 0), (True, 0), (True, 3)]:
+        qo = kL - qL if causal else 0
+        got = oracle.sdpa_q4kv_f64(q, W.words(kq), ones, zeros, W.words(vq), ones, zeros, scale=0.05,
+                                   causal=causal, window=window, q_offset=qo, dtype=dtype, threads=2)
+        ref = oracle.sdpa_f64(q, k, v, scale=0.05, causal=causal, window=window, q_offset=qo, dtype=dtype,
+                              threads=2)
+        assert np.array_equal(got, ref)
+
+
+@pytest.mark.parametrize("causal,window", [(False, 0), (True, 0), (True, 4)])
+def test_q4kv_matches_a_dense_softmax_over_the_dequantized_rows(oracle_lib, causal, window):
+    # random groups: against a dense numpy formulation over the dequantized
+    # values (scores, mask, softmax, weighted sum), GQA and batches included
+    for (B, Hq, Hkv, qL, kL, D, dtype) in [(2, 4, 2, 6, 11, 64, BF16), (1, 6, 3, 3, 8, 128, FP16)]:
+        q = W.bits(W.random_qkv(720 + D, B, Hq, Hkv, qL, kL, D, dtype)[0])
+        kq, ks, kb, vq, vs, vb = W.random_q4kv(721 + D, B, Hkv, kL, D, dtype)
+        qo = kL - qL if causal else 0
+        got = oracle.sdpa_q4kv_f64(q, W.words(kq), W.bits(ks), W.bits(kb), W.words(vq), W.bits(vs), W.bits(vb),
+                                   scale=0.11, causal=causal, window=window, q_offset=qo, dtype=dtype,
+                                   threads=2)
+        kd = oracle.dequant4_f64(W.words(kq), W.bits(ks), W.bits(kb), D=D, dtype=dtype)
+        vd = oracle.dequant4_f64(W.words(vq), W.bits(vs), W.bits(vb), D=D, dtype=dtype)
+        G = Hq // Hkv
+        kd, vd = np.repeat(kd, G, axis=1), np.repeat(vd, G, axis=1)
+        s = float(np.float32(0.11)) * np.einsum("bhid,bhjd->bhij", _widened(q, dtype), kd)
+        s = np.where(_mask(qL, kL, causal, window, qo)[None, None], s, -np.inf)
+        w = np.exp(s - s.max(axis=-1, keepdims=True))
+        ref = np.einsum("bhij,bhjd->bhid", w / w.sum(axis=-1, keepdims=True), vd)
+        np.testing.assert_allclose(got, ref, rtol=0, atol=1e-12)
+
+
+def test_q4kv_row_selection_equals_the_full_call(oracle_lib):
+    q = W.bits(W.random_qkv(730, 1, 4, 2, 5, 40, 64, BF16)[0])
+    kv = [W.words(t) if t.dtype == torch.int32 else W.bits(t) for t in W.random_q4kv(731, 1, 2, 40, 64, BF16)]
+    full = oracle.sdpa_q4kv_f64(q, *kv, scale=0.2, causal=True, q_offset=35, dtype=BF16, threads=2)
+    rows = np.array([0, 7, 19], dtype=np.int64)
+    sel = oracle.sdpa_q4kv_f64(q, *kv, scale=0.2, causal=True, q_offset=35, dtype=BF16, rows=rows, threads=2)
+    assert np.array_equal(sel, full.reshape(-1, 64)[rows])
