@@ -9,10 +9,11 @@ missing or cannot be loaded, every call raises.
 Raw entry points (same names and arguments as the C functions, pointers as
 integers): ``sdpa_forward``, ``sdpa_workspace_bytes``, ``sdpa_forward_kv_view``,
 ``sdpa_workspace_bytes_kv_view``, ``sdpa_forward_bias``, ``sdpa_forward_dv``,
-``sdpa_workspace_bytes_dv``, ``sdpa_last_error``, ``sdpa_version``.
+``sdpa_workspace_bytes_dv``, ``sdpa_forward_q4kv``, ``sdpa_last_error``, ``sdpa_version``.
 Convenience wrappers on torch tensors: ``sdpa`` (contiguous K/V, optionally an
-additive mask array, optionally a value head dim other than q's) and
-``sdpa_kv_cache`` (K/V in a cache, possibly a wrapped ring).
+additive mask array, optionally a value head dim other than q's),
+``sdpa_kv_cache`` (K/V in a cache, possibly a wrapped ring) and ``sdpa_q4kv``
+(decode / verify over 4-bit K/V).
 """
 
 from __future__ import annotations
@@ -25,8 +26,8 @@ __all__ = [
     "SDPA_OK", "SDPA_INVALID_ARG", "SDPA_UNSUPPORTED", "SDPA_WORKSPACE_TOO_SMALL",
     "SDPA_HIP_ERROR", "SDPA_FP16", "SDPA_BF16", "SdpaError", "library_path", "load_library",
     "sdpa_forward", "sdpa_workspace_bytes", "sdpa_forward_kv_view", "sdpa_workspace_bytes_kv_view",
-    "sdpa_forward_bias", "sdpa_forward_dv", "sdpa_workspace_bytes_dv",
-    "sdpa_last_error", "sdpa_version", "sdpa", "sdpa_kv_cache", "EXPORTED_SYMBOLS",
+    "sdpa_forward_bias", "sdpa_forward_dv", "sdpa_workspace_bytes_dv", "sdpa_forward_q4kv",
+    "sdpa_last_error", "sdpa_version", "sdpa", "sdpa_kv_cache", "sdpa_q4kv", "EXPORTED_SYMBOLS",
 ]
 
 SDPA_OK = 0
@@ -39,7 +40,7 @@ SDPA_BF16 = 1
 
 EXPORTED_SYMBOLS = ("sdpa_forward", "sdpa_workspace_bytes", "sdpa_forward_kv_view",
                     "sdpa_workspace_bytes_kv_view", "sdpa_forward_bias", "sdpa_forward_dv",
-                    "sdpa_workspace_bytes_dv", "sdpa_last_error", "sdpa_version")
+                    "sdpa_workspace_bytes_dv", "sdpa_forward_q4kv", "sdpa_last_error", "sdpa_version")
 
 # (q/k head dim, v head dim) pairs the library takes
 HEAD_DIMS = ((64, 64), (80, 80), (128, 128), (192, 192), (256, 256), (512, 512), (192, 256))
@@ -86,6 +87,8 @@ def load_library():
     lib.sdpa_forward_dv.restype = ci
     lib.sdpa_workspace_bytes_dv.argtypes = [ci] * 7
     lib.sdpa_workspace_bytes_dv.restype = sz
+    lib.sdpa_forward_q4kv.argtypes = [vp] * 8 + [ci] * 6 + [ctypes.c_float] + [ci] * 4 + [vp, sz, vp]
+    lib.sdpa_forward_q4kv.restype = ci
     lib.sdpa_last_error.argtypes = []
     lib.sdpa_last_error.restype = ctypes.c_char_p
     lib.sdpa_version.argtypes = []
@@ -138,6 +141,14 @@ def sdpa_forward_dv(q, k, v, out, B, Hq, Hkv, qL, kL, D, Dv, scale, causal, wind
 def sdpa_workspace_bytes_dv(B, Hq, Hkv, qL, kL, D, Dv) -> int:
     """``size_t sdpa_workspace_bytes_dv(...)``; (size_t)-1 for rejected shapes."""
     return load_library().sdpa_workspace_bytes_dv(B, Hq, Hkv, qL, kL, D, Dv)
+
+
+def sdpa_forward_q4kv(q, kq, ks, kb, vq, vs, vb, out, B, Hq, Hkv, qL, kL, D, scale, causal, window,
+                      q_offset, dtype, workspace, workspace_bytes, stream) -> int:
+    """``int sdpa_forward_q4kv(...)`` of the C ABI; pointer arguments are integers."""
+    return load_library().sdpa_forward_q4kv(q, kq, ks, kb, vq, vs, vb, out, B, Hq, Hkv, qL, kL, D, scale,
+                                            causal, window, q_offset, dtype, workspace, workspace_bytes,
+                                            stream)
 
 
 def sdpa_last_error() -> str:
@@ -270,6 +281,47 @@ def sdpa_kv_cache(q, k_cache, v_cache, kv_len: int, *, ring_start: int = 0,
                               Hq, Hkv, qL, int(kv_len), cap, int(ring_start), D, float(scale),
                               int(bool(causal)), int(window), int(q_offset), dtype, ws_ptr, ws_bytes,
                               stream.cuda_stream)
+    if rc != SDPA_OK:
+        raise SdpaError(rc, sdpa_last_error())
+    return out
+
+
+def sdpa_q4kv(q, kq, ks, kb, vq, vs, vb, *, scale: float | None = None, causal: bool = False,
+              window: int = 0, q_offset: int | None = None, out=None, workspace=None, stream=None):
+    """Decode / verify (qL <= 4) over 4-bit K and V (``sdpa_forward_q4kv``).
+
+    q: [B, Hq, qL, 256] fp16 or bf16.  kq, vq: [B, Hkv, kL, 32] int32 code words
+    (element 8 w + n of a row in bits 4 n .. 4 n + 3 of word w).  ks, kb, vs, vb:
+    [B, Hkv, kL, 4] of q's dtype, the scale and bias of each 64-element group;
+    element d of a row is scale[d // 64] * code_d + bias[d // 64].  Everything else
+    as in ``sdpa``.
+    """
+    import torch
+
+    if q.dim() != 4 or kq.dim() != 4 or vq.dim() != 4:
+        raise ValueError("q and the code words must be 4-D")
+    B, Hq, qL, D = q.shape
+    Bk, Hkv, kL, W = kq.shape
+    if q.dtype not in (torch.float16, torch.bfloat16) or kq.dtype != torch.int32 or vq.dtype != torch.int32:
+        raise ValueError("q must be fp16/bf16 and the code words int32")
+    if Bk != B or W * 8 != D or tuple(vq.shape) != tuple(kq.shape):
+        raise ValueError(f"shape mismatch: q {tuple(q.shape)}, kq {tuple(kq.shape)}, vq {tuple(vq.shape)}")
+    for t in (ks, kb, vs, vb):
+        if tuple(t.shape) != (B, Hkv, kL, D // 64) or t.dtype != q.dtype:
+            raise ValueError("scales and biases must be [B, Hkv, kL, D / 64] tensors of q's dtype")
+    ts = (q, kq, ks, kb, vq, vs, vb)
+    if not all(t.is_cuda and t.is_contiguous() for t in ts):
+        raise ValueError("all inputs must be contiguous GPU tensors")
+    dtype = SDPA_FP16 if q.dtype == torch.float16 else SDPA_BF16
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if q_offset is None:
+        q_offset = kL - qL if causal else 0
+    need = sdpa_workspace_bytes(B, Hq, Hkv, qL, kL, D)
+    out, ws_ptr, ws_bytes, stream = _prepare(q, need, D, out, workspace, stream)
+    rc = sdpa_forward_q4kv(*(t.data_ptr() for t in ts), out.data_ptr(), B, Hq, Hkv, qL, kL, D, float(scale),
+                           int(bool(causal)), int(window), int(q_offset), dtype, ws_ptr, ws_bytes,
+                           stream.cuda_stream)
     if rc != SDPA_OK:
         raise SdpaError(rc, sdpa_last_error())
     return out

@@ -236,7 +236,7 @@ constexpr float kRescaleLog2 = 8.f;
 // busy through the softmax.  K and V have separate double buffers, V one
 // tile behind K: step t reads K(t+1) and V(t) and loads K(t+2) and V(t+1).
 // ---------------------------------------------------------------------------
-template <int DT, int DK, int DV, bool RING, bool BIAS>
+template <int DT, int DK, int DV, bool RING, bool BIAS, bool Q4 = false>
 __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* lds) {
   // DK: head dim of q and k; DV: head dim of v and the output.
   // DK <= 256: a wave owns 32 rows and all DV output columns.  DK = DV =
@@ -248,7 +248,9 @@ __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* ld
   // per wave.
   constexpr bool PAIR = (DK == 512);
   // V3: a third V buffer; V loaded in the P V region (see the step below)
-  constexpr bool V3 = kv_tiles(BIAS, DK) == 5;
+  constexpr bool V3 = !Q4 && kv_tiles(BIAS, DK) == 5;
+  // Q4: 4-bit K and V, dequantized into the same LDS tiles through registers
+  static_assert(!Q4 || (DK == 256 && DV == 256 && !RING && !BIAS), "4-bit K/V: head dim 256 only");
   constexpr bool VLATE = PAIR || V3;
   constexpr int NVB = V3 ? 3 : 2;
   static_assert(PAIR == (DV == 512), "head dim 512 only with DK == DV");
@@ -424,6 +426,7 @@ __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* ld
     return src;
   };
   auto load_blk = [&](const TileSrc& src, uint16_t* buf, int n, bool is_v) {
+    if constexpr (Q4) return;  // 4-bit tiles come through registers (below)
     const uint32_t vo = is_v ? voff[n % VPAT] : koff[n % KPAT];
     uint16_t* dst = buf + (wave + NW * n) * 512;
     const uint32_t so = (uint32_t)(n * NW * RPB * row_bytes(is_v));
@@ -518,6 +521,77 @@ __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* ld
     return x * inv_scale;
   };
   auto load_v = [&](int t) { load_tile(vg, t, vbuf0 + ((t - t_first) % NVB) * TILE, true); };
+
+  // ---- 4-bit K/V (Q4) ------------------------------------------------------
+  // A 1 KiB LDS block of a tile gets, per lane, the 8 elements the direct
+  // load would have written there (key row r of the block's RPB rows, chunk
+  // c after the K or V swizzle): one 32-bit code word, the scale and the
+  // bias of its 64-element group, then fp32 scale * code + bias for each
+  // nibble, rounded to the input dtype.  Rows past kL repeat row kL - 1
+  // (finite values; their keys are masked, so their weights are exactly 0):
+  // no branch around a load, so the loads' waits stay counted.
+  // Loading waves: with one row-holding wave (G * qL <= 32 rows in the
+  // workgroup, a decode or verify step) the other three load, one step
+  // ahead through two register sets (q4 pipelined), and the computing wave
+  // issues no loads; otherwise every wave loads its share, issued at the
+  // start of a step and written to LDS at its end.
+  constexpr int NBLK = TILE * 2 / 1024;   // 1 KiB blocks per tile
+  constexpr int QB = (NBLK + 2) / 3;      // blocks per tile per loading wave (3 or 4 of them)
+  struct Q4Data {  // loaded values only: nothing is computed from them before the store
+    uint32_t w;     // code word
+    uint32_t s, b;  // scale and bias bit patterns
+  };
+  const int n_act = __builtin_amdgcn_readfirstlane(min(NW, (rows_end - row0 + kRowsPerWave - 1) / kRowsPerWave));
+  const bool q4_pipe = Q4 && n_act == 1;          // waves 1..3 load, one step ahead
+  const int q4_nl = q4_pipe ? NW - 1 : NW;        // loading waves
+  const int q4_li = q4_pipe ? wave - 1 : wave;    // this wave's index among them
+  const size_t q4_head = (size_t)(b * p.Hkv + hkv) * (size_t)p.kL;  // the head's first K/V row
+  auto q4_fetch = [&](int t, int blk, bool is_v) {
+    const int r = blk * RPB + lane / ROWCH, pch = lane % ROWCH;
+    const int c = is_v ? (pch ^ ((r & VSW) << 2)) : (pch ^ (r & 15));
+    const int key = min(t * BN + r, p.kL - 1);
+    Q4Data d{0u, 0u, 0u};
+    if constexpr (Q4) {
+      const size_t row = q4_head + (size_t)key;
+      d.w = (is_v ? p.vq4 : p.kq4)[row * (DK / 8) + c];
+      const size_t g = row * (DK / 64) + c / 8;
+      d.s = (is_v ? p.vs4 : p.ks4)[g];
+      d.b = (is_v ? p.vb4 : p.kb4)[g];
+    }
+    return d;
+  };
+  auto q4_widen = [](uint32_t h) {
+    if constexpr (DT == 1) return __builtin_bit_cast(float, h << 16);
+    else return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
+  };
+  auto q4_store = [&](const Q4Data& d, uint16_t* buf, int blk) {
+    const float sc = q4_widen(d.s), bi = q4_widen(d.b);
+    auto val = [&](int n) { return fmaf(sc, (float)((d.w >> (4 * n)) & 15u), bi); };
+    uint4 out;
+    out.x = Elem<DT>::pack2(val(0), val(1));
+    out.y = Elem<DT>::pack2(val(2), val(3));
+    out.z = Elem<DT>::pack2(val(4), val(5));
+    out.w = Elem<DT>::pack2(val(6), val(7));
+    *(uint4*)(buf + blk * 512 + 8 * lane) = out;
+  };
+  // this wave's blocks of K tile tk and V tile tv: issue, then store.
+  // Slots past the last block repeat it (the same bytes written twice), so
+  // that no branch separates a load from its store and every wait counts
+  auto q4_blk = [&](int i) { return min(q4_li + q4_nl * i, NBLK - 1); };
+  auto q4_issue = [&](Q4Data (&kd)[QB], Q4Data (&vd)[QB], int tk, int tv) {
+#pragma unroll
+    for (int i = 0; i < QB; ++i) {
+      kd[i] = q4_fetch(tk, q4_blk(i), false);
+      vd[i] = q4_fetch(tv, q4_blk(i), true);
+    }
+  };
+  auto q4_put = [&](const Q4Data (&kd)[QB], const Q4Data (&vd)[QB], uint16_t* kdst, uint16_t* vdst) {
+#pragma unroll
+    for (int i = 0; i < QB; ++i) {
+      q4_store(kd[i], kdst, q4_blk(i));
+      q4_store(vd[i], vdst, q4_blk(i));
+    }
+  };
 
   // the keys row `pos` sees form one interval [key_lo, key_hi] (empty if
   // key_hi < key_lo)
@@ -821,15 +895,28 @@ __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* ld
     for (int i = tid; i < NVB * TILE / 8; i += NW * 64) vz[i] = make_uint4(0, 0, 0, 0);
     __syncthreads();
   }
-  load_k(t_first);
-  load_b(t_first);
-  load_v(t_first);
-  if (t_first < t_last) {
-    load_k(t_first + 1);
-    load_b(t_first + 1);
-    if constexpr (V3) load_v(t_first + 1);
+  // Q4: the pipelined loaders' first register set, K(t0 + 2) and V(t0 + 1)
+  typename std::conditional<Q4, Q4Data, char>::type q4a_k[Q4 ? QB : 1], q4a_v[Q4 ? QB : 1];
+  if constexpr (Q4) {
+    if (q4_li >= 0) {  // wave 0 of a pipelined workgroup does not load
+      Q4Data k0[QB], v0[QB], k1[QB], v1[QB];
+      q4_issue(k0, v0, t_first, t_first);
+      q4_issue(k1, v1, min(t_first + 1, t_last), t_first);
+      q4_put(k0, v0, kbuf0, vbuf0);
+      q4_put(k1, v1, kbuf0 + TILE, vbuf0);  // V(t0) again, the same bytes
+      if (q4_pipe) q4_issue(q4a_k, q4a_v, min(t_first + 2, t_last), min(t_first + 1, t_last));
+    }
+  } else {
+    load_k(t_first);
+    load_b(t_first);
+    load_v(t_first);
+    if (t_first < t_last) {
+      load_k(t_first + 1);
+      load_b(t_first + 1);
+      if constexpr (V3) load_v(t_first + 1);
+    }
+    __builtin_amdgcn_s_waitcnt(0);
   }
-  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
   f32x16_t sA[KB], sB[KB];
@@ -887,6 +974,12 @@ __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* ld
     uint2 bw[KB * 4];
     const TileSrc vsrc = tile_src(vg, tv, true);
     uint16_t* const vdst = vbuf0 + (V3 ? (VB + 2) % 3 : 1 - P) * TILE;
+    // Q4 with every wave loading: this wave's blocks of K(t+2) and V(t+1),
+    // issued now and written to LDS at the end of the step
+    typename std::conditional<Q4, Q4Data, char>::type q4k[Q4 ? QB : 1], q4v[Q4 ? QB : 1];
+    if constexpr (Q4) {
+      if (!q4_pipe) q4_issue(q4k, q4v, tk, tv);
+    }
     const float psum = qk_weights(sn, kl, sc, pb, tile_src(kg, tk, false), kbuf0 + P * TILE,
                                   vsrc, vdst, BIAS ? bias_src(tk) : i32x4_t{}, bbuf0 + P * BTILE,
                                   bbuf0 + (1 - P) * BTILE, bw, a);
@@ -894,6 +987,9 @@ __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* ld
     l_run = l_run * alpha_cur + psum;
     if (!full_tile(t + 1)) mask(sn, t + 1);
     alpha_cur = pv_max(pb, vbuf0 + (V3 ? VB : P) * TILE, sn, has_next, bw, vsrc, vdst);
+    if constexpr (Q4) {
+      if (!q4_pipe) q4_put(q4k, q4v, kbuf0 + P * TILE, vdst);
+    }
     // VLATE: K(t+2) (and its bias) have landed, and with V3 V(t+1) too; the
     // V loads of this step may be in flight.  Otherwise everything has.
     if constexpr (VLATE) wait_vmem<PV_LOADS>();
@@ -923,6 +1019,33 @@ __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* ld
       for (int t = t_first; t <= t_last; t += 2) {
         step(t, sA, sB, I0{}, I0{});
         if (t + 1 <= t_last) step(t + 1, sB, sA, I1{}, I0{});
+      }
+    }
+  } else if constexpr (Q4) {  // no rows: this wave only loads (4-bit tiles)
+    if (q4_pipe) {
+      // one step ahead: set a holds K(t+2), V(t+1) when an even step starts
+      // (issued in the prologue or the last step), set b when an odd one does
+      Q4Data q4b_k[QB], q4b_v[QB];
+      // (the scheduling barriers keep each set's loads after the stores of
+      // the other, so that the stores never wait for loads just issued)
+      for (int t = t_first; t <= t_last; t += 2) {
+        q4_put(q4a_k, q4a_v, kbuf0, vbuf0 + TILE);
+        __builtin_amdgcn_sched_barrier(0);
+        q4_issue(q4b_k, q4b_v, min(t + 3, t_last), min(t + 2, t_last));
+        __syncthreads();
+        if (t + 1 > t_last) break;
+        q4_put(q4b_k, q4b_v, kbuf0 + TILE, vbuf0);
+        __builtin_amdgcn_sched_barrier(0);
+        q4_issue(q4a_k, q4a_v, min(t + 4, t_last), min(t + 3, t_last));
+        __syncthreads();
+      }
+    } else {
+      for (int t = t_first; t <= t_last; ++t) {
+        const int P = (t - t_first) & 1;
+        Q4Data kd[QB], vd[QB];
+        q4_issue(kd, vd, min(t + 2, t_last), min(t + 1, t_last));
+        q4_put(kd, vd, kbuf0 + P * TILE, vbuf0 + (1 - P) * TILE);
+        __syncthreads();
       }
     }
   } else {  // no rows: this wave only loads its share of every tile and
@@ -1027,6 +1150,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void attn_tile_kernel_d512(AttnParams p) {
   __shared__ __attribute__((aligned(16))) uint16_t lds[4 * 32 * 512 + 2 * 4 * 64 * 16 + (BIAS ? 2 * 64 * 32 : 0)];
   attn_pipe_body<DT, 512, 512, RING, BIAS>(p, lds);
+}
+
+// head dim 256 with 4-bit K and V (2 K + 2 V tiles)
+template <int DT>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void attn_tile_kernel_d256_q4(AttnParams p) {
+  __shared__ __attribute__((aligned(16))) uint16_t lds[4 * 64 * 256];
+  attn_pipe_body<DT, 256, 256, false, false, true>(p, lds);
 }
 
 // Merge of the per-split partials of each output row.  One workgroup of nw =
@@ -1255,6 +1386,13 @@ hipError_t launch_attention(const AttnParams& p, int D, int Dv, int dtype, bool 
   if (D == 192) return launch_attention_dd<192>(p, dtype, ring, stream);
   if (D == 256) return launch_attention_dd<256>(p, dtype, ring, stream);
   return launch_attention_dd<512>(p, dtype, ring, stream);
+}
+
+hipError_t launch_attention_q4(const AttnParams& p, int dtype, hipStream_t stream) {
+  const dim3 grid((unsigned)(p.B * p.Hkv * p.mblocks), (unsigned)p.nsplit, 1);
+  if (dtype == 0) hipLaunchKernelGGL((attn_tile_kernel_d256_q4<0>), grid, dim3(256), 0, stream, p);
+  else hipLaunchKernelGGL((attn_tile_kernel_d256_q4<1>), grid, dim3(256), 0, stream, p);
+  return hipGetLastError();
 }
 
 hipError_t launch_combine(const AttnParams& p, int D, int dtype, hipStream_t stream) {

@@ -141,11 +141,16 @@ int check_view(int kL, int kv_capacity, int ring_start) {
 // Both forward entry points: K/V rows of a head are kv_cap apart, logical
 // key j is physical row (ring_start + j) % kv_cap; chunk_cap is the cache
 // capacity the decode chunks are sized from (0: none).
+// 4-bit K/V of sdpa_forward_q4kv (k and v then point at the code words)
+struct Q4Args {
+  const void *ks, *kb, *vs, *vb;
+};
+
 int forward_impl(const void* q, const void* k, const void* v, const void* bias, int64_t bias_sb,
                  int64_t bias_sh, int64_t bias_sq, void* out, int B, int Hq, int Hkv, int qL, int kL,
                  int kv_cap, int ring_start, int chunk_cap, int D, int Dv, float scale, int causal,
                  int window, int q_offset, int dtype, void* workspace, size_t workspace_bytes,
-                 void* stream) {
+                 void* stream, const Q4Args* q4 = nullptr) {
   if (!q || !k || !v || !out) return fail(SDPA_INVALID_ARG, "q, k, v and out must be non-null");
   int rc = check_shape(B, Hq, Hkv, qL, kv_cap, D, Dv);
   if (rc != SDPA_OK) return rc;
@@ -162,10 +167,18 @@ int forward_impl(const void* q, const void* k, const void* v, const void* bias, 
                 "(got %d)",
                 kL - qL, q_offset);
   const size_t qbytes = (size_t)B * Hq * qL * D * 2, obytes = (size_t)B * Hq * qL * Dv * 2;
-  const size_t kbytes = (size_t)B * Hkv * kv_cap * D * 2, vbytes = (size_t)B * Hkv * kv_cap * Dv * 2;
+  // 4-bit rows: D / 2 bytes of codes, and D / 64 scales and biases
+  const size_t kbytes = (size_t)B * Hkv * kv_cap * (q4 ? D / 2 : D * 2);
+  const size_t vbytes = (size_t)B * Hkv * kv_cap * (q4 ? Dv / 2 : Dv * 2);
   if (overlap(out, obytes, q, qbytes) || overlap(out, obytes, k, kbytes) ||
       overlap(out, obytes, v, vbytes))
     return fail(SDPA_INVALID_ARG, "out must not overlap q, k or v");
+  if (q4) {
+    const size_t gbytes = (size_t)B * Hkv * kv_cap * (D / 64) * 2;
+    if (overlap(out, obytes, q4->ks, gbytes) || overlap(out, obytes, q4->kb, gbytes) ||
+        overlap(out, obytes, q4->vs, gbytes) || overlap(out, obytes, q4->vb, gbytes))
+      return fail(SDPA_INVALID_ARG, "out must not overlap the scales or biases");
+  }
 
   const SplitPlan sp = plan_split(B, Hq, Hkv, qL, kL, D, chunk_cap);
   const size_t need = workspace_for(sp, B, Hq, qL, Dv);
@@ -188,6 +201,12 @@ int forward_impl(const void* q, const void* k, const void* v, const void* bias, 
   p.kv_cap = kv_cap;
   p.ring_start = ring_start;
   p.bias = (const uint16_t*)bias;
+  p.kq4 = q4 ? (const uint32_t*)k : nullptr;
+  p.vq4 = q4 ? (const uint32_t*)v : nullptr;
+  p.ks4 = q4 ? (const uint16_t*)q4->ks : nullptr;
+  p.kb4 = q4 ? (const uint16_t*)q4->kb : nullptr;
+  p.vs4 = q4 ? (const uint16_t*)q4->vs : nullptr;
+  p.vb4 = q4 ? (const uint16_t*)q4->vb : nullptr;
   p.bias_sb = bias_sb;
   p.bias_sh = bias_sh;
   p.bias_sq = bias_sq;
@@ -214,7 +233,7 @@ int forward_impl(const void* q, const void* k, const void* v, const void* bias, 
   const bool ring = (int64_t)ring_start + kL > kv_cap;
 
   hipStream_t s = (hipStream_t)stream;
-  hipError_t e = launch_attention(p, D, Dv, dtype, ring, s);
+  hipError_t e = q4 ? launch_attention_q4(p, dtype, s) : launch_attention(p, D, Dv, dtype, ring, s);
   if (e == hipSuccess && sp.partials) e = launch_combine(p, Dv, dtype, s);
   if (e != hipSuccess) return fail(SDPA_HIP_ERROR, "kernel launch failed: %s", hipGetErrorString(e));
   return SDPA_OK;
@@ -245,7 +264,7 @@ SDPA_API size_t sdpa_workspace_bytes_kv_view(int B, int Hq, int Hkv, int qL, int
 
 SDPA_API const char* sdpa_last_error(void) { return g_last_error; }
 
-SDPA_API int sdpa_version(void) { return 300; }
+SDPA_API int sdpa_version(void) { return 400; }
 
 SDPA_API int sdpa_forward(const void* q, const void* k, const void* v, void* out, int B, int Hq,
                           int Hkv, int qL, int kL, int D, float scale, int causal, int window,
@@ -300,4 +319,22 @@ SDPA_API int sdpa_forward_kv_view(const void* q, const void* k, const void* v, v
   return forward_impl(q, k, v, nullptr, 0, 0, 0, out, B, Hq, Hkv, qL, kL, kv_capacity, ring_start,
                       kv_capacity, D, D, scale, causal, window, q_offset, dtype, workspace, workspace_bytes,
                       stream);
+}
+
+SDPA_API int sdpa_forward_q4kv(const void* q, const void* kq, const void* ks, const void* kb,
+                               const void* vq, const void* vs, const void* vb, void* out, int B,
+                               int Hq, int Hkv, int qL, int kL, int D, float scale, int causal,
+                               int window, int q_offset, int dtype, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  g_last_error[0] = '\0';
+  int rc = check_shape(B, Hq, Hkv, qL, kL, D, D);
+  if (rc != SDPA_OK) return rc;
+  if (D != 256) return fail(SDPA_UNSUPPORTED, "4-bit K/V: head dim %d is not supported (256 only)", D);
+  if (qL > kDecodeMaxRows)
+    return fail(SDPA_UNSUPPORTED, "4-bit K/V: qL %d is not supported (decode / verify, qL <= %d)", qL,
+                kDecodeMaxRows);
+  if (!ks || !kb || !vs || !vb) return fail(SDPA_INVALID_ARG, "scales and biases must be non-null");
+  const Q4Args q4{ks, kb, vs, vb};
+  return forward_impl(q, kq, vq, nullptr, 0, 0, 0, out, B, Hq, Hkv, qL, kL, kL, 0, 0, D, D, scale, causal,
+                      window, q_offset, dtype, workspace, workspace_bytes, stream, &q4);
 }

@@ -47,6 +47,14 @@ struct AttnParams {
   int B, Hq, Hkv, G, qL, kL;
   const uint16_t* bias;  // additive mask array or nullptr; keys contiguous within a row
   int64_t bias_sb, bias_sh, bias_sq;  // its batch, query-head and query-row strides (elements)
+  // 4-bit K and V (the q4 instances; k and v are unused then): code words
+  // [B, Hkv, kL, D / 8] (element 8 w + n in bits 4 n .. 4 n + 3 of word w),
+  // per-64-element-group scales and biases [B, Hkv, kL, D / 64] in the dtype;
+  // element d of a row is scale * code + bias
+  const uint32_t* kq4;
+  const uint16_t *ks4, *kb4;
+  const uint32_t* vq4;
+  const uint16_t *vs4, *vb4;
   int kv_cap;         // rows per KV head in k and v (head strides kv_cap * D, kv_cap * Dv), >= kL
   int ring_start;     // physical row of logical key 0; key j is row (ring_start + j) % kv_cap
   int causal, window, q_offset;
@@ -74,6 +82,8 @@ SplitPlan plan_split(int B, int Hq, int Hkv, int qL, int kL, int D, int kv_capac
 // the instances that add the mask array (never together with ring, and
 // neither with D != Dv)
 hipError_t launch_attention(const AttnParams& p, int D, int Dv, int dtype, bool ring, hipStream_t stream);
+// The 4-bit K/V instance (D = Dv = 256, no ring, no bias; p.kq4 ... set)
+hipError_t launch_attention_q4(const AttnParams& p, int dtype, hipStream_t stream);
 hipError_t launch_combine(const AttnParams& p, int Dv, int dtype, hipStream_t stream);
 
 }  // namespace sdpa

@@ -1,0 +1,106 @@
+"""Decode / verify over 4-bit K and V (sdpa_forward_q4kv) against the fp64 oracle.
+
+The 4-bit rows are the reading of the prefix KV cache that ml-explore/mlx PR
+#3660 keeps 4-bit quantized at rest (End-to-end section): affine, groups of
+64 elements, codes packed eight to a 32-bit word.  The kernel rounds each
+dequantized element to the input dtype once, which the tolerances cover.
+Verify rows must equal the single-row calls over their trimmed key prefixes
+byte for byte, as in the 16-bit path.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import flash_attention_head_amd as fa
+import oracle
+from flash_attention_head_amd import workloads as W
+from gpu_util import ORACLE_THREADS, check_close, ensure_library, f64, note
+
+pytestmark = pytest.mark.gpu
+
+FP16, BF16 = W.FP16, W.BF16
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    ensure_library()
+
+
+def _inputs(seed, B, Hq, Hkv, qL, kL, dtype):
+    q = W.random_qkv(seed, B, Hq, Hkv, qL, 1, 256, dtype)[0]
+    return (q,) + W.random_q4kv(seed + 1, B, Hkv, kL, 256, dtype)
+
+
+def _oracle(ins, dtype, **kw):
+    q, kq, ks, kb, vq, vs, vb = ins
+    return oracle.sdpa_q4kv_f64(W.bits(q), W.words(kq), W.bits(ks), W.bits(kb), W.words(vq), W.bits(vs),
+                                W.bits(vb), dtype=dtype, threads=ORACLE_THREADS, **kw)
+
+
+def _gpu(ins, **kw):
+    out = fa.sdpa_q4kv(*(t.cuda() for t in ins), **kw)
+    torch.cuda.synchronize()
+    return out.cpu()
+
+
+# (B, Hq, Hkv, qL, kL, dtype, window): G * qL <= 32 rows (three waves load
+# for the one that computes) and 64 rows (every wave loads its share)
+CASES = [(1, 16, 8, 4, 5000, BF16, 0), (1, 16, 8, 1, 5000, FP16, 0), (2, 8, 2, 3, 3000, BF16, 700),
+         (1, 32, 2, 4, 4100, BF16, 0), (1, 32, 2, 2, 2500, FP16, 300), (1, 4, 2, 4, 64, BF16, 0),
+         (1, 4, 1, 4, 70, FP16, 5)]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[f"B{c[0]}Hq{c[1]}Hkv{c[2]}q{c[3]}k{c[4]}w{c[6]}" for c in CASES])
+def test_every_row_against_the_oracle(case):
+    B, Hq, Hkv, qL, kL, dtype, window = case
+    ins = _inputs(9000 + kL + qL, B, Hq, Hkv, qL, kL, dtype)
+    note(f"q4kv {case}")
+    got = f64(_gpu(ins, causal=True, window=window))
+    ref = _oracle(ins, dtype, scale=float(np.float32(1 / 16)), causal=True, window=window, q_offset=kL - qL)
+    check_close(got, ref, dtype, f"q4kv {case}")
+
+
+def test_unmasked_decode_against_the_oracle():
+    ins = _inputs(9100, 2, 4, 2, 2, 3000, FP16)
+    note("q4kv unmasked")
+    got = f64(_gpu(ins, causal=False))
+    ref = _oracle(ins, FP16, scale=float(np.float32(1 / 16)), causal=False)
+    check_close(got, ref, FP16, "q4kv unmasked")
+
+
+def _check_verify_rows(ins, window, what):
+    q, kq, ks, kb, vq, vs, vb = (t.cuda() for t in ins)
+    qL, kL = q.shape[2], kq.shape[2]
+    note(f"{what}: block")
+    block = fa.sdpa_q4kv(q, kq, ks, kb, vq, vs, vb, causal=True, window=window)
+    torch.cuda.synchronize()
+    for r in range(qL):
+        n = kL - qL + r + 1
+        note(f"{what}: row {r} over {n} keys")
+        one = fa.sdpa_q4kv(q[:, :, r:r + 1].contiguous(), *(t[:, :, :n].contiguous() for t in (kq, ks, kb, vq, vs, vb)),
+                           causal=True, window=window)
+        torch.cuda.synchronize()
+        a = block[:, :, r:r + 1].contiguous().view(torch.int16)
+        assert torch.equal(a, one.view(torch.int16)), f"{what}: row {r} differs"
+
+
+@pytest.mark.parametrize("kL,window", [(20000, 0), (20000, 1024), (4097, 0), (4099, 3)])
+def test_verify_rows_equal_single_row_calls_with_three_loading_waves(kL, window):
+    _check_verify_rows(_inputs(9200 + kL, 1, 16, 8, 4, kL, BF16), window, f"q4kv G2 kL{kL} w{window}")
+
+
+def test_verify_rows_equal_single_row_calls_with_every_wave_loading():
+    # G = 16: a verify block is 64 packed rows, its single-row calls 16
+    _check_verify_rows(_inputs(9300, 1, 32, 2, 4, 9000, FP16), 0, "q4kv G16")
+
+
+@pytest.mark.timeout(600)
+def test_the_128k_key_verify_shape_every_row():
+    # the shape of the 128K-key decode workload (16 query / 8 KV heads, head dim
+    # 256, 4 rows at the end of 131072 keys), with 4-bit K and V
+    ins = _inputs(9400, 1, 16, 8, 4, 131072, BF16)
+    note("q4kv 128k verify")
+    got = f64(_gpu(ins, causal=True))
+    ref = _oracle(ins, BF16, scale=float(np.float32(1 / 16)), causal=True, q_offset=131068)
+    check_close(got, ref, BF16, "q4kv 128k")
