@@ -29,7 +29,7 @@ PEAK_HBM_GBS = 8000.0
 HEADLINE = "chunked_prefill_32k"
 EXTRA = ["causal_h64_16k", "sliding_32k", "global_d512_32k", "causal_d64_16k", "causal_d80_16k",
          "causal_d128_16k", "causal_d192_16k",
-         "causal_dk192_dv256_16k", "chunked_prefill_32k_bias", "decode_q4_128k", "decode_q1_128k", "tiny_causal"]
+         "causal_dk192_dv256_16k", "chunked_prefill_32k_bias", "decode_q4_128k", "decode_q1_128k", "decode_q4kv_128k", "tiny_causal"]
 
 
 def log(msg):
@@ -43,6 +43,8 @@ def time_workload(wl, steps, warmup):
     import flash_attention_head_amd as fa
     from flash_attention_head_amd import workloads as W
 
+    if wl.name in W.Q4KV:
+        return time_q4kv(wl, steps, warmup)
     q, k, v = (t.cuda() for t in W.draw(wl))
     bias = W.draw_bias(wl)
     bias = bias.cuda() if bias is not None else None
@@ -87,11 +89,47 @@ def time_workload(wl, steps, warmup):
                                                            "sdpa_forward_dv" if wl.dv != wl.D else "sdpa_forward")}
 
 
+def time_q4kv(wl, steps, warmup):
+    """Mean ms per sdpa_forward_q4kv call over 4-bit K/V (HIP events on its stream)."""
+    import torch
+
+    import flash_attention_head_amd as fa
+    from flash_attention_head_amd import workloads as W
+
+    ins = [t.cuda() for t in W.draw_q4kv(wl)]
+    out = torch.empty_like(ins[0])
+    need = fa.sdpa_workspace_bytes(wl.B, wl.Hq, wl.Hkv, wl.qL, wl.kL, wl.D)
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def call():
+        fa.sdpa_q4kv(*ins, scale=wl.scale, causal=wl.causal, window=wl.window, q_offset=wl.q_offset,
+                     out=out, workspace=ws, stream=stream)
+
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    t0 = time.perf_counter()
+    for a, b in ev:
+        a.record(stream)
+        call()
+        b.record(stream)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / steps
+    per = sorted(a.elapsed_time(b) for a, b in ev)
+    del ins, out, ws
+    torch.cuda.empty_cache()
+    return {"wall_ms": wall_ms, "event_ms_mean": sum(per) / len(per), "event_ms_min": per[0],
+            "event_ms_median": per[len(per) // 2], "workspace_bytes": need, "entry": "sdpa_forward_q4kv"}
+
+
 def summarize(wl, t):
     from flash_attention_head_amd import workloads as W
 
     fl = W.flops(wl)
-    io = W.io_bytes(wl.B, wl.Hq, wl.Hkv, wl.qL, wl.kL, wl.D, Dv=wl.dv)["total"]
+    io = (W.q4kv_bytes(wl) if wl.name in W.Q4KV else
+          W.io_bytes(wl.B, wl.Hq, wl.Hkv, wl.qL, wl.kL, wl.D, Dv=wl.dv)["total"])
     ms = t["event_ms_mean"]
     r = {"ms": round(ms, 4), "ms_min": round(t["event_ms_min"], 4),
          "tflops": round(fl / (ms * 1e-3) / 1e12, 2),

@@ -96,7 +96,13 @@ WORKLOADS = {
                           "verify block, B1 Hq16 Hkv8 D256 qL4 kL131072 bf16 causal bottom-right"),
     "decode_q1_128k": _wl("decode_q1_128k", 1, 16, 8, 1, 131072, 256, BF16, True, 0, 131072 - 1, 5,
                           "decode, B1 Hq16 Hkv8 D256 qL1 kL131072 bf16 (row 3 of the qL=4 draw)"),
+    "decode_q4kv_128k": _wl("decode_q4kv_128k", 1, 16, 8, 4, 131072, 256, BF16, True, 0, 131072 - 4, 5,
+                            "the verify block of decode_q4_128k over 4-bit K/V (random code words, "
+                            "per-64 scales/biases, seed 12)"),
 }
+
+# workloads whose K and V are 4-bit rows: name -> seed of random_q4kv
+Q4KV = {"decode_q4kv_128k": 12}
 
 
 # workloads that also pass an additive mask array: name -> (bias batch dim, bias head dim, seed)
@@ -111,6 +117,20 @@ def draw_bias(wl: Workload) -> "torch.Tensor | None":
     g = torch.Generator(device="cpu")
     g.manual_seed(seed)
     return torch.randn((bb, bh, wl.qL, wl.kL), generator=g, dtype=torch.float32).to(TORCH_DTYPES[wl.dtype])
+
+
+def draw_q4kv(wl: Workload):
+    """Q (the draw of the 16-bit workload of the same shape) and the seeded 4-bit
+    K/V rows (kq, ks, kb, vq, vs, vb) of a workload in Q4KV."""
+    q = draw(WORKLOADS["decode_q4_128k"] if wl.name == "decode_q4kv_128k" else wl)[0]
+    return (q,) + random_q4kv(Q4KV[wl.name], wl.B, wl.Hkv, wl.kL, wl.D, wl.dtype)
+
+
+def q4kv_bytes(wl: Workload) -> int:
+    """Bytes of Q, the 4-bit K and V rows (codes, scales, biases) and O, each once."""
+    q = wl.B * wl.Hq * wl.qL * wl.D * 2
+    rows = 2 * wl.B * wl.Hkv * wl.kL
+    return 2 * q + rows * (wl.D // 2 + 2 * (wl.D // 64) * 2)
 
 
 def draw(wl: Workload, device: str = "cpu"):

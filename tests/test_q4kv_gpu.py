@@ -96,11 +96,12 @@ def test_verify_rows_equal_single_row_calls_with_every_wave_loading():
 
 
 @pytest.mark.timeout(600)
-def test_the_128k_key_verify_shape_every_row():
-    # the shape of the 128K-key decode workload (16 query / 8 KV heads, head dim
-    # 256, 4 rows at the end of 131072 keys), with 4-bit K and V
-    ins = _inputs(9400, 1, 16, 8, 4, 131072, BF16)
-    note("q4kv 128k verify")
-    got = f64(_gpu(ins, causal=True))
-    ref = _oracle(ins, BF16, scale=float(np.float32(1 / 16)), causal=True, q_offset=131068)
-    check_close(got, ref, BF16, "q4kv 128k")
+def test_the_benchmarked_128k_key_verify_workload_every_row():
+    # the inputs and call the benchmark times: 16 query / 8 KV heads, head dim
+    # 256, 4 rows at the end of 131072 keys, 4-bit K and V
+    wl = W.WORKLOADS["decode_q4kv_128k"]
+    ins = W.draw_q4kv(wl)
+    note("q4kv 128k verify workload")
+    got = f64(_gpu(ins, scale=wl.scale, causal=wl.causal, window=wl.window, q_offset=wl.q_offset))
+    ref = _oracle(ins, wl.dtype, scale=wl.scale, causal=wl.causal, window=wl.window, q_offset=wl.q_offset)
+    check_close(got, ref, wl.dtype, "q4kv 128k workload")
