@@ -288,7 +288,8 @@ def sdpa_kv_cache(q, k_cache, v_cache, kv_len: int, *, ring_start: int = 0,
 
 def sdpa_q4kv(q, kq, ks, kb, vq, vs, vb, *, scale: float | None = None, causal: bool = False,
               window: int = 0, q_offset: int | None = None, out=None, workspace=None, stream=None):
-    """Decode / verify (qL <= 4) over 4-bit K and V (``sdpa_forward_q4kv``).
+    """``sdpa`` over 4-bit K and V (``sdpa_forward_q4kv``): decode / verify steps and
+    chunked prefill over a 4-bit prefix.
 
     q: [B, Hq, qL, 256] fp16 or bf16.  kq, vq: [B, Hkv, kL, 32] int32 code words
     (element 8 w + n of a row in bits 4 n .. 4 n + 3 of word w).  ks, kb, vs, vb:

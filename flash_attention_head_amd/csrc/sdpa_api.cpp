@@ -330,9 +330,6 @@ SDPA_API int sdpa_forward_q4kv(const void* q, const void* kq, const void* ks, co
   int rc = check_shape(B, Hq, Hkv, qL, kL, D, D);
   if (rc != SDPA_OK) return rc;
   if (D != 256) return fail(SDPA_UNSUPPORTED, "4-bit K/V: head dim %d is not supported (256 only)", D);
-  if (qL > kDecodeMaxRows)
-    return fail(SDPA_UNSUPPORTED, "4-bit K/V: qL %d is not supported (decode / verify, qL <= %d)", qL,
-                kDecodeMaxRows);
   if (!ks || !kb || !vs || !vb) return fail(SDPA_INVALID_ARG, "scales and biases must be non-null");
   const Q4Args q4{ks, kb, vs, vb};
   return forward_impl(q, kq, vq, nullptr, 0, 0, 0, out, B, Hq, Hkv, qL, kL, kL, 0, 0, D, D, scale, causal,

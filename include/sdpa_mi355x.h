@@ -192,9 +192,9 @@ int sdpa_forward_dv(const void* q, const void* k, const void* v, void* out, int 
 size_t sdpa_workspace_bytes_dv(int B, int Hq, int Hkv, int qL, int kL, int D, int Dv);
 
 /*
- * Decode / verify (qL <= 4) over 4-bit K and V: the prefix KV cache that
- * ml-explore/mlx PR #3660 keeps 4-bit quantized at rest (End-to-end
- * section).  The pages give no format; the affine, group-64 form that
+ * sdpa_forward over 4-bit K and V: the prefix KV cache that ml-explore/mlx
+ * PR #3660 keeps 4-bit quantized at rest (End-to-end section), read by
+ * decode / verify steps and by chunked prefill over that prefix.  The pages give no format; the affine, group-64 form that
  * lablup/mlxcel issue #2160 names for its checkpoints is taken:
  *
  *   kq, vq   device pointers, [B, Hkv, kL, D / 8] 32-bit words.  Element
@@ -211,8 +211,8 @@ size_t sdpa_workspace_bytes_dv(int B, int Hq, int Hkv, int qL, int kL, int D, in
  * is one rounding of each K and V element).  Everything else is
  * sdpa_forward's: masks, GQA, 1024-key chunks at absolute positions, and
  * each row's bytes equal to those of the single-row call over its own
- * trimmed key prefix.  D must be 256 and qL at most 4 (SDPA_UNSUPPORTED
- * otherwise); the workspace is sdpa_workspace_bytes(B, Hq, Hkv, qL, kL, D).
+ * trimmed key prefix (qL <= 4).  D must be 256 (SDPA_UNSUPPORTED otherwise);
+ * the workspace is sdpa_workspace_bytes(B, Hq, Hkv, qL, kL, D).
  */
 int sdpa_forward_q4kv(const void* q, const void* kq, const void* ks, const void* kb, const void* vq,
                       const void* vs, const void* vb, void* out, int B, int Hq, int Hkv, int qL, int kL,

@@ -273,7 +273,6 @@ def _call_q4(**kw):
 
 def test_q4kv_entry_point_rejects_what_it_does_not_take(lib):
     assert _call_q4(D=128) == fa.SDPA_UNSUPPORTED and "256" in fa.sdpa_last_error()
-    assert _call_q4(qL=5, q_offset=59) == fa.SDPA_UNSUPPORTED and "qL" in fa.sdpa_last_error()
     for name in ("ks", "kb", "vs", "vb"):
         assert _call_q4(**{name: None}) == fa.SDPA_INVALID_ARG and "non-null" in fa.sdpa_last_error()
     assert _call_q4(kq=None) == fa.SDPA_INVALID_ARG

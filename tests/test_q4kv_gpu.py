@@ -1,4 +1,4 @@
-"""Decode / verify over 4-bit K and V (sdpa_forward_q4kv) against the fp64 oracle.
+"""Attention over 4-bit K and V (sdpa_forward_q4kv) against the fp64 oracle.
 
 The 4-bit rows are the reading of the prefix KV cache that ml-explore/mlx PR
 #3660 keeps 4-bit quantized at rest (End-to-end section): affine, groups of
@@ -59,6 +59,22 @@ def test_every_row_against_the_oracle(case):
     got = f64(_gpu(ins, causal=True, window=window))
     ref = _oracle(ins, dtype, scale=float(np.float32(1 / 16)), causal=True, window=window, q_offset=kL - qL)
     check_close(got, ref, dtype, f"q4kv {case}")
+
+
+# chunked prefill over a 4-bit prefix: every wave holds rows and loads its
+# share; the last case splits its keys and merges the partials
+PREFILL = [(1, 4, 2, 100, 1000, BF16, 0), (1, 4, 2, 70, 1500, FP16, 300), (2, 2, 2, 33, 200, BF16, 0),
+           (1, 2, 1, 300, 9000, FP16, 0)]
+
+
+@pytest.mark.parametrize("case", PREFILL, ids=[f"B{c[0]}Hq{c[1]}Hkv{c[2]}q{c[3]}k{c[4]}w{c[6]}" for c in PREFILL])
+def test_prefill_over_a_4bit_prefix_against_the_oracle(case):
+    B, Hq, Hkv, qL, kL, dtype, window = case
+    ins = _inputs(9500 + kL + qL, B, Hq, Hkv, qL, kL, dtype)
+    note(f"q4kv prefill {case}")
+    got = f64(_gpu(ins, causal=True, window=window))
+    ref = _oracle(ins, dtype, scale=float(np.float32(1 / 16)), causal=True, window=window, q_offset=kL - qL)
+    check_close(got, ref, dtype, f"q4kv prefill {case}")
 
 
 def test_unmasked_decode_against_the_oracle():
