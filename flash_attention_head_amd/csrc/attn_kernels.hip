@@ -536,7 +536,8 @@ __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* ld
   // issues no loads; otherwise every wave loads its share, issued at the
   // start of a step and written to LDS at its end.
   constexpr int NBLK = TILE * 2 / 1024;   // 1 KiB blocks per tile
-  constexpr int QB = (NBLK + 2) / 3;      // blocks per tile per loading wave (3 or 4 of them)
+  constexpr int QB = (NBLK + 2) / 3;      // blocks per tile per loader of three (decode)
+  constexpr int QB4 = NBLK / 4;           // blocks per tile per wave when all four load
   struct Q4Data {  // loaded values only: nothing is computed from them before the store
     uint32_t w;     // code word
     uint32_t s, b;  // scale and bias bit patterns
@@ -578,16 +579,18 @@ __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* ld
   // Slots past the last block repeat it (the same bytes written twice), so
   // that no branch separates a load from its store and every wait counts
   auto q4_blk = [&](int i) { return min(q4_li + q4_nl * i, NBLK - 1); };
-  auto q4_issue = [&](Q4Data (&kd)[QB], Q4Data (&vd)[QB], int tk, int tv) {
+  auto q4_issue = [&](auto& kd, auto& vd, int tk, int tv) {
+    constexpr int N = sizeof(kd) / sizeof(kd[0]);
 #pragma unroll
-    for (int i = 0; i < QB; ++i) {
+    for (int i = 0; i < N; ++i) {
       kd[i] = q4_fetch(tk, q4_blk(i), false);
       vd[i] = q4_fetch(tv, q4_blk(i), true);
     }
   };
-  auto q4_put = [&](const Q4Data (&kd)[QB], const Q4Data (&vd)[QB], uint16_t* kdst, uint16_t* vdst) {
+  auto q4_put = [&](const auto& kd, const auto& vd, uint16_t* kdst, uint16_t* vdst) {
+    constexpr int N = sizeof(kd) / sizeof(kd[0]);
 #pragma unroll
-    for (int i = 0; i < QB; ++i) {
+    for (int i = 0; i < N; ++i) {
       q4_store(kd[i], kdst, q4_blk(i));
       q4_store(vd[i], vdst, q4_blk(i));
     }
@@ -896,7 +899,11 @@ __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* ld
     __syncthreads();
   }
   // Q4: the pipelined loaders' first register set, K(t0 + 2) and V(t0 + 1)
+  // With every wave loading, two sets of this wave's QB4 blocks: set P
+  // holds K(t+2), V(t+1) when step t (parity P) starts, issued one step
+  // earlier; the step issues the other set for K(t+3), V(t+2)
   typename std::conditional<Q4, Q4Data, char>::type q4a_k[Q4 ? QB : 1], q4a_v[Q4 ? QB : 1];
+  typename std::conditional<Q4, Q4Data, char>::type q4s_k[2][Q4 ? QB4 : 1], q4s_v[2][Q4 ? QB4 : 1];
   if constexpr (Q4) {
     if (q4_li >= 0) {  // wave 0 of a pipelined workgroup does not load
       Q4Data k0[QB], v0[QB], k1[QB], v1[QB];
@@ -905,6 +912,7 @@ __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* ld
       q4_put(k0, v0, kbuf0, vbuf0);
       q4_put(k1, v1, kbuf0 + TILE, vbuf0);  // V(t0) again, the same bytes
       if (q4_pipe) q4_issue(q4a_k, q4a_v, min(t_first + 2, t_last), min(t_first + 1, t_last));
+      else q4_issue(q4s_k[0], q4s_v[0], min(t_first + 2, t_last), min(t_first + 1, t_last));
     }
   } else {
     load_k(t_first);
@@ -974,11 +982,11 @@ __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* ld
     uint2 bw[KB * 4];
     const TileSrc vsrc = tile_src(vg, tv, true);
     uint16_t* const vdst = vbuf0 + (V3 ? (VB + 2) % 3 : 1 - P) * TILE;
-    // Q4 with every wave loading: this wave's blocks of K(t+2) and V(t+1),
-    // issued now and written to LDS at the end of the step
-    typename std::conditional<Q4, Q4Data, char>::type q4k[Q4 ? QB : 1], q4v[Q4 ? QB : 1];
+    // Q4 with every wave loading: issue this wave's blocks of K(t+3) and
+    // V(t+2) now; K(t+2) and V(t+1), issued in the last step, are written to
+    // LDS at the end of this one
     if constexpr (Q4) {
-      if (!q4_pipe) q4_issue(q4k, q4v, tk, tv);
+      if (!q4_pipe) q4_issue(q4s_k[1 - P], q4s_v[1 - P], min(t + 3, t_last), min(t + 2, t_last));
     }
     const float psum = qk_weights(sn, kl, sc, pb, tile_src(kg, tk, false), kbuf0 + P * TILE,
                                   vsrc, vdst, BIAS ? bias_src(tk) : i32x4_t{}, bbuf0 + P * BTILE,
@@ -988,7 +996,7 @@ __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* ld
     if (!full_tile(t + 1)) mask(sn, t + 1);
     alpha_cur = pv_max(pb, vbuf0 + (V3 ? VB : P) * TILE, sn, has_next, bw, vsrc, vdst);
     if constexpr (Q4) {
-      if (!q4_pipe) q4_put(q4k, q4v, kbuf0 + P * TILE, vdst);
+      if (!q4_pipe) q4_put(q4s_k[P], q4s_v[P], kbuf0 + P * TILE, vdst);
     }
     // VLATE: K(t+2) (and its bias) have landed, and with V3 V(t+1) too; the
     // V loads of this step may be in flight.  Otherwise everything has.
@@ -1039,12 +1047,14 @@ __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* ld
         q4_issue(q4a_k, q4a_v, min(t + 4, t_last), min(t + 3, t_last));
         __syncthreads();
       }
-    } else {
-      for (int t = t_first; t <= t_last; ++t) {
-        const int P = (t - t_first) & 1;
-        Q4Data kd[QB], vd[QB];
-        q4_issue(kd, vd, min(t + 2, t_last), min(t + 1, t_last));
-        q4_put(kd, vd, kbuf0 + P * TILE, vbuf0 + (1 - P) * TILE);
+    } else {  // every wave loads, one step ahead, as the row-holding waves do
+      for (int t = t_first; t <= t_last; t += 2) {
+        q4_issue(q4s_k[1], q4s_v[1], min(t + 3, t_last), min(t + 2, t_last));
+        q4_put(q4s_k[0], q4s_v[0], kbuf0, vbuf0 + TILE);
+        __syncthreads();
+        if (t + 1 > t_last) break;
+        q4_issue(q4s_k[0], q4s_v[0], min(t + 4, t_last), min(t + 3, t_last));
+        q4_put(q4s_k[1], q4s_v[1], kbuf0 + TILE, vbuf0);
         __syncthreads();
       }
     }
