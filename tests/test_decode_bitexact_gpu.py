@@ -122,3 +122,12 @@ def test_rows_whose_prefixes_straddle_a_power_of_two_of_chunks():
     # count to fill 256 workgroups would step from 2048 to 4096 keys
     q, k, v = W.random_qkv(73, 1, 16, 8, 4, 126978, 256, BF16)
     _check_rows(q, k, v, window=0, what="126978 keys")
+
+
+@pytest.mark.parametrize("dtype", [FP16, BF16])
+def test_verify_block_spanning_two_row_waves_at_group_of_sixteen(dtype):
+    # G = 16 at head dim 256: a 4-row verify block is 64 packed rows, held by
+    # two waves, while each single-row call's 16 rows sit in one wave
+    q, k, v = W.random_qkv(74, 1, 32, 2, 4, 9000, 256, dtype)
+    _check_rows(q, k, v, window=0, what=f"G16 dtype {dtype}")
+    _check_rows(q, k, v, window=2000, what=f"G16 window dtype {dtype}")
