@@ -98,12 +98,13 @@ def time_q4kv(wl, steps, warmup):
 
     ins = [t.cuda() for t in W.draw_q4kv(wl)]
     out = torch.empty_like(ins[0])
-    need = fa.sdpa_workspace_bytes(wl.B, wl.Hq, wl.Hkv, wl.qL, wl.kL, wl.D)
+    # a full 4-bit cache of kL rows
+    need = fa.sdpa_workspace_bytes_kv_view(wl.B, wl.Hq, wl.Hkv, wl.qL, wl.kL, wl.kL, wl.D)
     ws = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
     stream = torch.cuda.current_stream()
 
     def call():
-        fa.sdpa_q4kv(*ins, scale=wl.scale, causal=wl.causal, window=wl.window, q_offset=wl.q_offset,
+        fa.sdpa_q4kv(*ins, kv_len=wl.kL, scale=wl.scale, causal=wl.causal, window=wl.window, q_offset=wl.q_offset,
                      out=out, workspace=ws, stream=stream)
 
     for _ in range(warmup):

@@ -87,7 +87,7 @@ def load_library():
     lib.sdpa_forward_dv.restype = ci
     lib.sdpa_workspace_bytes_dv.argtypes = [ci] * 7
     lib.sdpa_workspace_bytes_dv.restype = sz
-    lib.sdpa_forward_q4kv.argtypes = [vp] * 8 + [ci] * 6 + [ctypes.c_float] + [ci] * 4 + [vp, sz, vp]
+    lib.sdpa_forward_q4kv.argtypes = [vp] * 8 + [ci] * 8 + [ctypes.c_float] + [ci] * 4 + [vp, sz, vp]
     lib.sdpa_forward_q4kv.restype = ci
     lib.sdpa_last_error.argtypes = []
     lib.sdpa_last_error.restype = ctypes.c_char_p
@@ -143,12 +143,12 @@ def sdpa_workspace_bytes_dv(B, Hq, Hkv, qL, kL, D, Dv) -> int:
     return load_library().sdpa_workspace_bytes_dv(B, Hq, Hkv, qL, kL, D, Dv)
 
 
-def sdpa_forward_q4kv(q, kq, ks, kb, vq, vs, vb, out, B, Hq, Hkv, qL, kL, D, scale, causal, window,
-                      q_offset, dtype, workspace, workspace_bytes, stream) -> int:
+def sdpa_forward_q4kv(q, kq, ks, kb, vq, vs, vb, out, B, Hq, Hkv, qL, kL, kv_capacity, ring_start, D, scale,
+                      causal, window, q_offset, dtype, workspace, workspace_bytes, stream) -> int:
     """``int sdpa_forward_q4kv(...)`` of the C ABI; pointer arguments are integers."""
-    return load_library().sdpa_forward_q4kv(q, kq, ks, kb, vq, vs, vb, out, B, Hq, Hkv, qL, kL, D, scale,
-                                            causal, window, q_offset, dtype, workspace, workspace_bytes,
-                                            stream)
+    return load_library().sdpa_forward_q4kv(q, kq, ks, kb, vq, vs, vb, out, B, Hq, Hkv, qL, kL, kv_capacity,
+                                            ring_start, D, scale, causal, window, q_offset, dtype, workspace,
+                                            workspace_bytes, stream)
 
 
 def sdpa_last_error() -> str:
@@ -286,42 +286,46 @@ def sdpa_kv_cache(q, k_cache, v_cache, kv_len: int, *, ring_start: int = 0,
     return out
 
 
-def sdpa_q4kv(q, kq, ks, kb, vq, vs, vb, *, scale: float | None = None, causal: bool = False,
-              window: int = 0, q_offset: int | None = None, out=None, workspace=None, stream=None):
-    """``sdpa`` over 4-bit K and V (``sdpa_forward_q4kv``): decode / verify steps and
-    chunked prefill over a 4-bit prefix.
+def sdpa_q4kv(q, kq, ks, kb, vq, vs, vb, *, kv_len: int | None = None, ring_start: int = 0,
+              scale: float | None = None, causal: bool = False, window: int = 0, q_offset: int | None = None,
+              out=None, workspace=None, stream=None):
+    """``sdpa_kv_cache`` over a 4-bit KV cache (``sdpa_forward_q4kv``): decode / verify
+    steps and chunked prefill over a 4-bit prefix.
 
-    q: [B, Hq, qL, 256] fp16 or bf16.  kq, vq: [B, Hkv, kL, 32] int32 code words
+    q: [B, Hq, qL, 256] fp16 or bf16.  kq, vq: [B, Hkv, capacity, 32] int32 code words
     (element 8 w + n of a row in bits 4 n .. 4 n + 3 of word w).  ks, kb, vs, vb:
-    [B, Hkv, kL, 4] of q's dtype, the scale and bias of each 64-element group;
-    element d of a row is scale[d // 64] * code_d + bias[d // 64].  Everything else
-    as in ``sdpa``.
+    [B, Hkv, capacity, 4] of q's dtype, the scale and bias of each 64-element group;
+    element d of a row is scale[d // 64] * code_d + bias[d // 64].  kv_len live keys
+    (default: the capacity), logical key j in row (ring_start + j) % capacity.  Decode
+    and verify calls over one cache use key chunks fixed by (B, Hkv, capacity), so a
+    verify row and the single-row call over its trimmed key count agree byte for byte.
     """
     import torch
 
     if q.dim() != 4 or kq.dim() != 4 or vq.dim() != 4:
         raise ValueError("q and the code words must be 4-D")
     B, Hq, qL, D = q.shape
-    Bk, Hkv, kL, W = kq.shape
+    Bk, Hkv, cap, W = kq.shape
     if q.dtype not in (torch.float16, torch.bfloat16) or kq.dtype != torch.int32 or vq.dtype != torch.int32:
         raise ValueError("q must be fp16/bf16 and the code words int32")
     if Bk != B or W * 8 != D or tuple(vq.shape) != tuple(kq.shape):
         raise ValueError(f"shape mismatch: q {tuple(q.shape)}, kq {tuple(kq.shape)}, vq {tuple(vq.shape)}")
     for t in (ks, kb, vs, vb):
-        if tuple(t.shape) != (B, Hkv, kL, D // 64) or t.dtype != q.dtype:
-            raise ValueError("scales and biases must be [B, Hkv, kL, D / 64] tensors of q's dtype")
+        if tuple(t.shape) != (B, Hkv, cap, D // 64) or t.dtype != q.dtype:
+            raise ValueError("scales and biases must be [B, Hkv, capacity, D / 64] tensors of q's dtype")
     ts = (q, kq, ks, kb, vq, vs, vb)
     if not all(t.is_cuda and t.is_contiguous() for t in ts):
         raise ValueError("all inputs must be contiguous GPU tensors")
     dtype = SDPA_FP16 if q.dtype == torch.float16 else SDPA_BF16
+    kL = cap if kv_len is None else int(kv_len)
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     if q_offset is None:
         q_offset = kL - qL if causal else 0
-    need = sdpa_workspace_bytes(B, Hq, Hkv, qL, kL, D)
+    need = sdpa_workspace_bytes_kv_view(B, Hq, Hkv, qL, kL, cap, D)
     out, ws_ptr, ws_bytes, stream = _prepare(q, need, D, out, workspace, stream)
-    rc = sdpa_forward_q4kv(*(t.data_ptr() for t in ts), out.data_ptr(), B, Hq, Hkv, qL, kL, D, float(scale),
-                           int(bool(causal)), int(window), int(q_offset), dtype, ws_ptr, ws_bytes,
+    rc = sdpa_forward_q4kv(*(t.data_ptr() for t in ts), out.data_ptr(), B, Hq, Hkv, qL, kL, cap, int(ring_start), D,
+                           float(scale), int(bool(causal)), int(window), int(q_offset), dtype, ws_ptr, ws_bytes,
                            stream.cuda_stream)
     if rc != SDPA_OK:
         raise SdpaError(rc, sdpa_last_error())

@@ -527,7 +527,9 @@ __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* ld
   // load would have written there (key row r of the block's RPB rows, chunk
   // c after the K or V swizzle): one 32-bit code word, the scale and the
   // bias of its 64-element group, then fp32 scale * code + bias for each
-  // nibble, rounded to the input dtype.  Rows past kL repeat row kL - 1
+  // nibble, rounded to the input dtype.  The rows are those of a KV cache
+  // (kv_cap rows per head, logical key j in row (ring_start + j) mod
+  // kv_cap), wrapped per lane.  Rows past kL repeat row kL - 1
   // (finite values; their keys are masked, so their weights are exactly 0):
   // no branch around a load, so the loads' waits stay counted.
   // Loading waves: with one row-holding wave (G * qL <= 32 rows in the
@@ -546,14 +548,18 @@ __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* ld
   const bool q4_pipe = Q4 && n_act == 1;          // waves 1..3 load, one step ahead
   const int q4_nl = q4_pipe ? NW - 1 : NW;        // loading waves
   const int q4_li = q4_pipe ? wave - 1 : wave;    // this wave's index among them
-  const size_t q4_head = (size_t)(b * p.Hkv + hkv) * (size_t)p.kL;  // the head's first K/V row
+  const size_t q4_head = (size_t)(b * p.Hkv + hkv) * (size_t)p.kv_cap;  // the head's first cache row
   auto q4_fetch = [&](int t, int blk, bool is_v) {
     const int r = blk * RPB + lane / ROWCH, pch = lane % ROWCH;
     const int c = is_v ? (pch ^ ((r & VSW) << 2)) : (pch ^ (r & 15));
     const int key = min(t * BN + r, p.kL - 1);
+    // logical key -> cache row: (ring_start + key) mod kv_cap, by one select
+    // (ring_start < kv_cap and key < kL <= kv_cap)
+    int phys = p.ring_start + key;
+    phys = phys >= p.kv_cap ? phys - p.kv_cap : phys;
     Q4Data d{0u, 0u, 0u};
     if constexpr (Q4) {
-      const size_t row = q4_head + (size_t)key;
+      const size_t row = q4_head + (size_t)phys;
       d.w = (is_v ? p.vq4 : p.kq4)[row * (DK / 8) + c];
       const size_t g = row * (DK / 64) + c / 8;
       d.s = (is_v ? p.vs4 : p.ks4)[g];

@@ -323,15 +323,17 @@ SDPA_API int sdpa_forward_kv_view(const void* q, const void* k, const void* v, v
 
 SDPA_API int sdpa_forward_q4kv(const void* q, const void* kq, const void* ks, const void* kb,
                                const void* vq, const void* vs, const void* vb, void* out, int B,
-                               int Hq, int Hkv, int qL, int kL, int D, float scale, int causal,
-                               int window, int q_offset, int dtype, void* workspace,
-                               size_t workspace_bytes, void* stream) {
+                               int Hq, int Hkv, int qL, int kL, int kv_capacity, int ring_start, int D,
+                               float scale, int causal, int window, int q_offset, int dtype,
+                               void* workspace, size_t workspace_bytes, void* stream) {
   g_last_error[0] = '\0';
   int rc = check_shape(B, Hq, Hkv, qL, kL, D, D);
+  if (rc != SDPA_OK) return rc;
+  rc = check_view(kL, kv_capacity, ring_start);
   if (rc != SDPA_OK) return rc;
   if (D != 256) return fail(SDPA_UNSUPPORTED, "4-bit K/V: head dim %d is not supported (256 only)", D);
   if (!ks || !kb || !vs || !vb) return fail(SDPA_INVALID_ARG, "scales and biases must be non-null");
   const Q4Args q4{ks, kb, vs, vb};
-  return forward_impl(q, kq, vq, nullptr, 0, 0, 0, out, B, Hq, Hkv, qL, kL, kL, 0, 0, D, D, scale, causal,
-                      window, q_offset, dtype, workspace, workspace_bytes, stream, &q4);
+  return forward_impl(q, kq, vq, nullptr, 0, 0, 0, out, B, Hq, Hkv, qL, kL, kv_capacity, ring_start, kv_capacity,
+                      D, D, scale, causal, window, q_offset, dtype, workspace, workspace_bytes, stream, &q4);
 }

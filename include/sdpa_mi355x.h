@@ -192,32 +192,37 @@ int sdpa_forward_dv(const void* q, const void* k, const void* v, void* out, int 
 size_t sdpa_workspace_bytes_dv(int B, int Hq, int Hkv, int qL, int kL, int D, int Dv);
 
 /*
- * sdpa_forward over 4-bit K and V: the prefix KV cache that ml-explore/mlx
- * PR #3660 keeps 4-bit quantized at rest (End-to-end section), read by
- * decode / verify steps and by chunked prefill over that prefix.  The pages give no format; the affine, group-64 form that
+ * sdpa_forward_kv_view over 4-bit K and V: the prefix KV cache that
+ * ml-explore/mlx PR #3660 keeps 4-bit quantized at rest (End-to-end
+ * section), read by decode / verify steps and by chunked prefill over that
+ * prefix.  The pages give no format; the affine, group-64 form that
  * lablup/mlxcel issue #2160 names for its checkpoints is taken:
  *
- *   kq, vq   device pointers, [B, Hkv, kL, D / 8] 32-bit words.  Element
- *            8 w + n of a key or value row is the 4-bit code in bits
+ *   kq, vq   device pointers, [B, Hkv, kv_capacity, D / 8] 32-bit words.
+ *            Element 8 w + n of a key or value row is the 4-bit code in bits
  *            4 n .. 4 n + 3 of word w of the row.
- *   ks, kb,  device pointers, [B, Hkv, kL, D / 64], element type `dtype`:
- *   vs, vb   the scale and the bias of each group of 64 consecutive
- *            elements of a row.  Element d of a row is
+ *   ks, kb,  device pointers, [B, Hkv, kv_capacity, D / 64], element type
+ *   vs, vb   `dtype`: the scale and the bias of each group of 64
+ *            consecutive elements of a row.  Element d of a row is
  *            scale[d / 64] * code_d + bias[d / 64].
+ *   kL, kv_capacity, ring_start   as in sdpa_forward_kv_view: kL live keys,
+ *            logical key j in row (ring_start + j) % kv_capacity of its head.
  *   q, out   as in sdpa_forward.  None of the inputs may overlap out.
  *
  * The kernel forms scale * code + bias in fp32 and rounds it to `dtype`
  * before the products (the plain definition keeps it exact; the difference
  * is one rounding of each K and V element).  Everything else is
- * sdpa_forward's: masks, GQA, 1024-key chunks at absolute positions, and
- * each row's bytes equal to those of the single-row call over its own
- * trimmed key prefix (qL <= 4).  D must be 256 (SDPA_UNSUPPORTED otherwise);
- * the workspace is sdpa_workspace_bytes(B, Hq, Hkv, qL, kL, D).
+ * sdpa_forward_kv_view's: masks, GQA, decode chunks sized from (B, Hkv,
+ * kv_capacity) at absolute positions, and each verify row's bytes equal to
+ * those of the single-row call over the same cache with its own trimmed
+ * key count (qL <= 4).  D must be 256 (SDPA_UNSUPPORTED otherwise); the
+ * workspace is sdpa_workspace_bytes_kv_view(B, Hq, Hkv, qL, kL,
+ * kv_capacity, D).
  */
 int sdpa_forward_q4kv(const void* q, const void* kq, const void* ks, const void* kb, const void* vq,
                       const void* vs, const void* vb, void* out, int B, int Hq, int Hkv, int qL, int kL,
-                      int D, float scale, int causal, int window, int q_offset, int dtype,
-                      void* workspace, size_t workspace_bytes, void* stream);
+                      int kv_capacity, int ring_start, int D, float scale, int causal, int window,
+                      int q_offset, int dtype, void* workspace, size_t workspace_bytes, void* stream);
 
 /* Message for the last non-zero status returned on the calling thread ("" if none). */
 const char* sdpa_last_error(void);

@@ -260,10 +260,10 @@ def test_value_dim_workspace_counts_value_columns(lib):
 
 # sdpa_forward_q4kv: decode / verify over 4-bit K and V
 Q4_BASE = dict(q=0x1000, kq=0x100000, ks=0x180000, kb=0x190000, vq=0x200000, vs=0x280000, vb=0x290000,
-               out=0x300000, B=1, Hq=4, Hkv=2, qL=4, kL=64, D=256, scale=0.0625, causal=1, window=0,
+               out=0x300000, B=1, Hq=4, Hkv=2, qL=4, kL=64, cap=64, ring=0, D=256, scale=0.0625, causal=1, window=0,
                q_offset=60, dtype=fa.SDPA_BF16, workspace=0x400000, workspace_bytes=1 << 30, stream=None)
-Q4_ORDER = ["q", "kq", "ks", "kb", "vq", "vs", "vb", "out", "B", "Hq", "Hkv", "qL", "kL", "D", "scale", "causal",
-            "window", "q_offset", "dtype", "workspace", "workspace_bytes", "stream"]
+Q4_ORDER = ["q", "kq", "ks", "kb", "vq", "vs", "vb", "out", "B", "Hq", "Hkv", "qL", "kL", "cap", "ring", "D",
+            "scale", "causal", "window", "q_offset", "dtype", "workspace", "workspace_bytes", "stream"]
 
 
 def _call_q4(**kw):
@@ -279,6 +279,8 @@ def test_q4kv_entry_point_rejects_what_it_does_not_take(lib):
     assert _call_q4(Hq=3) == fa.SDPA_INVALID_ARG and "multiple" in fa.sdpa_last_error()
     assert _call_q4(q_offset=61) == fa.SDPA_INVALID_ARG and "q_offset" in fa.sdpa_last_error()
     assert _call_q4(workspace_bytes=16) == fa.SDPA_WORKSPACE_TOO_SMALL
+    assert _call_q4(cap=63) == fa.SDPA_INVALID_ARG and "kv_capacity" in fa.sdpa_last_error()
+    assert _call_q4(ring=64) == fa.SDPA_INVALID_ARG and "ring_start" in fa.sdpa_last_error()
     # out is [1, 4, 4, 256] fp16/bf16 = 8 KiB: starting 4 KiB before kq it reaches into kq, and
     # starting inside the scales of K it overlaps them
     assert _call_q4(out=0x100000 - 4096) == fa.SDPA_INVALID_ARG and "overlap" in fa.sdpa_last_error()

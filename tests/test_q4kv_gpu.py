@@ -86,6 +86,8 @@ def test_unmasked_decode_against_the_oracle():
 
 
 def _check_verify_rows(ins, window, what):
+    # the block over a full cache of kL rows; each row alone over the same
+    # cache with its own trimmed key count, as a decode step issues it
     q, kq, ks, kb, vq, vs, vb = (t.cuda() for t in ins)
     qL, kL = q.shape[2], kq.shape[2]
     note(f"{what}: block")
@@ -94,11 +96,35 @@ def _check_verify_rows(ins, window, what):
     for r in range(qL):
         n = kL - qL + r + 1
         note(f"{what}: row {r} over {n} keys")
-        one = fa.sdpa_q4kv(q[:, :, r:r + 1].contiguous(), *(t[:, :, :n].contiguous() for t in (kq, ks, kb, vq, vs, vb)),
-                           causal=True, window=window)
+        one = fa.sdpa_q4kv(q[:, :, r:r + 1].contiguous(), kq, ks, kb, vq, vs, vb, kv_len=n, causal=True,
+                           window=window)
         torch.cuda.synchronize()
         a = block[:, :, r:r + 1].contiguous().view(torch.int16)
         assert torch.equal(a, one.view(torch.int16)), f"{what}: row {r} differs"
+
+
+def _to_cache(t, cap, ring_start):
+    """A [B, H, kL, ...] tensor laid into a cache of `cap` rows from row ring_start, wrapping."""
+    kL = t.shape[2]
+    c = torch.zeros(t.shape[:2] + (cap,) + t.shape[3:], dtype=t.dtype)
+    idx = (ring_start + torch.arange(kL)) % cap
+    c[:, :, idx] = t
+    return c
+
+
+@pytest.mark.parametrize("qL,kL,cap,rs", [(4, 3000, 3000, 1234), (4, 3000, 3500, 3301), (70, 2000, 2600, 2100)])
+def test_ring_cache_equals_the_same_keys_from_row_zero(qL, kL, cap, rs):
+    # logical key j in cache row (rs + j) % cap: the same bytes as the keys stored from row 0
+    ins = _inputs(9600 + rs, 1, 8, 2, qL, kL, BF16)
+    note(f"q4kv ring q{qL} k{kL} cap{cap} rs{rs}")
+    outs = []
+    for start in (rs, 0):
+        kv = [_to_cache(t, cap, start).cuda() for t in ins[1:]]
+        outs.append(fa.sdpa_q4kv(ins[0].cuda(), *kv, kv_len=kL, ring_start=start, causal=True).cpu())
+        torch.cuda.synchronize()
+    assert torch.equal(outs[0].view(torch.int16), outs[1].view(torch.int16))
+    ref = _oracle(ins, BF16, scale=float(np.float32(1 / 16)), causal=True, q_offset=kL - qL)
+    check_close(f64(outs[0]), ref, BF16, f"q4kv ring q{qL} k{kL} cap{cap} rs{rs}")
 
 
 @pytest.mark.parametrize("kL,window", [(20000, 0), (20000, 1024), (4097, 0), (4099, 3)])
