@@ -291,6 +291,16 @@ def main():
             extra[name] = summarize(w2, t2)
             log(f"[bench] {name}: {extra[name]}")
 
+    # null arm: the headline workload timed again after everything else, so
+    # the line carries its own run-to-run spread
+    null_arm = None
+    if args.extra:
+        log(f"[bench] {wl.name} again (null arm)")
+        t_again = time_workload(wl, args.steps, args.warmup)
+        null_arm = {"first_ms": round(t["event_ms_mean"], 4), "repeat_ms": round(t_again["event_ms_mean"], 4),
+                    "rel_diff": round(t_again["event_ms_mean"] / t["event_ms_mean"] - 1.0, 4)}
+        log(f"[bench] null arm: {null_arm}")
+
     read_ref = None
     if args.extra:
         log("[bench] plain streaming read (context for the decode lines)")
@@ -329,6 +339,7 @@ def main():
         "cpu_baseline": base,
         "extra": extra,
         "hbm_read_reference": read_ref,
+        "null_arm": null_arm,
     }
     print(json.dumps(line), flush=True)
 
