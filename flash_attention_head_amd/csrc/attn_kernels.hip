@@ -1087,7 +1087,13 @@ __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* ld
   // ---- epilogue ---------------------------------------------------------
   const float lsum = pair_sum(l_run);
   if (!valid) return;
-  const size_t orow = (size_t)(b * p.Hq + hq) * p.qL + qi;
+  int hq_o = hq, qi_o = qi;
+  if constexpr (Q4)
+    // the 4-bit instances hold their loaded code words, scales and biases
+    // across the step loop; left alone the compiler forms the 64-bit output
+    // offset before the loop and spills it, so it is formed here instead
+    asm volatile("" : "+v"(hq_o), "+v"(qi_o));
+  const size_t orow = (size_t)(b * p.Hq + hq_o) * p.qL + qi_o;
   if (!p.partials) {
     const float inv = lsum > 0.f ? 1.0f / lsum : 0.f;  // a row with no finite score: zeros
     uint16_t* dst = p.out + orow * DV + od0;
