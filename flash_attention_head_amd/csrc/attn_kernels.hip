@@ -549,6 +549,12 @@ __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* ld
   const int q4_nl = q4_pipe ? NW - 1 : NW;        // loading waves
   const int q4_li = q4_pipe ? wave - 1 : wave;    // this wave's index among them
   const size_t q4_head = (size_t)(b * p.Hkv + hkv) * (size_t)p.kv_cap;  // the head's first cache row
+  const uint32_t* const q4_kq = p.kq4 + q4_head * (DK / 8);
+  const uint32_t* const q4_vq = p.vq4 + q4_head * (DK / 8);
+  const uint16_t* const q4_ks = p.ks4 + q4_head * (DK / 64);
+  const uint16_t* const q4_kb = p.kb4 + q4_head * (DK / 64);
+  const uint16_t* const q4_vs = p.vs4 + q4_head * (DK / 64);
+  const uint16_t* const q4_vb = p.vb4 + q4_head * (DK / 64);
   auto q4_fetch = [&](int t, int blk, bool is_v) {
     const int r = blk * RPB + lane / ROWCH, pch = lane % ROWCH;
     const int c = is_v ? (pch ^ ((r & VSW) << 2)) : (pch ^ (r & 15));
@@ -559,11 +565,13 @@ __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* ld
     phys = phys >= p.kv_cap ? phys - p.kv_cap : phys;
     Q4Data d{0u, 0u, 0u};
     if constexpr (Q4) {
-      const size_t row = q4_head + (size_t)phys;
-      d.w = (is_v ? p.vq4 : p.kq4)[row * (DK / 8) + c];
-      const size_t g = row * (DK / 64) + c / 8;
-      d.s = (is_v ? p.vs4 : p.ks4)[g];
-      d.b = (is_v ? p.vb4 : p.kb4)[g];
+      // 32-bit byte offsets from the head's first row (a head's code words
+      // stay below 4 GiB: the entry point bounds kv_cap)
+      const uint32_t wb = ((uint32_t)phys * (DK / 8) + (uint32_t)c) * 4u;
+      const uint32_t gb = ((uint32_t)phys * (DK / 64) + (uint32_t)(c / 8)) * 2u;
+      d.w = *(const uint32_t*)((const char*)(is_v ? q4_vq : q4_kq) + wb);
+      d.s = *(const uint16_t*)((const char*)(is_v ? q4_vs : q4_ks) + gb);
+      d.b = *(const uint16_t*)((const char*)(is_v ? q4_vb : q4_kb) + gb);
     }
     return d;
   };
@@ -573,12 +581,30 @@ __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* ld
   };
   auto q4_store = [&](const Q4Data& d, uint16_t* buf, int blk) {
     const float sc = q4_widen(d.s), bi = q4_widen(d.b);
-    auto val = [&](int n) { return fmaf(sc, (float)((d.w >> (4 * n)) & 15u), bi); };
+    // even elements' codes in the bytes of lo, odd ones' in the bytes of hi:
+    // each code is then one byte-to-float conversion (from inline assembly:
+    // from the plain C the compiler forms a bit-field extract and a byte-0
+    // conversion per code, twice the instructions)
+    const uint32_t lo = d.w & 0x0F0F0F0Fu, hi = (d.w >> 4) & 0x0F0F0F0Fu;
+    auto byte_f = [](uint32_t x, auto kc) {  // v_cvt_f32_ubyte<k>: byte k of x as a float
+      constexpr int k = decltype(kc)::value;
+      float f;
+      if constexpr (k == 0) asm("v_cvt_f32_ubyte0 %0, %1" : "=v"(f) : "v"(x));
+      else if constexpr (k == 1) asm("v_cvt_f32_ubyte1 %0, %1" : "=v"(f) : "v"(x));
+      else if constexpr (k == 2) asm("v_cvt_f32_ubyte2 %0, %1" : "=v"(f) : "v"(x));
+      else asm("v_cvt_f32_ubyte3 %0, %1" : "=v"(f) : "v"(x));
+      return f;
+    };
+    auto val = [&](uint32_t x, auto kc) { return fmaf(sc, byte_f(x, kc), bi); };
+    using K0 = std::integral_constant<int, 0>;
+    using K1 = std::integral_constant<int, 1>;
+    using K2 = std::integral_constant<int, 2>;
+    using K3 = std::integral_constant<int, 3>;
     uint4 out;
-    out.x = Elem<DT>::pack2(val(0), val(1));
-    out.y = Elem<DT>::pack2(val(2), val(3));
-    out.z = Elem<DT>::pack2(val(4), val(5));
-    out.w = Elem<DT>::pack2(val(6), val(7));
+    out.x = Elem<DT>::pack2(val(lo, K0{}), val(hi, K0{}));
+    out.y = Elem<DT>::pack2(val(lo, K1{}), val(hi, K1{}));
+    out.z = Elem<DT>::pack2(val(lo, K2{}), val(hi, K2{}));
+    out.w = Elem<DT>::pack2(val(lo, K3{}), val(hi, K3{}));
     *(uint4*)(buf + blk * 512 + 8 * lane) = out;
   };
   // this wave's blocks of K tile tk and V tile tv: issue, then store.

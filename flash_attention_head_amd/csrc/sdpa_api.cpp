@@ -332,6 +332,10 @@ SDPA_API int sdpa_forward_q4kv(const void* q, const void* kq, const void* ks, co
   rc = check_view(kL, kv_capacity, ring_start);
   if (rc != SDPA_OK) return rc;
   if (D != 256) return fail(SDPA_UNSUPPORTED, "4-bit K/V: head dim %d is not supported (256 only)", D);
+  // the kernel addresses a head's rows by 32-bit byte offsets from its first row
+  if ((uint64_t)kv_capacity * (uint64_t)(D / 2) > (1ull << 32))
+    return fail(SDPA_UNSUPPORTED, "4-bit K/V: kv_capacity %d exceeds %d rows (a head's code words must fit in 4 GiB)",
+                kv_capacity, (int)((1ull << 32) / (uint64_t)(D / 2)));
   if (!ks || !kb || !vs || !vb) return fail(SDPA_INVALID_ARG, "scales and biases must be non-null");
   const Q4Args q4{ks, kb, vs, vb};
   return forward_impl(q, kq, vq, nullptr, 0, 0, 0, out, B, Hq, Hkv, qL, kL, kv_capacity, ring_start, kv_capacity,

@@ -215,7 +215,8 @@ size_t sdpa_workspace_bytes_dv(int B, int Hq, int Hkv, int qL, int kL, int D, in
  * sdpa_forward_kv_view's: masks, GQA, decode chunks sized from (B, Hkv,
  * kv_capacity) at absolute positions, and each verify row's bytes equal to
  * those of the single-row call over the same cache with its own trimmed
- * key count (qL <= 4).  D must be 256 (SDPA_UNSUPPORTED otherwise); the
+ * key count (qL <= 4).  D must be 256 and kv_capacity at most 33554432 rows
+ * (2^25: one head's code words within 4 GiB), SDPA_UNSUPPORTED otherwise; the
  * workspace is sdpa_workspace_bytes_kv_view(B, Hq, Hkv, qL, kL,
  * kv_capacity, D).
  */

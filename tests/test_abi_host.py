@@ -281,6 +281,8 @@ def test_q4kv_entry_point_rejects_what_it_does_not_take(lib):
     assert _call_q4(workspace_bytes=16) == fa.SDPA_WORKSPACE_TOO_SMALL
     assert _call_q4(cap=63) == fa.SDPA_INVALID_ARG and "kv_capacity" in fa.sdpa_last_error()
     assert _call_q4(ring=64) == fa.SDPA_INVALID_ARG and "ring_start" in fa.sdpa_last_error()
+    # a head's code words are addressed by 32-bit byte offsets: 2^25 rows at most
+    assert _call_q4(cap=(1 << 25) + 1) == fa.SDPA_UNSUPPORTED and "33554432" in fa.sdpa_last_error()
     # out is [1, 4, 4, 256] fp16/bf16 = 8 KiB: starting 4 KiB before kq it reaches into kq, and
     # starting inside the scales of K it overlaps them
     assert _call_q4(out=0x100000 - 4096) == fa.SDPA_INVALID_ARG and "overlap" in fa.sdpa_last_error()
