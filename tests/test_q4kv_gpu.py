@@ -127,6 +127,32 @@ def test_ring_cache_equals_the_same_keys_from_row_zero(qL, kL, cap, rs):
     check_close(f64(outs[0]), ref, BF16, f"q4kv ring q{qL} k{kL} cap{cap} rs{rs}")
 
 
+@pytest.mark.timeout(300)
+def test_largest_capacity_reads_the_last_rows_below_4_gib():
+    # 2^25 cache rows, the most the entry point takes: one head's code words
+    # span 4 GiB, addressed by 32-bit byte offsets from its first row.  The
+    # live keys wrap from the last 100 rows of the cache to its first rows,
+    # so the top offsets are read; the result equals the same keys stored
+    # from row 0 of the same cache, and the oracle.  (9 GiB of device memory;
+    # rows outside the live keys are zero and never read.)
+    cap, qL, kL = 1 << 25, 4, 300
+    ins = _inputs(9700, 1, 2, 1, qL, kL, BF16)
+    note(f"q4kv capacity 2^25, ring start {cap - 100}")
+    caches = [torch.zeros((1, 1, cap) + tuple(t.shape[3:]), dtype=t.dtype, device="cuda") for t in ins[1:]]
+    outs = []
+    for start in (cap - 100, 0):
+        idx = ((start + torch.arange(kL)) % cap).cuda()
+        for c, t in zip(caches, ins[1:]):
+            c[:, :, idx] = t.cuda()
+        outs.append(fa.sdpa_q4kv(ins[0].cuda(), *caches, kv_len=kL, ring_start=start, causal=True).cpu())
+        torch.cuda.synchronize()
+    del caches
+    torch.cuda.empty_cache()
+    assert torch.equal(outs[0].view(torch.int16), outs[1].view(torch.int16))
+    ref = _oracle(ins, BF16, scale=float(np.float32(1 / 16)), causal=True, q_offset=kL - qL)
+    check_close(f64(outs[0]), ref, BF16, "q4kv capacity 2^25")
+
+
 @pytest.mark.parametrize("kL,window", [(20000, 0), (20000, 1024), (4097, 0), (4099, 3)])
 def test_verify_rows_equal_single_row_calls_with_three_loading_waves(kL, window):
     _check_verify_rows(_inputs(9200 + kL, 1, 16, 8, 4, kL, BF16), window, f"q4kv G2 kL{kL} w{window}")
