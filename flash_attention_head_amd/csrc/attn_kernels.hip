@@ -485,14 +485,17 @@ __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* ld
     const int r = rb * kRowsPerWave + lr;  // this lane's row in the bias tile
     bbase = r * BN + 8 * (r & (BCPR - 1)) + 4 * lg;
   }
-  // batch b's bias from key t BN to the end of its extent.  The range check
-  // is per 4-byte word, so the range is rounded up to a whole word: a word
-  // that holds the extent's last element and the 2 bytes after it must not
-  // read as zero (those 2 bytes share its aligned 4-byte granule, so they
-  // are mapped; their value only reaches keys past kL, which are masked)
+  // batch b's bias from key t BN to the end of its extent, plus 2 bytes.
+  // The range check is per 4-byte word, and a row's words start at its
+  // first element, so with kL odd the word holding the extent's last element
+  // also holds the 2 bytes after it; it must not read as zero.  Those 2
+  // bytes only reach keys past kL, which are masked, and the entry point
+  // refuses a bias whose end is a 4 KiB page boundary when kL is odd (the 2
+  // bytes would lie on the next page).  No word reaches further.
   auto bias_src = [&](int t) {
     const int ts = __builtin_amdgcn_readfirstlane(t * BN);
-    return tile_rsrc(uniform_addr(bias_b + ts), __builtin_amdgcn_readfirstlane((int)(((bias_extent - ts) * 2 + 3) & ~3ll)));
+    return tile_rsrc(uniform_addr(bias_b + ts),
+                     __builtin_amdgcn_readfirstlane((int)(uint32_t)((bias_extent - ts) * 2 + 2)));
   };
   auto load_bblk = [&](const i32x4_t& src, uint16_t* buf, int n) {
     load_lds16(src, boff[n], 0u, buf + (wave + NW * n) * 512);

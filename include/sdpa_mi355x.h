@@ -161,6 +161,10 @@ size_t sdpa_workspace_bytes_kv_view(int B, int Hq, int Hkv, int qL, int kL, int 
  *            broadcasts that dimension.  Read only; must not overlap out.
  *            One batch's rows must lie within 2^30 elements
  *            (SDPA_UNSUPPORTED otherwise).  Entries are finite or -inf.
+ *            With kL odd the 2 bytes after the last element (row (B-1,
+ *            Hq-1, qL-1), key kL-1) are read and their value is not used;
+ *            a bias that ends exactly on a 4 KiB page boundary, where those
+ *            bytes may be unmapped, gets SDPA_UNSUPPORTED.
  *   A key whose biased score is -inf is excluded like a masked key; a row
  *   with no finite biased score comes out as zeros.
  *   The workspace is sdpa_workspace_bytes(B, Hq, Hkv, qL, kL, D), and qL <= 4

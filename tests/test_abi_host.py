@@ -221,6 +221,11 @@ def test_bias_entry_point_rejects_bad_bias_arguments(lib):
     assert call(sq=-1) == fa.SDPA_INVALID_ARG and "stride" in fa.sdpa_last_error()
     assert call(sh=1 << 31) == fa.SDPA_UNSUPPORTED and "2^30" in fa.sdpa_last_error()
     assert call(bias=0x300000 - 64) == fa.SDPA_INVALID_ARG and "overlap" in fa.sdpa_last_error()
+    # kL odd: the word holding the last element reaches 2 bytes past it, so a bias
+    # (8 rows of 63 keys, 1008 bytes) that ends on a 4 KiB page boundary is refused
+    rc = lib.sdpa_forward_bias(0x1000, 0x100000, 0x200000, 0x400000 - 1008, 0, 0, 63, 0x300000,
+                               1, 4, 2, 8, 63, 256, f, 1, 0, 55, 0, None, 0, None)
+    assert rc == fa.SDPA_UNSUPPORTED and "page" in fa.sdpa_last_error()
 
 
 # sdpa_forward_dv: q/k head dim D, v and out head dim Dv

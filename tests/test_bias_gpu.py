@@ -76,6 +76,25 @@ def test_bias_matches_the_oracle(case):
     check_close(got, ref, dtype, f"bias {case}")
 
 
+@pytest.mark.parametrize("B,Hq,Hkv,qL,kL,bb,bh", [(2, 12, 3, 3, 3, False, True), (1, 2, 1, 5, 333, False, False),
+                                                  (2, 4, 2, 333, 333, True, True)])
+def test_the_last_bias_element_counts_when_kl_is_odd(B, Hq, Hkv, qL, kL, bb, bh):
+    # the last row of the bias starts at an odd element (or kL is odd with an
+    # even start): the 4-byte word holding its last key reaches 2 bytes past
+    # the bias.  That key is visible (causal, the diagonal of the last row)
+    # and its bias is large, so reading it as zero would move the row far
+    # outside the tolerance
+    q, k, v = W.random_qkv(5200 + kL, B, Hq, Hkv, qL, kL, 256, FP16)
+    bias = make_bias(5300 + kL, (B if bb else 1, Hq if bh else 1, qL, kL), FP16, ninf_frac=0.0)
+    bias[..., -1, -1] = 6.0
+    note(f"last bias element, B{B} Hq{Hq} qL{qL} kL{kL}")
+    got = run_bias(q, k, v, bias, causal=True, q_offset=kL - qL)
+    scale = float(np.float32(1.0 / 16))
+    ref = oracle.sdpa_bias_f64(W.bits(q), W.bits(k), W.bits(v), W.bits(bias), scale=scale, causal=True,
+                               q_offset=kL - qL, dtype=FP16, threads=ORACLE_THREADS)
+    check_close(f64(got), ref, FP16, f"last bias element, B{B} Hq{Hq} qL{qL} kL{kL}")
+
+
 def test_rows_with_no_finite_biased_score_are_zero():
     q, k, v = W.random_qkv(5101, 1, 4, 2, 70, 300, 256, BF16)
     bias = make_bias(5102, (1, 4, 70, 300), BF16, ninf_frac=0.0)

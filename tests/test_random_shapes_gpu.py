@@ -5,8 +5,11 @@ lengths, head dim, dtype, mask (causal or not, window, bottom-right or other
 valid q_offset) and entry point from one seed, so that combinations the
 hand-picked cases do not name (ragged row blocks with several query heads
 per KV head, windows wider than the keys, a q_offset short of the end, qL
-above kL without a mask, 4-bit K/V) are exercised too.  The seeds are fixed:
-the cases are the same on every run.
+above kL without a mask, 4-bit K/V) are exercised too.  A second set of
+seeds draws the same kinds of shapes for the additive-mask entry (a bias
+broadcast or not over batch and heads, with -inf entries) and for q/k head
+dim 192 with v head dim 256.  The seeds are fixed: the cases are the same on
+every run.
 """
 
 import numpy as np
@@ -17,6 +20,7 @@ import flash_attention_head_amd as fa
 import oracle
 from flash_attention_head_amd import workloads as W
 from gpu_util import ORACLE_THREADS, check_close, ensure_library, f64, note, oracle_full
+from test_bias_gpu import make_bias
 
 pytestmark = pytest.mark.gpu
 
@@ -87,4 +91,42 @@ def test_random_shape_against_the_oracle(seed):
         torch.cuda.synchronize()
         ref = oracle_full(q, k, v, scale=scale, causal=c["causal"], window=c["window"],
                           q_offset=c["q_offset"], dtype=c["dtype"])
+    check_close(f64(got.cpu()), ref, c["dtype"], f"random case {seed}")
+
+
+BIAS_DV_SEEDS = list(range(760, 800))
+
+
+def _case_bias_dv(seed):
+    c = _case(seed)
+    r = np.random.default_rng(seed + 100000)
+    c["q4"] = False
+    c["entry"] = "dv" if r.random() < 0.3 else "bias"
+    if c["entry"] == "dv":
+        c["D"] = 192
+    c["bias_b"], c["bias_h"] = bool(r.random() < 0.5), bool(r.random() < 0.5)
+    return c
+
+
+@pytest.mark.parametrize("seed", BIAS_DV_SEEDS)
+def test_random_shape_with_a_bias_or_value_dim_256_against_the_oracle(seed):
+    c = _case_bias_dv(seed)
+    note(f"random case {seed}: {c}")
+    B, Hq, Hkv, qL, kL, D = c["B"], c["Hq"], c["Hkv"], c["qL"], c["kL"], c["D"]
+    mask = dict(causal=c["causal"], window=c["window"], q_offset=c["q_offset"])
+    scale = float(np.float32(1.0 / np.sqrt(D)))
+    if c["entry"] == "bias":
+        q, k, v = W.random_qkv(seed, B, Hq, Hkv, qL, kL, D, c["dtype"])
+        bias = make_bias(seed + 1, (B if c["bias_b"] else 1, Hq if c["bias_h"] else 1, qL, kL), c["dtype"])
+        got = fa.sdpa(q.cuda(), k.cuda(), v.cuda(), bias=bias.cuda(), **mask)
+        torch.cuda.synchronize()
+        ref = oracle.sdpa_bias_f64(W.bits(q), W.bits(k), W.bits(v), W.bits(bias), scale=scale, dtype=c["dtype"],
+                                   threads=ORACLE_THREADS, **mask)
+    else:
+        q, k, v = W.random_qkv(seed, B, Hq, Hkv, qL, kL, 192, c["dtype"], Dv=256)
+        got = fa.sdpa(q.cuda(), k.cuda(), v.cuda(), **mask)
+        torch.cuda.synchronize()
+        assert tuple(got.shape) == (B, Hq, qL, 256)
+        ref = oracle.sdpa_dv_f64(W.bits(q), W.bits(k), W.bits(v), scale=scale, dtype=c["dtype"],
+                                 threads=ORACLE_THREADS, **mask)
     check_close(f64(got.cpu()), ref, c["dtype"], f"random case {seed}")
