@@ -8,8 +8,10 @@ per KV head, windows wider than the keys, a q_offset short of the end, qL
 above kL without a mask, 4-bit K/V) are exercised too.  A second set of
 seeds draws the same kinds of shapes for the additive-mask entry (a bias
 broadcast or not over batch and heads, with -inf entries) and for q/k head
-dim 192 with v head dim 256.  The seeds are fixed: the cases are the same on
-every run.
+dim 192 with v head dim 256, and a third set lays the keys and values into
+a KV cache of random capacity from a random ring start (16-bit at every
+head dim, and 4-bit).  The seeds are fixed: the cases are the same on every
+run.
 """
 
 import numpy as np
@@ -129,4 +131,44 @@ def test_random_shape_with_a_bias_or_value_dim_256_against_the_oracle(seed):
         assert tuple(got.shape) == (B, Hq, qL, 256)
         ref = oracle.sdpa_dv_f64(W.bits(q), W.bits(k), W.bits(v), scale=scale, dtype=c["dtype"],
                                  threads=ORACLE_THREADS, **mask)
+    check_close(f64(got.cpu()), ref, c["dtype"], f"random case {seed}")
+
+
+CACHE_SEEDS = list(range(800, 840))
+
+
+def _lay(t, cap, start):
+    """A [B, H, kL, ...] tensor laid into a cache of `cap` rows from row `start`, wrapping."""
+    kL = t.shape[2]
+    c = torch.zeros(t.shape[:2] + (cap,) + t.shape[3:], dtype=t.dtype)
+    c[:, :, (start + torch.arange(kL)) % cap] = t
+    return c
+
+
+@pytest.mark.parametrize("seed", CACHE_SEEDS)
+def test_random_shape_over_a_kv_cache_against_the_oracle(seed):
+    c = _case(seed)
+    r = np.random.default_rng(seed + 200000)
+    cap = c["kL"] + int(r.integers(0, 3000))
+    start = int(r.integers(0, cap))
+    c.update(cap=cap, ring_start=start)
+    note(f"random case {seed}: {c}")
+    B, Hq, Hkv, qL, kL, D = c["B"], c["Hq"], c["Hkv"], c["qL"], c["kL"], c["D"]
+    mask = dict(causal=c["causal"], window=c["window"], q_offset=c["q_offset"])
+    scale = float(np.float32(1.0 / np.sqrt(D)))
+    if c["q4"]:
+        q = W.random_qkv(seed, B, Hq, Hkv, qL, 1, 256, c["dtype"])[0]
+        kv = W.random_q4kv(seed + 1, B, Hkv, kL, 256, c["dtype"])
+        got = fa.sdpa_q4kv(q.cuda(), *(_lay(t, cap, start).cuda() for t in kv), kv_len=kL, ring_start=start,
+                           **mask)
+        torch.cuda.synchronize()
+        kd, vd = (torch.from_numpy(oracle.dequant4_f64(W.words(a), W.bits(s_), W.bits(b), D=256, dtype=c["dtype"]))
+                  .to(W.TORCH_DTYPES[c["dtype"]]) for a, s_, b in (kv[0:3], kv[3:6]))
+        ref = oracle_full(q, kd, vd, scale=scale, dtype=c["dtype"], **mask)
+    else:
+        q, k, v = W.random_qkv(seed, B, Hq, Hkv, qL, kL, D, c["dtype"])
+        got = fa.sdpa_kv_cache(q.cuda(), _lay(k, cap, start).cuda(), _lay(v, cap, start).cuda(), kL,
+                               ring_start=start, **mask)
+        torch.cuda.synchronize()
+        ref = oracle_full(q, k, v, scale=scale, dtype=c["dtype"], **mask)
     check_close(f64(got.cpu()), ref, c["dtype"], f"random case {seed}")
