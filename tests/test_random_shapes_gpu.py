@@ -7,7 +7,8 @@ hand-picked cases do not name (ragged row blocks with several query heads
 per KV head, windows wider than the keys, a q_offset short of the end, qL
 above kL without a mask, 4-bit K/V) are exercised too.  A second set of
 seeds draws the same kinds of shapes for the additive-mask entry (a bias
-broadcast or not over batch and heads, with -inf entries) and for q/k head
+broadcast or not over batch and heads, with -inf entries, half of them
+views of wider rows) and for q/k head
 dim 192 with v head dim 256, and a third set lays the keys and values into
 a KV cache of random capacity from a random ring start (16-bit at every
 head dim, and 4-bit).  The seeds are fixed: the cases are the same on every
@@ -107,6 +108,8 @@ def _case_bias_dv(seed):
     if c["entry"] == "dv":
         c["D"] = 192
     c["bias_b"], c["bias_h"] = bool(r.random() < 0.5), bool(r.random() < 0.5)
+    # half the biases are views of wider rows (row stride kL + pad, keys still contiguous)
+    c["bias_pad"] = int(r.integers(1, 6)) if r.random() < 0.5 else 0
     return c
 
 
@@ -119,8 +122,13 @@ def test_random_shape_with_a_bias_or_value_dim_256_against_the_oracle(seed):
     scale = float(np.float32(1.0 / np.sqrt(D)))
     if c["entry"] == "bias":
         q, k, v = W.random_qkv(seed, B, Hq, Hkv, qL, kL, D, c["dtype"])
-        bias = make_bias(seed + 1, (B if c["bias_b"] else 1, Hq if c["bias_h"] else 1, qL, kL), c["dtype"])
-        got = fa.sdpa(q.cuda(), k.cuda(), v.cuda(), bias=bias.cuda(), **mask)
+        wide = make_bias(seed + 1, (B if c["bias_b"] else 1, Hq if c["bias_h"] else 1, qL, kL + c["bias_pad"]),
+                         c["dtype"])
+        bias = wide[..., :kL]
+        # sliced on the device, so that the kernel sees the row stride kL + pad
+        gbias = wide.cuda()[..., :kL]
+        assert c["bias_pad"] == 0 or gbias.stride(2) == kL + c["bias_pad"]
+        got = fa.sdpa(q.cuda(), k.cuda(), v.cuda(), bias=gbias, **mask)
         torch.cuda.synchronize()
         ref = oracle.sdpa_bias_f64(W.bits(q), W.bits(k), W.bits(v), W.bits(bias), scale=scale, dtype=c["dtype"],
                                    threads=ORACLE_THREADS, **mask)
