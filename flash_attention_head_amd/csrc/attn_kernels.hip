@@ -585,20 +585,16 @@ __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* ld
   auto q4_store = [&](const Q4Data& d, uint16_t* buf, int blk) {
     const float sc = q4_widen(d.s), bi = q4_widen(d.b);
     // even elements' codes in the bytes of lo, odd ones' in the bytes of hi:
-    // each code is then one byte-to-float conversion (from inline assembly:
-    // from the plain C the compiler forms a bit-field extract and a byte-0
-    // conversion per code, twice the instructions)
-    const uint32_t lo = d.w & 0x0F0F0F0Fu, hi = (d.w >> 4) & 0x0F0F0F0Fu;
-    auto byte_f = [](uint32_t x, auto kc) {  // v_cvt_f32_ubyte<k>: byte k of x as a float
+    // each code is then one byte-to-float conversion (v_cvt_f32_ubyte<k>).
+    // The empty asm hides that the bytes' high nibbles are zero; knowing it,
+    // the compiler forms a bit-field extract and a byte-0 conversion per
+    // code instead, twice the instructions
+    uint32_t lo = d.w & 0x0F0F0F0Fu, hi = (d.w >> 4) & 0x0F0F0F0Fu;
+    asm("" : "+v"(lo), "+v"(hi));
+    auto val = [&](uint32_t x, auto kc) {
       constexpr int k = decltype(kc)::value;
-      float f;
-      if constexpr (k == 0) asm("v_cvt_f32_ubyte0 %0, %1" : "=v"(f) : "v"(x));
-      else if constexpr (k == 1) asm("v_cvt_f32_ubyte1 %0, %1" : "=v"(f) : "v"(x));
-      else if constexpr (k == 2) asm("v_cvt_f32_ubyte2 %0, %1" : "=v"(f) : "v"(x));
-      else asm("v_cvt_f32_ubyte3 %0, %1" : "=v"(f) : "v"(x));
-      return f;
+      return fmaf(sc, (float)((x >> (8 * k)) & 0xFFu), bi);
     };
-    auto val = [&](uint32_t x, auto kc) { return fmaf(sc, byte_f(x, kc), bi); };
     using K0 = std::integral_constant<int, 0>;
     using K1 = std::integral_constant<int, 1>;
     using K2 = std::integral_constant<int, 2>;
