@@ -471,31 +471,57 @@ __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* ld
   int bbase = 0;
   int64_t bias_extent = 0;
   const uint16_t* bias_b = nullptr;
+  // The descriptor's range ends exactly at the end of batch b's bias extent
+  // (bias_src below), and its range check is per 4-byte word; a row's words
+  // start at its first element.  So with kL odd, the word that holds key
+  // kL - 1 of a row that ends the extent also covers the 2 bytes after the
+  // extent: it is out of range and reads as zero, and nothing past the
+  // extent is read.  That one element is written into the tile afterwards
+  // (bias_patch): a lane whose load n covers it has bit n of bpatch set,
+  // bias_last is its value (one 2-byte load from inside the extent) and
+  // bpatch_e its place in the lane's 8 elements.  Only the tile holding key
+  // kL - 1 (t_bend) needs it.
+  uint32_t bpatch = 0;
+  uint32_t bias_last = 0;
+  int bpatch_e = 0;
+  const int t_bend = __builtin_amdgcn_readfirstlane((p.kL - 1) / BN);
   if constexpr (BIAS) {
+    bias_b = p.bias + b * p.bias_sb;
+    bias_extent = (int64_t)(p.Hq - 1) * p.bias_sh + (int64_t)(p.qL - 1) * p.bias_sq + p.kL;
+    const int64_t last_row = bias_extent - p.kL;         // start of the rows that end the extent
+    const int c_last = ((p.kL - 1) % BN) / 8;             // chunk of key kL - 1 within its tile
+    bpatch_e = (p.kL - 1) % 8;
 #pragma unroll
     for (int n = 0; n < BLOADS; ++n) {
       const int r = (wave + NW * n) * BRPB + lane / BCPR;  // bias tile row
       const int c = (lane % BCPR) ^ (r & (BCPR - 1));
       const int prow = row0 + r;
       const int pq = prow / p.G, ph = hkv * p.G + prow % p.G;
-      boff[n] = prow < rows_end ? (uint32_t)((ph * p.bias_sh + pq * p.bias_sq + 8 * c) * 2) : 0xfffffff0u;
+      const int64_t start = (int64_t)ph * p.bias_sh + (int64_t)pq * p.bias_sq;
+      boff[n] = prow < rows_end ? (uint32_t)((start + 8 * c) * 2) : 0xfffffff0u;
+      if ((p.kL & 1) && prow < rows_end && start == last_row && c == c_last) bpatch |= 1u << n;
     }
-    bias_b = p.bias + b * p.bias_sb;
-    bias_extent = (int64_t)(p.Hq - 1) * p.bias_sh + (int64_t)(p.qL - 1) * p.bias_sq + p.kL;
+    if ((p.kL & 1) && t_last == t_bend) bias_last = bias_b[bias_extent - 1];
+    else bpatch = 0;
     const int r = rb * kRowsPerWave + lr;  // this lane's row in the bias tile
     bbase = r * BN + 8 * (r & (BCPR - 1)) + 4 * lg;
   }
-  // batch b's bias from key t BN to the end of its extent, plus 2 bytes.
-  // The range check is per 4-byte word, and a row's words start at its
-  // first element, so with kL odd the word holding the extent's last element
-  // also holds the 2 bytes after it; it must not read as zero.  Those 2
-  // bytes only reach keys past kL, which are masked, and the entry point
-  // refuses a bias whose end is a 4 KiB page boundary when kL is odd (the 2
-  // bytes would lie on the next page).  No word reaches further.
+  // batch b's bias from key t BN to the end of its extent
   auto bias_src = [&](int t) {
     const int ts = __builtin_amdgcn_readfirstlane(t * BN);
     return tile_rsrc(uniform_addr(bias_b + ts),
-                     __builtin_amdgcn_readfirstlane((int)(uint32_t)((bias_extent - ts) * 2 + 2)));
+                     __builtin_amdgcn_readfirstlane((int)(uint32_t)((bias_extent - ts) * 2)));
+  };
+  // after this wave's loads of tile t into bias buffer buf have landed and
+  // before the barrier that publishes it: the element the range check zeroed
+  auto bias_patch = [&](int t, uint16_t* buf) {
+    if constexpr (BIAS) {
+      if (t == t_bend && bpatch != 0) {
+#pragma unroll
+        for (int n = 0; n < BLOADS; ++n)
+          if (bpatch & (1u << n)) buf[(wave + NW * n) * 512 + 8 * lane + bpatch_e] = (uint16_t)bias_last;
+      }
+    }
   };
   auto load_bblk = [&](const i32x4_t& src, uint16_t* buf, int n) {
     load_lds16(src, boff[n], 0u, buf + (wave + NW * n) * 512);
@@ -955,6 +981,8 @@ __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* ld
       if constexpr (V3) load_v(t_first + 1);
     }
     __builtin_amdgcn_s_waitcnt(0);
+    bias_patch(t_first, bbuf0);
+    if (t_first < t_last) bias_patch(t_first + 1, bbuf0 + BTILE);
   }
   __syncthreads();
 
@@ -1033,6 +1061,7 @@ __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* ld
     // V loads of this step may be in flight.  Otherwise everything has.
     if constexpr (VLATE) wait_vmem<PV_LOADS>();
     else __builtin_amdgcn_s_waitcnt(0);
+    bias_patch(tk, bbuf0 + P * BTILE);
     __syncthreads();
   };
 
@@ -1103,6 +1132,7 @@ __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* ld
       if constexpr (PAIR)
         if (t < t_last) load_v(t + 1);
       __builtin_amdgcn_s_waitcnt(0);
+      if (t + 2 <= t_last) bias_patch(t + 2, bbuf0 + ((t + 2 - t_first) & 1) * BTILE);
       __syncthreads();
     }
   }

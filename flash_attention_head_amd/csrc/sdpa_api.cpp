@@ -302,13 +302,6 @@ SDPA_API int sdpa_forward_bias(const void* q, const void* k, const void* v, cons
   const size_t qbytes = (size_t)B * Hq * qL * D * 2;
   const size_t bbytes = (size_t)(((int64_t)(B - 1) * bias_stride_b + extent) * 2);
   if (overlap(out, qbytes, bias, bbytes)) return fail(SDPA_INVALID_ARG, "out must not overlap the bias");
-  // with kL odd the 4-byte word that holds the bias's last element reaches 2
-  // bytes past it; those bytes share its page unless the bias ends exactly
-  // on a 4 KiB boundary
-  if ((kL & 1) && (((uintptr_t)bias + bbytes) & 4095u) == 0)
-    return fail(SDPA_UNSUPPORTED,
-                "with kL odd the kernel reads the 2 bytes after the bias's last element, and this bias ends on a "
-                "4 KiB page boundary: place it so that those 2 bytes are readable");
   return forward_impl(q, k, v, bias, bias_stride_b, bias_stride_h, bias_stride_q, out, B, Hq, Hkv, qL, kL,
                       kL, 0, 0, D, D, scale, causal, window, q_offset, dtype, workspace, workspace_bytes, stream);
 }

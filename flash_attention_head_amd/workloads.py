@@ -163,6 +163,32 @@ def random_qkv(seed: int, B: int, Hq: int, Hkv: int, qL: int, kL: int, D: int, d
     return q, k, v
 
 
+def ramp_qkv(seed: int, B: int, Hq: int, Hkv: int, qL: int, kL: int, D: int, dtype: int,
+             rise: float = 40.0, Dv: int = 0):
+    """Seeded Q, K, V whose scores climb along the keys (same draw order as ``draw``).
+
+    Per (batch, KV head) a direction u of N(0, 1) entries.  Query row i of each
+    head is c_i u + N(0, 1), with c_i ~ U(-0.5, 1.5) drawn per row; key j is
+    (rise * j / kL) * u / sqrt(D) + N(0, 1); values are N(0, 1).  With scale
+    1/sqrt(D) the scores of row i then grow by about c_i * rise over the keys,
+    so that the rows with c_i > 0 see later keys overtake every earlier maximum
+    again and again, by far more than the same-magnitude noise of N(0, 1)
+    inputs ever does; rows with c_i < 0 have their maximum among the first keys.
+    Holds none of the attention arithmetic (it only shapes the inputs).
+    """
+    g = torch.Generator(device="cpu")
+    g.manual_seed(seed)
+    dt = TORCH_DTYPES[dtype]
+    u = torch.randn((B, Hkv, 1, D), generator=g, dtype=torch.float32)
+    uq = u.repeat_interleave(Hq // Hkv, dim=1)
+    c = torch.rand((B, Hq, qL, 1), generator=g, dtype=torch.float32) * 2.0 - 0.5
+    q = (c * uq + torch.randn((B, Hq, qL, D), generator=g, dtype=torch.float32)).to(dt)
+    r = (rise * torch.arange(kL, dtype=torch.float32) / kL).view(1, 1, kL, 1)
+    k = (r * u / math.sqrt(D) + torch.randn((B, Hkv, kL, D), generator=g, dtype=torch.float32)).to(dt)
+    v = torch.randn((B, Hkv, kL, Dv or D), generator=g, dtype=torch.float32).to(dt)
+    return q, k, v
+
+
 def random_q4kv(seed: int, B: int, Hkv: int, kL: int, D: int, dtype: int):
     """Seeded 4-bit K and V rows: (kq, ks, kb, vq, vs, vb).
 

@@ -161,10 +161,8 @@ size_t sdpa_workspace_bytes_kv_view(int B, int Hq, int Hkv, int qL, int kL, int 
  *            broadcasts that dimension.  Read only; must not overlap out.
  *            One batch's rows must lie within 2^30 elements
  *            (SDPA_UNSUPPORTED otherwise).  Entries are finite or -inf.
- *            With kL odd the 2 bytes after the last element (row (B-1,
- *            Hq-1, qL-1), key kL-1) are read and their value is not used;
- *            a bias that ends exactly on a 4 KiB page boundary, where those
- *            bytes may be unmapped, gets SDPA_UNSUPPORTED.
+ *            No byte outside the rows the strides name is read, so the
+ *            bias may end anywhere, a page boundary included.
  *   A key whose biased score is -inf is excluded like a masked key; a row
  *   with no finite biased score comes out as zeros.
  *   The workspace is sdpa_workspace_bytes(B, Hq, Hkv, qL, kL, D), and qL <= 4
@@ -229,10 +227,22 @@ int sdpa_forward_q4kv(const void* q, const void* kq, const void* ks, const void*
                       int kv_capacity, int ring_start, int D, float scale, int causal, int window,
                       int q_offset, int dtype, void* workspace, size_t workspace_bytes, void* stream);
 
-/* Message for the last non-zero status returned on the calling thread ("" if none). */
+/*
+ * Message for the last non-zero status returned on the calling thread ("" if
+ * none).  Failures are reported, never raised: the error-handling note of
+ * lablup/mlxcel issue #2160 (Implementation Notes) asks that a failed check
+ * fall back cleanly with its reason reported and without introducing any
+ * crash, and this string is that reason.  The pointer stays valid until the thread's
+ * next call into the library; the caller must not free it.
+ */
 const char* sdpa_last_error(void);
 
-/* Library version, major * 10000 + minor * 100 + patch. */
+/*
+ * Library version, major * 10000 + minor * 100 + patch.  A caller that
+ * declines to use the library (the fail-closed path of the same
+ * Implementation Notes) can compare it against the version it was built
+ * for; it never fails.
+ */
 int sdpa_version(void);
 
 #ifdef __cplusplus

@@ -11,8 +11,12 @@ library and marshals numpy arrays of fp16/bf16 bit patterns into it.
 What it computes, and the readings taken where the pages leave a step open,
 are stated in the header of ``sdpa_oracle.c``.
 
-Every function here has a pin in ``tests/test_oracle_pins.py``; none is
-"parity unpinned".
+``dense.py`` holds the same function written as the unfused matrix product,
+softmax and matrix product in numpy (``sdpa_dense_rows_f64``), for row checks
+at full size.
+
+Every function here has a pin in ``tests/test_oracle_pins.py`` or
+``tests/test_oracle_dense_pins.py``; none is "parity unpinned".
 """
 
 from __future__ import annotations
@@ -22,6 +26,8 @@ import os
 import subprocess
 
 import numpy as np
+
+from .dense import sdpa_dense_rows_f64  # noqa: F401  (numpy, no C library)
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "sdpa_oracle.c")

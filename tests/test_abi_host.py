@@ -221,11 +221,13 @@ def test_bias_entry_point_rejects_bad_bias_arguments(lib):
     assert call(sq=-1) == fa.SDPA_INVALID_ARG and "stride" in fa.sdpa_last_error()
     assert call(sh=1 << 31) == fa.SDPA_UNSUPPORTED and "2^30" in fa.sdpa_last_error()
     assert call(bias=0x300000 - 64) == fa.SDPA_INVALID_ARG and "overlap" in fa.sdpa_last_error()
-    # kL odd: the word holding the last element reaches 2 bytes past it, so a bias
-    # (8 rows of 63 keys, 1008 bytes) that ends on a 4 KiB page boundary is refused
-    rc = lib.sdpa_forward_bias(0x1000, 0x100000, 0x200000, 0x400000 - 1008, 0, 0, 63, 0x300000,
-                               1, 4, 2, 8, 63, 256, f, 1, 0, 55, 0, None, 0, None)
-    assert rc == fa.SDPA_UNSUPPORTED and "page" in fa.sdpa_last_error()
+    # kL odd and a bias (4 rows of 63 keys, 504 bytes) that ends on a 4 KiB page
+    # boundary: the kernels read nothing past the bias, so the layout passes every
+    # bias check.  The call stops at the next check instead (a verify block needs
+    # a workspace and none is given), before anything could be launched.
+    rc = lib.sdpa_forward_bias(0x1000, 0x100000, 0x200000, 0x400000 - 504, 0, 0, 63, 0x300000,
+                               1, 4, 2, 4, 63, 256, f, 1, 0, 59, 0, None, 0, None)
+    assert rc == fa.SDPA_WORKSPACE_TOO_SMALL, (rc, fa.sdpa_last_error())
 
 
 # sdpa_forward_dv: q/k head dim D, v and out head dim Dv
@@ -292,3 +294,4 @@ def test_q4kv_entry_point_rejects_what_it_does_not_take(lib):
     # starting inside the scales of K it overlaps them
     assert _call_q4(out=0x100000 - 4096) == fa.SDPA_INVALID_ARG and "overlap" in fa.sdpa_last_error()
     assert _call_q4(out=0x180000 + 256) == fa.SDPA_INVALID_ARG and "overlap" in fa.sdpa_last_error()
+

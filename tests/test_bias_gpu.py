@@ -155,3 +155,28 @@ def test_full_size_bias_workload_on_sampled_rows():
     ref = oracle.sdpa_bias_f64(W.bits(q), W.bits(k), W.bits(v), W.bits(bias), scale=wl.scale, causal=wl.causal,
                                q_offset=wl.q_offset, dtype=wl.dtype, rows=rows, threads=ORACLE_THREADS)
     check_close(f64(got.reshape(-1, wl.D)[torch.from_numpy(rows)]), ref, wl.dtype, f"{wl.name} ({rows.size} rows)")
+
+
+@pytest.mark.parametrize("qL,kL,dtype", [(128, 4097, FP16), (33, 1025, BF16)])
+def test_contiguous_odd_bias_ending_on_a_page_boundary(qL, kL, dtype):
+    # a [1, 16, qL, kL] bias whose last byte ends a 4 KiB page: the layout the
+    # library used to refuse; it must read nothing past the bias and count the
+    # last element (set large on the diagonal key of the last row)
+    B, Hq, Hkv, D = 1, 16, 8, 256
+    q, k, v = W.random_qkv(5400 + kL, B, Hq, Hkv, qL, kL, D, dtype)
+    bias = make_bias(5401 + kL, (B, Hq, qL, kL), dtype, ninf_frac=0.0)
+    bias[..., -1, -1] = 6.0
+    n = bias.numel()
+    pool = torch.empty(n + 8192, dtype=bias.dtype, device="cuda")
+    end = (pool.data_ptr() + 2 * n + 4095) // 4096 * 4096   # first page boundary at or past n elements
+    off = (end - pool.data_ptr()) // 2 - n
+    view = pool[off:off + n].view(B, Hq, qL, kL)
+    assert (view.data_ptr() + 2 * n) % 4096 == 0
+    view.copy_(bias.cuda())
+    note(f"bias ending on a page boundary, qL {qL} kL {kL}")
+    out = fa.sdpa(q.cuda(), k.cuda(), v.cuda(), bias=view, causal=True)
+    torch.cuda.synchronize()
+    scale = float(np.float32(1.0 / 16))
+    ref = oracle.sdpa_bias_f64(W.bits(q), W.bits(k), W.bits(v), W.bits(bias), scale=scale, causal=True,
+                               q_offset=kL - qL, dtype=dtype, threads=ORACLE_THREADS)
+    check_close(f64(out.cpu()), ref, dtype, f"bias ending on a page boundary, qL {qL} kL {kL}")

@@ -17,8 +17,8 @@ import pytest
 from flash_attention_head_amd import build as B
 
 KERNELS = ("attn_tile_kernel_d64", "attn_tile_kernel_d80", "attn_tile_kernel_d128", "attn_tile_kernel_d192", "attn_tile_kernel_dk192_dv256", "attn_tile_kernel_d256",
-           "attn_tile_kernel_d512",
-           "combine_kernel")
+           "attn_tile_kernel_d512", "attn_tile_kernel_d256_q4",
+           "combine_kernel", "combine_few_kernel")
 
 
 @pytest.fixture(scope="module")

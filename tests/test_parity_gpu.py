@@ -12,8 +12,9 @@ import pytest
 import torch
 
 from flash_attention_head_amd import workloads as W
-from gpu_util import (TOL, check_close, ensure_library, f64, note, oracle_full, oracle_rows,
-                      run_gpu, sample_rows)
+import flash_attention_head_amd as fa
+from gpu_util import (TOL, check_close, ensure_library, f64, launch_rows, note, oracle_dense_rows, oracle_full,
+                      oracle_rows, run_gpu, sample_rows)
 
 pytestmark = pytest.mark.gpu
 
@@ -112,23 +113,83 @@ def test_tiny_causal_workload_every_row():
 
 FULL = [("chunked_prefill_32k", 160), ("causal_h64_16k", 160), ("sliding_32k", 200),
         ("global_d512_32k", 64), ("causal_d64_16k", 96), ("causal_d80_16k", 96), ("causal_d128_16k", 96),
-        ("causal_d192_16k", 96), ("decode_q4_128k", 32),
+        ("causal_d192_16k", 96), ("causal_dk192_dv256_16k", 64), ("decode_q4_128k", 32),
         ("decode_q1_128k", 16)]
 
 
 @pytest.mark.timeout(600)
 @pytest.mark.parametrize("name,n_random", FULL, ids=[f[0] for f in FULL])
 def test_full_size_workloads_on_sampled_rows(name, n_random):
+    # edge and random rows against the C oracle; for the prefill calls also one
+    # row of every launched workgroup and of every key split it runs, against
+    # the dense (matmul + softmax + matmul) oracle
     wl = W.WORKLOADS[name]
     q, k, v = W.draw(wl)
     note(f"{name} full size")
     got = run_gpu(q, k, v, causal=wl.causal, window=wl.window, q_offset=wl.q_offset)
     assert torch.isfinite(got.float()).all()
+    flat = got.reshape(-1, wl.dv)
     rows = sample_rows(wl, n_random, seed=wl.seed)
     ref = oracle_rows(q, k, v, rows, scale=wl.scale, causal=wl.causal, window=wl.window,
-                      q_offset=wl.q_offset, dtype=wl.dtype)
-    check_close(f64(got.reshape(-1, wl.D)[torch.from_numpy(rows)]), ref, wl.dtype,
-                f"{name} ({rows.size} rows)")
+                      q_offset=wl.q_offset, dtype=wl.dtype) if wl.dv == wl.D else \
+        oracle_dense_rows(q, k, v, rows, scale=wl.scale, causal=wl.causal, window=wl.window,
+                          q_offset=wl.q_offset, dtype=wl.dtype)
+    check_close(f64(flat[torch.from_numpy(rows)]), ref, wl.dtype, f"{name} ({rows.size} rows)")
+    if wl.qL > 4:
+        wrows, geo = launch_rows(wl, seed=wl.seed + 1)
+        assert geo["covered"] == geo["workgroups"] or wl.window, geo
+        ref = oracle_dense_rows(q, k, v, wrows, scale=wl.scale, causal=wl.causal, window=wl.window,
+                                q_offset=wl.q_offset, dtype=wl.dtype)
+        check_close(f64(flat[torch.from_numpy(wrows)]), ref, wl.dtype,
+                    f"{name}: {wrows.size} rows covering {geo['covered']} of {geo['workgroups']} "
+                    f"(workgroup, split) pairs")
+
+
+@pytest.mark.timeout(300)
+@pytest.mark.parametrize("name", ["decode_q4_128k", "decode_q1_128k"])
+def test_benchmarked_decode_call_every_row(name):
+    # the call the benchmark times: sdpa_forward_kv_view over a full cache of
+    # kL = 131072 rows per head, whose plan is 32 chunks of 4096 keys merged by
+    # the many-split combine (two chunks per wave); every row against the oracle
+    wl = W.WORKLOADS[name]
+    q, k, v = W.draw(wl)
+    need = fa.sdpa_workspace_bytes_kv_view(wl.B, wl.Hq, wl.Hkv, wl.qL, wl.kL, wl.kL, wl.D)
+    assert need == wl.B * wl.Hq * wl.qL * 32 * (wl.D + 2) * 4, need  # 32 splits of 4096 keys
+    note(f"{name} through sdpa_forward_kv_view, capacity {wl.kL}")
+    out = fa.sdpa_kv_cache(q.cuda(), k.cuda(), v.cuda(), wl.kL, scale=wl.scale, causal=wl.causal,
+                           window=wl.window, q_offset=wl.q_offset)
+    torch.cuda.synchronize()
+    got = f64(out.cpu())
+    ref = oracle_full(q, k, v, scale=wl.scale, causal=wl.causal, window=wl.window, q_offset=wl.q_offset,
+                      dtype=wl.dtype)
+    check_close(got, ref, wl.dtype, f"{name} kv view (all {got.size // wl.D} rows)")
+
+
+# the fused-vs-unfused validation grid of ml-explore/mlx PR #3660 (Validation):
+# 16 query / 8 KV heads at head dim 256, fp16 and bf16, qL in {1024, 2048}, kL
+# in {64K, 128K}; the page names no mask, so each shape runs both unmasked and
+# causal bottom-right aligned (a prefill chunk over the prefix)
+GRID = [(qL, kL, dt) for dt in (FP16, BF16) for qL in (1024, 2048) for kL in (65536, 131072)]
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("dtype", [FP16, BF16], ids=["f16", "bf16"])
+def test_validation_grid_of_the_pages(dtype):
+    q_all, k_all, v_all = W.random_qkv(3660 + dtype, 1, 16, 8, 2048, 131072, 256, dtype)
+    scale = float(np.float32(1 / 16))
+    for qL, kL, _ in [g for g in GRID if g[2] == dtype]:
+        q = q_all[:, :, :qL].contiguous()
+        k = k_all[:, :, :kL].contiguous()
+        v = v_all[:, :, :kL].contiguous()
+        rows = sample_rows(W.WORKLOADS["chunked_prefill_32k"].with_(qL=qL, kL=kL), 96, seed=qL + kL)
+        for causal in (False, True):
+            qo = kL - qL if causal else 0
+            note(f"validation grid qL {qL} kL {kL} dtype {dtype} causal {causal}")
+            got = run_gpu(q, k, v, causal=causal, q_offset=qo)
+            ref = oracle_dense_rows(q, k, v, rows, scale=scale, causal=causal, window=0, q_offset=qo,
+                                    dtype=dtype)
+            check_close(f64(got.reshape(-1, 256)[torch.from_numpy(rows)]), ref, dtype,
+                        f"grid qL {qL} kL {kL} causal {causal} ({rows.size} rows)")
 
 
 @pytest.mark.timeout(600)
