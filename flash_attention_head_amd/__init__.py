@@ -9,7 +9,8 @@ missing or cannot be loaded, every call raises.
 Raw entry points (same names and arguments as the C functions, pointers as
 integers): ``sdpa_forward``, ``sdpa_workspace_bytes``, ``sdpa_forward_kv_view``,
 ``sdpa_workspace_bytes_kv_view``, ``sdpa_forward_bias``, ``sdpa_forward_dv``,
-``sdpa_workspace_bytes_dv``, ``sdpa_forward_q4kv``, ``sdpa_last_error``, ``sdpa_version``.
+``sdpa_workspace_bytes_dv``, ``sdpa_forward_q4kv``, ``sdpa_forward_noalloc``, ``sdpa_last_error``,
+``sdpa_version``.
 Convenience wrappers on torch tensors: ``sdpa`` (contiguous K/V, optionally an
 additive mask array, optionally a value head dim other than q's),
 ``sdpa_kv_cache`` (K/V in a cache, possibly a wrapped ring) and ``sdpa_q4kv``
@@ -27,7 +28,8 @@ __all__ = [
     "SDPA_HIP_ERROR", "SDPA_FP16", "SDPA_BF16", "SdpaError", "library_path", "load_library",
     "sdpa_forward", "sdpa_workspace_bytes", "sdpa_forward_kv_view", "sdpa_workspace_bytes_kv_view",
     "sdpa_forward_bias", "sdpa_forward_dv", "sdpa_workspace_bytes_dv", "sdpa_forward_q4kv",
-    "sdpa_last_error", "sdpa_version", "sdpa", "sdpa_kv_cache", "sdpa_q4kv", "EXPORTED_SYMBOLS",
+    "sdpa_forward_noalloc", "NOALLOC_SCRATCH_BYTES", "sdpa_last_error", "sdpa_version", "sdpa",
+    "sdpa_kv_cache", "sdpa_q4kv", "EXPORTED_SYMBOLS",
 ]
 
 SDPA_OK = 0
@@ -40,7 +42,11 @@ SDPA_BF16 = 1
 
 EXPORTED_SYMBOLS = ("sdpa_forward", "sdpa_workspace_bytes", "sdpa_forward_kv_view",
                     "sdpa_workspace_bytes_kv_view", "sdpa_forward_bias", "sdpa_forward_dv",
-                    "sdpa_workspace_bytes_dv", "sdpa_forward_q4kv", "sdpa_last_error", "sdpa_version")
+                    "sdpa_workspace_bytes_dv", "sdpa_forward_q4kv", "sdpa_forward_noalloc", "sdpa_last_error",
+                    "sdpa_version")
+
+# SDPA_NOALLOC_SCRATCH_BYTES of the header: the largest workspace sdpa_forward_noalloc serves
+NOALLOC_SCRATCH_BYTES = 64 * 1024 * 1024
 
 # (q/k head dim, v head dim) pairs the library takes
 HEAD_DIMS = ((64, 64), (80, 80), (128, 128), (192, 192), (256, 256), (512, 512), (192, 256))
@@ -89,6 +95,8 @@ def load_library():
     lib.sdpa_workspace_bytes_dv.restype = sz
     lib.sdpa_forward_q4kv.argtypes = [vp] * 8 + [ci] * 8 + [ctypes.c_float] + [ci] * 4 + [vp, sz, vp]
     lib.sdpa_forward_q4kv.restype = ci
+    lib.sdpa_forward_noalloc.argtypes = [vp, vp, vp, vp] + [ci] * 6 + [ctypes.c_float] + [ci] * 4 + [vp]
+    lib.sdpa_forward_noalloc.restype = ci
     lib.sdpa_last_error.argtypes = []
     lib.sdpa_last_error.restype = ctypes.c_char_p
     lib.sdpa_version.argtypes = []
@@ -149,6 +157,14 @@ def sdpa_forward_q4kv(q, kq, ks, kb, vq, vs, vb, out, B, Hq, Hkv, qL, kL, kv_cap
     return load_library().sdpa_forward_q4kv(q, kq, ks, kb, vq, vs, vb, out, B, Hq, Hkv, qL, kL, kv_capacity,
                                             ring_start, D, scale, causal, window, q_offset, dtype, workspace,
                                             workspace_bytes, stream)
+
+
+def sdpa_forward_noalloc(q, k, v, out, B, Hq, Hkv, qL, kL, D, scale, causal, window, q_offset, dtype,
+                         stream) -> int:
+    """``int sdpa_forward_noalloc(...)`` of the C ABI (sdpa_forward without a workspace
+    argument: the library's own per-GPU scratch array); pointer arguments are integers."""
+    return load_library().sdpa_forward_noalloc(q, k, v, out, B, Hq, Hkv, qL, kL, D, scale, causal, window,
+                                               q_offset, dtype, stream)
 
 
 def sdpa_last_error() -> str:

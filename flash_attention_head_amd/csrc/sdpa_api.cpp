@@ -12,9 +12,10 @@
 #define SDPA_API extern "C" __attribute__((visibility("default")))
 
 namespace sdpa {
-namespace {
 
+namespace {
 thread_local char g_last_error[512] = "";
+}  // namespace
 
 int fail(int status, const char* fmt, ...) {
   va_list ap;
@@ -23,6 +24,10 @@ int fail(int status, const char* fmt, ...) {
   va_end(ap);
   return status;
 }
+
+void clear_error() { g_last_error[0] = '\0'; }
+
+namespace {
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
@@ -150,7 +155,7 @@ int forward_impl(const void* q, const void* k, const void* v, const void* bias, 
                  int64_t bias_sh, int64_t bias_sq, void* out, int B, int Hq, int Hkv, int qL, int kL,
                  int kv_cap, int ring_start, int chunk_cap, int D, int Dv, float scale, int causal,
                  int window, int q_offset, int dtype, void* workspace, size_t workspace_bytes,
-                 void* stream, const Q4Args* q4 = nullptr) {
+                 void* stream, const Q4Args* q4 = nullptr, bool launch = true) {
   if (!q || !k || !v || !out) return fail(SDPA_INVALID_ARG, "q, k, v and out must be non-null");
   int rc = check_shape(B, Hq, Hkv, qL, kv_cap, D, Dv);
   if (rc != SDPA_OK) return rc;
@@ -186,6 +191,7 @@ int forward_impl(const void* q, const void* k, const void* v, const void* bias, 
     return fail(SDPA_WORKSPACE_TOO_SMALL, "workspace of %zu bytes needed, %zu given", need,
                 workspace ? workspace_bytes : (size_t)0);
   if (sp.nsplit > 65535) return fail(SDPA_INVALID_ARG, "too many key splits (%d)", sp.nsplit);
+  if (!launch) return SDPA_OK;  // every check passed; nothing enqueued
 
   AttnParams p;
   p.q = (const uint16_t*)q;
@@ -240,6 +246,14 @@ int forward_impl(const void* q, const void* k, const void* v, const void* bias, 
 }
 
 }  // namespace
+
+int forward_plain(const void* q, const void* k, const void* v, void* out, int B, int Hq, int Hkv, int qL,
+                  int kL, int D, float scale, int causal, int window, int q_offset, int dtype, void* workspace,
+                  size_t workspace_bytes, void* stream, bool launch) {
+  return forward_impl(q, k, v, nullptr, 0, 0, 0, out, B, Hq, Hkv, qL, kL, kL, 0, 0, D, D, scale, causal, window,
+                      q_offset, dtype, workspace, workspace_bytes, stream, nullptr, launch);
+}
+
 }  // namespace sdpa
 
 using namespace sdpa;
@@ -270,16 +284,16 @@ SDPA_API int sdpa_forward(const void* q, const void* k, const void* v, void* out
                           int Hkv, int qL, int kL, int D, float scale, int causal, int window,
                           int q_offset, int dtype, void* workspace, size_t workspace_bytes,
                           void* stream) {
-  g_last_error[0] = '\0';
-  return forward_impl(q, k, v, nullptr, 0, 0, 0, out, B, Hq, Hkv, qL, kL, kL, 0, 0, D, D, scale, causal,
-                      window, q_offset, dtype, workspace, workspace_bytes, stream);
+  clear_error();
+  return forward_plain(q, k, v, out, B, Hq, Hkv, qL, kL, D, scale, causal, window, q_offset, dtype, workspace,
+                       workspace_bytes, stream, true);
 }
 
 SDPA_API int sdpa_forward_dv(const void* q, const void* k, const void* v, void* out, int B, int Hq,
                              int Hkv, int qL, int kL, int D, int Dv, float scale, int causal,
                              int window, int q_offset, int dtype, void* workspace,
                              size_t workspace_bytes, void* stream) {
-  g_last_error[0] = '\0';
+  clear_error();
   return forward_impl(q, k, v, nullptr, 0, 0, 0, out, B, Hq, Hkv, qL, kL, kL, 0, 0, D, Dv, scale, causal,
                       window, q_offset, dtype, workspace, workspace_bytes, stream);
 }
@@ -289,7 +303,7 @@ SDPA_API int sdpa_forward_bias(const void* q, const void* k, const void* v, cons
                                long long bias_stride_q, void* out, int B, int Hq, int Hkv, int qL,
                                int kL, int D, float scale, int causal, int window, int q_offset,
                                int dtype, void* workspace, size_t workspace_bytes, void* stream) {
-  g_last_error[0] = '\0';
+  clear_error();
   int rc = check_shape(B, Hq, Hkv, qL, kL, D, D);
   if (rc != SDPA_OK) return rc;
   if (!bias) return fail(SDPA_INVALID_ARG, "bias must be non-null");
@@ -311,7 +325,7 @@ SDPA_API int sdpa_forward_kv_view(const void* q, const void* k, const void* v, v
                                   int D, float scale, int causal, int window, int q_offset,
                                   int dtype, void* workspace, size_t workspace_bytes,
                                   void* stream) {
-  g_last_error[0] = '\0';
+  clear_error();
   int rc = check_shape(B, Hq, Hkv, qL, kL, D, D);
   if (rc != SDPA_OK) return rc;
   rc = check_view(kL, kv_capacity, ring_start);
@@ -326,7 +340,7 @@ SDPA_API int sdpa_forward_q4kv(const void* q, const void* kq, const void* ks, co
                                int Hq, int Hkv, int qL, int kL, int kv_capacity, int ring_start, int D,
                                float scale, int causal, int window, int q_offset, int dtype,
                                void* workspace, size_t workspace_bytes, void* stream) {
-  g_last_error[0] = '\0';
+  clear_error();
   int rc = check_shape(B, Hq, Hkv, qL, kL, D, D);
   if (rc != SDPA_OK) return rc;
   rc = check_view(kL, kv_capacity, ring_start);

@@ -86,4 +86,15 @@ hipError_t launch_attention(const AttnParams& p, int D, int Dv, int dtype, bool 
 hipError_t launch_attention_q4(const AttnParams& p, int dtype, hipStream_t stream);
 hipError_t launch_combine(const AttnParams& p, int Dv, int dtype, hipStream_t stream);
 
+// The calling thread's message for the last failed call: fail() formats it
+// and returns `status`; clear_error() empties it.
+int fail(int status, const char* fmt, ...);
+void clear_error();
+
+// sdpa_forward's argument checks and, when `launch` is set, its launches with
+// the workspace given here.  With launch false it only checks (no HIP call).
+int forward_plain(const void* q, const void* k, const void* v, void* out, int B, int Hq, int Hkv, int qL,
+                  int kL, int D, float scale, int causal, int window, int q_offset, int dtype, void* workspace,
+                  size_t workspace_bytes, void* stream, bool launch);
+
 }  // namespace sdpa

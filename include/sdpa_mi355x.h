@@ -228,6 +228,30 @@ int sdpa_forward_q4kv(const void* q, const void* kq, const void* ks, const void*
                       int q_offset, int dtype, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * sdpa_forward for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same computation, arguments and bytes out, without the workspace
+ * arguments.  The key-split partials that sdpa_forward keeps in the caller's
+ * workspace live instead in a scratch array of SDPA_NOALLOC_SCRATCH_BYTES
+ * that the library holds on each GPU it runs on, from the first call on that
+ * GPU until the process ends (that first call also looks up the array's
+ * device address).  No call allocates or frees anything.
+ *
+ * Calls whose sdpa_workspace_bytes(B, Hq, Hkv, qL, kL, D) exceeds
+ * SDPA_NOALLOC_SCRATCH_BYTES return SDPA_WORKSPACE_TOO_SMALL before anything
+ * is enqueued; other status codes as sdpa_forward.  Every call on one GPU
+ * shares that GPU's array, and it keeps what the last call left there (a
+ * call needs nothing cleared: it writes every partial it reads).  Calls that
+ * may overlap on one GPU -- on different streams, or from several host
+ * threads without ordering -- race on the array and must be serialised by
+ * the caller; calls on one stream are ordered by it.
+ */
+#define SDPA_NOALLOC_SCRATCH_BYTES (64u * 1024u * 1024u)
+int sdpa_forward_noalloc(const void* q, const void* k, const void* v, void* out, int B, int Hq, int Hkv,
+                         int qL, int kL, int D, float scale, int causal, int window, int q_offset,
+                         int dtype, void* stream);
+
+/*
  * Message for the last non-zero status returned on the calling thread ("" if
  * none).  Failures are reported, never raised: the error-handling note of
  * lablup/mlxcel issue #2160 (Implementation Notes) asks that a failed check

@@ -295,3 +295,41 @@ def test_q4kv_entry_point_rejects_what_it_does_not_take(lib):
     assert _call_q4(out=0x100000 - 4096) == fa.SDPA_INVALID_ARG and "overlap" in fa.sdpa_last_error()
     assert _call_q4(out=0x180000 + 256) == fa.SDPA_INVALID_ARG and "overlap" in fa.sdpa_last_error()
 
+
+# sdpa_forward_noalloc: sdpa_forward without workspace arguments
+NOALLOC_ORDER = [n for n in ORDER if n not in ("workspace", "workspace_bytes")]
+
+
+def _call_noalloc(**kw):
+    args = dict(GOOD, **kw)
+    return fa.sdpa_forward_noalloc(*[args[n] for n in NOALLOC_ORDER])
+
+
+def test_noalloc_entry_point_checks_arguments_before_any_hip_call(lib):
+    # the same checks and codes as sdpa_forward, all before the scratch array
+    # is looked up (no call here reaches the GPU)
+    assert _call_noalloc(q=None) == fa.SDPA_INVALID_ARG and "non-null" in fa.sdpa_last_error()
+    assert _call_noalloc(D=96) == fa.SDPA_UNSUPPORTED
+    assert _call_noalloc(Hq=3) == fa.SDPA_INVALID_ARG
+    assert _call_noalloc(q_offset=57) == fa.SDPA_INVALID_ARG and "q_offset" in fa.sdpa_last_error()
+    assert _call_noalloc(dtype=7) == fa.SDPA_UNSUPPORTED
+    assert _call_noalloc(window=5, causal=0) == fa.SDPA_INVALID_ARG
+    assert _call_noalloc(out=0x1000) == fa.SDPA_INVALID_ARG and "overlap" in fa.sdpa_last_error()
+
+
+def test_noalloc_entry_point_rejects_calls_beyond_its_scratch(lib):
+    # a verify block of 4 rows over 2^21 keys at 64 query heads needs
+    # 64 * 4 * 2048 * 258 * 4 bytes of partials, past the 64 MiB array
+    B, Hq, Hkv, qL, kL, D = 1, 64, 8, 4, 1 << 21, 256
+    need = fa.sdpa_workspace_bytes(B, Hq, Hkv, qL, kL, D)
+    assert need > fa.NOALLOC_SCRATCH_BYTES
+    rc = fa.sdpa_forward_noalloc(0x1000, 0x10000000, 0x40000000, 0x100000, B, Hq, Hkv, qL, kL, D, 0.0625, 1, 0,
+                                 kL - qL, fa.SDPA_BF16, None)
+    assert rc == fa.SDPA_WORKSPACE_TOO_SMALL
+    assert str(need) in fa.sdpa_last_error() and str(fa.NOALLOC_SCRATCH_BYTES) in fa.sdpa_last_error()
+
+
+def test_noalloc_scratch_size_matches_the_header():
+    text = open(HEADER).read()
+    m = re.search(r"#define SDPA_NOALLOC_SCRATCH_BYTES \((\d+)u \* (\d+)u \* (\d+)u\)", text)
+    assert m and int(m[1]) * int(m[2]) * int(m[3]) == fa.NOALLOC_SCRATCH_BYTES
