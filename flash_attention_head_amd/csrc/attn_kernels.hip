@@ -236,8 +236,15 @@ constexpr float kRescaleLog2 = 8.f;
 // busy through the softmax.  K and V have separate double buffers, V one
 // tile behind K: step t reads K(t+1) and V(t) and loads K(t+2) and V(t+1).
 // ---------------------------------------------------------------------------
-template <int DT, int DK, int DV, bool RING, bool BIAS, bool Q4 = false>
+template <int DT, int DK, int DV, bool RING, bool BIAS, int Q4M = 0>
 __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* lds) {
+  // Q4M: 0 for 16-bit K/V; 4-bit K/V with 1: one row-holding wave (at most 32
+  // packed rows: decode and verify steps), the other three load; 2: the
+  // general instance (prefill over a 4-bit prefix), in which every wave loads
+  // its share unless the workgroup has a single row-holding wave.  The host
+  // picks the instance from the packed row count; the decode instance holds
+  // only its own loaders' registers.
+  constexpr bool Q4 = Q4M != 0;
   // DK: head dim of q and k; DV: head dim of v and the output.
   // DK <= 256: a wave owns 32 rows and all DV output columns.  DK = DV =
   // 512: the two waves of a pair own the same 32 rows; wave h multiplies Q
@@ -247,6 +254,13 @@ __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* ld
   // output columns [256 h, 256 h + 256).  Up to 32 x 256 fp32 accumulators
   // per wave.
   constexpr bool PAIR = (DK == 512);
+  // MT: the 16-bit type of the staged K/V tiles, Q, P and the MFMAs.  The
+  // input type, except for 4-bit K/V: there the dequantized elements are
+  // staged as fp16 whatever the input type, since fp16 keeps 11 significant
+  // bits to bf16's 8; a bf16 Q converts to fp16 exactly (for values inside
+  // fp16's range), and the output is still rounded to the input type.
+  constexpr int MT = Q4 ? 0 : DT;
+  using EM = Elem<MT>;
   // V3: a third V buffer; V loaded in the P V region (see the step below)
   constexpr bool V3 = !Q4 && kv_tiles(BIAS, DK) == 5;
   // Q4: 4-bit K and V, dequantized into the same LDS tiles through registers
@@ -336,6 +350,48 @@ __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* ld
 #pragma unroll
     for (int dc = 0; dc < DC; ++dc)
       qf[dc] = valid ? *(const uint4*)(qrow + dc * 16 + lg * 8) : make_uint4(0, 0, 0, 0);
+    if constexpr (MT != DT) {  // bf16 Q to the fp16 of the staged tiles (RNE; exact in fp16's range)
+      auto cvt = [](uint32_t w) {
+        return Elem<0>::pack2(__builtin_bit_cast(float, w << 16), __builtin_bit_cast(float, w & 0xffff0000u));
+      };
+#pragma unroll
+      for (int dc = 0; dc < DC; ++dc) qf[dc] = make_uint4(cvt(qf[dc].x), cvt(qf[dc].y), cvt(qf[dc].z), cvt(qf[dc].w));
+    }
+  }
+  // 4-bit K: the B operand of the group-constant MFMA.  Q_g, the sum of the
+  // row's 64 (fp16) q elements of group g, in fp32 (the two lanes of a row
+  // hold halves of each group: their sums are added in either order, a + b
+  // == b + a), split into fp16 high and low parts.  Entries k = 0..15 of the
+  // B column: Q_g high at k = g and 8 + g, Q_g low at k = 4 + g, zero at
+  // 12..15; against the A entries b_g high at g and 4 + g and b_g low at 8 +
+  // g, the product sums b_g (Q_g high + low) + b_g low Q_g high.
+  // It is kept in LDS after the K operands (each lane reads back only its own
+  // 16 bytes, in program order: no barrier), not in registers across the loop.
+  uint16_t* const q4_qs = lds + 4 * TILE + 2 * 1024 + 8 * tid;
+  auto q4_qsum = [&]() { return *(const uint4*)q4_qs; };
+  if constexpr (Q4) {
+    float qs[4];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      float a = 0.f;
+#pragma unroll
+      for (int dc = 4 * g; dc < 4 * g + 4; ++dc) {
+        const uint32_t w[4] = {qf[dc].x, qf[dc].y, qf[dc].z, qf[dc].w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          a += (float)__builtin_bit_cast(_Float16, (uint16_t)(w[i] & 0xffffu)) +
+               (float)__builtin_bit_cast(_Float16, (uint16_t)(w[i] >> 16));
+      }
+      qs[g] = pair_sum(a);
+    }
+    uint32_t hi[2], lo[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const _Float16 h0 = (_Float16)qs[2 * i], h1 = (_Float16)qs[2 * i + 1];
+      hi[i] = (uint32_t)__builtin_bit_cast(uint16_t, h0) | ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
+      lo[i] = Elem<0>::pack2(qs[2 * i] - (float)h0, qs[2 * i + 1] - (float)h1);
+    }
+    *(uint4*)q4_qs = lg == 0 ? make_uint4(hi[0], hi[1], lo[0], lo[1]) : make_uint4(hi[0], hi[1], 0u, 0u);
   }
 
   f32x16_t o[DB];
@@ -573,8 +629,10 @@ __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* ld
     uint32_t w;     // code word
     uint32_t s, b;  // scale and bias bit patterns
   };
+  // waves 1..3 load, one step ahead (always in the decode instance; in the
+  // general one when the workgroup has a single row-holding wave)
   const int n_act = __builtin_amdgcn_readfirstlane(min(NW, (rows_end - row0 + kRowsPerWave - 1) / kRowsPerWave));
-  const bool q4_pipe = Q4 && n_act == 1;          // waves 1..3 load, one step ahead
+  const bool q4_pipe = Q4M == 1 || (Q4M == 2 && n_act == 1);
   const int q4_nl = q4_pipe ? NW - 1 : NW;        // loading waves
   const int q4_li = q4_pipe ? wave - 1 : wave;    // this wave's index among them
   const size_t q4_head = (size_t)(b * p.Hkv + hkv) * (size_t)p.kv_cap;  // the head's first cache row
@@ -608,8 +666,31 @@ __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* ld
     if constexpr (DT == 1) return __builtin_bit_cast(float, h << 16);
     else return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
   };
-  auto q4_store = [&](const Q4Data& d, uint16_t* buf, int blk) {
-    const float sc = q4_widen(d.s), bi = q4_widen(d.b);
+  // K(t)'s group-constant operand: per key row r of the tile, 16 fp16 entries
+  // at q4_kc + ((t - t_first) & 1) * 1024 + 16 r (see the K elements below)
+  uint16_t* const q4_kc = lds + 4 * TILE;
+  auto q4_store = [&](const Q4Data& d, uint16_t* buf, int blk, bool is_k) {
+    const float sc = q4_widen(d.s);
+    // V: element scale * code + bias.  K: the centred element scale *
+    // (code - 8), exact in fp16 for a bf16 scale (8 significant bits times an
+    // integer of at most 3), and the group's constant bias + 8 scale goes to
+    // the key row's operand entries g, g + 4 (its fp16 high part) and 8 + g
+    // (the low part), written by the lane holding the group's first chunk;
+    // the scores take it through one MFMA per key block against the
+    // query's group sums (q4_qsum)
+    const float bi = is_k ? -8.f * sc : q4_widen(d.b);
+    if (is_k) {
+      const int r = blk * RPB + lane / ROWCH, c = (lane % ROWCH) ^ (r & 15);
+      if ((c & 7) == 0) {
+        const float bg = q4_widen(d.b) + 8.f * sc;
+        const _Float16 h = (_Float16)bg;
+        const _Float16 l = (_Float16)(bg - (float)h);
+        uint16_t* e = q4_kc + (buf == kbuf0 ? 0 : 1024) + 16 * r + c / 8;
+        e[0] = __builtin_bit_cast(uint16_t, h);
+        e[4] = __builtin_bit_cast(uint16_t, h);
+        e[8] = __builtin_bit_cast(uint16_t, l);
+      }
+    }
     // even elements' codes in the bytes of lo, odd ones' in the bytes of hi:
     // each code is then one byte-to-float conversion (v_cvt_f32_ubyte<k>).
     // The empty asm hides that the bytes' high nibbles are zero; knowing it,
@@ -626,10 +707,10 @@ __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* ld
     using K2 = std::integral_constant<int, 2>;
     using K3 = std::integral_constant<int, 3>;
     uint4 out;
-    out.x = Elem<DT>::pack2(val(lo, K0{}), val(hi, K0{}));
-    out.y = Elem<DT>::pack2(val(lo, K1{}), val(hi, K1{}));
-    out.z = Elem<DT>::pack2(val(lo, K2{}), val(hi, K2{}));
-    out.w = Elem<DT>::pack2(val(lo, K3{}), val(hi, K3{}));
+    out.x = EM::pack2(val(lo, K0{}), val(hi, K0{}));
+    out.y = EM::pack2(val(lo, K1{}), val(hi, K1{}));
+    out.z = EM::pack2(val(lo, K2{}), val(hi, K2{}));
+    out.w = EM::pack2(val(lo, K3{}), val(hi, K3{}));
     *(uint4*)(buf + blk * 512 + 8 * lane) = out;
   };
   // this wave's blocks of K tile tk and V tile tv: issue, then store.
@@ -648,8 +729,8 @@ __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* ld
     constexpr int N = sizeof(kd) / sizeof(kd[0]);
 #pragma unroll
     for (int i = 0; i < N; ++i) {
-      q4_store(kd[i], kdst, q4_blk(i));
-      q4_store(vd[i], vdst, q4_blk(i));
+      q4_store(kd[i], kdst, q4_blk(i), true);
+      q4_store(vd[i], vdst, q4_blk(i), false);
     }
   };
 
@@ -666,12 +747,21 @@ __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* ld
   //      can interleave them with sched_group_barrier patterns) -------------
   // S^T = K(t) Q^T, K operands read PF MFMAs ahead; the two key-block chains
   // alternate
+  // 4-bit K: the A operand of the group-constant MFMA of key block kb, from
+  // the operand entries of the K buffer whose tile starts at kl
+  auto q4_kc_read = [&](const uint16_t* kl, int kb) {
+    return *(const uint4*)(q4_kc + (kl == kbuf0 ? 0 : 1024) + 16 * (32 * kb + lr) + 8 * lg);
+  };
   auto qk = [&](f32x16_t (&s)[KB], const uint16_t* kl) {
     constexpr int PF = 4;
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
       for (int j = 0; j < 16; ++j) s[kb][j] = 0.f;
+    if constexpr (Q4) {
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) s[kb] = EM::mfma(q4_kc_read(kl, kb), q4_qsum(), s[kb]);
+    }
     auto kread = [&](int n) {
       const int kb = n % KB, dc = n / KB;
       return *(const uint4*)(kl + kaddr(kb, dc));
@@ -683,7 +773,7 @@ __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* ld
     for (int n = 0; n < NQK; ++n) {
       const uint4 cur_a = a[n % PF];
       if (n + PF < NQK) a[n % PF] = kread(n + PF);
-      s[n % KB] = Elem<DT>::mfma(cur_a, qf[n / KB], s[n % KB]);
+      s[n % KB] = EM::mfma(cur_a, qf[n / KB], s[n % KB]);
     }
   };
   // keys of tile t a row may not see -> -inf.  Score element (kb, j) holds
@@ -757,7 +847,7 @@ __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* ld
   auto qk_weights = [&](f32x16_t (&sn)[KB], const uint16_t* kl, f32x16_t (&sc)[KB],
                         uint4 (&pb)[KB * 2], const TileSrc& ksrc, uint16_t* kdst, const TileSrc& vsrc,
                         uint16_t* vdst, const i32x4_t& bsrc, uint16_t* bdst, const uint16_t* bl,
-                        uint2 (&bw)[KB * 4], uint4 (&a)[4]) {
+                        uint2 (&bw)[KB * 4], uint4 (&a)[4], const uint4 (&kc)[KB + 1]) {
     constexpr int PF = 4;
     // the slots of K block group i, V block group i (unless VLATE) and bias
     // block group i: spread evenly over the region, V half a spacing after
@@ -774,6 +864,10 @@ __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* ld
     for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
       for (int j = 0; j < 16; ++j) sn[kb][j] = 0.f;
+    if constexpr (Q4) {  // the key rows' group constants times the query's group sums first
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) sn[kb] = EM::mfma(kc[kb], kc[KB], sn[kb]);
+    }
     // K operand of MFMA n: key block n % KB, d step n / KB; the XOR part of
     // its address is a register, the rest an immediate
     auto kread = [&](int n, int x) { return kread_at(kl, n, x); };
@@ -801,7 +895,7 @@ __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* ld
     for (int n = 0; n < NQK; ++n) {
       const uint4 cur_a = a[n % PF];
       if (n + PF < NQK) a[n % PF] = kread(n + PF, x_next);
-      sn[n % KB] = Elem<DT>::mfma(cur_a, qf[n / KB], sn[n % KB]);
+      sn[n % KB] = EM::mfma(cur_a, qf[n / KB], sn[n % KB]);
       if (n + PF + 1 < NQK) x_next = kx(n + PF + 1);
       // loads: K, V and bias block group i at slots kslot(i), vslot(i), bslot(i)
       if constexpr (EVEN) {
@@ -836,12 +930,12 @@ __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* ld
       // per dot2, one slot after the pair is packed
       if (n > 0) {
 #pragma unroll
-        for (int i = 0; i < npacks(n - 1); ++i) psum = Elem<DT>::sum2(wlast[i], psum);
+        for (int i = 0; i < npacks(n - 1); ++i) psum = EM::sum2(wlast[i], psum);
       }
 #pragma unroll
       for (int e = es(n); e < es(n + 1); ++e) {
         if (e & 1) {  // pack the pair (e - 1, e): P half kh = e / 8
-          const uint32_t w = Elem<DT>::pack2(get(e - 1), get(e));
+          const uint32_t w = EM::pack2(get(e - 1), get(e));
           wlast[e - es(n) > 1 ? 1 : 0] = w;
           uint4& q = pb[e / 8];
           switch ((e % 8) / 2) {
@@ -855,7 +949,7 @@ __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* ld
       __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
-    for (int i = 0; i < npacks(NQK - 1); ++i) psum = Elem<DT>::sum2(wlast[i], psum);
+    for (int i = 0; i < npacks(NQK - 1); ++i) psum = EM::sum2(wlast[i], psum);
     m0_restore(m0);
     // an empty volatile use: the sum is formed here, slot by slot, not sunk
     // past the next region as a serial chain
@@ -892,7 +986,7 @@ __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* ld
     for (int n = 0; n < NPV; ++n) {
       const uint4 cur_b = bv[n % PF];
       if (n + PF < NPV) bv[n % PF] = vread(n + PF, x_next);
-      o[n % DB] = Elem<DT>::mfma(cur_b, pb[n / DB], o[n % DB]);
+      o[n % DB] = EM::mfma(cur_b, pb[n / DB], o[n % DB]);
       if (n + PF + 1 < NPV) x_next = vx(n + PF + 1);
       if (VLATE && n % LSV == LSV / 2) load_blk(vsrc, vdst, n / LSV, true);
       // the pairs (e - 1, e) whose odd element is one of this slot's
@@ -950,6 +1044,9 @@ __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* ld
   // a V tile never hold uninitialised LDS (a zero weight times a NaN bit
   // pattern would still be NaN); K rows past kL need nothing, their scores
   // are masked to -inf.
+  if constexpr (Q4) {  // operand entries 12..15 of the 2 x 64 key rows: zero, never written again
+    if (tid < 2 * BN) *(uint2*)(q4_kc + 16 * tid + 12) = make_uint2(0, 0);
+  }
   if ((t_last + 1) * BN > p.kL) {
     uint4* vz = (uint4*)vbuf0;
     for (int i = tid; i < NVB * TILE / 8; i += NW * 64) vz[i] = make_uint4(0, 0, 0, 0);
@@ -960,7 +1057,7 @@ __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* ld
   // holds K(t+2), V(t+1) when step t (parity P) starts, issued one step
   // earlier; the step issues the other set for K(t+3), V(t+2)
   typename std::conditional<Q4, Q4Data, char>::type q4a_k[Q4 ? QB : 1], q4a_v[Q4 ? QB : 1];
-  typename std::conditional<Q4, Q4Data, char>::type q4s_k[2][Q4 ? QB4 : 1], q4s_v[2][Q4 ? QB4 : 1];
+  typename std::conditional<Q4, Q4Data, char>::type q4s_k[2][Q4M == 2 ? QB4 : 1], q4s_v[2][Q4M == 2 ? QB4 : 1];
   if constexpr (Q4) {
     if (q4_li >= 0) {  // wave 0 of a pipelined workgroup does not load
       Q4Data k0[QB], v0[QB], k1[QB], v1[QB];
@@ -1038,6 +1135,12 @@ __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* ld
 #pragma unroll
     for (int i = 0; i < 4; ++i) a[i] = kread_at(kl, i, kx(i));
     rescale(alpha_cur);
+    uint4 kc[KB + 1];  // 4-bit K: the group-constant operands, A per key block and B
+#pragma unroll
+    for (int kb = 0; kb <= KB; ++kb) {
+      if constexpr (Q4) kc[kb] = kb < KB ? q4_kc_read(kl, kb) : q4_qsum();
+      else kc[kb] = make_uint4(0, 0, 0, 0);
+    }
     uint2 bw[KB * 4];
     const TileSrc vsrc = tile_src(vg, tv, true);
     uint16_t* const vdst = vbuf0 + (V3 ? (VB + 2) % 3 : 1 - P) * TILE;
@@ -1049,7 +1152,7 @@ __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* ld
     }
     const float psum = qk_weights(sn, kl, sc, pb, tile_src(kg, tk, false), kbuf0 + P * TILE,
                                   vsrc, vdst, BIAS ? bias_src(tk) : i32x4_t{}, bbuf0 + P * BTILE,
-                                  bbuf0 + (1 - P) * BTILE, bw, a);
+                                  bbuf0 + (1 - P) * BTILE, bw, a, kc);
     exchange(sn, true);  // D = 512: also the V(t) barrier
     l_run = l_run * alpha_cur + psum;
     if (!full_tile(t + 1)) mask(sn, t + 1);
@@ -1229,12 +1332,14 @@ void attn_tile_kernel_d512(AttnParams p) {
   attn_pipe_body<DT, 512, 512, RING, BIAS>(p, lds);
 }
 
-// head dim 256 with 4-bit K and V (2 K + 2 V tiles)
-template <int DT>
+// head dim 256 with 4-bit K and V (2 K + 2 V tiles); Q4M as in attn_pipe_body
+template <int DT, int Q4M>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void attn_tile_kernel_d256_q4(AttnParams p) {
-  __shared__ __attribute__((aligned(16))) uint16_t lds[4 * 64 * 256];
-  attn_pipe_body<DT, 256, 256, false, false, true>(p, lds);
+  // 2 K + 2 V tiles, then the K tiles' group-constant operands (2 x 64 keys x
+  // 16) and each lane's query group sums (256 lanes x 8)
+  __shared__ __attribute__((aligned(16))) uint16_t lds[4 * 64 * 256 + 2 * 64 * 16 + 256 * 8];
+  attn_pipe_body<DT, 256, 256, false, false, Q4M>(p, lds);
 }
 
 // Merge of the per-split partials of each output row.  One workgroup of nw =
@@ -1467,8 +1572,15 @@ hipError_t launch_attention(const AttnParams& p, int D, int Dv, int dtype, bool 
 
 hipError_t launch_attention_q4(const AttnParams& p, int dtype, hipStream_t stream) {
   const dim3 grid((unsigned)(p.B * p.Hkv * p.mblocks), (unsigned)p.nsplit, 1);
-  if (dtype == 0) hipLaunchKernelGGL((attn_tile_kernel_d256_q4<0>), grid, dim3(256), 0, stream, p);
-  else hipLaunchKernelGGL((attn_tile_kernel_d256_q4<1>), grid, dim3(256), 0, stream, p);
+  // at most 32 packed rows: every workgroup has one row-holding wave
+  const bool one = p.rows <= kRowsPerWave;
+  if (dtype == 0) {
+    if (one) hipLaunchKernelGGL((attn_tile_kernel_d256_q4<0, 1>), grid, dim3(256), 0, stream, p);
+    else hipLaunchKernelGGL((attn_tile_kernel_d256_q4<0, 2>), grid, dim3(256), 0, stream, p);
+  } else {
+    if (one) hipLaunchKernelGGL((attn_tile_kernel_d256_q4<1, 1>), grid, dim3(256), 0, stream, p);
+    else hipLaunchKernelGGL((attn_tile_kernel_d256_q4<1, 2>), grid, dim3(256), 0, stream, p);
+  }
   return hipGetLastError();
 }
 

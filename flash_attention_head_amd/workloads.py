@@ -213,6 +213,48 @@ def random_q4kv(seed: int, B: int, Hkv: int, kL: int, D: int, dtype: int):
     return tuple(out)
 
 
+def shaped_q4kv(seed: int, B: int, Hq: int, Hkv: int, qL: int, kL: int, dtype: int, kind: str):
+    """Seeded Q and 4-bit K/V rows (q, kq, ks, kb, vq, vs, vb) of a chosen shape of values.
+
+    kind "narrow": value groups with scale U(0.09, 0.11) and bias U(2.0, 2.3), so
+    that every value and every output lies in [2, 4), where a bf16 spacing is
+    2^-6; key groups with scale U(0.05, 0.15) and bias -7.5 scale + N(0, 0.1).
+    kind "ramp": query row i is c_i + N(0, 1) in every element, c_i ~ U(-0.5, 1.5)
+    per row; key groups have scale U(0.05, 0.1) and a bias that grows from 0 to 4
+    along the keys (plus N(0, 0.05)), so that the scores of rows with c_i > 0
+    climb by tens of natural units over the keys; values as in ``random_q4kv``.
+    Code words are uniformly random bits.  Holds none of the attention or
+    dequantization arithmetic.
+    """
+    g = torch.Generator(device="cpu")
+    g.manual_seed(seed)
+    dt = TORCH_DTYPES[dtype]
+    if kind == "ramp":
+        c = torch.rand((B, Hq, qL, 1), generator=g, dtype=torch.float32) * 2.0 - 0.5
+        q = (c + torch.randn((B, Hq, qL, 256), generator=g, dtype=torch.float32)).to(dt)
+    else:
+        q = torch.randn((B, Hq, qL, 256), generator=g, dtype=torch.float32).to(dt)
+    out = [q]
+    for which in ("k", "v"):
+        words = torch.randint(-(1 << 31), 1 << 31, (B, Hkv, kL, 32), generator=g, dtype=torch.int64)
+        u = torch.rand((B, Hkv, kL, 4), generator=g, dtype=torch.float32)
+        n = torch.randn((B, Hkv, kL, 4), generator=g, dtype=torch.float32)
+        if which == "k" and kind == "ramp":
+            sc = u * 0.05 + 0.05
+            bi = 4.0 * (torch.arange(kL, dtype=torch.float32) / kL).view(1, 1, kL, 1) + 0.05 * n
+        elif which == "k":
+            sc = u * 0.1 + 0.05
+            bi = -7.5 * sc + 0.1 * n
+        elif kind == "narrow":
+            sc = u * 0.02 + 0.09
+            bi = 2.0 + 0.3 * torch.rand((B, Hkv, kL, 4), generator=g, dtype=torch.float32)
+        else:
+            sc = u * 0.2 + 0.3
+            bi = -7.5 * sc + 0.1 * n
+        out += [words.to(torch.int32), sc.to(dt), bi.to(dt)]
+    return tuple(out)
+
+
 def words(t: torch.Tensor) -> np.ndarray:
     """uint32 views of a CPU int32 tensor of 4-bit code words."""
     return t.contiguous().numpy().view(np.uint32)

