@@ -236,8 +236,10 @@ constexpr float kRescaleLog2 = 8.f;
 // busy through the softmax.  K and V have separate double buffers, V one
 // tile behind K: step t reads K(t+1) and V(t) and loads K(t+2) and V(t+1).
 // ---------------------------------------------------------------------------
-template <int DT, int DK, int DV, bool RING, bool BIAS, int Q4M = 0>
+template <int DT, int DK, int DV, bool RING, bool BIAS, int Q4M = 0, bool PERS = false>
 __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* lds) {
+  // PERS: the workgroup runs several row blocks of one (batch, KV head) with
+  // one software pipeline (see the persistent loop below)
   // Q4M: 0 for 16-bit K/V; 4-bit K/V with 1: one row-holding wave (at most 32
   // packed rows: decode and verify steps), the other three load; 2: the
   // general instance (prefill over a 4-bit prefix), in which every wave loads
@@ -304,35 +306,51 @@ __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* ld
   const int nheads = p.B * p.Hkv;
   const int head = blockIdx.x % nheads;
   const int mbr = blockIdx.x / nheads;
-  const int mb = p.causal ? (p.mblocks - 1 - mbr) : mbr;
+  // PERS: workgroup w of a head runs row blocks w, w + S, w + 2 S, ... (S =
+  // p.pers_stride workgroups per head), so that the workgroups that run at
+  // the same time on an XCD work on neighbouring blocks and share K/V tiles
+  // through its L2, as separate workgroups would
+  const int mb = PERS ? mbr : p.causal ? (p.mblocks - 1 - mbr) : mbr;
   const int split = blockIdx.y;
   const int b = head / p.Hkv, hkv = head % p.Hkv;
 
-  const int row0 = mb * BM;
-  const int rows_end = min(p.rows, row0 + BM);
-  const int wrow0 = row0 + rb * kRowsPerWave;
-  const bool wave_active = wrow0 < rows_end;
-  const int my = wrow0 + lr;
-  const bool valid = my < rows_end;
-  const int qi = valid ? my / p.G : 0;
-  const int hq = hkv * p.G + (valid ? my % p.G : 0);
-  const int pos = p.q_offset + qi;
-  // first and last query position of the wave's rows (uniform; scalar
-  // registers, so that tile tests on them are scalar branches)
-  const int wp_lo = __builtin_amdgcn_readfirstlane(p.q_offset + wrow0 / p.G);
-  const int wp_hi = __builtin_amdgcn_readfirstlane(p.q_offset + (min(rows_end, wrow0 + kRowsPerWave) - 1) / p.G);
-
-  int kbeg = 0, kend = p.kL;
-  {
-    const int bp_lo = p.q_offset + row0 / p.G;
-    const int bp_hi = p.q_offset + (rows_end - 1) / p.G;
-    if (p.causal) kend = min(kend, bp_hi + 1);
-    if (p.window > 0) kbeg = max(0, bp_lo - p.window + 1);
+  // the rows of row block mb: this wave's, this lane's, and the key range
+  // they see (mutable only in the persistent loop, which moves to the next
+  // block)
+  int row0, rows_end, wrow0, my, qi, hq, pos, wp_lo, wp_hi;
+  bool wave_active, valid;
+  auto set_rows = [&](int mbx) {
+    row0 = mbx * BM;
+    rows_end = min(p.rows, row0 + BM);
+    wrow0 = row0 + rb * kRowsPerWave;
+    wave_active = wrow0 < rows_end;
+    my = wrow0 + lr;
+    valid = my < rows_end;
+    qi = valid ? my / p.G : 0;
+    hq = hkv * p.G + (valid ? my % p.G : 0);
+    pos = p.q_offset + qi;
+    // first and last query position of the wave's rows (uniform; scalar
+    // registers, so that tile tests on them are scalar branches)
+    wp_lo = __builtin_amdgcn_readfirstlane(p.q_offset + wrow0 / p.G);
+    wp_hi = __builtin_amdgcn_readfirstlane(p.q_offset + (min(rows_end, wrow0 + kRowsPerWave) - 1) / p.G);
+  };
+  set_rows(mb);
+  // the tiles row block mbx's rows see (within this split)
+  auto block_keys = [&](int mbx, int& kb0, int& ke0) {
+    const int r0 = mbx * BM, re = min(p.rows, r0 + BM);
+    const int bp_lo = p.q_offset + r0 / p.G;
+    const int bp_hi = p.q_offset + (re - 1) / p.G;
+    kb0 = 0;
+    ke0 = p.kL;
+    if (p.causal) ke0 = min(ke0, bp_hi + 1);
+    if (p.window > 0) kb0 = max(0, bp_lo - p.window + 1);
     if (p.partials) {
-      kbeg = max(kbeg, split * p.split_len);
-      kend = min(kend, (split + 1) * p.split_len);
+      kb0 = max(kb0, split * p.split_len);
+      ke0 = min(ke0, (split + 1) * p.split_len);
     }
-  }
+  };
+  int kbeg, kend;
+  block_keys(mb, kbeg, kend);
   if (kbeg >= kend) return;
   const int t_first = __builtin_amdgcn_readfirstlane(kbeg / BN);
   const int t_last = __builtin_amdgcn_readfirstlane((kend - 1) / BN);
@@ -344,12 +362,19 @@ __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* ld
   const uint16_t* __restrict__ kg = p.k + kv_row * DK;
   const uint16_t* __restrict__ vg = p.v + kv_row * DV;
 
+  // this lane's Q row of row block mbx (zeros for a row past the block's end)
+  auto load_q = [&](uint4 (&dst)[DC], int mbx) {
+    const int r0 = mbx * BM, re = min(p.rows, r0 + BM);
+    const int m = r0 + rb * kRowsPerWave + lr;
+    const bool ok = m < re;
+    const uint16_t* qrow =
+        p.q + ((size_t)(b * p.Hq + hkv * p.G + (ok ? m % p.G : 0)) * p.qL + (ok ? m / p.G : 0)) * DK + qd0;
+#pragma unroll
+    for (int dc = 0; dc < DC; ++dc) dst[dc] = ok ? *(const uint4*)(qrow + dc * 16 + lg * 8) : make_uint4(0, 0, 0, 0);
+  };
   uint4 qf[DC];
   {
-    const uint16_t* qrow = p.q + ((size_t)(b * p.Hq + hq) * p.qL + qi) * DK + qd0;
-#pragma unroll
-    for (int dc = 0; dc < DC; ++dc)
-      qf[dc] = valid ? *(const uint4*)(qrow + dc * 16 + lg * 8) : make_uint4(0, 0, 0, 0);
+    load_q(qf, mb);
     if constexpr (MT != DT) {  // bf16 Q to the fp16 of the staged tiles (RNE; exact in fp16's range)
       auto cvt = [](uint32_t w) {
         return Elem<0>::pack2(__builtin_bit_cast(float, w << 16), __builtin_bit_cast(float, w & 0xffff0000u));
@@ -736,8 +761,12 @@ __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* ld
 
   // the keys row `pos` sees form one interval [key_lo, key_hi] (empty if
   // key_hi < key_lo)
-  const int key_lo = p.window > 0 ? max(0, pos - p.window + 1) : 0;
-  const int key_hi = p.causal ? min(pos, p.kL - 1) : p.kL - 1;
+  int key_lo, key_hi;
+  auto set_keys = [&]() {
+    key_lo = p.window > 0 ? max(0, pos - p.window + 1) : 0;
+    key_hi = p.causal ? min(pos, p.kL - 1) : p.kL - 1;
+  };
+  set_keys();
   auto full_tile = [&](int t) {  // every key of tile t visible to every row of this wave
     const int ts = t * BN, te = ts + BN - 1;
     return (te < p.kL) && (!p.causal || te <= wp_lo) && (p.window == 0 || ts >= wp_hi - p.window + 1);
@@ -1038,6 +1067,165 @@ __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* ld
     }
   };
 
+  // ---- persistent loop (PERS) ------------------------------------------
+  // Row blocks w, w + S, ... of this (batch, KV head) run as one sequence of
+  // tiles: each block's tiles in ascending order, then the next block's.  The
+  // software pipeline runs across the block boundaries: the K/V loads of the
+  // next block's first tiles are issued during the current block's last
+  // steps, its Q rows are loaded a whole block ahead into a second register
+  // set, and the step that finishes a block already computes the next
+  // block's first scores.  At a boundary the step switches the rows' context
+  // (Q, visible-key interval, reference max) between its S and P V regions;
+  // after it, the finished block's output is normalised and stored while the
+  // next block runs.  Every wave runs every step: a wave whose rows lie past
+  // the end of a ragged last block computes on zero queries and stores
+  // nothing.
+  if constexpr (PERS) {
+    static_assert(V3 && !RING && !BIAS && !Q4 && !PAIR, "the persistent loop takes the three-V-buffer pipeline");
+    const int S = p.pers_stride;
+    const int nblk = __builtin_amdgcn_readfirstlane((p.mblocks - mbr + S - 1) / S);
+    auto block_mb = [&](int j) { return mbr + j * S; };
+    // a position in the tile sequence: block j, tile t, the block's last tile
+    struct Cur {
+      int j, t, tl;
+    };
+    auto first_of = [&](int j) {
+      int kb0, ke0;
+      block_keys(block_mb(j), kb0, ke0);
+      return Cur{j, __builtin_amdgcn_readfirstlane(kb0 / BN), __builtin_amdgcn_readfirstlane((ke0 - 1) / BN)};
+    };
+    // the next position; past the last tile of the last block it stays there
+    auto adv = [&](const Cur& c) {
+      if (c.t < c.tl) return Cur{c.j, c.t + 1, c.tl};
+      if (c.j + 1 < nblk) return first_of(c.j + 1);
+      return c;
+    };
+    auto is_end = [&](const Cur& c) { return c.j == nblk - 1 && c.t == c.tl; };
+    const Cur c_end = [&]() {  // the very last tile (its loads may be ragged)
+      Cur c = first_of(nblk - 1);
+      return c;
+    }();
+    if ((c_end.tl + 1) * BN > p.kL) {  // rows past kL of a V tile: zeros, never garbage
+      uint4* vz = (uint4*)vbuf0;
+      for (int i = tid; i < NVB * TILE / 8; i += NW * 64) vz[i] = make_uint4(0, 0, 0, 0);
+      __syncthreads();
+    }
+    uint4 qn[DC];  // the next block's Q rows, loaded a block ahead
+    if (nblk > 1) load_q(qn, block_mb(1));
+
+    // prologue: K(v0), V(v0), K(v1), V(v1); S(v0) and its row max
+    const Cur c0 = first_of(0), c1 = adv(c0);
+    load_tile(kg, c0.t, kbuf0, false);
+    load_tile(vg, c0.t, vbuf0, true);
+    load_tile(kg, c1.t, kbuf0 + TILE, false);
+    load_tile(vg, c1.t, vbuf0 + TILE, true);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    f32x16_t sA[KB], sB[KB];
+    qk(sA, kbuf0);
+    if (!full_tile(c0.t)) mask(sA, c0.t);
+    float alpha_cur = row_max(sA);
+    __syncthreads();  // every wave is done with K(v0) before K(v2) overwrites it
+
+    // the finished block's output rows (its row context, saved at the switch)
+    auto store_rows = [&](bool ok, int hq_o, int qi_o) {
+      const float lsum = pair_sum(l_run);
+      if (ok) {
+        const float inv = lsum > 0.f ? 1.0f / lsum : 0.f;
+        uint16_t* dst = p.out + ((size_t)(b * p.Hq + hq_o) * p.qL + qi_o) * DV + od0;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4) {
+            if (db * 32 + 8 * q4 >= DO) continue;
+            const int d = db * 32 + 8 * q4 + 4 * lg;
+            uint2 wv;
+            wv.x = Elem<DT>::pack2(o[db][4 * q4 + 0] * inv, o[db][4 * q4 + 1] * inv);
+            wv.y = Elem<DT>::pack2(o[db][4 * q4 + 2] * inv, o[db][4 * q4 + 3] * inv);
+            *(uint2*)(dst + d) = wv;
+          }
+      }
+    };
+    // one step at position c (tile v): as `step` below, with the next tiles
+    // taken from the sequence and the block switch at a boundary
+    auto pstep = [&](const Cur& c, f32x16_t (&sc)[KB], f32x16_t (&sn)[KB], auto parity, auto vbuf) {
+      constexpr int P = decltype(parity)::value, VB = decltype(vbuf)::value;
+      const Cur n1 = adv(c), n2 = adv(n1);
+      const bool has_next = !is_end(c);
+      const bool boundary = has_next && n1.j != c.j;
+      if (boundary) {  // S(v + 1) is the next block's: its Q rows
+#pragma unroll
+        for (int dc = 0; dc < DC; ++dc) qf[dc] = qn[dc];
+      }
+      uint4 pb[KB * 2];
+      const uint16_t* const kl = kbuf0 + (1 - P) * TILE;
+      uint4 a[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a[i] = kread_at(kl, i, kx(i));
+      rescale(alpha_cur);
+      uint4 kc[KB + 1];
+#pragma unroll
+      for (int kb = 0; kb <= KB; ++kb) kc[kb] = make_uint4(0, 0, 0, 0);
+      uint2 bw[KB * 4];
+      const TileSrc vsrc = tile_src(vg, n2.t, true);
+      uint16_t* const vdst = vbuf0 + ((VB + 2) % 3) * TILE;
+      const float psum = qk_weights(sn, kl, sc, pb, tile_src(kg, n2.t, false), kbuf0 + P * TILE, vsrc, vdst,
+                                    i32x4_t{}, bbuf0, bbuf0, bw, a, kc);
+      l_run = l_run * alpha_cur + psum;
+      bool ok_o = false;
+      int hq_o = 0, qi_o = 0;
+      if (boundary) {  // tile v closed this block: the next one's rows from here on
+        ok_o = valid;
+        hq_o = hq;
+        qi_o = qi;
+        set_rows(block_mb(n1.j));
+        set_keys();
+        m_ref = -INFINITY;
+        if (n1.j + 1 < nblk) load_q(qn, block_mb(n1.j + 1));
+      }
+      if (!full_tile(n1.t)) mask(sn, n1.t);
+      alpha_cur = pv_max(pb, vbuf0 + VB * TILE, sn, has_next, bw, vsrc, vdst);
+      wait_vmem<PV_LOADS>();
+      __syncthreads();
+      if (boundary) {  // O now holds the closed block's rows
+        store_rows(ok_o, hq_o, qi_o);
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int jj = 0; jj < 16; ++jj) o[db][jj] = 0.f;
+        l_run = 0.f;
+      }
+      return n1;
+    };
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    Cur c = c0;
+    for (;;) {
+      bool end = is_end(c);
+      c = pstep(c, sA, sB, I0{}, I0{});
+      if (end) break;
+      end = is_end(c);
+      c = pstep(c, sB, sA, I1{}, I1{});
+      if (end) break;
+      end = is_end(c);
+      c = pstep(c, sA, sB, I0{}, I2{});
+      if (end) break;
+      end = is_end(c);
+      c = pstep(c, sB, sA, I1{}, I0{});
+      if (end) break;
+      end = is_end(c);
+      c = pstep(c, sA, sB, I0{}, I1{});
+      if (end) break;
+      end = is_end(c);
+      c = pstep(c, sB, sA, I1{}, I2{});
+      if (end) break;
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    store_rows(valid, hq, qi);  // the last block
+    return;
+  }
+
   // ---- prologue: K(t0), V(t0), K(t0 + 1); S(t0) and its row max ------------
   // Rows past kL are out of the loads' range.  When this workgroup's last
   // tile has such rows, the V buffers start as zeros, so that those rows of
@@ -1325,6 +1513,13 @@ void attn_tile_kernel_d256(AttnParams p) {
   __shared__ __attribute__((aligned(16))) uint16_t lds[kv_tiles(BIAS, 256) * 64 * 256 + (BIAS ? 2 * 128 * 64 : 0)];
   attn_pipe_body<DT, 256, 256, RING, BIAS>(p, lds);
 }
+// head dim 256, the persistent loop over several row blocks per workgroup
+template <int DT>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void attn_tile_kernel_d256_pers(AttnParams p) {
+  __shared__ __attribute__((aligned(16))) uint16_t lds[kv_tiles(false, 256) * 64 * 256];
+  attn_pipe_body<DT, 256, 256, false, false, 0, true>(p, lds);
+}
 template <int DT, bool RING, bool BIAS>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void attn_tile_kernel_d512(AttnParams p) {
@@ -1560,6 +1755,13 @@ hipError_t launch_attention(const AttnParams& p, int D, int Dv, int dtype, bool 
     const dim3 grid((unsigned)(p.B * p.Hkv * p.mblocks), (unsigned)p.nsplit, 1);
     if (dtype == 0) hipLaunchKernelGGL((attn_tile_kernel_dk192_dv256<0>), grid, dim3(256), 0, stream, p);
     else hipLaunchKernelGGL((attn_tile_kernel_dk192_dv256<1>), grid, dim3(256), 0, stream, p);
+    return hipGetLastError();
+  }
+  if (p.pers_stride > 0) {  // the host sets it only for D = 256 without ring, bias or key split
+    if (D != 256 || ring || p.bias || p.partials) return hipErrorInvalidValue;
+    const dim3 grid((unsigned)(p.B * p.Hkv * p.pers_stride), 1, 1);
+    if (dtype == 0) hipLaunchKernelGGL((attn_tile_kernel_d256_pers<0>), grid, dim3(256), 0, stream, p);
+    else hipLaunchKernelGGL((attn_tile_kernel_d256_pers<1>), grid, dim3(256), 0, stream, p);
     return hipGetLastError();
   }
   if (D == 64) return launch_attention_dd<64>(p, dtype, ring, stream);

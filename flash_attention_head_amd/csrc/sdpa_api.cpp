@@ -237,6 +237,15 @@ int forward_impl(const void* q, const void* k, const void* v, const void* bias, 
   // the rows of some tile wrap around the end of the cache rows only if the
   // live keys do
   const bool ring = (int64_t)ring_start + kL > kv_cap;
+  // sliding-window prefill at head dim 256: a workgroup runs several row
+  // blocks of its (batch, KV head) in one pipeline, S workgroups per head
+  // (enough to fill the CUs once), workgroup w taking blocks w, w + S, ...
+  p.pers_stride = 0;
+  if (!q4 && !bias && !ring && D == 256 && Dv == 256 && window > 0 && !sp.partials) {
+    const int64_t heads = (int64_t)B * Hkv;
+    const int64_t S = ceil_div(kPlannedCUs, heads);
+    if (S < p.mblocks) p.pers_stride = (int)S;
+  }
 
   hipStream_t s = (hipStream_t)stream;
   hipError_t e = q4 ? launch_attention_q4(p, dtype, s) : launch_attention(p, D, Dv, dtype, ring, s);

@@ -65,6 +65,8 @@ struct AttnParams {
   int nsplit;         // key splits
   int split_len;      // keys per split, a multiple of the tile width
   int partials;       // 1: write partials for the combine pass
+  int pers_stride;    // > 0: S workgroups per (b, kv head), workgroup w running row
+                      // blocks w, w + S, ... in one pipeline (head dim 256 only)
 };
 
 // Split plan for a shape: how many key splits, how long each, and whether

@@ -64,6 +64,24 @@ def test_peak_is_inputs_plus_output_plus_workspace_and_linear_in_kL():
         print("%d\t%d\t%.0f\t%.0f\t%.1f\t%.1f" % r, flush=True)
 
 
+@pytest.mark.timeout(300)
+def test_peak_of_the_64_head_causal_layer_is_linear_in_L():
+    # the 64-query/64-KV-head layer at head dim 256 (the shape of the large-head
+    # causal workload) over L = 2K .. 16K: every call fills the chip without a
+    # key split, so the peak is inputs + output, 4 x L x 64 x 256 x 2 bytes
+    for L in (2048, 4096, 8192, 16384):
+        note(f"peak memory 64 heads L{L}")
+        q, k, v = _alloc(1, 64, 64, L, L, 256, torch.bfloat16)
+        inputs = sum(t.numel() * t.element_size() for t in (q, k, v))
+        assert fa.sdpa_workspace_bytes(1, 64, 64, L, L, 256) == 0
+        peak, out = _peak_of_call(q, k, v, causal=True)
+        outb = out.numel() * out.element_size()
+        print(f"64 heads L {L}: inputs {inputs / MiB:.0f} MiB, peak {peak / MiB:.0f} MiB", flush=True)
+        assert 0 <= peak - inputs - outb <= 4 * MiB, (L, peak, inputs, outb)
+        assert peak <= 4 * L * 64 * 256 * 2 + 4 * MiB
+        del q, k, v, out
+
+
 def test_library_allocates_no_device_memory():
     q, k, v = _alloc(1, 16, 8, 4, 131072, 256, torch.bfloat16)
     out = torch.empty_like(q)

@@ -87,6 +87,44 @@ def test_every_tile_count_of_the_step_loop(D, ntile):
         check_close(got, ref, dtype, f"step loop D{D} tiles {ntile} causal {causal}")
 
 
+# Sliding-window prefill at head dim 256 runs a persistent kernel when the row
+# blocks outnumber the workgroups that fill the chip once: S = ceil(256 / (B *
+# Hkv)) workgroups per KV head, workgroup w running row blocks w, w + S, ...
+# (128 packed rows each) in one pipeline.  These shapes all take it, with
+# ragged last blocks, several blocks per workgroup and a query offset.
+PERSISTENT = [
+    (2, 64, 32, 1000, 1000, 256, BF16, True, 200, 0),     # 4 blocks per workgroup, ragged last block
+    (1, 32, 16, 4096, 4096, 256, FP16, True, 1024, 0),    # the sliding layer's heads at L 4096
+    (1, 64, 32, 1500, 4000, 256, FP16, True, 333, 2500),  # a chunk over a prefix, 3 blocks per workgroup
+    (1, 64, 64, 700, 700, 256, BF16, True, 64, 0),        # window of one tile
+]
+
+
+def _persistent(B, Hq, Hkv, qL, window, D):
+    S = -(-256 // (B * Hkv))
+    return window > 0 and D == 256 and S < -(-(Hq // Hkv) * qL // 128)
+
+
+@pytest.mark.parametrize("case", PERSISTENT, ids=[f"B{c[0]}Hq{c[1]}Hkv{c[2]}q{c[3]}k{c[4]}w{c[8]}" for c in PERSISTENT])
+def test_persistent_sliding_window_every_row(case):
+    B, Hq, Hkv, qL, kL, D, dtype, causal, window, q_offset = case
+    assert _persistent(B, Hq, Hkv, qL, window, D)
+    q, k, v = W.random_qkv(1200 + qL + kL, B, Hq, Hkv, qL, kL, D, dtype)
+    scale = float(np.float32(1.0 / np.sqrt(D)))
+    note(f"persistent {case}")
+    got = f64(run_gpu(q, k, v, causal=causal, window=window, q_offset=q_offset))
+    ref = oracle_full(q, k, v, scale=scale, causal=causal, window=window, q_offset=q_offset, dtype=dtype)
+    check_close(got, ref, dtype, f"persistent {case}")
+
+
+def test_persistent_unit_window_returns_the_diagonal_value_rows_exactly():
+    q, k, v = W.random_qkv(1299, 1, 64, 64, 600, 600, 256, BF16)
+    assert _persistent(1, 64, 64, 600, 1, 256)
+    note("persistent window 1")
+    got = run_gpu(q, k, v, causal=True, window=1, q_offset=0)
+    assert torch.equal(got.view(torch.int16), v.view(torch.int16))
+
+
 @pytest.mark.parametrize("case", SMALL, ids=[f"B{c[0]}Hq{c[1]}Hkv{c[2]}q{c[3]}k{c[4]}D{c[5]}"
                                              f"{'bf16' if c[6] else 'f16'}c{int(c[7])}w{c[8]}"
                                              for c in SMALL])
