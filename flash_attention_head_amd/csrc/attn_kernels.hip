@@ -304,8 +304,15 @@ __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* ld
   const int od0 = h * DO;                    // first output column this wave owns
 
   const int nheads = p.B * p.Hkv;
-  const int head = blockIdx.x % nheads;
-  const int mbr = blockIdx.x / nheads;
+  // Workgroups are handed to the 8 XCDs round-robin by their linear index,
+  // and each XCD has its own L2.  With p.xcd_heads the index maps so that an
+  // XCD runs its heads one after another (all its workgroups on one head,
+  // heaviest row blocks first), so each K/V tile fetched into its L2 serves
+  // every workgroup of the head there; otherwise consecutive indices take
+  // consecutive heads.
+  const int xcd = blockIdx.x % 8, slot = blockIdx.x / 8;
+  const int head = p.xcd_heads ? xcd + 8 * (slot / p.mblocks) : (int)(blockIdx.x % nheads);
+  const int mbr = p.xcd_heads ? slot % p.mblocks : (int)(blockIdx.x / nheads);
   // PERS: workgroup w of a head runs row blocks w, w + S, w + 2 S, ... (S =
   // p.pers_stride workgroups per head), so that the workgroups that run at
   // the same time on an XCD work on neighbouring blocks and share K/V tiles

@@ -240,12 +240,16 @@ int forward_impl(const void* q, const void* k, const void* v, const void* bias, 
   // sliding-window prefill at head dim 256: a workgroup runs several row
   // blocks of its (batch, KV head) in one pipeline, S workgroups per head
   // (enough to fill the CUs once), workgroup w taking blocks w, w + S, ...
+  // more than 8 heads (a multiple of 8) and no key split: each XCD takes
+  // whole heads, one at a time (see the kernels' index mapping)
+  p.xcd_heads = ((int64_t)B * Hkv > 8 && ((int64_t)B * Hkv) % 8 == 0 && sp.nsplit == 1) ? 1 : 0;
   p.pers_stride = 0;
   if (!q4 && !bias && !ring && D == 256 && Dv == 256 && window > 0 && !sp.partials) {
     const int64_t heads = (int64_t)B * Hkv;
     const int64_t S = ceil_div(kPlannedCUs, heads);
     if (S < p.mblocks) p.pers_stride = (int)S;
   }
+  if (p.pers_stride > 0) p.xcd_heads = 0;  // the persistent grid maps its own way
 
   hipStream_t s = (hipStream_t)stream;
   hipError_t e = q4 ? launch_attention_q4(p, dtype, s) : launch_attention(p, D, Dv, dtype, ring, s);

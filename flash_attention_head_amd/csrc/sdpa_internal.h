@@ -67,6 +67,8 @@ struct AttnParams {
   int partials;       // 1: write partials for the combine pass
   int pers_stride;    // > 0: S workgroups per (b, kv head), workgroup w running row
                       // blocks w, w + S, ... in one pipeline (head dim 256 only)
+  int xcd_heads;      // 1: workgroup index -> (head, row block) so that each XCD runs
+                      // whole heads one at a time (B * Hkv a multiple of 8, one split)
 };
 
 // Split plan for a shape: how many key splits, how long each, and whether

@@ -117,6 +117,28 @@ def test_persistent_sliding_window_every_row(case):
     check_close(got, ref, dtype, f"persistent {case}")
 
 
+# More than 8 KV heads (a multiple of 8) without a key split: the workgroup
+# index maps so that each of the 8 XCDs runs whole heads one at a time.
+XCD_HEADS = [
+    (2, 16, 8, 300, 300, 256, BF16, True, 0, 0),        # 16 heads, 3 ragged row blocks each
+    (1, 48, 24, 200, 700, 128, FP16, True, 0, 500),     # 24 heads, head dim 128, a chunk over a prefix
+    (1, 16, 16, 150, 150, 512, BF16, False, 0, 0),      # head dim 512, unmasked
+    (3, 8, 8, 260, 260, 64, FP16, True, 40, 0),          # 24 heads, head dim 64, window
+]
+
+
+@pytest.mark.parametrize("case", XCD_HEADS, ids=[f"B{c[0]}Hq{c[1]}Hkv{c[2]}q{c[3]}D{c[5]}" for c in XCD_HEADS])
+def test_heads_run_whole_per_xcd_every_row(case):
+    B, Hq, Hkv, qL, kL, D, dtype, causal, window, q_offset = case
+    assert B * Hkv > 8 and (B * Hkv) % 8 == 0 and fa.sdpa_workspace_bytes(B, Hq, Hkv, qL, kL, D) == 0
+    q, k, v = W.random_qkv(1400 + qL + D, B, Hq, Hkv, qL, kL, D, dtype)
+    scale = float(np.float32(1.0 / np.sqrt(D)))
+    note(f"xcd heads {case}")
+    got = f64(run_gpu(q, k, v, causal=causal, window=window, q_offset=q_offset))
+    ref = oracle_full(q, k, v, scale=scale, causal=causal, window=window, q_offset=q_offset, dtype=dtype)
+    check_close(got, ref, dtype, f"xcd heads {case}")
+
+
 def test_persistent_unit_window_returns_the_diagonal_value_rows_exactly():
     q, k, v = W.random_qkv(1299, 1, 64, 64, 600, 600, 256, BF16)
     assert _persistent(1, 64, 64, 600, 1, 256)
