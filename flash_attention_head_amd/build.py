@@ -14,7 +14,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 LIB = os.path.join(PKG, "libsdpa_mi355x.so")
 SOURCES = [os.path.join(PKG, "csrc", "attn_kernels.hip"), os.path.join(PKG, "csrc", "sdpa_api.cpp"),
-           os.path.join(PKG, "csrc", "sdpa_noalloc.hip")]
+           os.path.join(PKG, "csrc", "sdpa_noalloc.hip"), os.path.join(PKG, "csrc", "attn_q4_decode.hip")]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

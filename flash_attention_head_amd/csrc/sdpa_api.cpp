@@ -252,7 +252,9 @@ int forward_impl(const void* q, const void* k, const void* v, const void* bias, 
   if (p.pers_stride > 0) p.xcd_heads = 0;  // the persistent grid maps its own way
 
   hipStream_t s = (hipStream_t)stream;
-  hipError_t e = q4 ? launch_attention_q4(p, dtype, s) : launch_attention(p, D, Dv, dtype, ring, s);
+  hipError_t e = !q4                        ? launch_attention(p, D, Dv, dtype, ring, s)
+                 : qL <= kDecodeMaxRows      ? launch_attention_q4_decode(p, dtype, s)
+                                             : launch_attention_q4(p, dtype, s);
   if (e == hipSuccess && sp.partials) e = launch_combine(p, Dv, dtype, s);
   if (e != hipSuccess) return fail(SDPA_HIP_ERROR, "kernel launch failed: %s", hipGetErrorString(e));
   return SDPA_OK;

@@ -88,6 +88,9 @@ SplitPlan plan_split(int B, int Hq, int Hkv, int qL, int kL, int D, int kv_capac
 hipError_t launch_attention(const AttnParams& p, int D, int Dv, int dtype, bool ring, hipStream_t stream);
 // The 4-bit K/V instance (D = Dv = 256, no ring, no bias; p.kq4 ... set)
 hipError_t launch_attention_q4(const AttnParams& p, int dtype, hipStream_t stream);
+// The 4-bit decode/verify kernel (qL <= kDecodeMaxRows, D = Dv = 256, key
+// splits with partials; p.kq4 ... set)
+hipError_t launch_attention_q4_decode(const AttnParams& p, int dtype, hipStream_t stream);
 hipError_t launch_combine(const AttnParams& p, int Dv, int dtype, hipStream_t stream);
 
 // The calling thread's message for the last failed call: fail() formats it

@@ -17,18 +17,26 @@ import pytest
 from flash_attention_head_amd import build as B
 
 KERNELS = ("attn_tile_kernel_d256_pers", "attn_tile_kernel_d64", "attn_tile_kernel_d80", "attn_tile_kernel_d128", "attn_tile_kernel_d192", "attn_tile_kernel_dk192_dv256", "attn_tile_kernel_d256",
-           "attn_tile_kernel_d512", "attn_tile_kernel_d256_q4",
+           "attn_tile_kernel_d512", "attn_tile_kernel_d256_q4", "attn_q4_decode_kernel",
            "combine_kernel", "combine_few_kernel")
+
+# the sources that hold kernels
+KERNEL_SOURCES = [s for s in B.SOURCES if os.path.basename(s) in ("attn_kernels.hip", "attn_q4_decode.hip")]
 
 
 @pytest.fixture(scope="module")
 def asm(tmp_path_factory):
-    out = str(tmp_path_factory.mktemp("asm") / "attn_kernels.s")
+    assert len(KERNEL_SOURCES) == 2, B.SOURCES
+    d = tmp_path_factory.mktemp("asm")
     flags = [f for f in B.FLAGS if f not in ("-shared", "-fPIC", "-fvisibility=hidden")]
-    cmd = [B.HIPCC, *flags, "--cuda-device-only", "-S", B.SOURCES[0], "-o", out]
-    r = subprocess.run(cmd, capture_output=True, text=True)
-    assert r.returncode == 0, r.stderr[-2000:]
-    return open(out).read()
+    text = []
+    for src in KERNEL_SOURCES:
+        out = str(d / (os.path.basename(src) + ".s"))
+        r = subprocess.run([B.HIPCC, *flags, "--cuda-device-only", "-S", src, "-o", out], capture_output=True,
+                           text=True)
+        assert r.returncode == 0, r.stderr[-2000:]
+        text.append(open(out).read())
+    return "\n".join(text)
 
 
 def _functions(text):
@@ -87,7 +95,7 @@ def test_no_scratch_memory(asm):
     vector-register lanes, and the instance named above vector registers in
     accumulation registers: neither is memory traffic."""
     meta = _metadata(asm)
-    assert len(meta) >= 24, sorted(meta)
+    assert len(meta) >= 26, sorted(meta)
     for name, f in meta.items():
         assert int(f["private_segment_fixed_size"]) == 0, (name, f)
         if not any(k in name for k in SPILL_TO_REGISTERS_ONLY):
