@@ -9,13 +9,14 @@
 //
 // A workgroup takes one (batch, KV head, key chunk) and up to 16 packed
 // query rows (row r: query position r / G of query head hk G + r % G).  The
-// chunk's keys go in 32-key sub-tiles to the four waves in turn, and each
-// wave runs its own online softmax over its sub-tiles with 16x16x32 MFMAs:
+// chunk's keys go in 32-key sub-tiles to the eight waves (two per SIMD) in
+// turn, and each wave runs its own online softmax over its sub-tiles with
+// 16x16x32 MFMAs:
 //   S^T = K Q^T   A = the key codes, turned into fp16 operands in registers
 //                 straight from the loaded words; B = Q, held in registers
 //   O^T += V^T P^T  A = V^T, staged through the wave's own LDS buffer and read
 //                 back transposed; B = the weights, straight from S's registers
-// The waves never wait for each other until the end, where their four
+// The waves never wait for each other until the end, where their eight
 // (max, sum, output) states are merged in wave order into the chunk's
 // partial for the combine pass.  Nothing a row computes depends on the other
 // rows of the call, so a verify row gets the same bits as the single-row
@@ -47,10 +48,13 @@ typedef short short4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) short4_t lds_short4_t;
 
 constexpr int kD = 256;                  // head dim
-constexpr int kNW = 4;                   // waves per workgroup
+constexpr int kNW = 8;                   // waves per workgroup (two per SIMD)
+constexpr int kThreads = 64 * kNW;
 constexpr int kSub = 32;                 // keys per sub-tile
 constexpr int kVBuf = kSub * kD;         // one staged V sub-tile, fp16 elements
-constexpr int kOStride = kD + 4;         // merge area row stride, floats
+constexpr int kVBufs = kNW == 4 ? 2 : 1;  // staged V buffers per wave (LDS: 128 KiB in all)
+constexpr int kOStride = kVBufs == 2 ? kD + 4 : kD;  // merge area row stride, floats (fits the wave's LDS)
+constexpr int kMergeWords = 512 / kThreads;          // code words' columns per thread in the merge
 constexpr float kRescaleLog2 = 8.f;      // lazy reference max, as in the 16-bit kernels
 constexpr uint32_t kMagic = 0x64006400u;  // 1024.0 in both fp16 halves
 
@@ -157,11 +161,11 @@ struct Loads {
 };
 
 template <int DT>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kNW / 4, kNW / 4)))
 void attn_q4_decode_kernel(AttnParams p) {
-  // per wave two staged V sub-tiles (2 x 16 KiB; at the end its merge area),
-  // then the waves' (max, sum) per row
-  __shared__ __attribute__((aligned(16))) uint16_t lds[kNW * 2 * kVBuf];
+  // per wave its staged V sub-tile(s) (16 KiB each; at the end its merge
+  // area), then the waves' (max, sum) per row
+  __shared__ __attribute__((aligned(16))) uint16_t lds[kNW * kVBufs * kVBuf];
   __shared__ float ml_lds[kNW][16][2];
 
   const int tid = threadIdx.x;
@@ -285,10 +289,10 @@ void attn_q4_decode_kernel(AttnParams p) {
   };
 
   // staged V: key row k of the sub-tile (16 blk + r) at k * 256; code word W's
-  // 8 values in chunk W ^ 2 (k & 7) (16-byte chunks), in the operand entry
-  // order.  The XOR spreads both the writes and the transposed reads of four
-  // consecutive rows over the banks.
-  uint16_t* const vbuf = lds + wave * 2 * kVBuf;
+  // 8 values in chunk W ^ (k & 15) (16-byte chunks), in the operand entry
+  // order.  The XOR spreads the writes (16 rows, 4 words) and the transposed
+  // reads (16 rows, 2 chunks) over all 16 four-bank groups.
+  uint16_t* const vbuf = lds + wave * kVBufs * kVBuf;
   const int g_a = lq >> 1, g_b = 2 + (lq >> 1);  // the groups of this lane's two runs of words
   auto stage_v = [&](const Loads& ld, uint16_t* vs) {
 #pragma unroll
@@ -312,7 +316,7 @@ void attn_q4_decode_kernel(AttnParams p) {
         const uint4 wv = ld.vw[blk][run];
         const uint32_t w = (s & 3) == 0 ? wv.x : (s & 3) == 1 ? wv.y : (s & 3) == 2 ? wv.z : wv.w;
         const int word = run == 0 ? 4 * lq + (s & 3) : 16 + 4 * lq + (s & 3);
-        *(uint4*)(rowp + 8 * (word ^ (2 * (k & 7)))) = value_row(w, s2[run], b2[run], b16[run], magic);
+        *(uint4*)(rowp + 8 * (word ^ (k & 15))) = value_row(w, s2[run], b2[run], b16[run], magic);
       }
     }
   };
@@ -320,9 +324,9 @@ void attn_q4_decode_kernel(AttnParams p) {
   // lane group q, key rows 4 q .. 4 q + 3 and 16 + 4 q .. 16 + 4 q + 3, the
   // key order of the weights this lane holds
   const int tr_a = r16 & 3, tr_t = r16 >> 2;
-  const int tr_row = 4 * lq + tr_t;  // + 16 for the second read (same row & 7)
+  const int tr_row = 4 * lq + tr_t;  // + 16 for the second read (same row & 15)
   auto v_operand = [&](const uint16_t* vs, int db) {
-    const int chunk = (2 * db + (tr_a >> 1)) ^ (2 * (tr_row & 7));
+    const int chunk = (2 * db + (tr_a >> 1)) ^ (tr_row & 15);
     const uint16_t* a = vs + tr_row * kD + 8 * chunk + 4 * (tr_a & 1);
     const uint2 x = read_tr(a), y = read_tr(a + 16 * kD);
     return make_uint4(x.x, x.y, y.x, y.y);
@@ -374,12 +378,14 @@ void attn_q4_decode_kernel(AttnParams p) {
       }
     }
     stage_v(ld, vs);
-    // the V^T operands of all 16 output blocks, read now so that their
-    // latency is hidden by the softmax (the same wave wrote them: LDS
-    // operations of a wave complete in order)
-    uint4 va[16];
+    // the V^T operands of the first kVA output blocks, read now so that
+    // their latency is hidden by the softmax (the same wave wrote them: LDS
+    // operations of a wave complete in order); each later one is read kVA
+    // MFMAs ahead
+    constexpr int kVA = 4;
+    uint4 va[kVA];
 #pragma unroll
-    for (int db = 0; db < 16; ++db) va[db] = v_operand(vs, db);
+    for (int db = 0; db < kVA; ++db) va[db] = v_operand(vs, db);
 
     // mask (only sub-tiles some row cannot wholly see)
     const int k0 = t * kSub;
@@ -420,7 +426,11 @@ void attn_q4_decode_kernel(AttnParams p) {
     // O^T += V^T P^T: B entries 8 q + j are keys 4 q + j (j < 4) and 16 + 4
     // q + j - 4, the keys of the staged rows v_operand reads
 #pragma unroll
-    for (int db = 0; db < 16; ++db) o[db] = mfma16(va[db], pw, o[db]);
+    for (int db = 0; db < 16; ++db) {
+      const uint4 cur = va[db % kVA];
+      if (db + kVA < 16) va[db % kVA] = v_operand(vs, db + kVA);
+      o[db] = mfma16(cur, pw, o[db]);
+    }
   };
 
   // ---- the wave's sub-tiles, loads one ahead (no branch around a load) ----
@@ -431,12 +441,12 @@ void attn_q4_decode_kernel(AttnParams p) {
       issue(lb, sub_t(i + 1));
       compute(la, tw0 + kNW * i, vbuf);
       issue(la, sub_t(i + 2));
-      if (i + 1 < nsub) compute(lb, tw0 + kNW * (i + 1), vbuf + kVBuf);
+      if (i + 1 < nsub) compute(lb, tw0 + kNW * (i + 1), vbuf + (kVBufs - 1) * kVBuf);
     }
   }
   __builtin_amdgcn_s_waitcnt(0);
 
-  // ---- merge the four waves' states in wave order -------------------------
+  // ---- merge the waves' states in wave order ------------------------------
   const float lsum = sum32(sum16(l_run));  // the row's four lanes, same bits in each
   float* const om = (float*)vbuf;          // this wave's own LDS: rows of kOStride floats
 #pragma unroll
@@ -447,9 +457,9 @@ void attn_q4_decode_kernel(AttnParams p) {
   }
   __syncthreads();
 
-  // thread t: row t / 16, code words 2 (t % 16) and 2 (t % 16) + 1 (output
-  // columns 16 (t % 16) .. + 15)
-  const int mr = tid >> 4, mw = 2 * (tid & 15);
+  // thread t: row t / (32 / kMergeWords), kMergeWords code words' output
+  // columns from word kMergeWords (t % (32 / kMergeWords)) on
+  const int mr = tid / (32 / kMergeWords), mw = kMergeWords * (tid % (32 / kMergeWords));
   const int mrow = row0 + mr;
   if (mrow >= rend) return;
   float mw_[kNW], f[kNW];
@@ -469,12 +479,12 @@ void attn_q4_decode_kernel(AttnParams p) {
   const size_t prow = ((size_t)(b * p.Hq + mhq) * p.qL + mqi) * p.nsplit + split;
   float* const dst = p.part_o + prow * kD;
 #pragma unroll
-  for (int c = 0; c < 2; ++c) {
+  for (int c = 0; c < kMergeWords; ++c) {
     const int word = mw + c;
     float acc[8];
 #pragma unroll
     for (int w = 0; w < kNW; ++w) {
-      const float* ow = (const float*)(lds + w * 2 * kVBuf) + mr * kOStride + 8 * word;
+      const float* ow = (const float*)(lds + w * kVBufs * kVBuf) + mr * kOStride + 8 * word;
       const float4 x = *(const float4*)ow, y = *(const float4*)(ow + 4);
       const float e[8] = {x.x, x.y, x.z, x.w, y.x, y.y, y.z, y.w};
 #pragma unroll
@@ -488,7 +498,7 @@ void attn_q4_decode_kernel(AttnParams p) {
     *(float4*)(dst + 8 * word) = make_float4(out[0], out[1], out[2], out[3]);
     *(float4*)(dst + 8 * word + 4) = make_float4(out[4], out[5], out[6], out[7]);
   }
-  if ((tid & 15) == 0) {
+  if (tid % (32 / kMergeWords) == 0) {
     p.part_ml[prow * 2 + 0] = (mmax == -INFINITY) ? -INFINITY : mmax * sl2;
     p.part_ml[prow * 2 + 1] = lt;
   }
@@ -499,8 +509,8 @@ void attn_q4_decode_kernel(AttnParams p) {
 hipError_t launch_attention_q4_decode(const AttnParams& p, int dtype, hipStream_t stream) {
   const int passes = (p.rows + 15) / 16;
   const dim3 grid((unsigned)(p.B * p.Hkv * passes), (unsigned)p.nsplit, 1);
-  if (dtype == 0) hipLaunchKernelGGL((attn_q4_decode_kernel<0>), grid, dim3(256), 0, stream, p);
-  else hipLaunchKernelGGL((attn_q4_decode_kernel<1>), grid, dim3(256), 0, stream, p);
+  if (dtype == 0) hipLaunchKernelGGL((attn_q4_decode_kernel<0>), grid, dim3(kThreads), 0, stream, p);
+  else hipLaunchKernelGGL((attn_q4_decode_kernel<1>), grid, dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }
 
