@@ -170,8 +170,9 @@ def measured_traffic(wl_name):
             k, _, v = line.partition(":")
             fields[k.strip()] = v.strip()
     h = hashlib.sha256()
-    for f in ("attn_kernels.hip", "sdpa_api.cpp", "sdpa_internal.h"):
-        with open(os.path.join(ROOT, "flash_attention_head_amd", "csrc", f), "rb") as fh:
+    csrc = os.path.join(ROOT, "flash_attention_head_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):  # every kernel and host source
+        with open(os.path.join(csrc, f), "rb") as fh:
             h.update(fh.read())
     if fields.get("kernel_source_sha256") != h.hexdigest():
         return None
