@@ -1571,6 +1571,25 @@ __global__ __launch_bounds__(64 * kCombineWaves) void combine_kernel(AttnParams 
   const int key_lo = p.window > 0 ? max(0, pos - p.window + 1) : 0;
   const int c_lo = key_lo / p.split_len, c_hi = key_hi / p.split_len;
   const float* ml = p.part_ml + row * p.nsplit * 2;
+  const float* po = p.part_o + row * (size_t)p.nsplit * D + lane * PER;
+
+  // this wave's first kPre chunks (c_lo + wave + k nw) are loaded now, so that
+  // their loads fly with the max pass's instead of after it
+  constexpr int kPre = 4;
+  float4 pre[kPre][PER / 4];
+  float2 pml[kPre];
+#pragma unroll
+  for (int k = 0; k < kPre; ++k) {
+    const int c = c_lo + wave + k * nw;
+    pml[k] = make_float2(-INFINITY, 0.f);
+    if (c <= c_hi) {
+      pml[k] = *(const float2*)(ml + 2 * c);
+      if (cols) {
+#pragma unroll
+        for (int e = 0; e < PER / 4; ++e) pre[k][e] = *(const float4*)(po + (size_t)c * D + 4 * e);
+      }
+    }
+  }
 
   // the row's largest reference max (max is exact in any order)
   float m = -INFINITY;
@@ -1587,21 +1606,30 @@ __global__ __launch_bounds__(64 * kCombineWaves) void combine_kernel(AttnParams 
   for (int e = 0; e < PER; ++e) acc[e] = 0.f;
   float L = 0.f;
   if (M != -INFINITY) {
-    const float* po = p.part_o + row * (size_t)p.nsplit * D + lane * PER;
-    for (int c = c_lo + wave; c <= c_hi; c += nw) {
-      const float mc = ml[2 * c];
-      const float w = (mc == -INFINITY) ? 0.f : fast_exp2(mc - M);
-      L += ml[2 * c + 1] * w;
-      const float* src = po + (size_t)c * D;
-      if (!cols) continue;
+    // the same chunks in the same order; the first kPre from the registers
+    // loaded above
+    auto add = [&](float2 mlc, const float4 (&x)[PER / 4]) {
+      const float w = (mlc.x == -INFINITY) ? 0.f : fast_exp2(mlc.x - M);
+      L += mlc.y * w;
+      if (!cols) return;
 #pragma unroll
-      for (int e = 0; e < PER; e += 4) {
-        const float4 x = *(const float4*)(src + e);
-        acc[e + 0] += x.x * w;
-        acc[e + 1] += x.y * w;
-        acc[e + 2] += x.z * w;
-        acc[e + 3] += x.w * w;
+      for (int e = 0; e < PER / 4; ++e) {
+        acc[4 * e + 0] += x[e].x * w;
+        acc[4 * e + 1] += x[e].y * w;
+        acc[4 * e + 2] += x[e].z * w;
+        acc[4 * e + 3] += x[e].w * w;
       }
+    };
+#pragma unroll
+    for (int k = 0; k < kPre; ++k)
+      if (c_lo + wave + k * nw <= c_hi) add(pml[k], pre[k]);
+    for (int c = c_lo + wave + kPre * nw; c <= c_hi; c += nw) {
+      float4 x[PER / 4];
+      if (cols) {
+#pragma unroll
+        for (int e = 0; e < PER / 4; ++e) x[e] = *(const float4*)(po + (size_t)c * D + 4 * e);
+      }
+      add(*(const float2*)(ml + 2 * c), x);
     }
   }
   if (cols) {
