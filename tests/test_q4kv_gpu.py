@@ -63,6 +63,24 @@ def test_every_row_against_the_oracle(case):
     check_close(got, ref, dtype, f"q4kv {case}")
 
 
+# the decode kernel's edges: a single key, fewer keys than one sub-tile (most
+# waves get no sub-tile), packed rows that are not a multiple of the 16 a
+# workgroup holds (G = 3: 12 rows; G = 5: 20 rows in two row passes, the
+# second ragged), a window inside the first sub-tile
+EDGES = [(1, 2, 1, 1, 1, FP16, 0), (1, 4, 2, 4, 5, BF16, 0), (2, 2, 2, 3, 31, FP16, 2),
+         (1, 15, 5, 4, 3000, FP16, 0), (1, 20, 4, 4, 2000, BF16, 100), (1, 20, 4, 3, 33, BF16, 7)]
+
+
+@pytest.mark.parametrize("case", EDGES, ids=[f"B{c[0]}Hq{c[1]}Hkv{c[2]}q{c[3]}k{c[4]}w{c[6]}" for c in EDGES])
+def test_decode_kernel_edges_against_the_oracle(case):
+    B, Hq, Hkv, qL, kL, dtype, window = case
+    ins = _inputs(9400 + kL + qL + Hq, B, Hq, Hkv, qL, kL, dtype)
+    note(f"q4kv edge {case}")
+    got = f64(_gpu(ins, causal=True, window=window))
+    ref = _oracle(ins, dtype, scale=float(np.float32(1 / 16)), causal=True, window=window, q_offset=kL - qL)
+    check_close(got, ref, dtype, f"q4kv edge {case}")
+
+
 # chunked prefill over a 4-bit prefix: every wave holds rows and loads its
 # share; the last case splits its keys and merges the partials
 PREFILL = [(1, 4, 2, 100, 1000, BF16, 0), (1, 4, 2, 70, 1500, FP16, 300), (2, 2, 2, 33, 200, BF16, 0),
