@@ -97,6 +97,8 @@ PERSISTENT = [
     (1, 32, 16, 4096, 4096, 256, FP16, True, 1024, 0),    # the sliding layer's heads at L 4096
     (1, 64, 32, 1500, 4000, 256, FP16, True, 333, 2500),  # a chunk over a prefix, 3 blocks per workgroup
     (1, 64, 64, 700, 700, 256, BF16, True, 64, 0),        # window of one tile
+    (1, 64, 32, 2100, 2100, 256, BF16, True, 700, 0),     # 32 heads, 8 workgroups each, ragged last block
+    (2, 16, 8, 2500, 2600, 256, FP16, True, 900, 100),    # two batches of 8 heads, a query offset
 ]
 
 
