@@ -252,7 +252,8 @@ void attn_q4_decode_kernel(AttnParams p) {
     qc = lq == 0 ? h4 : lq == 1 ? make_uint4(h4.x, h4.y, 0u, 0u) : make_uint4(0, 0, 0, 0);
   }
 
-  // ---- the wave's sub-tiles of this chunk: T = T0 + wave + 4 i ------------
+  // ---- the wave's sub-tiles of this chunk: every kNW-th from the first -----
+  // (sub-tile T to wave T mod kNW; chunks start at multiples of kNW sub-tiles)
   const int t_first = kbeg / kSub, t_last = (kend - 1) / kSub;
   const int tw0 = t_first + ((wave - t_first) % kNW + kNW) % kNW;
   const int nsub = tw0 <= t_last ? (t_last - tw0) / kNW + 1 : 0;
@@ -459,19 +460,19 @@ void attn_q4_decode_kernel(AttnParams p) {
 
   // thread t: row t / (32 / kMergeWords), kMergeWords code words' output
   // columns from word kMergeWords (t % (32 / kMergeWords)) on
-  const int mr = tid / (32 / kMergeWords), mw = kMergeWords * (tid % (32 / kMergeWords));
+  const int mr = tid / (32 / kMergeWords), word0 = kMergeWords * (tid % (32 / kMergeWords));
   const int mrow = row0 + mr;
   if (mrow >= rend) return;
-  float mw_[kNW], f[kNW];
+  float m_w[kNW], f[kNW];  // each wave's reference max, and its factor
   float mmax = -INFINITY;
 #pragma unroll
   for (int w = 0; w < kNW; ++w) {
-    mw_[w] = ml_lds[w][mr][0];
-    mmax = fmaxf(mmax, mw_[w]);
+    m_w[w] = ml_lds[w][mr][0];
+    mmax = fmaxf(mmax, m_w[w]);
   }
 #pragma unroll
   for (int w = 0; w < kNW; ++w)
-    f[w] = (mw_[w] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((mw_[w] - mmax) * sl2);
+    f[w] = (m_w[w] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((m_w[w] - mmax) * sl2);
   float lt = f[0] * ml_lds[0][mr][1];
 #pragma unroll
   for (int w = 1; w < kNW; ++w) lt = fmaf(f[w], ml_lds[w][mr][1], lt);
@@ -480,7 +481,7 @@ void attn_q4_decode_kernel(AttnParams p) {
   float* const dst = p.part_o + prow * kD;
 #pragma unroll
   for (int c = 0; c < kMergeWords; ++c) {
-    const int word = mw + c;
+    const int word = word0 + c;
     float acc[8];
 #pragma unroll
     for (int w = 0; w < kNW; ++w) {
