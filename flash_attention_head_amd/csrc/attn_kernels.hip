@@ -359,8 +359,8 @@ __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* ld
   int kbeg, kend;
   block_keys(mb, kbeg, kend);
   if (kbeg >= kend) return;
-  const int t_first = __builtin_amdgcn_readfirstlane(kbeg / BN);
-  const int t_last = __builtin_amdgcn_readfirstlane((kend - 1) / BN);
+  int t_first = __builtin_amdgcn_readfirstlane(kbeg / BN);  // (the persistent loop moves them)
+  int t_last = __builtin_amdgcn_readfirstlane((kend - 1) / BN);
 
   // K/V rows of a head are kv_cap apart; logical key j is physical row
   // (ring_start + j) % kv_cap.  Without a wrap the live keys are one run of
@@ -1074,368 +1074,330 @@ __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* ld
     }
   };
 
-  // ---- persistent loop (PERS) ------------------------------------------
-  // Row blocks w, w + S, ... of this (batch, KV head) run as one sequence of
-  // tiles: each block's tiles in ascending order, then the next block's.  The
-  // software pipeline runs across the block boundaries: the K/V loads of the
-  // next block's first tiles are issued during the current block's last
-  // steps, its Q rows are loaded a whole block ahead into a second register
-  // set, and the step that finishes a block already computes the next
-  // block's first scores.  At a boundary the step switches the rows' context
-  // (Q, visible-key interval, reference max) between its S and P V regions;
-  // after it, the finished block's output is normalised and stored while the
-  // next block runs.  Every wave runs every step: a wave whose rows lie past
-  // the end of a ragged last block computes on zero queries and stores
-  // nothing.
-  if constexpr (PERS) {
-    static_assert(V3 && !RING && !BIAS && !Q4 && !PAIR, "the persistent loop takes the three-V-buffer pipeline");
-    const int S = p.pers_stride;
-    const int nblk = __builtin_amdgcn_readfirstlane((p.mblocks - mbr + S - 1) / S);
-    auto block_mb = [&](int j) { return mbr + j * S; };
-    // a position in the tile sequence: block j, tile t, the block's last tile
-    struct Cur {
-      int j, t, tl;
-    };
-    auto first_of = [&](int j) {
-      int kb0, ke0;
-      block_keys(block_mb(j), kb0, ke0);
-      return Cur{j, __builtin_amdgcn_readfirstlane(kb0 / BN), __builtin_amdgcn_readfirstlane((ke0 - 1) / BN)};
-    };
-    // the next position; past the last tile of the last block it stays there
-    auto adv = [&](const Cur& c) {
-      if (c.t < c.tl) return Cur{c.j, c.t + 1, c.tl};
-      if (c.j + 1 < nblk) return first_of(c.j + 1);
-      return c;
-    };
-    auto is_end = [&](const Cur& c) { return c.j == nblk - 1 && c.t == c.tl; };
-    const Cur c_end = [&]() {  // the very last tile (its loads may be ragged)
-      Cur c = first_of(nblk - 1);
-      return c;
-    }();
-    if ((c_end.tl + 1) * BN > p.kL) {  // rows past kL of a V tile: zeros, never garbage
+  // ---- one row block: prologue and step loop ---------------------------
+  // `prefetched`: the block's Q rows and its first K/V tiles were loaded by
+  // the persistent loop below while the previous block's output was stored.
+  auto run_block = [&](bool prefetched) {
+    // ---- prologue: K(t0), V(t0), K(t0 + 1); S(t0) and its row max ------------
+    // Rows past kL are out of the loads' range.  When this workgroup's last
+    // tile has such rows, the V buffers start as zeros, so that those rows of
+    // a V tile never hold uninitialised LDS (a zero weight times a NaN bit
+    // pattern would still be NaN); K rows past kL need nothing, their scores
+    // are masked to -inf.  (The persistent loop zeroes them once, before its
+    // first block: rows past kL are never loaded, and a later block finds
+    // there what an earlier tile or the zeroing left, finite either way.)
+    if constexpr (Q4) {  // operand entries 12..15 of the 2 x 64 key rows: zero, never written again
+      if (tid < 2 * BN) *(uint2*)(q4_kc + 16 * tid + 12) = make_uint2(0, 0);
+    }
+    if (!PERS && (t_last + 1) * BN > p.kL) {
       uint4* vz = (uint4*)vbuf0;
       for (int i = tid; i < NVB * TILE / 8; i += NW * 64) vz[i] = make_uint4(0, 0, 0, 0);
       __syncthreads();
     }
-    uint4 qn[DC];  // the next block's Q rows, loaded a block ahead
-    if (nblk > 1) load_q(qn, block_mb(1));
-
-    // prologue: K(v0), V(v0), K(v1), V(v1); S(v0) and its row max
-    const Cur c0 = first_of(0), c1 = adv(c0);
-    load_tile(kg, c0.t, kbuf0, false);
-    load_tile(vg, c0.t, vbuf0, true);
-    load_tile(kg, c1.t, kbuf0 + TILE, false);
-    load_tile(vg, c1.t, vbuf0 + TILE, true);
-    __builtin_amdgcn_s_waitcnt(0);
+    // Q4: the pipelined loaders' first register set, K(t0 + 2) and V(t0 + 1)
+    // With every wave loading, two sets of this wave's QB4 blocks: set P
+    // holds K(t+2), V(t+1) when step t (parity P) starts, issued one step
+    // earlier; the step issues the other set for K(t+3), V(t+2)
+    typename std::conditional<Q4, Q4Data, char>::type q4a_k[Q4 ? QB : 1], q4a_v[Q4 ? QB : 1];
+    typename std::conditional<Q4, Q4Data, char>::type q4s_k[2][Q4M == 2 ? QB4 : 1], q4s_v[2][Q4M == 2 ? QB4 : 1];
+    if constexpr (Q4) {
+      if (q4_li >= 0) {  // wave 0 of a pipelined workgroup does not load
+        Q4Data k0[QB], v0[QB], k1[QB], v1[QB];
+        q4_issue(k0, v0, t_first, t_first);
+        q4_issue(k1, v1, min(t_first + 1, t_last), t_first);
+        q4_put(k0, v0, kbuf0, vbuf0);
+        q4_put(k1, v1, kbuf0 + TILE, vbuf0);  // V(t0) again, the same bytes
+        if (q4_pipe) q4_issue(q4a_k, q4a_v, min(t_first + 2, t_last), min(t_first + 1, t_last));
+        else q4_issue(q4s_k[0], q4s_v[0], min(t_first + 2, t_last), min(t_first + 1, t_last));
+      }
+    } else {
+      if (!prefetched) {
+        load_k(t_first);
+        load_b(t_first);
+        load_v(t_first);
+        if (t_first < t_last) {
+          load_k(t_first + 1);
+          load_b(t_first + 1);
+        }
+      }
+      __builtin_amdgcn_s_waitcnt(0);
+      bias_patch(t_first, bbuf0);
+      if (t_first < t_last) bias_patch(t_first + 1, bbuf0 + BTILE);
+    }
     __syncthreads();
-    f32x16_t sA[KB], sB[KB];
-    qk(sA, kbuf0);
-    if (!full_tile(c0.t)) mask(sA, c0.t);
-    float alpha_cur = row_max(sA);
-    __syncthreads();  // every wave is done with K(v0) before K(v2) overwrites it
+    // V3: V(t0 + 1) is first read in step t0 + 1, so it loads now, in flight
+    // through S(t0) and step t0, whose closing wait (everything but that
+    // step's own V loads) and barrier publish it
+    if constexpr (V3)
+      if (t_first < t_last) load_v(t_first + 1);
 
-    // the finished block's output rows (its row context, saved at the switch)
-    auto store_rows = [&](bool ok, int hq_o, int qi_o) {
-      const float lsum = pair_sum(l_run);
-      if (ok) {
-        const float inv = lsum > 0.f ? 1.0f / lsum : 0.f;
-        uint16_t* dst = p.out + ((size_t)(b * p.Hq + hq_o) * p.qL + qi_o) * DV + od0;
+    f32x16_t sA[KB], sB[KB];
+    float alpha_cur = 1.f;
+    if (wave_active) qk(sA, kbuf0);
+    exchange(sA, wave_active);
+    if (wave_active) {
+      if constexpr (BIAS) {
+        uint2 bw0[KB * 4];
 #pragma unroll
-        for (int db = 0; db < DB; ++db)
+        for (int g = 0; g < KB * 4; ++g) bw0[g] = bias_read(bbuf0, g);
 #pragma unroll
-          for (int q4 = 0; q4 < 4; ++q4) {
-            if (db * 32 + 8 * q4 >= DO) continue;
-            const int d = db * 32 + 8 * q4 + 4 * lg;
-            uint2 wv;
-            wv.x = Elem<DT>::pack2(o[db][4 * q4 + 0] * inv, o[db][4 * q4 + 1] * inv);
-            wv.y = Elem<DT>::pack2(o[db][4 * q4 + 2] * inv, o[db][4 * q4 + 3] * inv);
-            *(uint2*)(dst + d) = wv;
-          }
+        for (int e = 0; e < NE; ++e) sA[e / 16][e % 16] += bias_val(bw0, e);
       }
-    };
-    // one step at position c (tile v): as `step` below, with the next tiles
-    // taken from the sequence and the block switch at a boundary
-    auto pstep = [&](const Cur& c, f32x16_t (&sc)[KB], f32x16_t (&sn)[KB], auto parity, auto vbuf) {
+      if (!full_tile(t_first)) mask(sA, t_first);
+      alpha_cur = row_max(sA);
+    }
+    __syncthreads();  // every wave is done with K(t0) before K(t0 + 2) overwrites it
+
+    // One pipelined step: tile t's scores are in sc, tile t + 1's go to sn.
+    // Straight-line for every tile: a tile no row of this wave sees is masked
+    // like any other (its weights are 0), and in the step after the last tile
+    // the scores of the stale buffer are computed but never used (live ==
+    // false).  Loads past the last tile reload the last tile into a buffer no
+    // later step reads.
+    // P = (t - t_first) & 1, a compile-time constant: K(t+1) is in K buffer
+    // 1 - P; K(t+2) goes to K buffer P, loaded in the S region.  The V loads
+    // take one of three schedules (VLATE: in the P V region, so that each
+    // load has a whole region to land in and a tile's loads spread over both
+    // regions):
+    // - two V buffers (head dims up to 128, and bias instances): V(t) is in
+    //   V buffer P, V(t+1) is loaded into V buffer 1 - P in the S region, and
+    //   the barrier at the end of the step publishes it with K(t+2);
+    // - D = 512 (PAIR, VLATE), whose steps already have a barrier between the
+    //   regions, the pair exchange: V(t+1) is loaded into V buffer 1 - P in
+    //   the P V region, and the next step's exchange barrier publishes it;
+    // - three V buffers (V3, VLATE: D 192 and 256 without a bias): V(t) is in
+    //   V buffer VB = (t - t_first) % 3 (the steps come in sixes, so that it
+    //   is a compile-time constant too), and step t loads V(t+2) in its P V
+    //   region into the buffer V(t-1) held; the barrier at the end of step
+    //   t+1 publishes it, with no barrier between the regions.
+    auto step = [&](int t, f32x16_t (&sc)[KB], f32x16_t (&sn)[KB], auto parity, auto vbuf) {
       constexpr int P = decltype(parity)::value, VB = decltype(vbuf)::value;
-      const Cur n1 = adv(c), n2 = adv(n1);
-      const bool has_next = !is_end(c);
-      const bool boundary = has_next && n1.j != c.j;
-      if (boundary) {  // S(v + 1) is the next block's: its Q rows
-#pragma unroll
-        for (int dc = 0; dc < DC; ++dc) qf[dc] = qn[dc];
-      }
+      const bool has_next = t < t_last;
+      const int tk = min(t + 2, t_last), tv = min(t + (V3 ? 2 : 1), t_last);
       uint4 pb[KB * 2];
+      // the first K operands of the S region, then the rescale for tile t (its
+      // factor is known since the last step), so that the interleaved regions
+      // are straight-line code
       const uint16_t* const kl = kbuf0 + (1 - P) * TILE;
       uint4 a[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) a[i] = kread_at(kl, i, kx(i));
       rescale(alpha_cur);
-      uint4 kc[KB + 1];
+      uint4 kc[KB + 1];  // 4-bit K: the group-constant operands, A per key block and B
 #pragma unroll
-      for (int kb = 0; kb <= KB; ++kb) kc[kb] = make_uint4(0, 0, 0, 0);
+      for (int kb = 0; kb <= KB; ++kb) {
+        if constexpr (Q4) kc[kb] = kb < KB ? q4_kc_read(kl, kb) : q4_qsum();
+        else kc[kb] = make_uint4(0, 0, 0, 0);
+      }
       uint2 bw[KB * 4];
-      const TileSrc vsrc = tile_src(vg, n2.t, true);
-      uint16_t* const vdst = vbuf0 + ((VB + 2) % 3) * TILE;
-      const float psum = qk_weights(sn, kl, sc, pb, tile_src(kg, n2.t, false), kbuf0 + P * TILE, vsrc, vdst,
-                                    i32x4_t{}, bbuf0, bbuf0, bw, a, kc);
+      const TileSrc vsrc = tile_src(vg, tv, true);
+      uint16_t* const vdst = vbuf0 + (V3 ? (VB + 2) % 3 : 1 - P) * TILE;
+      // Q4 with every wave loading: issue this wave's blocks of K(t+3) and
+      // V(t+2) now; K(t+2) and V(t+1), issued in the last step, are written to
+      // LDS at the end of this one
+      if constexpr (Q4) {
+        if (!q4_pipe) q4_issue(q4s_k[1 - P], q4s_v[1 - P], min(t + 3, t_last), min(t + 2, t_last));
+      }
+      const float psum = qk_weights(sn, kl, sc, pb, tile_src(kg, tk, false), kbuf0 + P * TILE,
+                                    vsrc, vdst, BIAS ? bias_src(tk) : i32x4_t{}, bbuf0 + P * BTILE,
+                                    bbuf0 + (1 - P) * BTILE, bw, a, kc);
+      exchange(sn, true);  // D = 512: also the V(t) barrier
       l_run = l_run * alpha_cur + psum;
-      bool ok_o = false;
-      int hq_o = 0, qi_o = 0;
-      if (boundary) {  // tile v closed this block: the next one's rows from here on
-        ok_o = valid;
-        hq_o = hq;
-        qi_o = qi;
-        set_rows(block_mb(n1.j));
-        set_keys();
-        m_ref = -INFINITY;
-        if (n1.j + 1 < nblk) load_q(qn, block_mb(n1.j + 1));
+      if (!full_tile(t + 1)) mask(sn, t + 1);
+      alpha_cur = pv_max(pb, vbuf0 + (V3 ? VB : P) * TILE, sn, has_next, bw, vsrc, vdst);
+      if constexpr (Q4) {
+        if (!q4_pipe) q4_put(q4s_k[P], q4s_v[P], kbuf0 + P * TILE, vdst);
       }
-      if (!full_tile(n1.t)) mask(sn, n1.t);
-      alpha_cur = pv_max(pb, vbuf0 + VB * TILE, sn, has_next, bw, vsrc, vdst);
-      wait_vmem<PV_LOADS>();
+      // VLATE: K(t+2) (and its bias) have landed, and with V3 V(t+1) too; the
+      // V loads of this step may be in flight.  Otherwise everything has.
+      if constexpr (VLATE) wait_vmem<PV_LOADS>();
+      else __builtin_amdgcn_s_waitcnt(0);
+      bias_patch(tk, bbuf0 + P * BTILE);
       __syncthreads();
-      if (boundary) {  // O now holds the closed block's rows
-        store_rows(ok_o, hq_o, qi_o);
-#pragma unroll
-        for (int db = 0; db < DB; ++db)
-#pragma unroll
-          for (int jj = 0; jj < 16; ++jj) o[db][jj] = 0.f;
-        l_run = 0.f;
-      }
-      return n1;
     };
+
     using I0 = std::integral_constant<int, 0>;
     using I1 = std::integral_constant<int, 1>;
     using I2 = std::integral_constant<int, 2>;
-    Cur c = c0;
-    for (;;) {
-      bool end = is_end(c);
-      c = pstep(c, sA, sB, I0{}, I0{});
-      if (end) break;
-      end = is_end(c);
-      c = pstep(c, sB, sA, I1{}, I1{});
-      if (end) break;
-      end = is_end(c);
-      c = pstep(c, sA, sB, I0{}, I2{});
-      if (end) break;
-      end = is_end(c);
-      c = pstep(c, sB, sA, I1{}, I0{});
-      if (end) break;
-      end = is_end(c);
-      c = pstep(c, sA, sB, I0{}, I1{});
-      if (end) break;
-      end = is_end(c);
-      c = pstep(c, sB, sA, I1{}, I2{});
-      if (end) break;
+    if (wave_active) {
+      if constexpr (V3) {
+        for (int t = t_first; t <= t_last; t += 6) {
+          step(t, sA, sB, I0{}, I0{});
+          if (t + 1 > t_last) break;
+          step(t + 1, sB, sA, I1{}, I1{});
+          if (t + 2 > t_last) break;
+          step(t + 2, sA, sB, I0{}, I2{});
+          if (t + 3 > t_last) break;
+          step(t + 3, sB, sA, I1{}, I0{});
+          if (t + 4 > t_last) break;
+          step(t + 4, sA, sB, I0{}, I1{});
+          if (t + 5 > t_last) break;
+          step(t + 5, sB, sA, I1{}, I2{});
+        }
+      } else {
+        for (int t = t_first; t <= t_last; t += 2) {
+          step(t, sA, sB, I0{}, I0{});
+          if (t + 1 <= t_last) step(t + 1, sB, sA, I1{}, I0{});
+        }
+      }
+    } else if constexpr (Q4) {  // no rows: this wave only loads (4-bit tiles)
+      if (q4_pipe) {
+        // one step ahead: set a holds K(t+2), V(t+1) when an even step starts
+        // (issued in the prologue or the last step), set b when an odd one does
+        Q4Data q4b_k[QB], q4b_v[QB];
+        // (the scheduling barriers keep each set's loads after the stores of
+        // the other, so that the stores never wait for loads just issued)
+        for (int t = t_first; t <= t_last; t += 2) {
+          q4_put(q4a_k, q4a_v, kbuf0, vbuf0 + TILE);
+          __builtin_amdgcn_sched_barrier(0);
+          q4_issue(q4b_k, q4b_v, min(t + 3, t_last), min(t + 2, t_last));
+          __syncthreads();
+          if (t + 1 > t_last) break;
+          q4_put(q4b_k, q4b_v, kbuf0 + TILE, vbuf0);
+          __builtin_amdgcn_sched_barrier(0);
+          q4_issue(q4a_k, q4a_v, min(t + 4, t_last), min(t + 3, t_last));
+          __syncthreads();
+        }
+      } else {  // every wave loads, one step ahead, as the row-holding waves do
+        for (int t = t_first; t <= t_last; t += 2) {
+          q4_issue(q4s_k[1], q4s_v[1], min(t + 3, t_last), min(t + 2, t_last));
+          q4_put(q4s_k[0], q4s_v[0], kbuf0, vbuf0 + TILE);
+          __syncthreads();
+          if (t + 1 > t_last) break;
+          q4_issue(q4s_k[0], q4s_v[0], min(t + 4, t_last), min(t + 3, t_last));
+          q4_put(q4s_k[1], q4s_v[1], kbuf0 + TILE, vbuf0);
+          __syncthreads();
+        }
+      }
+    } else {  // no rows: this wave only loads its share of every tile and
+              // meets the same barriers
+      for (int t = t_first; t <= t_last; ++t) {
+        if (t + 2 <= t_last) {
+          load_k(t + 2);
+          load_b(t + 2);
+          if constexpr (V3) load_v(t + 2);
+        }
+        if constexpr (!VLATE)
+          if (t < t_last) load_v(t + 1);
+        exchange(sA, false);
+        if constexpr (PAIR)
+          if (t < t_last) load_v(t + 1);
+        __builtin_amdgcn_s_waitcnt(0);
+        if (t + 2 <= t_last) bias_patch(t + 2, bbuf0 + ((t + 2 - t_first) & 1) * BTILE);
+        __syncthreads();
+      }
     }
+    // no direct load may still be writing this workgroup's LDS when it ends
     __builtin_amdgcn_s_waitcnt(0);
-    store_rows(valid, hq, qi);  // the last block
-    return;
-  }
-
-  // ---- prologue: K(t0), V(t0), K(t0 + 1); S(t0) and its row max ------------
-  // Rows past kL are out of the loads' range.  When this workgroup's last
-  // tile has such rows, the V buffers start as zeros, so that those rows of
-  // a V tile never hold uninitialised LDS (a zero weight times a NaN bit
-  // pattern would still be NaN); K rows past kL need nothing, their scores
-  // are masked to -inf.
-  if constexpr (Q4) {  // operand entries 12..15 of the 2 x 64 key rows: zero, never written again
-    if (tid < 2 * BN) *(uint2*)(q4_kc + 16 * tid + 12) = make_uint2(0, 0);
-  }
-  if ((t_last + 1) * BN > p.kL) {
-    uint4* vz = (uint4*)vbuf0;
-    for (int i = tid; i < NVB * TILE / 8; i += NW * 64) vz[i] = make_uint4(0, 0, 0, 0);
-    __syncthreads();
-  }
-  // Q4: the pipelined loaders' first register set, K(t0 + 2) and V(t0 + 1)
-  // With every wave loading, two sets of this wave's QB4 blocks: set P
-  // holds K(t+2), V(t+1) when step t (parity P) starts, issued one step
-  // earlier; the step issues the other set for K(t+3), V(t+2)
-  typename std::conditional<Q4, Q4Data, char>::type q4a_k[Q4 ? QB : 1], q4a_v[Q4 ? QB : 1];
-  typename std::conditional<Q4, Q4Data, char>::type q4s_k[2][Q4M == 2 ? QB4 : 1], q4s_v[2][Q4M == 2 ? QB4 : 1];
-  if constexpr (Q4) {
-    if (q4_li >= 0) {  // wave 0 of a pipelined workgroup does not load
-      Q4Data k0[QB], v0[QB], k1[QB], v1[QB];
-      q4_issue(k0, v0, t_first, t_first);
-      q4_issue(k1, v1, min(t_first + 1, t_last), t_first);
-      q4_put(k0, v0, kbuf0, vbuf0);
-      q4_put(k1, v1, kbuf0 + TILE, vbuf0);  // V(t0) again, the same bytes
-      if (q4_pipe) q4_issue(q4a_k, q4a_v, min(t_first + 2, t_last), min(t_first + 1, t_last));
-      else q4_issue(q4s_k[0], q4s_v[0], min(t_first + 2, t_last), min(t_first + 1, t_last));
-    }
-  } else {
-    load_k(t_first);
-    load_b(t_first);
-    load_v(t_first);
-    if (t_first < t_last) {
-      load_k(t_first + 1);
-      load_b(t_first + 1);
-      if constexpr (V3) load_v(t_first + 1);
-    }
-    __builtin_amdgcn_s_waitcnt(0);
-    bias_patch(t_first, bbuf0);
-    if (t_first < t_last) bias_patch(t_first + 1, bbuf0 + BTILE);
-  }
-  __syncthreads();
-
-  f32x16_t sA[KB], sB[KB];
-  float alpha_cur = 1.f;
-  if (wave_active) qk(sA, kbuf0);
-  exchange(sA, wave_active);
-  if (wave_active) {
-    if constexpr (BIAS) {
-      uint2 bw0[KB * 4];
-#pragma unroll
-      for (int g = 0; g < KB * 4; ++g) bw0[g] = bias_read(bbuf0, g);
-#pragma unroll
-      for (int e = 0; e < NE; ++e) sA[e / 16][e % 16] += bias_val(bw0, e);
-    }
-    if (!full_tile(t_first)) mask(sA, t_first);
-    alpha_cur = row_max(sA);
-  }
-  __syncthreads();  // every wave is done with K(t0) before K(t0 + 2) overwrites it
-
-  // One pipelined step: tile t's scores are in sc, tile t + 1's go to sn.
-  // Straight-line for every tile: a tile no row of this wave sees is masked
-  // like any other (its weights are 0), and in the step after the last tile
-  // the scores of the stale buffer are computed but never used (live ==
-  // false).  Loads past the last tile reload the last tile into a buffer no
-  // later step reads.
-  // P = (t - t_first) & 1, a compile-time constant: K(t+1) is in K buffer
-  // 1 - P; K(t+2) goes to K buffer P, loaded in the S region.  The V loads
-  // take one of three schedules (VLATE: in the P V region, so that each
-  // load has a whole region to land in and a tile's loads spread over both
-  // regions):
-  // - two V buffers (head dims up to 128, and bias instances): V(t) is in
-  //   V buffer P, V(t+1) is loaded into V buffer 1 - P in the S region, and
-  //   the barrier at the end of the step publishes it with K(t+2);
-  // - D = 512 (PAIR, VLATE), whose steps already have a barrier between the
-  //   regions, the pair exchange: V(t+1) is loaded into V buffer 1 - P in
-  //   the P V region, and the next step's exchange barrier publishes it;
-  // - three V buffers (V3, VLATE: D 192 and 256 without a bias): V(t) is in
-  //   V buffer VB = (t - t_first) % 3 (the steps come in sixes, so that it
-  //   is a compile-time constant too), and step t loads V(t+2) in its P V
-  //   region into the buffer V(t-1) held; the barrier at the end of step
-  //   t+1 publishes it, with no barrier between the regions.
-  auto step = [&](int t, f32x16_t (&sc)[KB], f32x16_t (&sn)[KB], auto parity, auto vbuf) {
-    constexpr int P = decltype(parity)::value, VB = decltype(vbuf)::value;
-    const bool has_next = t < t_last;
-    const int tk = min(t + 2, t_last), tv = min(t + (V3 ? 2 : 1), t_last);
-    uint4 pb[KB * 2];
-    // the first K operands of the S region, then the rescale for tile t (its
-    // factor is known since the last step), so that the interleaved regions
-    // are straight-line code
-    const uint16_t* const kl = kbuf0 + (1 - P) * TILE;
-    uint4 a[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) a[i] = kread_at(kl, i, kx(i));
-    rescale(alpha_cur);
-    uint4 kc[KB + 1];  // 4-bit K: the group-constant operands, A per key block and B
-#pragma unroll
-    for (int kb = 0; kb <= KB; ++kb) {
-      if constexpr (Q4) kc[kb] = kb < KB ? q4_kc_read(kl, kb) : q4_qsum();
-      else kc[kb] = make_uint4(0, 0, 0, 0);
-    }
-    uint2 bw[KB * 4];
-    const TileSrc vsrc = tile_src(vg, tv, true);
-    uint16_t* const vdst = vbuf0 + (V3 ? (VB + 2) % 3 : 1 - P) * TILE;
-    // Q4 with every wave loading: issue this wave's blocks of K(t+3) and
-    // V(t+2) now; K(t+2) and V(t+1), issued in the last step, are written to
-    // LDS at the end of this one
-    if constexpr (Q4) {
-      if (!q4_pipe) q4_issue(q4s_k[1 - P], q4s_v[1 - P], min(t + 3, t_last), min(t + 2, t_last));
-    }
-    const float psum = qk_weights(sn, kl, sc, pb, tile_src(kg, tk, false), kbuf0 + P * TILE,
-                                  vsrc, vdst, BIAS ? bias_src(tk) : i32x4_t{}, bbuf0 + P * BTILE,
-                                  bbuf0 + (1 - P) * BTILE, bw, a, kc);
-    exchange(sn, true);  // D = 512: also the V(t) barrier
-    l_run = l_run * alpha_cur + psum;
-    if (!full_tile(t + 1)) mask(sn, t + 1);
-    alpha_cur = pv_max(pb, vbuf0 + (V3 ? VB : P) * TILE, sn, has_next, bw, vsrc, vdst);
-    if constexpr (Q4) {
-      if (!q4_pipe) q4_put(q4s_k[P], q4s_v[P], kbuf0 + P * TILE, vdst);
-    }
-    // VLATE: K(t+2) (and its bias) have landed, and with V3 V(t+1) too; the
-    // V loads of this step may be in flight.  Otherwise everything has.
-    if constexpr (VLATE) wait_vmem<PV_LOADS>();
-    else __builtin_amdgcn_s_waitcnt(0);
-    bias_patch(tk, bbuf0 + P * BTILE);
-    __syncthreads();
   };
 
-  using I0 = std::integral_constant<int, 0>;
-  using I1 = std::integral_constant<int, 1>;
-  using I2 = std::integral_constant<int, 2>;
-  if (wave_active) {
-    if constexpr (V3) {
-      for (int t = t_first; t <= t_last; t += 6) {
-        step(t, sA, sB, I0{}, I0{});
-        if (t + 1 > t_last) break;
-        step(t + 1, sB, sA, I1{}, I1{});
-        if (t + 2 > t_last) break;
-        step(t + 2, sA, sB, I0{}, I2{});
-        if (t + 3 > t_last) break;
-        step(t + 3, sB, sA, I1{}, I0{});
-        if (t + 4 > t_last) break;
-        step(t + 4, sA, sB, I0{}, I1{});
-        if (t + 5 > t_last) break;
-        step(t + 5, sB, sA, I1{}, I2{});
-      }
-    } else {
-      for (int t = t_first; t <= t_last; t += 2) {
-        step(t, sA, sB, I0{}, I0{});
-        if (t + 1 <= t_last) step(t + 1, sB, sA, I1{}, I0{});
-      }
-    }
-  } else if constexpr (Q4) {  // no rows: this wave only loads (4-bit tiles)
-    if (q4_pipe) {
-      // one step ahead: set a holds K(t+2), V(t+1) when an even step starts
-      // (issued in the prologue or the last step), set b when an odd one does
-      Q4Data q4b_k[QB], q4b_v[QB];
-      // (the scheduling barriers keep each set's loads after the stores of
-      // the other, so that the stores never wait for loads just issued)
-      for (int t = t_first; t <= t_last; t += 2) {
-        q4_put(q4a_k, q4a_v, kbuf0, vbuf0 + TILE);
-        __builtin_amdgcn_sched_barrier(0);
-        q4_issue(q4b_k, q4b_v, min(t + 3, t_last), min(t + 2, t_last));
-        __syncthreads();
-        if (t + 1 > t_last) break;
-        q4_put(q4b_k, q4b_v, kbuf0 + TILE, vbuf0);
-        __builtin_amdgcn_sched_barrier(0);
-        q4_issue(q4a_k, q4a_v, min(t + 4, t_last), min(t + 3, t_last));
-        __syncthreads();
-      }
-    } else {  // every wave loads, one step ahead, as the row-holding waves do
-      for (int t = t_first; t <= t_last; t += 2) {
-        q4_issue(q4s_k[1], q4s_v[1], min(t + 3, t_last), min(t + 2, t_last));
-        q4_put(q4s_k[0], q4s_v[0], kbuf0, vbuf0 + TILE);
-        __syncthreads();
-        if (t + 1 > t_last) break;
-        q4_issue(q4s_k[0], q4s_v[0], min(t + 4, t_last), min(t + 3, t_last));
-        q4_put(q4s_k[1], q4s_v[1], kbuf0 + TILE, vbuf0);
+  // ---- persistent loop (PERS) ------------------------------------------
+  // Row blocks w, w + S, ... of this (batch, KV head) run one after another,
+  // each through the same prologue and step loop as a single block.  When a
+  // block's step loop ends, the next block's Q rows and first two K/V tiles
+  // are loaded (every LDS buffer is free by then), and the finished block's
+  // output is stored while they are in flight; the next prologue waits for
+  // them.  Every wave runs every block: a wave whose rows lie past the end
+  // of a ragged last block computes on repeated rows and stores nothing.
+  if constexpr (PERS) {
+    static_assert(V3 && !RING && !BIAS && !Q4 && !PAIR, "the persistent loop takes the three-V-buffer pipeline");
+    const int S = p.pers_stride;
+    const int nblk = __builtin_amdgcn_readfirstlane((p.mblocks - mbr + S - 1) / S);
+    // Q rows of block mbx: rows past a ragged block repeat its last row
+    // (they are never stored, and a row's arithmetic never depends on the
+    // other rows), so that the loads take no branches
+    auto load_q_pers = [&](int mbx) {
+      const int r0 = mbx * BM, re = min(p.rows, r0 + BM);
+      const int m = min(r0 + rb * kRowsPerWave + lr, re - 1);
+      const uint16_t* qrow = p.q + ((size_t)(b * p.Hq + hkv * p.G + m % p.G) * p.qL + m / p.G) * DK + qd0;
+#pragma unroll
+      for (int dc = 0; dc < DC; ++dc) qf[dc] = *(const uint4*)(qrow + dc * 16 + lg * 8);
+    };
+    auto set_block = [&](int mbx) {  // rows, visible keys and tiles of block mbx
+      set_rows(mbx);
+      set_keys();
+      int kb0, ke0;
+      block_keys(mbx, kb0, ke0);
+      t_first = __builtin_amdgcn_readfirstlane(kb0 / BN);
+      t_last = __builtin_amdgcn_readfirstlane((ke0 - 1) / BN);
+    };
+    {  // V rows past kL in any block's last tile: zeros before the first load
+      int kb0, ke0;
+      block_keys(mbr + (nblk - 1) * S, kb0, ke0);
+      if (ke0 > kb0 && ((ke0 - 1) / BN + 1) * BN > p.kL) {
+        uint4* vz = (uint4*)vbuf0;
+        for (int i = tid; i < NVB * TILE / 8; i += NW * 64) vz[i] = make_uint4(0, 0, 0, 0);
         __syncthreads();
       }
     }
-  } else {  // no rows: this wave only loads its share of every tile and
-            // meets the same barriers
-    for (int t = t_first; t <= t_last; ++t) {
-      if (t + 2 <= t_last) {
-        load_k(t + 2);
-        load_b(t + 2);
-        if constexpr (V3) load_v(t + 2);
-      }
-      if constexpr (!VLATE)
-        if (t < t_last) load_v(t + 1);
-      exchange(sA, false);
-      if constexpr (PAIR)
-        if (t < t_last) load_v(t + 1);
-      __builtin_amdgcn_s_waitcnt(0);
-      if (t + 2 <= t_last) bias_patch(t + 2, bbuf0 + ((t + 2 - t_first) & 1) * BTILE);
+    for (int j = 0;;) {
+      run_block(j > 0);
+      // every wave's loads have landed (each waited for its own) before any
+      // wave writes LDS below: the last steps re-load their last tile, into
+      // buffers that include the one the output goes through
       __syncthreads();
+      const float lsum = pair_sum(l_run);
+      const bool wave_o = wave_active;
+      const int wrow0_o = wrow0, rows_end_o = rows_end;
+      const bool more = ++j < nblk;
+      if (more) {  // the next block's Q rows and K(t0), V(t0), K(t0 + 1)
+        set_block(mbr + j * S);
+        load_q_pers(mbr + j * S);
+        load_k(t_first);
+        load_v(t_first);
+        if (t_first < t_last) load_k(t_first + 1);
+      }
+      // The finished block's output, normalised and rounded, goes through
+      // this wave's 32 rows x 144 bytes of the third V buffer (no load
+      // targets it until the next block's first step), 64 columns at a
+      // time, so that each lane then stores 16 contiguous bytes and each
+      // store instruction writes eight whole 128-byte lines instead of 16
+      // bytes in each of 32 rows.  A wave's LDS operations run in
+      // order, so its reads see its writes and the next chunk's writes
+      // follow this chunk's reads.
+      if (wave_o) {
+        const float inv = lsum > 0.f ? 1.0f / lsum : 0.f;  // a row with no finite score: zeros
+        constexpr int TS = 72;                               // LDS row stride, 16-bit elements (144 bytes)
+        uint16_t* const tw = vbuf0 + 2 * TILE + wave * (32 * TS);
+        const int sr = lane >> 3, sc = 8 * (lane & 7);      // this lane's row (+ 8 s) and column (+ 64 c)
+        size_t orow[4];
+        bool okr[4];
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          const int m = wrow0_o + 8 * s + sr;
+          okr[s] = m < rows_end_o;
+          orow[s] = ((size_t)(b * p.Hq + hkv * p.G + (okr[s] ? m % p.G : 0)) * p.qL + (okr[s] ? m / p.G : 0)) * DV;
+        }
+#pragma unroll
+        for (int c = 0; c < DB / 2; ++c) {
+#pragma unroll
+          for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+              const int db = 2 * c + h2;
+              uint2 w;
+              w.x = Elem<DT>::pack2(o[db][4 * q4 + 0] * inv, o[db][4 * q4 + 1] * inv);
+              w.y = Elem<DT>::pack2(o[db][4 * q4 + 2] * inv, o[db][4 * q4 + 3] * inv);
+              *(uint2*)(tw + lr * TS + 32 * h2 + 8 * q4 + 4 * lg) = w;
+            }
+#pragma unroll
+          for (int s = 0; s < 4; ++s) {
+            const uint4 v = *(const uint4*)(tw + (8 * s + sr) * TS + sc);
+            if (okr[s]) *(uint4*)(p.out + orow[s] + 64 * c + sc) = v;
+          }
+        }
+      }
+      if (!more) break;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int jj = 0; jj < 16; ++jj) o[db][jj] = 0.f;
+      l_run = 0.f;
+      m_ref = -INFINITY;
     }
+    return;
   }
-  // no direct load may still be writing this workgroup's LDS when it ends
-  __builtin_amdgcn_s_waitcnt(0);
+  run_block(false);
 
   // ---- epilogue ---------------------------------------------------------
   const float lsum = pair_sum(l_run);

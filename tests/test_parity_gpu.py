@@ -149,6 +149,22 @@ def test_persistent_unit_window_returns_the_diagonal_value_rows_exactly():
     assert torch.equal(got.view(torch.int16), v.view(torch.int16))
 
 
+# Two query heads per KV head and window 1: a row block is 64 positions and
+# sees exactly one 64-key tile, so every step of the persistent loop is the
+# step before a block boundary (the next block's Q rows are loaded in each,
+# and in the prologue); window 1 returns each position's own value row.
+@pytest.mark.parametrize("q_offset", [0, 64, 1])
+def test_persistent_one_tile_blocks_return_the_diagonal_value_rows_exactly(q_offset):
+    qL = 1200
+    kL = qL + q_offset
+    q, k, v = W.random_qkv(1301 + q_offset, 1, 64, 32, qL, kL, 256, FP16)
+    assert _persistent(1, 64, 32, qL, 1, 256)
+    note(f"persistent window 1, G 2, q_offset {q_offset}")
+    got = run_gpu(q, k, v, causal=True, window=1, q_offset=q_offset)
+    want = v[:, :, q_offset:q_offset + qL].repeat_interleave(2, dim=1)
+    assert torch.equal(got.view(torch.int16), want.contiguous().view(torch.int16))
+
+
 @pytest.mark.parametrize("case", SMALL, ids=[f"B{c[0]}Hq{c[1]}Hkv{c[2]}q{c[3]}k{c[4]}D{c[5]}"
                                              f"{'bf16' if c[6] else 'f16'}c{int(c[7])}w{c[8]}"
                                              for c in SMALL])
