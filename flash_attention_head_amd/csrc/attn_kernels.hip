@@ -1294,10 +1294,10 @@ __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* ld
   // ---- persistent loop (PERS) ------------------------------------------
   // Row blocks w, w + S, ... of this (batch, KV head) run one after another,
   // each through the same prologue and step loop as a single block.  When a
-  // block's step loop ends, the next block's Q rows and first two K/V tiles
-  // are loaded (every LDS buffer is free by then), and the finished block's
-  // output is stored while they are in flight; the next prologue waits for
-  // them.  Every wave runs every block: a wave whose rows lie past the end
+  // block's step loop ends, the next block's Q rows and K(t0), V(t0),
+  // K(t0 + 1) are loaded (every LDS buffer is free by then), and the
+  // finished block's output is stored while they are in flight; the next
+  // prologue waits for them and loads V(t0 + 1).  Every wave runs every block: a wave whose rows lie past the end
   // of a ragged last block computes on repeated rows and stores nothing.
   if constexpr (PERS) {
     static_assert(V3 && !RING && !BIAS && !Q4 && !PAIR, "the persistent loop takes the three-V-buffer pipeline");
