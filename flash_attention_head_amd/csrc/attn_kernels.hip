@@ -151,6 +151,19 @@ __device__ __forceinline__ void load_lds16(i32x4_t rsrc, uint32_t voff, uint32_t
       "s"(rsrc), "s"(__builtin_amdgcn_readfirstlane(soff)), "s"(m0v));
 }
 
+// The same with M0 = m0base + m0off formed in the asm: the constant m0off
+// needs no register of its own between loads (the compiler re-creates a
+// constant instead of keeping it), and only one base per buffer stays live.
+__device__ __forceinline__ void load_lds16_off(i32x4_t rsrc, uint32_t voff, uint32_t soff, unsigned m0base,
+                                               unsigned m0off) {
+  asm volatile(
+      "s_add_u32 m0, %3, %4\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %0, %1, %2 offen lds" ::"v"(voff),
+      "s"(rsrc), "s"(__builtin_amdgcn_readfirstlane(soff)), "s"(m0base), "s"(m0off)
+      : "scc");
+}
+
 // The same for a block whose rows lie on both sides of the end of a ring of
 // cache rows: the lanes in exec_a read through ra, the lanes in exec_b
 // (the complement) through rb.  A lane outside the exec mask of a load
@@ -361,6 +374,19 @@ __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* ld
   if (kbeg >= kend) return;
   int t_first = __builtin_amdgcn_readfirstlane(kbeg / BN);  // (the persistent loop moves them)
   int t_last = __builtin_amdgcn_readfirstlane((kend - 1) / BN);
+  // The persistent loop numbers its steps across blocks: its block starts at
+  // step phase phase0 (mod 6), which sets the K (mod 2) and V (mod 3) buffer
+  // of each tile, and when the next block's first two tiles follow this
+  // block's last in the sequence (pf_steps), the last two steps load them
+  // (nxt_first: the next block's first tile).  0, false: a single block.
+  int phase0 = 0, nxt_first = 0;
+  bool pf_steps = false;
+  // the tile n places after tile t in this workgroup's sequence of loads
+  // (past the last tile without a next block: the last tile again)
+  auto ahead = [&](int t, int n) {
+    if constexpr (PERS) return t + n <= t_last ? t + n : pf_steps ? nxt_first + (t + n - t_last - 1) : t_last;
+    else return min(t + n, t_last);
+  };
 
   // K/V rows of a head are kv_cap apart; logical key j is physical row
   // (ring_start + j) % kv_cap.  Without a wrap the live keys are one run of
@@ -447,10 +473,14 @@ __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* ld
     vlane = kq * LD + (od0 ^ (32 * (kq & VSW))) + 16 * (g & 1) + 4 * (lane & 3);
   }
   // K(t) lives in K buffer (t - t_first) & 1, V(t) in V buffer (t - t_first)
-  // & 1: the steps come in pairs, so inside a step every buffer offset is a
-  // compile-time immediate of the LDS instructions
+  // & 1 (% 3 with three V buffers): the steps come in pairs (sixes), so
+  // inside a step every buffer offset is a compile-time immediate of the LDS
+  // instructions.  The persistent loop rotates them by its block's phase.
   uint16_t* const kbuf0 = lds;
   uint16_t* const vbuf0 = lds + 2 * TILE;
+  // the K and V buffers of the block's step slots x (mod 2) and y (mod 3)
+  auto kbuf_at = [&](int x) { return kbuf0 + ((x + phase0) & 1) * TILE; };
+  auto vbuf_at = [&](int y) { return vbuf0 + ((y + phase0) % NVB) * TILE; };
   float* const xch = (float*)(lds + 4 * TILE);  // pair score exchange (D = 512)
 
   // Direct loads of one K or V tile: LOADS blocks of 1 KiB of LDS (RPB key
@@ -518,7 +548,10 @@ __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* ld
     const uint32_t vo = is_v ? voff[n % VPAT] : koff[n % KPAT];
     uint16_t* dst = buf + (wave + NW * n) * 512;
     const uint32_t so = (uint32_t)(n * NW * RPB * row_bytes(is_v));
-    if constexpr (!RING) {
+    if constexpr (PERS) {  // its buffers rotate with the block's phase: one base each
+      load_lds16_off(src.a, vo, so, __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)(buf + wave * 512)),
+                     (unsigned)(NW * n * 1024));
+    } else if constexpr (!RING) {
       load_lds16(src.a, vo, so, dst);
     } else {
       // lanes of rows before the wrap: lanes [LPR i, LPR (i + 1)) hold row
@@ -540,7 +573,7 @@ __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* ld
     for (int n = 0; n < LOADS; ++n) load_blk(src, buf, n, is_v);
     m0_restore(m0);
   };
-  auto load_k = [&](int t) { load_tile(kg, t, kbuf0 + ((t - t_first) & 1) * TILE, false); };
+  auto load_k = [&](int t) { load_tile(kg, t, kbuf0 + ((t - t_first + phase0) & 1) * TILE, false); };
 
   // Additive mask array (BIAS).  A bias tile holds this workgroup's BM
   // packed rows x BN keys for one K/V tile, in LDS after K, V (and the pair
@@ -637,7 +670,7 @@ __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* ld
     else x = (float)__builtin_bit_cast(_Float16, (uint16_t)h);
     return x * inv_scale;
   };
-  auto load_v = [&](int t) { load_tile(vg, t, vbuf0 + ((t - t_first) % NVB) * TILE, true); };
+  auto load_v = [&](int t) { load_tile(vg, t, vbuf0 + ((t - t_first + phase0) % NVB) * TILE, true); };
 
   // ---- 4-bit K/V (Q4) ------------------------------------------------------
   // A 1 KiB LDS block of a tile gets, per lane, the 8 elements the direct
@@ -1075,9 +1108,11 @@ __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* ld
   };
 
   // ---- one row block: prologue and step loop ---------------------------
-  // `prefetched`: the block's Q rows and its first K/V tiles were loaded by
-  // the persistent loop below while the previous block's output was stored.
-  auto run_block = [&](bool prefetched) {
+  // pf (persistent loop): 0, nothing loaded yet; 1, the block's Q rows and
+  // K(t0), V(t0), K(t0 + 1) were loaded while the previous block's output
+  // was stored; 2, the Q rows so, and K and V of t0 and t0 + 1 by the
+  // previous block's last two steps.
+  auto run_block = [&](int pf) {
     // ---- prologue: K(t0), V(t0), K(t0 + 1); S(t0) and its row max ------------
     // Rows past kL are out of the loads' range.  When this workgroup's last
     // tile has such rows, the V buffers start as zeros, so that those rows of
@@ -1111,7 +1146,7 @@ __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* ld
         else q4_issue(q4s_k[0], q4s_v[0], min(t_first + 2, t_last), min(t_first + 1, t_last));
       }
     } else {
-      if (!prefetched) {
+      if (pf == 0) {
         load_k(t_first);
         load_b(t_first);
         load_v(t_first);
@@ -1129,11 +1164,11 @@ __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* ld
     // through S(t0) and step t0, whose closing wait (everything but that
     // step's own V loads) and barrier publish it
     if constexpr (V3)
-      if (t_first < t_last) load_v(t_first + 1);
+      if (pf != 2 && t_first < t_last) load_v(t_first + 1);
 
     f32x16_t sA[KB], sB[KB];
     float alpha_cur = 1.f;
-    if (wave_active) qk(sA, kbuf0);
+    if (wave_active) qk(sA, kbuf_at(0));
     exchange(sA, wave_active);
     if (wave_active) {
       if constexpr (BIAS) {
@@ -1173,12 +1208,12 @@ __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* ld
     auto step = [&](int t, f32x16_t (&sc)[KB], f32x16_t (&sn)[KB], auto parity, auto vbuf) {
       constexpr int P = decltype(parity)::value, VB = decltype(vbuf)::value;
       const bool has_next = t < t_last;
-      const int tk = min(t + 2, t_last), tv = min(t + (V3 ? 2 : 1), t_last);
+      const int tk = ahead(t, 2), tv = ahead(t, V3 ? 2 : 1);
       uint4 pb[KB * 2];
       // the first K operands of the S region, then the rescale for tile t (its
       // factor is known since the last step), so that the interleaved regions
       // are straight-line code
-      const uint16_t* const kl = kbuf0 + (1 - P) * TILE;
+      const uint16_t* const kl = kbuf_at(1 - P);
       uint4 a[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) a[i] = kread_at(kl, i, kx(i));
@@ -1191,22 +1226,22 @@ __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* ld
       }
       uint2 bw[KB * 4];
       const TileSrc vsrc = tile_src(vg, tv, true);
-      uint16_t* const vdst = vbuf0 + (V3 ? (VB + 2) % 3 : 1 - P) * TILE;
+      uint16_t* const vdst = vbuf_at(V3 ? (VB + 2) % 3 : 1 - P);
       // Q4 with every wave loading: issue this wave's blocks of K(t+3) and
       // V(t+2) now; K(t+2) and V(t+1), issued in the last step, are written to
       // LDS at the end of this one
       if constexpr (Q4) {
         if (!q4_pipe) q4_issue(q4s_k[1 - P], q4s_v[1 - P], min(t + 3, t_last), min(t + 2, t_last));
       }
-      const float psum = qk_weights(sn, kl, sc, pb, tile_src(kg, tk, false), kbuf0 + P * TILE,
+      const float psum = qk_weights(sn, kl, sc, pb, tile_src(kg, tk, false), kbuf_at(P),
                                     vsrc, vdst, BIAS ? bias_src(tk) : i32x4_t{}, bbuf0 + P * BTILE,
                                     bbuf0 + (1 - P) * BTILE, bw, a, kc);
       exchange(sn, true);  // D = 512: also the V(t) barrier
       l_run = l_run * alpha_cur + psum;
       if (!full_tile(t + 1)) mask(sn, t + 1);
-      alpha_cur = pv_max(pb, vbuf0 + (V3 ? VB : P) * TILE, sn, has_next, bw, vsrc, vdst);
+      alpha_cur = pv_max(pb, vbuf_at(V3 ? VB : P), sn, has_next, bw, vsrc, vdst);
       if constexpr (Q4) {
-        if (!q4_pipe) q4_put(q4s_k[P], q4s_v[P], kbuf0 + P * TILE, vdst);
+        if (!q4_pipe) q4_put(q4s_k[P], q4s_v[P], kbuf_at(P), vdst);
       }
       // VLATE: K(t+2) (and its bias) have landed, and with V3 V(t+1) too; the
       // V loads of this step may be in flight.  Otherwise everything has.
@@ -1272,7 +1307,12 @@ __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* ld
     } else {  // no rows: this wave only loads its share of every tile and
               // meets the same barriers
       for (int t = t_first; t <= t_last; ++t) {
-        if (t + 2 <= t_last) {
+        if constexpr (PERS) {  // the tiles two places on, also into the next block
+          if (t + 2 <= t_last || pf_steps) {
+            load_tile(kg, ahead(t, 2), kbuf0 + ((t + 2 - t_first + phase0) & 1) * TILE, false);
+            load_tile(vg, ahead(t, 2), vbuf0 + ((t + 2 - t_first + phase0) % NVB) * TILE, true);
+          }
+        } else if (t + 2 <= t_last) {
           load_k(t + 2);
           load_b(t + 2);
           if constexpr (V3) load_v(t + 2);
@@ -1330,35 +1370,50 @@ __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* ld
         __syncthreads();
       }
     }
-    for (int j = 0;;) {
-      run_block(j > 0);
+    for (int j = 0, pf = 0;;) {
+      const bool more = j + 1 < nblk;
+      int nf = 0, nl = 0;
+      if (more) {
+        int kb0, ke0;
+        block_keys(mbr + (j + 1) * S, kb0, ke0);
+        nf = __builtin_amdgcn_readfirstlane(kb0 / BN);
+        nl = __builtin_amdgcn_readfirstlane((ke0 - 1) / BN);
+      }
+      // this block's last two steps load the next block's first two tiles
+      // when both blocks have two or more
+      pf_steps = more && t_last > t_first && nl > nf;
+      nxt_first = nf;
+      run_block(pf);
       // every wave's loads have landed (each waited for its own) before any
-      // wave writes LDS below: the last steps re-load their last tile, into
-      // buffers that include the one the output goes through
+      // wave writes LDS below: the last steps load into the buffers
       __syncthreads();
       const float lsum = pair_sum(l_run);
       const bool wave_o = wave_active;
       const int wrow0_o = wrow0, rows_end_o = rows_end;
-      const bool more = ++j < nblk;
-      if (more) {  // the next block's Q rows and K(t0), V(t0), K(t0 + 1)
-        set_block(mbr + j * S);
-        load_q_pers(mbr + j * S);
-        load_k(t_first);
-        load_v(t_first);
-        if (t_first < t_last) load_k(t_first + 1);
+      if (more) {  // the next block: its rows and tiles, its phase, its Q rows (and K(t0), V(t0), K(t0 + 1))
+        const int ntiles = t_last - t_first + 1;
+        set_block(mbr + (j + 1) * S);
+        phase0 = (phase0 + ntiles) % 6;
+        load_q_pers(mbr + (j + 1) * S);
+        if (!pf_steps) {
+          load_k(t_first);
+          load_v(t_first);
+          if (t_first < t_last) load_k(t_first + 1);
+        }
       }
+      pf = pf_steps ? 2 : 1;
       // The finished block's output, normalised and rounded, goes through
-      // this wave's 32 rows x 144 bytes of the third V buffer (no load
-      // targets it until the next block's first step), 64 columns at a
-      // time, so that each lane then stores 16 contiguous bytes and each
-      // store instruction writes eight whole 128-byte lines instead of 16
-      // bytes in each of 32 rows.  A wave's LDS operations run in
-      // order, so its reads see its writes and the next chunk's writes
-      // follow this chunk's reads.
+      // this wave's 32 rows x 144 bytes of the V buffer that holds neither
+      // V(t0) nor V(t0 + 1) of the next block (no load targets it until the
+      // next block's first step), 64 columns at a time, so that each lane
+      // then stores 16 contiguous bytes and each store instruction writes
+      // eight whole 128-byte lines instead of 16 bytes in each of 32 rows.
+      // A wave's LDS operations run in order, so its reads see its writes
+      // and the next chunk's writes follow this chunk's reads.
       if (wave_o) {
         const float inv = lsum > 0.f ? 1.0f / lsum : 0.f;  // a row with no finite score: zeros
         constexpr int TS = 72;                               // LDS row stride, 16-bit elements (144 bytes)
-        uint16_t* const tw = vbuf0 + 2 * TILE + wave * (32 * TS);
+        uint16_t* const tw = vbuf0 + ((phase0 + 2) % NVB) * TILE + wave * (32 * TS);
         const int sr = lane >> 3, sc = 8 * (lane & 7);      // this lane's row (+ 8 s) and column (+ 64 c)
         size_t orow[4];
         bool okr[4];
@@ -1380,13 +1435,19 @@ __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* ld
               w.y = Elem<DT>::pack2(o[db][4 * q4 + 2] * inv, o[db][4 * q4 + 3] * inv);
               *(uint2*)(tw + lr * TS + 32 * h2 + 8 * q4 + 4 * lg) = w;
             }
+          // the four reads first, all waited for at once (left alone, the
+          // compiler moves each into its row's conditional store and waits
+          // for the LDS once per store)
+          i32x4_t v[4];
 #pragma unroll
-          for (int s = 0; s < 4; ++s) {
-            const uint4 v = *(const uint4*)(tw + (8 * s + sr) * TS + sc);
-            if (okr[s]) *(uint4*)(p.out + orow[s] + 64 * c + sc) = v;
-          }
+          for (int s = 0; s < 4; ++s) v[s] = *(const i32x4_t*)(tw + (8 * s + sr) * TS + sc);
+          asm volatile("" ::"v"(v[0]), "v"(v[1]), "v"(v[2]), "v"(v[3]));
+#pragma unroll
+          for (int s = 0; s < 4; ++s)
+            if (okr[s]) *(i32x4_t*)(p.out + orow[s] + 64 * c + sc) = v[s];
         }
       }
+      ++j;
       if (!more) break;
 #pragma unroll
       for (int db = 0; db < DB; ++db)
@@ -1397,7 +1458,7 @@ __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* ld
     }
     return;
   }
-  run_block(false);
+  run_block(0);
 
   // ---- epilogue ---------------------------------------------------------
   const float lsum = pair_sum(l_run);
