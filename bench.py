@@ -10,9 +10,9 @@ JSON line.
 Measurement protocol (after the null-arm method of lablup/mlxcel issue #2160,
 Acceptance Criteria): every workload ("arm") is drawn and uploaded once; then
 after one untimed round over every arm, the arms are timed in turn, round
-after round (at least 3 rounds), each time
-with HIP events around each of `steps` calls on the stream the library runs
-on.  The headline is timed twice per round (its second arm is the null arm:
+after round (at least 3 rounds, every other one in the reverse order), each
+time with HIP events around each of `steps` calls on the stream the library
+runs on.  The headline is timed twice per round (its second arm is the null arm:
 the same call, so its spread is run-to-run noise).  Reported per arm: the
 median and the minimum over all timed calls, and each round's median.  A few
 paired comparisons (4-bit against 16-bit decode, the additive mask against
@@ -344,7 +344,9 @@ def main():
             arms[n].call()
     torch.cuda.synchronize()
     for r in range(rounds):
-        for n in names:
+        # every other round in the reverse order: an arm's place in a round
+        # moves its time (fixed-order A/B runs of one kernel read 1-3% apart)
+        for n in (names if r % 2 == 0 else names[::-1]):
             steps = args.steps if n.split("#")[0] == head else max(5, args.steps // 2)
             arms[n].time(steps, 1)
         log(f"[bench] round {r + 1}: " + ", ".join(f"{n} {statistics.median(arms[n].rounds[-1]):.4f}"
