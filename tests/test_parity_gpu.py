@@ -149,10 +149,11 @@ def test_persistent_unit_window_returns_the_diagonal_value_rows_exactly():
     assert torch.equal(got.view(torch.int16), v.view(torch.int16))
 
 
-# Two query heads per KV head and window 1: a row block is 64 positions and
-# sees exactly one 64-key tile, so every step of the persistent loop is the
-# step before a block boundary (the next block's Q rows are loaded in each,
-# and in the prologue); window 1 returns each position's own value row.
+# Two query heads per KV head and window 1: a row block is 64 positions.
+# With the query offset a multiple of 64 it sees exactly one 64-key tile, so
+# the last steps of a block cannot load the next block's first two tiles and
+# the block end loads them; with offset 1 each block sees two tiles and the
+# last two steps load them.  Window 1 returns each position's own value row.
 @pytest.mark.parametrize("q_offset", [0, 64, 1])
 def test_persistent_one_tile_blocks_return_the_diagonal_value_rows_exactly(q_offset):
     qL = 1200
