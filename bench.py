@@ -302,7 +302,7 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print(f"bench.py: this build measures one GPU only (got --gpus {args.gpus}); the "
+        print(f"bench.py: measures one GPU only (got --gpus {args.gpus}); the "
               "attention path has no multi-GPU mode", file=sys.stderr)
         sys.exit(2)
 
@@ -371,7 +371,7 @@ def main():
                 m = statistics.median(rr)
                 comparisons.append({"arm": a, "against": b, "median_ratio_minus_1": round(m, 4),
                                     "round_ratios": [round(x, 4) for x in rr],
-                                    "verdict": "resolved" if abs(m) > spread else "unresolved"})
+                                    "status": "resolved" if abs(m) > spread else "unresolved"})
         log(f"[bench] null arm {null_arm}; comparisons {comparisons}")
 
     read_ref = None
