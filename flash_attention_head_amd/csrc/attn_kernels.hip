@@ -164,6 +164,28 @@ __device__ __forceinline__ void load_lds16_off(i32x4_t rsrc, uint32_t voff, uint
       : "scc");
 }
 
+// Loads of four consecutive 1 KiB blocks share one M0 value: the load's
+// immediate offset moves its LDS destination (M0 + offset + 16 lane) and
+// its source (base + soff + voff + offset) together, and the range check
+// covers voff + soff + offset.  Load k of a group (k = 0..3) takes offset
+// 1024 k; load 0 writes M0 (m0base + m0off) first.  Nothing between the
+// loads of a group may write M0.
+template <int K>
+__device__ __forceinline__ void load_lds16_grp(i32x4_t rsrc, uint32_t voff, uint32_t soff, unsigned m0base,
+                                               unsigned m0off) {
+  if constexpr (K == 0) {
+    asm volatile(
+        "s_add_u32 m0, %3, %4\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %0, %1, %2 offen lds" ::"v"(voff),
+        "s"(rsrc), "s"(__builtin_amdgcn_readfirstlane(soff)), "s"(m0base), "s"(m0off)
+        : "scc");
+  } else {
+    asm volatile("buffer_load_dwordx4 %0, %1, %2 offen offset:%3 lds" ::"v"(voff), "s"(rsrc),
+                 "s"(__builtin_amdgcn_readfirstlane(soff)), "i"(1024 * K));
+  }
+}
+
 // The same for a block whose rows lie on both sides of the end of a ring of
 // cache rows: the lanes in exec_a read through ra, the lanes in exec_b
 // (the complement) through rb.  A lane outside the exec mask of a load
@@ -282,6 +304,12 @@ __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* ld
   static_assert(!Q4 || (DK == 256 && DV == 256 && !RING && !BIAS), "4-bit K/V: head dim 256 only");
   constexpr bool VLATE = PAIR || V3;
   constexpr int NVB = V3 ? 3 : 2;
+  // GRP (D = 512 without a ring or bias): each wave loads contiguous 1 KiB
+  // blocks of a tile, four to an M0 value (load_lds16_grp).  The K and the V
+  // loads of a step each run in a region of their own, and a block is one
+  // key row both in LDS and in memory.  (At D = 256 the same grouping gave
+  // the same times.)
+  constexpr bool GRP = PAIR && !RING && !BIAS;
   static_assert(PAIR == (DV == 512), "head dim 512 only with DK == DV");
   constexpr int NW = 4, RBW = PAIR ? 2 : 4;  // 32-row blocks per workgroup
   constexpr int BM = RBW * kRowsPerWave, BN = tile_keys(DK), KB = BN / 32;
@@ -495,18 +523,23 @@ __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* ld
   // before key kL form the buffer descriptor, so rows past kL read zeros
   // (the range check covers the scalar offset too).
   constexpr int RPB = 1024 / (2 * LD);  // key rows per 1 KiB block
-  constexpr int KPAT = 16 / (NW * RPB) > 1 ? 16 / (NW * RPB) : 1;
-  constexpr int VPAT = (VSW + 1) / (NW * RPB) > 1 ? (VSW + 1) / (NW * RPB) : 1;
+  // the n-th load of this wave fills block blk(n): wave + NW n, or with GRP
+  // LOADS wave + n; its lane offsets repeat every KPAT (K) or VPAT (V) loads
+  constexpr int KPAT = GRP ? (16 / RPB < LOADS ? 16 / RPB : LOADS) : 16 / (NW * RPB) > 1 ? 16 / (NW * RPB) : 1;
+  constexpr int VPAT = GRP ? ((VSW + 1) / RPB < LOADS ? (VSW + 1) / RPB : LOADS)
+                           : (VSW + 1) / (NW * RPB) > 1 ? (VSW + 1) / (NW * RPB) : 1;
+  auto blk = [&](int n) { return GRP ? LOADS * wave + n : wave + NW * n; };
   static_assert(RPB * ROWCH == 64 && LOADS % KPAT == 0 && LOADS % VPAT == 0, "block geometry");
   // above any tile's bytes, and far enough below 2^32 that adding a scalar
   // offset cannot wrap it
   constexpr uint32_t kPastRange = 0x40000000u;
   auto row_bytes = [](bool is_v) { return 2 * (is_v ? DV : DK); };
   auto lane_off = [&](bool is_v, int n) {  // offset of the n-th load from its block group
-    const int r = (wave + NW * n) * RPB + lane / ROWCH;  // key row in the tile
+    const int r = blk(n) * RPB + lane / ROWCH;  // key row in the tile
     const int pch = lane % ROWCH;
     const int c = is_v ? (pch ^ ((r & VSW) << 2)) : (pch ^ (r & 15));
-    return 16 * c < row_bytes(is_v) ? (uint32_t)((r - n * NW * RPB) * row_bytes(is_v) + 16 * c) : kPastRange;
+    const int rn = GRP ? n * RPB : n * NW * RPB;  // rows the scalar and immediate offsets hold
+    return 16 * c < row_bytes(is_v) ? (uint32_t)((r - rn) * row_bytes(is_v) + 16 * c) : kPastRange;
   };
   uint32_t koff[KPAT], voff[VPAT];
 #pragma unroll
@@ -546,7 +579,21 @@ __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* ld
   auto load_blk = [&](const TileSrc& src, uint16_t* buf, int n, bool is_v) {
     if constexpr (Q4) return;  // 4-bit tiles come through registers (below)
     const uint32_t vo = is_v ? voff[n % VPAT] : koff[n % KPAT];
-    uint16_t* dst = buf + (wave + NW * n) * 512;
+    uint16_t* dst = buf + blk(n) * 512;
+    if constexpr (GRP) {
+      // group n / 4 of this wave's blocks: scalar offset and M0 at its first
+      // block, load n % 4 of the group through the immediate offset
+      const uint32_t so = (uint32_t)((n & ~3) * 1024);
+      const unsigned mb = __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)(buf + LOADS * wave * 512));
+      const unsigned mo = (unsigned)((n & ~3) * 1024);
+      switch (n & 3) {
+        case 0: load_lds16_grp<0>(src.a, vo, so, mb, mo); break;
+        case 1: load_lds16_grp<1>(src.a, vo, so, mb, mo); break;
+        case 2: load_lds16_grp<2>(src.a, vo, so, mb, mo); break;
+        default: load_lds16_grp<3>(src.a, vo, so, mb, mo); break;
+      }
+      return;
+    }
     const uint32_t so = (uint32_t)(n * NW * RPB * row_bytes(is_v));
     if constexpr (PERS) {  // its buffers rotate with the block's phase: one base each
       load_lds16_off(src.a, vo, so, __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)(buf + wave * 512)),
@@ -557,7 +604,7 @@ __device__ __forceinline__ void attn_pipe_body(const AttnParams& p, uint16_t* ld
       // lanes of rows before the wrap: lanes [LPR i, LPR (i + 1)) hold row
       // i of the block's RPB rows
       constexpr int LPR = 64 / RPB;
-      const int rb0 = (wave + NW * n) * RPB;
+      const int rb0 = blk(n) * RPB;
       uint64_t ea = 0;
 #pragma unroll
       for (int i = 0; i < RPB; ++i)
